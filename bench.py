@@ -1,0 +1,315 @@
+"""Benchmark of the W4A8 per-group GEMM path on one MI355X.
+
+Default workload: the Llama-3-8B fused QKV projection (K=4096, N=6144, group 128)
+at decode batches M = 1, 16 and 64.  One step = for each M, the per-token INT8
+activation quantizer followed by the W4A8 GEMM with its fp16 epilogue, on inputs
+already resident in HBM; the weights are packed once, offline, before timing (the
+method quantizes and reorders weights offline).  Weight buffers are rotated over
+copies totalling >= 1 GiB so that the 256 MB MALL and the L2 do not serve them.
+
+Prints ONE JSON line (rank 0) with the throughput, the roofline fraction of the
+dominant kernel (timed with HIP events on the stream the kernels run on) and the
+CPU oracle timed on the host cores.
+
+--sweep runs every layer shape / batch size of the workload registry and writes a
+table to gpurun_out/sweep.json (not the headline line).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 GEMM TOPS and weight GB/s vs MI355X roofline, M=1..4096"
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layer", default="llama3_8b_qkv")
+    ap.add_argument("--ms", default="")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-launches", type=int, default=200)
+    return ap.parse_args()
+
+
+class Case:
+    """Resident, rotated buffers for one (layer, M)."""
+
+    def __init__(self, L, M, dev, packed_sets):
+        import torch
+        from w4a8_mixed_precision_amd import workloads as wl
+        self.L, self.M = L, M
+        self.sets = packed_sets
+        x16 = wl.activations_fp16(L, M)
+        self.x = torch.from_numpy(x16).to(dev)
+        self.qx = torch.empty((M, L.K), dtype=torch.int8, device=dev)
+        self.sx = torch.empty(M, dtype=torch.float16, device=dev)
+        self.out = torch.empty((M, L.N), dtype=torch.float16, device=dev)
+        self.ops = wl.algorithmic_ops(M, L.N, L.K)
+        self.bytes = wl.algorithmic_bytes(M, L.N, L.K)
+        self.i = 0
+
+    def step(self, q):
+        p, m, s = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        q.quantize_activations(self.x, out=(self.qx, self.sx))
+        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out)
+
+    def gemm_only(self, q):
+        p, m, s = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out)
+
+    def quant_only(self, q):
+        q.quantize_activations(self.x, out=(self.qx, self.sx))
+
+
+def packed_sets_for(L, dev, q, max_sets=128):
+    """Pack the layer's weights once, then clone the packed buffers until the
+    rotation covers ROTATE_BYTES (at least 2 sets)."""
+    import torch
+    from w4a8_mixed_precision_amd import workloads as wl
+    w = torch.from_numpy(wl.weights_fp16(L)).to(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    p, m, s = q.quantize_pack_weights(w)
+    torch.cuda.synchronize()
+    pack_s = time.perf_counter() - t0
+    del w
+    wbytes = p.numel() + m.numel() * 2 + s.numel() * 2
+    n = max(2, min(max_sets, -(-ROTATE_BYTES // wbytes)))
+    sets = [(p, m, s)] + [(p.clone(), m.clone(), s.clone()) for _ in range(n - 1)]
+    torch.cuda.synchronize()
+    return sets, pack_s
+
+
+def capture(fn, n, torch):
+    """HIP graph of n back-to-back calls of fn.  The library launches on torch's
+    current stream, which is the capture stream inside torch.cuda.graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, torch):
+    """Seconds per replay of graph g, from HIP events recorded on the current stream
+    (graph replays run on it)."""
+    st = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def time_launches(fn, n, torch, reps=3):
+    """Average duration per launch of fn: n launches captured in one HIP graph
+    (host launch overhead removed), replayed reps times, timed with HIP events."""
+    g = capture(fn, n, torch)
+    return time_graph(g, reps, torch) / n
+
+
+def cpu_baseline(L, Ms, seconds):
+    """The CPU oracle (unchanged) over the same step: activation quantization,
+    dequantization of the stored codes, exact contraction, fp32 epilogue."""
+    import numpy as np
+    from oracle import qoq_oracle as o
+    from w4a8_mixed_precision_amd import workloads as wl
+    w16 = wl.weights_fp16(L)
+    q0, s_w = o.quantize_weights_level0(w16)
+    q_u4, z, s_u8 = o.quantize_weights_level1(q0)
+    xs = {M: wl.activations_fp16(L, M) for M in Ms}
+    ops = sum(wl.algorithmic_ops(M, L.N, L.K) for M in Ms)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for M in Ms:
+            qx, s_x = o.quantize_activations(xs[M])
+            w_hat = o.dequantize_level1(q_u4, z, s_u8)
+            acc = o.contract(qx, w_hat)
+            o.epilogue(acc, s_x, s_w)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_step = el / steps
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    return {
+        "value": ops / per_step / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"{steps} full step(s) of {L.name} M={list(Ms)} (activation quant + dequant + exact "
+                  f"fp64 contraction + epilogue), {el:.1f} s, host cpu_count={os.cpu_count()}",
+        "s_per_step": per_step,
+    }
+
+
+def run_case_metrics(c, q, torch, launches):
+    g = time_launches(lambda: c.gemm_only(q), launches, torch)
+    a = time_launches(lambda: c.quant_only(q), launches, torch)
+    b = c.bytes
+    return {
+        "M": c.M, "K": c.L.K, "N": c.L.N, "plan": q.gemm_plan(c.M, c.L.N, c.L.K),
+        "gemm_us": g * 1e6, "quant_us": a * 1e6,
+        "TOPS": c.ops / g / 1e12,
+        "weight_GBps": b["weight"] / g / 1e9,
+        "total_GBps": b["total"] / g / 1e9,
+        "hbm_frac": b["total"] / g / 1e9 / HBM_PEAK_GBPS,
+        "mfma_frac": c.ops / g / 1e12 / INT8_PEAK_TOPS,
+        "roofline_frac": max(b["total"] / (HBM_PEAK_GBPS * 1e9), c.ops / (INT8_PEAK_TOPS * 1e12)) / g,
+        "quant_GBps": (3 * c.M * c.L.K + 2 * c.M) / a / 1e9,
+        "rotation_sets": len(c.sets),
+    }
+
+
+def copy_ceiling(q, torch, dev, nbytes=1 << 30, reps=10):
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    q.stream_copy(src, dst)
+    t = time_launches(lambda: q.stream_copy(src, dst), reps, torch, reps=1)
+    del src, dst
+    return {"bytes_per_launch": 2 * nbytes, "us": t * 1e6, "GBps": 2 * nbytes / t / 1e9}
+
+
+def sweep(q, torch, dev, launches):
+    from w4a8_mixed_precision_amd import workloads as wl
+    rows = []
+    for L in wl.LAYERS:
+        sets, pack_s = packed_sets_for(L, dev, q)
+        for M in L.Ms:
+            c = Case(L, M, dev, sets)
+            for _ in range(3):
+                c.step(q)
+            torch.cuda.synchronize()
+            r = run_case_metrics(c, q, torch, launches)
+            r.update({"layer": L.name, "pack_ms": pack_s * 1e3})
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+            del c
+        del sets
+        torch.cuda.empty_cache()
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", "sweep.json"), "w") as f:
+        json.dump(rows, f, indent=1)
+    return rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding is "
+              f"described in DESIGN.md and is not measured here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from w4a8_mixed_precision_amd import qoq
+    from w4a8_mixed_precision_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    qoq.lib()
+
+    if args.sweep:
+        sweep(qoq, torch, dev, args.kernel_launches)
+        return
+
+    L = wl.find(args.layer)
+    Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else L.Ms
+    sets, pack_s = packed_sets_for(L, dev, qoq)
+    cases = [Case(L, M, dev, sets) for M in Ms]
+
+    def step():
+        for c in cases:
+            c.step(qoq)
+
+    # warmup steps run eagerly; the K timed steps are one HIP graph of exactly K steps
+    # (each step rotates to the next packed-weight copy), replayed once between a
+    # synchronize on both sides and timed with HIP events on the replay stream.
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    g_steps = capture(step, args.steps, torch)
+    g_steps.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_host0 = time.perf_counter()
+    e0.record(st)
+    g_steps.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    per_case = [run_case_metrics(c, qoq, torch, args.kernel_launches) for c in cases]
+    ops = sum(c.ops for c in cases)
+    wbytes = sum(c.bytes["weight"] for c in cases)
+    # dominant kernel: the GEMM launch with the largest time in the step
+    dom = max(per_case, key=lambda r: r["gemm_us"])
+    dom_case = cases[per_case.index(dom)]
+    achieved = dom_case.bytes["total"] / (dom["gemm_us"] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": ops / step_s / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{L.name}: W4A8 g128 GEMM K={L.K} N={L.N}, M in {list(Ms)}, "
+                               f"per-token INT8 activation quant + GEMM + fp16 epilogue per M",
+                   "K": L.K, "N": L.N, "M": list(Ms), "group": 128},
+        "weight_GBps_step": wbytes / step_s / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": dom["plan"], "M": dom["M"],
+                     "bytes_per_launch": dom_case.bytes["total"], "launch_us": dom["gemm_us"]},
+        "cases": per_case,
+        "offline_pack_ms": pack_s * 1e3,
+        "copy_ceiling": copy_ceiling(qoq, torch, dev),
+        "host_wall_s": t_host,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(L, Ms, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * qoq.h — C ABI of the QoQ W4A8 per-group GEMM library for MI355X (gfx950).
+ *
+ * The method (QServe / QoQ, "QServe: W4A8KV4 Quantization and System Co-design for
+ * Efficient LLM Serving", sections "渐进式组量化" progressive group quantization,
+ * "保护性量化范围" protective quantization range and "逐组W4A8 GEMM中的快速反量化"
+ * per-group fast dequantization):
+ *   weights    W [N,K] fp16  -> level 0: per-output-channel symmetric INT8 codes in
+ *                               the protective range [-119, 119], fp16 scale s_W[n]
+ *                            -> level 1: per group of 128 consecutive k, asymmetric
+ *                               UINT4 codes with a UINT4 zero z and a UINT8 scale s_u8
+ *   activations X [M,K] fp16 -> per-token symmetric INT8 codes qx, fp16 scale s_X[m]
+ *   GEMM       acc[m,n] = sum_k qx[m,k] * (q_u4[n,k] - z[n,k/128]) * s_u8[n,k/128]
+ *              (exact INT32; the dequantized weight always fits INT8)
+ *              out[m,n] = fp16( float(acc) * (float(s_X[m]) * float(s_W[n])) )
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or retains them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     compute call validates its arguments on the host, then enqueues its kernels on
+ *     `stream` and returns without synchronising.
+ *   - Return value: QOQ_OK (0) or a negative qoq_status.  On any error nothing is
+ *     launched and no output is touched.  No C++ exception crosses this interface.
+ *   - The library holds no mutable global state; calls are thread-safe.  Calls on
+ *     different streams that write the same output race, as any GPU work does.
+ *   - Only group == 128 is supported (QOQ_ERR_UNSUPPORTED otherwise).
+ *   - Shapes: N % 16 == 0, K % 128 == 0, 0 < K <= 139648 (keeps every INT32
+ *     accumulator exact: 127 * 121 * K < 2^31), M >= 0 (M == 0 is a no-op).
+ *   - Inputs must be finite; behaviour for inf/NaN inputs is unspecified.
+ *
+ * Storage layout of the packed weights (this library's own order; the pages fix only
+ * that weights, zeros and scales are stored offline in the order the kernel consumes
+ * them so that each lane issues one 128-bit load — "QServe：把 W4A8KV4 ..." review,
+ * §3.2 compute-aware weight reordering):
+ *   strip b = n / 16, c = n % 16, group j = k / 128, G = K / 128,
+ *   k = 128 j + 64 half + 16 h + i   (half in {0,1}, h in 0..3, i in 0..15)
+ *   packed_w[((b*G + j)*64 + 16*h + c)*16 + i]
+ *       = q_u4[n, 128j + 16h + i] | q_u4[n, 128j + 64 + 16h + i] << 4      (uint8)
+ *   group_meta[(b*G + j)*16 + c] = s_u8[n, j] | z[n, j] << 8               (uint16)
+ *   s_w: fp16 [N], natural order.
+ */
+#ifndef QOQ_H
+#define QOQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QOQ_OK = 0,
+  QOQ_ERR_INVALID = -1,      /* null pointer, negative or non-multiple shape */
+  QOQ_ERR_UNSUPPORTED = -2,  /* group != 128, K beyond the exact-INT32 limit */
+  QOQ_ERR_ALIGNMENT = -3,    /* pointer not aligned as the call requires */
+  QOQ_ERR_WORKSPACE = -4,    /* workspace smaller than qoq_gemm_workspace_bytes */
+  QOQ_ERR_HIP = -5           /* the HIP runtime reported an error at launch */
+} qoq_status;
+
+/* Library ABI version (increments when a signature or the storage layout changes). */
+int qoq_version(void);
+
+/* Human-readable text of a qoq_status value; never NULL, static storage. */
+const char *qoq_status_string(int status);
+
+/* Sizes in bytes of the three buffers qoq_quantize_pack_weights writes for W [N,K]:
+ * packed_w = N*K/2, group_meta = 2*N*K/128, s_w = 2*N.  Any output pointer may be
+ * NULL.  Errors: INVALID for bad N/K, UNSUPPORTED for group != 128. */
+int qoq_weight_buffer_sizes(int64_t N, int64_t K, int32_t group, size_t *packed_w_bytes,
+                            size_t *group_meta_bytes, size_t *s_w_bytes);
+
+/* Offline weight quantization and packing ("QServe ..." summary, progressive group
+ * quantization and protective quantization range; review §3.1):
+ *   s_W[n] = fp16(max_k |W[n,k]| / 119)            (fp32 IEEE divide, then RNE to fp16)
+ *   q_s8   = clamp(rint(W / s_W), -119, 119)         (0 for a row whose s_W is 0)
+ *   per group: lo = min(0, min q_s8), hi = max(0, max q_s8),
+ *   s_u8 = max(1, ceil((hi - lo) / 15)), z = clamp(rne(-lo / s_u8), 0, 15),
+ *   q_u4 = clamp(z + rne(q_s8 / s_u8), 0, 15)        (rne = round half to even)
+ * w_fp16: [N,K] row-major fp16, 16-byte aligned.  packed_w: N*K/2 bytes, 16-byte
+ * aligned.  group_meta: N*K/128 uint16, 2-byte aligned.  s_w_fp16: N fp16.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, HIP. */
+int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t group,
+                              void *packed_w, void *group_meta, void *s_w_fp16, void *stream);
+
+/* Per-token symmetric INT8 activation quantization (the activation side of the
+ * epilogue scale s_W x s_X, "QServe ..." summary; symmetric quantizer of
+ * "01 inference papers and experiments" §4.1):
+ *   s_X[m] = fp16(max_k |X[m,k]| / 127), qx = clamp(rint(X / s_X), -127, 127)
+ *   (all-zero token: s_X = 0, qx = 0).
+ * x_fp16: [M,K] row-major fp16; qx_i8: [M,K] row-major int8; s_x_fp16: [M] fp16.
+ * K % 8 == 0 here (the GEMM itself needs K % 128 == 0); x and qx 16-byte aligned.
+ * Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_i8,
+                             void *s_x_fp16, void *stream);
+
+/* Workspace the GEMM entry points need for this problem (currently 0 for every
+ * shape: split-K partial sums are reduced on chip).  Errors: INVALID, UNSUPPORTED. */
+int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes);
+
+/* W4A8 per-group GEMM with the fp16 epilogue ("QServe ..." summary, per-group
+ * W4A8 GEMM fast dequantization and the epilogue O = (Q_X Q_W) ⊙ (s_W x s_X);
+ * review §4 step 3: INT4 -> INT8 by multiply-then-subtract in registers, INT8
+ * matrix-core products, INT32 accumulation, fp16 output):
+ *   out[m,n] = fp16( float(acc[m,n]) * (float(s_X[m]) * float(s_W[n])) )
+ * qx_i8 [M,K] int8 (16-byte aligned), s_x_fp16 [M], packed_w / group_meta / s_w_fp16
+ * as written by qoq_quantize_pack_weights for the same N, K; out_fp16 [M,N]
+ * row-major fp16 (4-byte aligned).  workspace may be NULL when
+ * qoq_gemm_workspace_bytes reports 0.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
+int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w,
+                  const void *group_meta, const void *s_w_fp16, void *out_fp16, int64_t M,
+                  int64_t N, int64_t K, int32_t group, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* Same main loop as qoq_w4a8_gemm with an INT32 epilogue: acc_i32 [M,N] row-major
+ * receives the exact integer accumulators (for bit-exact verification).
+ * Errors: as qoq_w4a8_gemm. */
+int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group_meta,
+                      int32_t *acc_i32, int64_t M, int64_t N, int64_t K, int32_t group,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Name of the kernel configuration qoq_w4a8_gemm launches for this shape (static
+ * string, "invalid" for a shape the GEMM rejects).  Used to match profiler output. */
+const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K);
+
+/* ---- diagnostics (verification and measurement; not on the GEMM path) ---- */
+
+/* Dequantize packed weights with the GEMM's own in-register routine:
+ * w_i8 [N,K] row-major int8 = (q_u4 - z) * s_u8.  Same buffer rules as the GEMM.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, HIP. */
+int qoq_dequantize_packed(const void *packed_w, const void *group_meta, int64_t N,
+                          int64_t K, int32_t group, void *w_i8, void *stream);
+
+/* Plain device-to-device copy kernel of `bytes` bytes (bytes % 16 == 0, both
+ * pointers 16-byte aligned): the streaming ceiling and the reference for hardware
+ * byte counters.  Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* One v_mfma_i32_16x16x64_i8 on a single wave: lane l supplies 16 A bytes at
+ * a_frag + 16*l and 16 B bytes at b_frag + 16*l and receives its 4 INT32 results at
+ * d_frag + 16*l.  Used to pin the operand and result lane layout.
+ * Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_mfma_probe(const void *a_frag, const void *b_frag, void *d_frag, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QOQ_H */

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qoq.h declares, and rejects bad arguments with the documented status
+before anything is launched (no call here reaches the HIP runtime)."""
+import ctypes
+
+import pytest
+
+from w4a8_mixed_precision_amd import qoq
+
+OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10001)        # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qoq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = qoq.header_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert qoq.version() >= 1
+    for s in (OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR):
+        assert qoq.status_string(s)
+    assert qoq.status_string(12345) == "unknown status"
+
+
+def test_weight_buffer_sizes():
+    s = qoq.weight_buffer_sizes(6144, 4096)
+    assert s == {"packed_w": 6144 * 4096 // 2, "group_meta": 6144 * 32 * 2, "s_w": 6144 * 2}
+    with pytest.raises(qoq.QoQError) as e:
+        qoq.weight_buffer_sizes(6144, 4096, group=64)
+    assert e.value.status == UNSUPPORTED
+    for N, K in [(0, 128), (17, 128), (16, 100), (16, -128)]:
+        with pytest.raises(qoq.QoQError) as e:
+            qoq.weight_buffer_sizes(N, K)
+        assert e.value.status == INVALID
+    with pytest.raises(qoq.QoQError) as e:
+        qoq.weight_buffer_sizes(16, 139648 + 128)
+    assert e.value.status == UNSUPPORTED
+
+
+def test_workspace_and_plan():
+    assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
+    assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
+    assert qoq.gemm_plan(4096, 28672, 4096).startswith("tiled")
+    assert qoq.gemm_plan(1, 17, 4096) == "invalid"
+    assert qoq.gemm_plan(0, 16, 128) == "invalid"
+
+
+def test_pack_validation(L):
+    f = L.qoq_quantize_pack_weights
+    assert f(FAKE, 32, 256, 64, FAKE, FAKE, FAKE, NUL) == UNSUPPORTED
+    assert f(FAKE, 33, 256, 128, FAKE, FAKE, FAKE, NUL) == INVALID
+    assert f(FAKE, 32, 200, 128, FAKE, FAKE, FAKE, NUL) == INVALID
+    assert f(NUL, 32, 256, 128, FAKE, FAKE, FAKE, NUL) == INVALID
+    assert f(ODD, 32, 256, 128, FAKE, FAKE, FAKE, NUL) == ALIGNMENT
+    assert f(FAKE, 32, 256, 128, ODD, FAKE, FAKE, NUL) == ALIGNMENT
+
+
+def test_activation_validation(L):
+    f = L.qoq_quantize_activations
+    assert f(FAKE, -1, 256, FAKE, FAKE, NUL) == INVALID
+    assert f(FAKE, 4, 12, FAKE, FAKE, NUL) == INVALID
+    assert f(FAKE, 4, 0, FAKE, FAKE, NUL) == INVALID
+    assert f(NUL, 0, 256, NUL, NUL, NUL) == OK          # empty batch: nothing to do
+    assert f(NUL, 4, 256, FAKE, FAKE, NUL) == INVALID
+    assert f(ODD, 4, 256, FAKE, FAKE, NUL) == ALIGNMENT
+
+
+def test_gemm_validation(L):
+    f = L.qoq_w4a8_gemm
+    args = lambda qx=FAKE, sx=FAKE, pw=FAKE, md=FAKE, sw=FAKE, out=FAKE, M=4, N=32, K=256, g=128: (
+        qx, sx, pw, md, sw, out, M, N, K, g, NUL, 0, NUL)
+    assert f(*args(g=32)) == UNSUPPORTED
+    assert f(*args(N=40)) == INVALID
+    assert f(*args(K=192)) == INVALID
+    assert f(*args(M=-1)) == INVALID
+    assert f(*args(M=0, qx=NUL, out=NUL)) == OK
+    assert f(*args(qx=NUL)) == INVALID
+    assert f(*args(sx=NUL)) == INVALID
+    assert f(*args(qx=ODD)) == ALIGNMENT
+    assert f(*args(pw=ODD)) == ALIGNMENT
+    assert f(*args(out=ODD)) == ALIGNMENT
+    assert f(*args(K=139648 + 128)) == UNSUPPORTED
+    g = L.qoq_w4a8_gemm_i32
+    assert g(FAKE, FAKE, FAKE, NUL, 4, 32, 256, 128, NUL, 0, NUL) == INVALID
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 32, 256, 96, NUL, 0, NUL) == UNSUPPORTED
+
+
+def test_diag_validation(L):
+    assert L.qoq_stream_copy(FAKE, FAKE, 17, NUL) == INVALID
+    assert L.qoq_stream_copy(ODD, FAKE, 32, NUL) == ALIGNMENT
+    assert L.qoq_stream_copy(FAKE, FAKE, 0, NUL) == OK
+    assert L.qoq_mfma_probe(NUL, FAKE, FAKE, NUL) == INVALID
+    assert L.qoq_mfma_probe(ODD, FAKE, FAKE, NUL) == ALIGNMENT
+    assert L.qoq_dequantize_packed(FAKE, FAKE, 32, 100, 128, FAKE, NUL) == INVALID
+    assert L.qoq_dequantize_packed(ODD, FAKE, 32, 256, 128, FAKE, NUL) == ALIGNMENT
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        qoq.quantize_activations(x)

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: activation codes and scales, packed weights, group metadata, channel
+scales, in-register dequantization and INT32 accumulators.  FP16 output: every
+element within max(1e-3 * |ref32|, 2^-24) of the oracle's fp32 epilogue (the count
+of elements that are not bit-equal to the oracle's fp16 output is also asserted to
+be zero: both sides round the same fp32 product once).
+
+Small cases are compared element by element; the layer shapes at full size are
+compared on sampled strips / rows / columns that the oracle computes directly.
+"""
+import functools
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qoq_oracle as o
+from w4a8_mixed_precision_amd import qoq
+from w4a8_mixed_precision_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-3
+ATOL = 2.0 ** -24
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_fp16(out16, acc, s_x, s_w):
+    ref32 = o.epilogue_fp32(acc, s_x, s_w)
+    got = out16.astype(np.float32)
+    err = np.abs(got - ref32)
+    tol = np.maximum(RTOL * np.abs(ref32), ATOL)
+    assert np.all(err <= tol), f"max err {err.max()} (rel {np.max(err / np.maximum(np.abs(ref32), 1e-30))})"
+    assert int(np.sum(out16.view(np.uint16) != ref32.astype(np.float16).view(np.uint16))) == 0
+
+
+# ---------------------------------------------------------------------------
+# MFMA operand / result layout
+# ---------------------------------------------------------------------------
+def test_mfma_probe_layout(gpu):
+    say("mfma probe")
+    rng = np.random.default_rng(5)
+    A = rng.integers(-128, 128, (16, 64)).astype(np.int8)     # rows x k
+    B = rng.integers(-128, 128, (64, 16)).astype(np.int8)     # k x cols
+    a = np.zeros((64, 16), np.int8)
+    b = np.zeros((64, 16), np.int8)
+    for l in range(64):
+        a[l] = A[l % 16, 16 * (l // 16): 16 * (l // 16) + 16]
+        b[l] = B[16 * (l // 16): 16 * (l // 16) + 16, l % 16]
+    d = host(qoq.mfma_probe(to_dev(a, gpu), to_dev(b, gpu)))
+    D = A.astype(np.int64) @ B.astype(np.int64)
+    for l in range(64):
+        for i in range(4):
+            assert d[l, i] == D[4 * (l // 16) + i, l % 16]
+
+
+# ---------------------------------------------------------------------------
+# activation quantizer
+# ---------------------------------------------------------------------------
+def _act_cases():
+    yield "tiny_M8", wl.activations_fp16(wl.find("tiny"), 8)
+    for L in wl.LAYERS[1:]:
+        for M in L.Ms:
+            if M * L.K <= 64 * 2 ** 20:
+                yield f"{L.name}_M{M}", wl.activations_fp16(L, M)
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((7, 40960)) * 3).astype(np.float16)     # rows longer than the register budget
+    x[1] = 0.0                                                         # all-zero token
+    x[2] *= np.float16(1e-6)                                           # fp16 subnormal scale territory
+    x[3, 5] = np.float16(65504.0)                                      # fp16 max
+    x[4, :] = np.float16(-2.5)                                         # ties
+    yield "edge_K40960", x
+    yield "ragged_K136", (rng.standard_normal((3, 136)) * 2).astype(np.float16)
+
+
+@pytest.mark.parametrize("name,x", list(_act_cases()), ids=lambda v: v if isinstance(v, str) else "")
+def test_quantize_activations_bit_exact(gpu, name, x):
+    say(f"quantize_activations {name} {x.shape}")
+    qx, sx = qoq.quantize_activations(to_dev(x, gpu))
+    want_q, want_s = o.quantize_activations(x)
+    assert np.array_equal(host(qx), want_q)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+
+
+def test_quantize_activations_large_sampled(gpu):
+    L = wl.find("llama3_8b_down_prefill")
+    say(f"quantize_activations {L.name} M=8192")
+    x = wl.activations_fp16(L, 8192)
+    qx, sx = qoq.quantize_activations(to_dev(x, gpu))
+    rows = np.r_[0:8, 4090:4100, 8184:8192]
+    want_q, want_s = o.quantize_activations(x[rows])
+    assert np.array_equal(host(qx)[rows], want_q)
+    assert np.array_equal(host(sx)[rows].view(np.uint16), want_s.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# weight packer
+# ---------------------------------------------------------------------------
+def _check_pack_strips(packed, meta, s_w, w16, strips, K):
+    G = K // 128
+    rows = np.concatenate([np.arange(16 * b, 16 * b + 16) for b in strips])
+    p_ref, m_ref, s_ref = o.quantize_pack_weights(w16[rows])
+    p_ref = p_ref.reshape(len(strips), G * 1024)
+    m_ref = m_ref.reshape(len(strips), G * 16)
+    p = packed.reshape(-1, G * 1024)
+    m = meta.view(np.uint16).reshape(-1, G * 16)
+    for i, b in enumerate(strips):
+        assert np.array_equal(p[b], p_ref[i]), f"packed strip {b}"
+        assert np.array_equal(m[b], m_ref[i]), f"meta strip {b}"
+    assert np.array_equal(s_w[rows].view(np.uint16), s_ref.view(np.uint16))
+
+
+def test_pack_tiny_bit_exact(gpu):
+    L = wl.find("tiny")
+    say("pack tiny")
+    w16 = wl.weights_fp16(L)
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    p_ref, m_ref, s_ref = o.quantize_pack_weights(w16)
+    assert np.array_equal(host(packed), p_ref)
+    assert np.array_equal(host(meta).view(np.uint16), m_ref)
+    assert np.array_equal(host(s_w).view(np.uint16), s_ref.view(np.uint16))
+
+
+def test_pack_edge_rows(gpu):
+    """Zero rows, rows whose scale underflows fp16, constant rows, single-sign
+    groups and a single huge outlier per row."""
+    say("pack edge rows")
+    rng = np.random.default_rng(9)
+    N, K = 64, 384
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[0] = 0.0
+    w[1] *= 1e-6
+    w[2] = 0.75
+    w[3] = -np.abs(w[3])
+    w[4, 100] = 60000.0
+    w[5, :128] = np.abs(w[5, :128])
+    w16 = w.astype(np.float16)
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    p_ref, m_ref, s_ref = o.quantize_pack_weights(w16)
+    assert np.array_equal(host(packed), p_ref)
+    assert np.array_equal(host(meta).view(np.uint16), m_ref)
+    assert np.array_equal(host(s_w).view(np.uint16), s_ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("name", [L.name for L in wl.LAYERS[1:7]])
+def test_pack_layers_sampled(gpu, name):
+    L = wl.find(name)
+    say(f"pack {name} N={L.N} K={L.K}")
+    w16 = wl.weights_fp16(L)
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    NS = L.N // 16
+    strips = sorted(set([0, 1, NS // 3, NS // 2, NS - 2, NS - 1]))
+    _check_pack_strips(host(packed), host(meta), host(s_w), w16, strips, L.K)
+
+
+# ---------------------------------------------------------------------------
+# dequantization routine, exhaustively over every admissible (q, s, z)
+# ---------------------------------------------------------------------------
+def test_dequant_exhaustive(gpu):
+    say("dequant exhaustive")
+    # every (s, z) pair; each column cycles through the codes q whose dequantized
+    # value (q - z) * s fits INT8 (the only condition the byte-lane arithmetic needs)
+    combos = [(s, z) for s in range(1, 18) for z in range(16)]
+    N = 16 * ((len(combos) + 15) // 16)
+    K = 128
+    q = np.zeros((N, K), np.uint8)
+    zz = np.zeros((N, 1), np.uint8)
+    ss = np.ones((N, 1), np.uint8)
+    n_checked = 0
+    for n, (s, z) in enumerate(combos):
+        ok = [v for v in range(16) if -128 <= (v - z) * s <= 127]
+        if not ok:
+            continue
+        q[n] = np.array([ok[k % len(ok)] for k in range(K)], np.uint8)
+        zz[n, 0], ss[n, 0] = z, s
+        n_checked += len(ok)
+    packed, meta = o.pack_weights(q, zz, ss)
+    w = host(qoq.dequantize_packed(to_dev(packed, gpu), to_dev(meta.view(np.int16), gpu), N, K))
+    want = o.dequantize_level1(q, zz, ss)
+    assert np.array_equal(w.astype(np.int16), want)
+    assert n_checked > 2000
+
+
+def test_dequant_matches_oracle_layer(gpu):
+    L = wl.find("tiny")
+    say("dequant tiny layer")
+    w16 = wl.weights_fp16(L)
+    r_q, r_s = o.quantize_weights_level0(w16)
+    q, z, s = o.quantize_weights_level1(r_q)
+    packed, meta, _ = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    w = host(qoq.dequantize_packed(packed, meta, L.N, L.K))
+    assert np.array_equal(w.astype(np.int16), o.dequantize_level1(q, z, s))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def _gemm_full(dev, x16, w16, regime=None):
+    if regime:
+        os.environ["QOQ_GEMM_REGIME"] = regime
+    try:
+        N = w16.shape[0]
+        packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, dev))
+        qx, s_x = qoq.quantize_activations(to_dev(x16, dev))
+        acc = qoq.w4a8_gemm_i32(qx, packed, meta, N)
+        out = qoq.w4a8_gemm(qx, s_x, packed, meta, s_w, N)
+        return host(acc), host(out)
+    finally:
+        os.environ.pop("QOQ_GEMM_REGIME", None)
+
+
+SMALL_SHAPES = [  # (M, N, K): tiles, ragged tails and the degenerate sizes
+    (1, 16, 128), (8, 512, 512), (3, 48, 256), (17, 64, 384), (33, 80, 640), (64, 128, 1024),
+    (65, 144, 256), (100, 272, 512), (129, 256, 384), (257, 160, 256), (300, 528, 768),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+@pytest.mark.parametrize("regime", ["auto", "skinny", "tiled"])
+def test_gemm_small_exact(gpu, M, N, K, regime):
+    say(f"gemm M={M} N={N} K={K} regime={regime}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+    w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+    r = o.w4a8_reference(x16, w16)
+    acc, out = _gemm_full(gpu, x16, w16, None if regime == "auto" else regime)
+    assert np.array_equal(acc, r["acc"])
+    check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_gemm_tiny_config_exact(gpu):
+    L = wl.find("tiny")
+    say("gemm tiny config M=8 K=512 N=512")
+    x16 = wl.activations_fp16(L, 8)
+    w16 = wl.weights_fp16(L)
+    r = o.w4a8_reference(x16, w16)
+    acc, out = _gemm_full(gpu, x16, w16)
+    assert np.array_equal(acc, r["acc"])
+    check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_gemm_extreme_accumulators(gpu):
+    """Largest |acc| the format allows at this K: every qx = +-127 and every
+    dequantized weight +-119 or the group extremes."""
+    say("gemm extreme accumulators")
+    M, N, K = 16, 32, 4096
+    x16 = np.full((M, K), 1.0, np.float16)
+    x16[1::2] = -1.0
+    w16 = np.full((N, K), 0.5, np.float16)
+    w16[::3] = -0.5
+    r = o.w4a8_reference(x16, w16)
+    acc, out = _gemm_full(gpu, x16, w16)
+    assert np.abs(r["acc"]).max() > 119 * 127 * K * 0.9
+    assert np.array_equal(acc, r["acc"])
+    check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_gemm_empty_batch(gpu):
+    say("gemm M=0")
+    N, K = 32, 256
+    w16 = np.ones((N, K), np.float16)
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    qx = torch.empty((0, K), dtype=torch.int8, device=gpu)
+    s_x = torch.empty((0,), dtype=torch.float16, device=gpu)
+    out = qoq.w4a8_gemm(qx, s_x, packed, meta, s_w, N)
+    assert out.shape == (0, N)
+
+
+_LAYER_CASES = [(L.name, M) for L in wl.LAYERS[1:] for M in L.Ms]
+
+
+@functools.lru_cache(maxsize=1)
+def _layer_weights(name):
+    return wl.weights_fp16(wl.find(name))
+
+
+@pytest.mark.parametrize("name,M", _LAYER_CASES)
+def test_gemm_layers_sampled(gpu, name, M):
+    """Full-size layer shapes in the launch configuration the library picks;
+    the oracle recomputes sampled rows x columns (covering first / last tiles)."""
+    L = wl.find(name)
+    say(f"gemm {name} M={M} N={L.N} K={L.K} plan={qoq.gemm_plan(M, L.N, L.K)}")
+    w16 = _layer_weights(name)
+    x16 = wl.activations_fp16(L, M)
+    acc, out = _gemm_full(gpu, x16, w16)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, min(M, 24))])
+    cols = np.unique(np.r_[0:16, L.N - 16:L.N, rng.integers(0, L.N, 200)])
+    q0, sw = o.quantize_weights_level0(w16[cols])
+    q, z, s = o.quantize_weights_level1(q0)
+    w_hat = o.dequantize_level1(q, z, s)
+    qx, sx = o.quantize_activations(x16[rows])
+    want = o.contract(qx, w_hat)
+    assert np.array_equal(acc[np.ix_(rows, cols)], want)
+    check_fp16(out[np.ix_(rows, cols)], want, sx, sw)
+
+
+def test_gemm_deterministic(gpu):
+    L = wl.find("llama3_8b_qkv")
+    say("gemm determinism qkv M=16 and M=300")
+    w16 = wl.weights_fp16(L)
+    for M in (16, 300):
+        x16 = wl.activations_fp16(L, M)
+        a1, o1 = _gemm_full(gpu, x16, w16)
+        a2, o2 = _gemm_full(gpu, x16, w16)
+        assert np.array_equal(a1, a2) and np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
+
+
+def test_regimes_agree_on_layer(gpu):
+    L = wl.find("llama3_8b_down")
+    say("skinny vs tiled on down-proj M=96")
+    w16 = wl.weights_fp16(L)
+    x16 = wl.activations_fp16(L, 96)
+    a1, _ = _gemm_full(gpu, x16, w16, "skinny")
+    a2, _ = _gemm_full(gpu, x16, w16, "tiled")
+    assert np.array_equal(a1, a2)

@@ -1,0 +1,163 @@
+// C ABI of the QoQ W4A8 library: argument validation, then launches on the
+// caller's stream.  Declarations and the contract of every entry point are in
+// include/qoq.h.
+#include "../../include/qoq.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "qoq_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 139648;   // largest multiple of 128 with 127*121*K < 2^31
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
+}
+
+// shape rules shared by the weight and GEMM calls
+int check_nk(int64_t N, int64_t K, int32_t group) {
+  if (group != 128) return QOQ_ERR_UNSUPPORTED;
+  if (N <= 0 || K <= 0 || N % 16 != 0 || K % 128 != 0) return QOQ_ERR_INVALID;
+  if (K > kMaxK) return QOQ_ERR_UNSUPPORTED;
+  if (N > kMaxDim || N * K / 2 > kMaxDim * 8) return QOQ_ERR_UNSUPPORTED;
+  return QOQ_OK;
+}
+
+int check_gemm(int64_t M, int64_t N, int64_t K, int32_t group) {
+  int st = check_nk(N, K, group);
+  if (st != QOQ_OK) return st;
+  if (M < 0) return QOQ_ERR_INVALID;
+  if (M > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  // row / column indices are 32-bit inside the kernels; element offsets are 64-bit
+  if ((M + 63) / 64 > 65535) return QOQ_ERR_UNSUPPORTED;
+  return QOQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qoq_version(void) { return 1; }
+
+const char *qoq_status_string(int status) {
+  switch (status) {
+    case QOQ_OK: return "ok";
+    case QOQ_ERR_INVALID: return "invalid argument (null pointer or shape not allowed)";
+    case QOQ_ERR_UNSUPPORTED: return "unsupported configuration (group != 128 or size beyond limits)";
+    case QOQ_ERR_ALIGNMENT: return "pointer alignment requirement not met";
+    case QOQ_ERR_WORKSPACE: return "workspace smaller than required";
+    case QOQ_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int qoq_weight_buffer_sizes(int64_t N, int64_t K, int32_t group, size_t *packed_w_bytes,
+                            size_t *group_meta_bytes, size_t *s_w_bytes) {
+  int st = check_nk(N, K, group);
+  if (st != QOQ_OK) return st;
+  if (packed_w_bytes) *packed_w_bytes = static_cast<size_t>(N) * static_cast<size_t>(K) / 2;
+  if (group_meta_bytes) *group_meta_bytes = static_cast<size_t>(N) * static_cast<size_t>(K / 128) * 2;
+  if (s_w_bytes) *s_w_bytes = static_cast<size_t>(N) * 2;
+  return QOQ_OK;
+}
+
+int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t group, void *packed_w,
+                              void *group_meta, void *s_w_fp16, void *stream) {
+  int st = check_nk(N, K, group);
+  if (st != QOQ_OK) return st;
+  if (!w_fp16 || !packed_w || !group_meta || !s_w_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(w_fp16, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 2) || !aligned(s_w_fp16, 2))
+    return QOQ_ERR_ALIGNMENT;
+  qoq::launch_quantize_pack_weights(w_fp16, N, K, packed_w, group_meta, s_w_fp16, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_i8, void *s_x_fp16,
+                             void *stream) {
+  if (M < 0 || K <= 0 || K % 8 != 0) return QOQ_ERR_INVALID;
+  if (M > kMaxDim || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !qx_i8 || !s_x_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(qx_i8, 16) || !aligned(s_x_fp16, 2)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_quantize_activations(x_fp16, M, K, qx_i8, s_x_fp16, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
+  int st = check_gemm(M, N, K, group);
+  if (st != QOQ_OK) return st;
+  if (!bytes) return QOQ_ERR_INVALID;
+  *bytes = 0;
+  return QOQ_OK;
+}
+
+static int gemm_common(const void *qx_i8, const void *s_x_fp16, const void *packed_w, const void *group_meta,
+                       const void *s_w_fp16, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
+                       int32_t group, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;   // no shape needs a workspace (checked against 0 below)
+  int st = check_gemm(M, N, K, group);
+  if (st != QOQ_OK) return st;
+  if (M == 0) return QOQ_OK;
+  if (!qx_i8 || !packed_w || !group_meta || !out) return QOQ_ERR_INVALID;
+  if (out_kind == 0 && (!s_x_fp16 || !s_w_fp16)) return QOQ_ERR_INVALID;
+  if (!aligned(qx_i8, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 2) || !aligned(out, 4))
+    return QOQ_ERR_ALIGNMENT;
+  if (out_kind == 0 && (!aligned(s_x_fp16, 2) || !aligned(s_w_fp16, 2))) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_w4a8_gemm(qx_i8, s_x_fp16, packed_w, group_meta, s_w_fp16, out, out_kind, M, N, K,
+                        as_stream(stream));
+  return launch_status();
+}
+
+int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w, const void *group_meta,
+                  const void *s_w_fp16, void *out_fp16, int64_t M, int64_t N, int64_t K, int32_t group,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  return gemm_common(qx_i8, s_x_fp16, packed_w, group_meta, s_w_fp16, out_fp16, 0, M, N, K, group, workspace,
+                     workspace_bytes, stream);
+}
+
+int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group_meta, int32_t *acc_i32,
+                      int64_t M, int64_t N, int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  return gemm_common(qx_i8, nullptr, packed_w, group_meta, nullptr, acc_i32, 1, M, N, K, group, workspace,
+                     workspace_bytes, stream);
+}
+
+const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm(M, N, K, 128) != QOQ_OK || M == 0) return "invalid";
+  return qoq::gemm_plan_name(M, N, K);
+}
+
+int qoq_dequantize_packed(const void *packed_w, const void *group_meta, int64_t N, int64_t K, int32_t group,
+                          void *w_i8, void *stream) {
+  int st = check_nk(N, K, group);
+  if (st != QOQ_OK) return st;
+  if (!packed_w || !group_meta || !w_i8) return QOQ_ERR_INVALID;
+  if (!aligned(packed_w, 16) || !aligned(group_meta, 2) || !aligned(w_i8, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_dequantize_packed(packed_w, group_meta, N, K, w_i8, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (!src || !dst || bytes % 16 != 0) return QOQ_ERR_INVALID;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return QOQ_ERR_ALIGNMENT;
+  if (bytes == 0) return QOQ_OK;
+  qoq::launch_stream_copy(src, dst, bytes, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_mfma_probe(const void *a_frag, const void *b_frag, void *d_frag, void *stream) {
+  if (!a_frag || !b_frag || !d_frag) return QOQ_ERR_INVALID;
+  if (!aligned(a_frag, 16) || !aligned(b_frag, 16) || !aligned(d_frag, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_mfma_probe(a_frag, b_frag, d_frag, as_stream(stream));
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Device helpers shared by the library's HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qoq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;       // weights per (output channel, group)
+constexpr int kWQmax = 119;       // protective range of the level-0 weight codes
+constexpr int kXQmax = 127;       // symmetric INT8 activation range
+
+// ---------------------------------------------------------------------------
+// fp16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(unsigned bits) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits)));
+}
+
+// max over the 8 halves of a 16-byte chunk of |x|, as an fp16 bit pattern with the
+// sign cleared (for non-NaN values the integer order of these patterns is the order
+// of the magnitudes, subnormals and infinities included)
+__device__ __forceinline__ unsigned absmax_bits8(uint4 v, unsigned acc) {
+  unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned lo = w[i] & 0x7fffu;
+    unsigned hi = (w[i] >> 16) & 0x7fffu;
+    acc = max(acc, max(lo, hi));
+  }
+  return acc;
+}
+
+// fp16(fp32(a * b)): the product is rounded to fp32 first, then to fp16.  The empty
+// asm pins the fp32 product in a register, so the compiler cannot fold multiply and
+// narrowing into one mixed-precision FMA (a single rounding of the exact product,
+// which differs from the two-step rounding whenever the fp32 product lands on an
+// fp16 tie).
+__device__ __forceinline__ __half mul_round_half(float a, float b) {
+  float p = a * b;
+  __asm__ volatile("" : "+v"(p));
+  return __float2half_rn(p);
+}
+
+// symmetric scale: fp16( fp32(absmax) / qmax ) with an IEEE-correct fp32 divide
+__device__ __forceinline__ __half sym_scale(unsigned absmax_bits, float qmax) {
+  float q = __fdiv_rn(half_bits_to_float(absmax_bits), qmax);
+  __asm__ volatile("" : "+v"(q));     // the fp32 quotient is rounded before narrowing
+  return __float2half_rn(q);
+}
+
+// code = clamp(rint(x / s), -qmax, qmax); s == 0 gives 0
+__device__ __forceinline__ int sym_code(float x, float s, float qmax) {
+  if (s == 0.0f) return 0;
+  float r = rintf(__fdiv_rn(x, s));
+  r = fminf(fmaxf(r, -qmax), qmax);
+  return static_cast<int>(r);
+}
+
+// ---------------------------------------------------------------------------
+// wave-wide reductions (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// exact integer a / b rounded half to even (b > 0)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rne_div(int a, int b) {
+  int fl = (a >= 0) ? a / b : -((-a + b - 1) / b);   // floor(a / b)
+  int r = a - fl * b;                                 // 0 <= r < b
+  int up = (2 * r > b) || (2 * r == b && (fl & 1));
+  return fl + up;
+}
+
+// ---------------------------------------------------------------------------
+// INT4 -> INT8 dequantization by multiply-then-subtract, four weights per 32-bit
+// register ("QServe ..." summary, per-group fast dequantization; review §3.2:
+// the 8-bit scale is applied to four byte lanes at once and the zero point is
+// subtracted afterwards; the protective range keeps every byte product in range).
+//
+// Each byte lane holds an unsigned code q in [0,15].  For one group the constants
+// are s2 = s | s << 16 and, per 16-bit half, c16 = ((128 - z*s) * 257) mod 2^16.
+// v_pk_mad_u16 computes q_lo*s + 256*q_hi*s + c16 modulo 2^16, which is congruent
+// to (q_lo*s - z*s + 128) + 256*(q_hi*s - z*s + 128).  Every q*s and z*s is at most
+// 255 and every q*s - z*s + 128 lies in [7, 249], so that integer is in [0, 2^16)
+// and its two bytes are exactly the biased values.  XOR 0x80 per byte then turns
+// each biased byte into the two's-complement INT8 (q - z)*s.
+// ---------------------------------------------------------------------------
+struct GroupConsts {
+  unsigned s2;
+  unsigned c;
+};
+
+__device__ __forceinline__ GroupConsts group_consts(unsigned meta16) {
+  unsigned s = meta16 & 0xffu;
+  unsigned z = (meta16 >> 8) & 0xffu;
+  int bias = 128 - static_cast<int>(z * s);                 // in [-127, 128]
+  unsigned c16 = static_cast<unsigned>(bias * 257) & 0xffffu;
+  GroupConsts g;
+  g.s2 = s | (s << 16);
+  g.c = c16 | (c16 << 16);
+  return g;
+}
+
+__device__ __forceinline__ unsigned dequant4(unsigned codes4, GroupConsts g) {
+  u16x2 q = __builtin_bit_cast(u16x2, codes4);
+  u16x2 s = __builtin_bit_cast(u16x2, g.s2);
+  u16x2 c = __builtin_bit_cast(u16x2, g.c);
+  u16x2 r = q * s + c;
+  return __builtin_bit_cast(unsigned, r) ^ 0x80808080u;
+}
+
+// One lane's 16 packed bytes (32 codes of one column and one group) -> the two
+// 16-byte B operands of a pair of 16x16x64 MFMAs: lo nibbles give the first
+// 64-wide k block, hi nibbles the second.
+__device__ __forceinline__ void dequant_lane(uint4 p, GroupConsts g, v4i &b_lo, v4i &b_hi) {
+  unsigned w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    unsigned lo = w[r] & 0x0f0f0f0fu;
+    unsigned hi = (w[r] >> 4) & 0x0f0f0f0fu;
+    b_lo[r] = static_cast<int>(dequant4(lo, g));
+    b_hi[r] = static_cast<int>(dequant4(hi, g));
+  }
+}
+
+__device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qoq

@@ -1,0 +1,64 @@
+// Diagnostic kernels: in-register dequantization to memory (verifies the GEMM's
+// own dequantization routine), a streaming copy (bandwidth ceiling and the
+// reference for hardware byte counters) and a one-instruction MFMA probe (pins the
+// operand / result lane layout of v_mfma_i32_16x16x64_i8).
+#include "qoq_device.h"
+#include "qoq_internal.h"
+
+namespace qoq {
+
+// one wave per (strip, group) chunk: lane l = 16 h + c holds column 16 b + c and
+// codes k = 128 j + 16 h + i (low nibbles) and k + 64 (high nibbles), i = 0..15
+__global__ __launch_bounds__(256) void dequant_packed_kernel(const uint4 *__restrict__ packed,
+                                                             const uint16_t *__restrict__ meta, int N, int K,
+                                                             int8_t *__restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int G = K >> 7;
+  const long chunk = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (chunk >= static_cast<long>(N >> 4) * G) return;
+  const int b = static_cast<int>(chunk / G), j = static_cast<int>(chunk % G);
+  const int c = lane & 15, h = lane >> 4;
+  const uint4 p = packed[chunk * 64 + lane];
+  const unsigned md = meta[chunk * 16 + c];
+  v4i b0, b1;
+  dequant_lane(p, group_consts(md), b0, b1);
+  int8_t *row = w + static_cast<size_t>(16 * b + c) * K + 128 * j + 16 * h;
+  *reinterpret_cast<v4i *>(row) = b0;
+  *reinterpret_cast<v4i *>(row + 64) = b1;
+}
+
+void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, int64_t K, void *w_i8,
+                              hipStream_t stream) {
+  const long chunks = (N / 16) * (K / 128);
+  hipLaunchKernelGGL(dequant_packed_kernel, dim3(static_cast<unsigned>((chunks + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const uint4 *>(packed), static_cast<const uint16_t *>(meta), static_cast<int>(N),
+                     static_cast<int>(K), static_cast<int8_t *>(w_i8));
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                          size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+void launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16);
+}
+
+__global__ __launch_bounds__(64) void mfma_probe_kernel(const v4i *__restrict__ a, const v4i *__restrict__ b,
+                                                        v4i *__restrict__ d) {
+  const int l = threadIdx.x;
+  d[l] = mfma16x16x64(a[l], b[l], v4i{0, 0, 0, 0});
+}
+
+void launch_mfma_probe(const void *a, const void *b, void *d, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(1), dim3(64), 0, stream, static_cast<const v4i *>(a),
+                     static_cast<const v4i *>(b), static_cast<v4i *>(d));
+}
+
+}  // namespace qoq

@@ -1,0 +1,27 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+// Arguments are validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qoq {
+
+void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, void *sx,
+                                 hipStream_t stream);
+void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *packed, void *meta,
+                                  void *sw, hipStream_t stream);
+
+// GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators
+void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta,
+                      const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream);
+const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
+
+void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, int64_t K, void *w_i8,
+                              hipStream_t stream);
+void launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+void launch_mfma_probe(const void *a, const void *b, void *d, hipStream_t stream);
+
+}  // namespace qoq

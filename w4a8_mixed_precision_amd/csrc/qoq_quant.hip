@@ -1,0 +1,149 @@
+// Per-token INT8 activation quantizer and offline QoQ weight packer (gfx950).
+//
+// Activation side: per-token symmetric INT8 ("QServe: W4A8KV4 Quantization and
+// System Co-design ..." summary, the s_X factor of the epilogue; symmetric
+// quantizer of "01 inference papers and experiments" §4.1).
+// Weight side: progressive group quantization with the protective range
+// ("QServe ..." summary, sections on progressive group quantization and the
+// protective quantization range; "QServe：把 W4A8KV4 ..." review §3.1) and the
+// compute-order storage layout (review §3.2), bytes as described in include/qoq.h.
+#include "qoq_device.h"
+#include "qoq_internal.h"
+
+namespace qoq {
+
+// ---------------------------------------------------------------------------
+// activation quantizer: one 256-thread workgroup per token row.  Each thread keeps
+// up to kActChunks 16-byte chunks of the row in registers so the row is read from
+// HBM once; longer rows re-read the remainder (L2-resident) in the second pass.
+// ---------------------------------------------------------------------------
+constexpr int kActThreads = 256;
+constexpr int kActChunks = 16;   // 16 x 8 halves x 256 threads = rows up to K = 32768
+
+__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s) {
+  unsigned w[4] = {v.x, v.y, v.z, v.w};
+  unsigned out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = half_bits_to_float(w[i] & 0xffffu);
+    float hi = half_bits_to_float(w[i] >> 16);
+    unsigned q0 = static_cast<unsigned>(sym_code(lo, s, kXQmax)) & 0xffu;
+    unsigned q1 = static_cast<unsigned>(sym_code(hi, s, kXQmax)) & 0xffu;
+    out[i >> 1] |= (q0 | (q1 << 8)) << (16 * (i & 1));
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+__global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half *__restrict__ x, int K,
+                                                                   int8_t *__restrict__ qx,
+                                                                   __half *__restrict__ sx) {
+  __shared__ unsigned red[kActThreads / 64];
+  const int row = blockIdx.x;
+  const int nchunk = K >> 3;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(row) * K);
+  uint2 *qr = reinterpret_cast<uint2 *>(qx + static_cast<size_t>(row) * K);
+
+  uint4 v[kActChunks];
+  unsigned amax = 0;
+#pragma unroll
+  for (int c = 0; c < kActChunks; ++c) {
+    int idx = threadIdx.x + c * kActThreads;
+    if (idx < nchunk) {
+      v[c] = xr[idx];
+      amax = absmax_bits8(v[c], amax);
+    }
+  }
+  for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads)
+    amax = absmax_bits8(xr[idx], amax);
+
+  amax = wave_max_u32(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kActThreads / 64; ++w) amax = max(amax, red[w]);
+
+  const __half sh = sym_scale(amax, static_cast<float>(kXQmax));
+  const float s = __half2float(sh);
+  if (threadIdx.x == 0) sx[row] = sh;
+
+#pragma unroll
+  for (int c = 0; c < kActChunks; ++c) {
+    int idx = threadIdx.x + c * kActThreads;
+    if (idx < nchunk) qr[idx] = quant_chunk8(v[c], s);
+  }
+  for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads)
+    qr[idx] = quant_chunk8(xr[idx], s);
+}
+
+void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, void *sx,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(quantize_act_kernel, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
+                     static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
+                     static_cast<__half *>(sx));
+}
+
+// ---------------------------------------------------------------------------
+// weight packer: one wave per output channel n (four channels per workgroup).
+//   pass 1: absmax of the row -> s_W[n]
+//   pass 2: per group of 128: level-0 codes (two per lane), wave min/max, level-1
+//           scale / zero / codes, then the bytes of the storage layout.
+// Lane l holds k = 2l, 2l+1 of the group.  For l < 32 those are the low-nibble
+// codes of bytes i = 2l mod 16, i+1 in slot h = l / 8; lane l + 32 holds the
+// matching high-nibble codes (k + 64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int w_code(unsigned half_bits, float s) {
+  return sym_code(half_bits_to_float(half_bits), s, kWQmax);
+}
+
+__global__ __launch_bounds__(256) void pack_weights_kernel(const __half *__restrict__ w, int N, int K,
+                                                           uint8_t *__restrict__ packed,
+                                                           uint16_t *__restrict__ meta,
+                                                           __half *__restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const __half *wr = w + static_cast<size_t>(n) * K;
+
+  unsigned amax = 0;
+  for (int k = lane * 8; k < K; k += 64 * 8)
+    amax = absmax_bits8(*reinterpret_cast<const uint4 *>(wr + k), amax);
+  amax = wave_max_u32(amax);
+  const __half sh = sym_scale(amax, static_cast<float>(kWQmax));
+  const float s = __half2float(sh);
+  if (lane == 0) sw[n] = sh;
+
+  const int G = K / kGroup;
+  const int b = n >> 4, c = n & 15;
+  for (int j = 0; j < G; ++j) {
+    unsigned pair = *reinterpret_cast<const unsigned *>(wr + kGroup * j + 2 * lane);
+    int q0 = w_code(pair & 0xffffu, s);
+    int q1 = w_code(pair >> 16, s);
+    int lo = wave_min_i32(min(min(q0, q1), 0));
+    int hi = wave_max_i32(max(max(q0, q1), 0));
+    int su = max(1, (hi - lo + 14) / 15);            // ceil((hi - lo) / 15), at least 1
+    int z = min(max(rne_div(-lo, su), 0), 15);
+    unsigned u0 = static_cast<unsigned>(min(max(z + rne_div(q0, su), 0), 15));
+    unsigned u1 = static_cast<unsigned>(min(max(z + rne_div(q1, su), 0), 15));
+    unsigned two = u0 | (u1 << 8);                                    // low nibbles
+    unsigned upper = static_cast<unsigned>(__shfl_down(static_cast<int>(two), 32, 64));
+    unsigned bytes2 = two | (upper << 4);                             // valid for lane < 32
+    unsigned next = static_cast<unsigned>(__shfl_down(static_cast<int>(bytes2), 1, 64));
+    if (lane < 32 && (lane & 1) == 0) {
+      const int h = lane >> 3;
+      const int i = (2 * lane) & 15;                                  // 0, 4, 8, 12
+      size_t off = (static_cast<size_t>(b * G + j) * 64 + 16 * h + c) * 16 + i;
+      *reinterpret_cast<unsigned *>(packed + off) = (bytes2 & 0xffffu) | (next << 16);
+    }
+    if (lane == 0) meta[static_cast<size_t>(b * G + j) * 16 + c] = static_cast<uint16_t>(su | (z << 8));
+  }
+}
+
+void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *packed, void *meta, void *sw,
+                                  hipStream_t stream) {
+  unsigned blocks = static_cast<unsigned>((N + 3) / 4);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const __half *>(w),
+                     static_cast<int>(N), static_cast<int>(K), static_cast<uint8_t *>(packed),
+                     static_cast<uint16_t *>(meta), static_cast<__half *>(sw));
+}
+
+}  // namespace qoq

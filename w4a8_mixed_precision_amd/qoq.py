@@ -1,0 +1,232 @@
+"""Thin Python binding over the C ABI of ``libqoq.so`` (declared in include/qoq.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of the
+library.  PyTorch supplies device memory and the current HIP stream.  There is no
+fallback: a missing library, a CPU tensor or a non-zero status raises.
+
+The functions carry the C names without the ``qoq_`` prefix and take torch tensors;
+``lib()`` exposes the raw ctypes handle for callers that work with pointers.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libqoq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qoq.h")
+
+GROUP = 128
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "qoq_version": ([], ctypes.c_int),
+    "qoq_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "qoq_weight_buffer_sizes": ([_c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz), ctypes.POINTER(_c_sz),
+                                 ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "qoq_quantize_pack_weights": ([_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_quantize_activations": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_gemm_workspace_bytes": ([_c_i64, _c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "qoq_w4a8_gemm": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz,
+                       _c_vp], ctypes.c_int),
+    "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
+                          ctypes.c_int),
+    "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_stream_copy": ([_c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
+    "qoq_mfma_probe": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+}
+
+_lib = None
+
+
+class QoQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/qoq.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(qoq_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().qoq_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().qoq_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise QoQError(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a HIP device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_or_null(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+def weight_buffer_sizes(N: int, K: int, group: int = GROUP) -> dict:
+    a, b, c = _c_sz(), _c_sz(), _c_sz()
+    _check("qoq_weight_buffer_sizes",
+           lib().qoq_weight_buffer_sizes(N, K, group, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return {"packed_w": a.value, "group_meta": b.value, "s_w": c.value}
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    v = _c_sz()
+    _check("qoq_gemm_workspace_bytes", lib().qoq_gemm_workspace_bytes(M, N, K, group, ctypes.byref(v)))
+    return v.value
+
+
+def gemm_plan(M: int, N: int, K: int) -> str:
+    return lib().qoq_gemm_plan(M, N, K).decode()
+
+
+# ---------------------------------------------------------------------------
+# offline weight quantization + packing
+# ---------------------------------------------------------------------------
+def quantize_pack_weights(w: torch.Tensor, group: int = GROUP, out=None):
+    """W fp16 [N, K] -> (packed uint8 [N*K/2], meta int16 [N*K/128] (uint16 bits), s_w fp16 [N])."""
+    N, K = w.shape
+    sizes = weight_buffer_sizes(N, K, group)
+    if out is None:
+        packed = torch.empty(sizes["packed_w"], dtype=torch.uint8, device=w.device)
+        meta = torch.empty(sizes["group_meta"] // 2, dtype=torch.int16, device=w.device)
+        s_w = torch.empty(N, dtype=torch.float16, device=w.device)
+    else:
+        packed, meta, s_w = out
+    _check("qoq_quantize_pack_weights",
+           lib().qoq_quantize_pack_weights(_dev(w, "w", torch.float16), N, K, group,
+                                           _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
+                                           _dev(s_w, "s_w", torch.float16), _stream(w)))
+    return packed, meta, s_w
+
+
+# ---------------------------------------------------------------------------
+# per-token activation quantization
+# ---------------------------------------------------------------------------
+def quantize_activations(x: torch.Tensor, out=None):
+    """X fp16 [M, K] -> (qx int8 [M, K], s_x fp16 [M])."""
+    M, K = x.shape
+    if out is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        s_x = torch.empty(M, dtype=torch.float16, device=x.device)
+    else:
+        qx, s_x = out
+    _check("qoq_quantize_activations",
+           lib().qoq_quantize_activations(_dev(x, "x", torch.float16), M, K, _dev(qx, "qx", torch.int8),
+                                          _dev(s_x, "s_x", torch.float16), _stream(x)))
+    return qx, s_x
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def w4a8_gemm(qx, s_x, packed, meta, s_w, N: int, out=None, group: int = GROUP, workspace=None):
+    """out fp16 [M, N] = fp16(acc * (s_x[m] * s_w[n]))."""
+    M, K = qx.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=qx.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("qoq_w4a8_gemm",
+           lib().qoq_w4a8_gemm(_dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
+                               _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
+                               _dev(s_w, "s_w", torch.float16), _dev(out, "out", torch.float16), M, N, K, group,
+                               _ptr_or_null(workspace), ws_bytes, _stream(qx)))
+    return out
+
+
+def w4a8_gemm_i32(qx, packed, meta, N: int, out=None, group: int = GROUP, workspace=None):
+    """acc int32 [M, N]: the exact integer accumulators of the same main loop."""
+    M, K = qx.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=qx.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("qoq_w4a8_gemm_i32",
+           lib().qoq_w4a8_gemm_i32(_dev(qx, "qx", torch.int8), _dev(packed, "packed", torch.uint8),
+                                   _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K, group,
+                                   _ptr_or_null(workspace), ws_bytes, _stream(qx)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# diagnostics
+# ---------------------------------------------------------------------------
+def dequantize_packed(packed, meta, N: int, K: int, group: int = GROUP, out=None):
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check("qoq_dequantize_packed",
+           lib().qoq_dequantize_packed(_dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16), N, K,
+                                       group, _dev(out, "w_i8", torch.int8), _stream(packed)))
+    return out
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check("qoq_stream_copy", lib().qoq_stream_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(src)))
+    return dst
+
+
+def mfma_probe(a: torch.Tensor, b: torch.Tensor):
+    """a, b int8 [64, 16] per-lane operand bytes -> d int32 [64, 4] per-lane results."""
+    if a.shape != (64, 16) or b.shape != (64, 16):
+        raise ValueError("a and b must be int8 [64, 16]")
+    d = torch.empty((64, 4), dtype=torch.int32, device=a.device)
+    _check("qoq_mfma_probe", lib().qoq_mfma_probe(_dev(a, "a", torch.int8), _dev(b, "b", torch.int8),
+                                                  _dev(d, "d", torch.int32), _stream(a)))
+    return d
+
+
+# ---------------------------------------------------------------------------
+# convenience: the runtime path in one call (two launches)
+# ---------------------------------------------------------------------------
+def w4a8_linear(x: torch.Tensor, packed, meta, s_w, N: int):
+    qx, s_x = quantize_activations(x)
+    return w4a8_gemm(qx, s_x, packed, meta, s_w, N)

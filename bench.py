@@ -28,6 +28,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W4A8 GEMM TOPS and weight GB/s vs MI355X roofline, M=1..4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_llama3_8b_qkv.md")
+GEMM_SOURCES = [os.path.join(ROOT, "w4a8_mixed_precision_amd", "csrc", f)
+                for f in ("qoq_gemm.hip", "qoq_device.h")]
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 ROTATE_BYTES = 1 << 30
@@ -96,6 +99,38 @@ def packed_sets_for(L, dev, q, max_sets=128):
     sets = [(p, m, s)] + [(p.clone(), m.clone(), s.clone()) for _ in range(n - 1)]
     torch.cuda.synchronize()
     return sets, pack_s
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(plan: str, M: int, N: int, K: int):
+    """HBM bytes per launch of this GEMM from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the factor the same counter shows for a
+    copy kernel of known size), or None when the summary is absent, covers another
+    shape, or was taken with different GEMM sources."""
+    import re
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != gemm_source_hash():
+        return None
+    for k in rec.get("kernels", []):
+        if k["plan"] == plan and (k["M"], k["N"], k["K"]) == (M, N, K):
+            return k["fetch_bytes"] + k["write_bytes"]
+    return None
 
 
 def capture(fn, n, torch):
@@ -298,7 +333,8 @@ def main():
                    "K": L.K, "N": L.N, "M": list(Ms), "group": 128},
         "weight_GBps_step": wbytes / step_s / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(dom["plan"], dom["M"], L.N, L.K),
                      "kernel": dom["plan"], "M": dom["M"],
                      "bytes_per_launch": dom_case.bytes["total"], "launch_us": dom["gemm_us"]},
         "cases": per_case,

@@ -125,6 +125,12 @@ int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group
  * string, "invalid" for a shape the GEMM rejects).  Used to match profiler output. */
 const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K);
 
+/* Name of the index-th kernel configuration the library contains (0-based), NULL past
+ * the last.  Setting the environment variable QOQ_GEMM_CONFIG to one of these names
+ * makes the GEMM entry points use that configuration for every shape (a measurement
+ * and verification override; results are identical, only speed changes). */
+const char *qoq_gemm_config_name(int index);
+
 /* ---- diagnostics (verification and measurement; not on the GEMM path) ---- */
 
 /* Dequantize packed weights with the GEMM's own in-register routine:
@@ -137,6 +143,13 @@ int qoq_dequantize_packed(const void *packed_w, const void *group_meta, int64_t 
  * pointers 16-byte aligned): the streaming ceiling and the reference for hardware
  * byte counters.  Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Read-only streaming kernel over `bytes` bytes (bytes % 16 == 0, src 16-byte
+ * aligned): `blocks` workgroups of 256 threads, each thread keeping `unroll` (1, 4
+ * or 8) 16-byte loads in flight; `sink` (4 bytes, device) is written only in a case
+ * the data never produces.  Measures the practical HBM read ceiling for a given
+ * size.  Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, void *stream);
 
 /* One v_mfma_i32_16x16x64_i8 on a single wave: lane l supplies 16 A bytes at
  * a_frag + 16*l and 16 B bytes at b_frag + 16*l and receives its 4 INT32 results at

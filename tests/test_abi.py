@@ -47,6 +47,28 @@ def test_weight_buffer_sizes():
     assert e.value.status == UNSUPPORTED
 
 
+def test_config_names():
+    names = qoq.gemm_configs()
+    assert len(names) >= 4 and len(set(names)) == len(names)
+    assert any(n.startswith("skinny") for n in names) and any(n.startswith("tiled") for n in names)
+    assert qoq.gemm_plan(1, 6144, 4096) in names
+
+
+@pytest.mark.parametrize("regime", [None, "skinny", "tiled"])
+def test_plan_defined_for_every_shape(regime, monkeypatch):
+    """The planner (host code) returns a real configuration for every batch size,
+    also under the measurement overrides."""
+    if regime:
+        monkeypatch.setenv("QOQ_GEMM_REGIME", regime)
+    names = set(qoq.gemm_configs())
+    for (N, K) in [(16, 128), (6144, 4096), (4096, 14336), (59136, 8192), (8192, 29568)]:
+        for M in list(range(1, 300)) + [511, 512, 1023, 4096, 8192, 100000]:
+            assert qoq.gemm_plan(M, N, K) in names, (M, N, K, regime)
+    for name in names:
+        monkeypatch.setenv("QOQ_GEMM_CONFIG", name)
+        assert qoq.gemm_plan(77, 6144, 4096) == name
+
+
 def test_workspace_and_plan():
     assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
     assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
@@ -99,6 +121,9 @@ def test_diag_validation(L):
     assert L.qoq_stream_copy(FAKE, FAKE, 17, NUL) == INVALID
     assert L.qoq_stream_copy(ODD, FAKE, 32, NUL) == ALIGNMENT
     assert L.qoq_stream_copy(FAKE, FAKE, 0, NUL) == OK
+    assert L.qoq_stream_read(FAKE, 32, NUL, 4, 8, NUL) == INVALID
+    assert L.qoq_stream_read(FAKE, 17, FAKE, 4, 8, NUL) == INVALID
+    assert L.qoq_stream_read(ODD, 32, FAKE, 4, 8, NUL) == ALIGNMENT
     assert L.qoq_mfma_probe(NUL, FAKE, FAKE, NUL) == INVALID
     assert L.qoq_mfma_probe(ODD, FAKE, FAKE, NUL) == ALIGNMENT
     assert L.qoq_dequantize_packed(FAKE, FAKE, 32, 100, 128, FAKE, NUL) == INVALID

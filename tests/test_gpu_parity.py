@@ -209,9 +209,11 @@ def test_dequant_matches_oracle_layer(gpu):
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
-def _gemm_full(dev, x16, w16, regime=None):
+def _gemm_full(dev, x16, w16, regime=None, config=None):
     if regime:
         os.environ["QOQ_GEMM_REGIME"] = regime
+    if config:
+        os.environ["QOQ_GEMM_CONFIG"] = config
     try:
         N = w16.shape[0]
         packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, dev))
@@ -221,6 +223,7 @@ def _gemm_full(dev, x16, w16, regime=None):
         return host(acc), host(out)
     finally:
         os.environ.pop("QOQ_GEMM_REGIME", None)
+        os.environ.pop("QOQ_GEMM_CONFIG", None)
 
 
 SMALL_SHAPES = [  # (M, N, K): tiles, ragged tails and the degenerate sizes
@@ -240,6 +243,27 @@ def test_gemm_small_exact(gpu, M, N, K, regime):
     acc, out = _gemm_full(gpu, x16, w16, None if regime == "auto" else regime)
     assert np.array_equal(acc, r["acc"])
     check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def _all_configs():
+    try:
+        return qoq.gemm_configs()
+    except Exception:
+        return []
+
+
+@pytest.mark.parametrize("config", _all_configs())
+def test_every_config_exact(gpu, config):
+    """Every kernel configuration, forced for all shapes, on ragged shapes."""
+    for (M, N, K) in [(1, 16, 128), (21, 80, 1152), (70, 272, 896), (130, 160, 384)]:
+        say(f"gemm config={config} M={M} N={N} K={K}")
+        rng = np.random.default_rng(M + N + K)
+        x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+        r = o.w4a8_reference(x16, w16)
+        acc, out = _gemm_full(gpu, x16, w16, config=config)
+        assert np.array_equal(acc, r["acc"])
+        check_fp16(out, r["acc"], r["s_x"], r["s_w"])
 
 
 def test_gemm_tiny_config_exact(gpu):

@@ -135,6 +135,8 @@ const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K) {
   return qoq::gemm_plan_name(M, N, K);
 }
 
+const char *qoq_gemm_config_name(int index) { return qoq::gemm_config_name(index); }
+
 int qoq_dequantize_packed(const void *packed_w, const void *group_meta, int64_t N, int64_t K, int32_t group,
                           void *w_i8, void *stream) {
   int st = check_nk(N, K, group);
@@ -150,6 +152,14 @@ int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream) {
   if (!aligned(src, 16) || !aligned(dst, 16)) return QOQ_ERR_ALIGNMENT;
   if (bytes == 0) return QOQ_OK;
   qoq::launch_stream_copy(src, dst, bytes, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, void *stream) {
+  if (!src || !sink || bytes % 16 != 0 || blocks <= 0 || unroll <= 0) return QOQ_ERR_INVALID;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return QOQ_ERR_ALIGNMENT;
+  if (bytes == 0) return QOQ_OK;
+  qoq::launch_stream_read(src, bytes, sink, unroll, blocks, as_stream(stream));
   return launch_status();
 }
 

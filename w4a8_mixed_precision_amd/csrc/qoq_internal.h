@@ -18,10 +18,12 @@ void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const 
                       const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
                       hipStream_t stream);
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
+const char *gemm_config_name(int index);
 
 void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, int64_t K, void *w_i8,
                               hipStream_t stream);
 void launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+void launch_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, hipStream_t stream);
 void launch_mfma_probe(const void *a, const void *b, void *d, hipStream_t stream);
 
 }  // namespace qoq

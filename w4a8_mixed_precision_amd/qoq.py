@@ -40,9 +40,11 @@ _SIGNATURES = {
     "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
                           ctypes.c_int),
     "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_gemm_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "qoq_stream_copy": ([_c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
     "qoq_mfma_probe": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_stream_read": ([_c_vp, _c_sz, _c_vp, ctypes.c_int, ctypes.c_int, _c_vp], ctypes.c_int),
 }
 
 _lib = None
@@ -125,6 +127,17 @@ def gemm_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
 
 def gemm_plan(M: int, N: int, K: int) -> str:
     return lib().qoq_gemm_plan(M, N, K).decode()
+
+
+def gemm_configs() -> list:
+    """Names of every kernel configuration in the library."""
+    out, i = [], 0
+    while True:
+        n = lib().qoq_gemm_config_name(i)
+        if n is None:
+            return out
+        out.append(n.decode())
+        i += 1
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +225,12 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor):
         raise ValueError("dst smaller than src")
     _check("qoq_stream_copy", lib().qoq_stream_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(src)))
     return dst
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, unroll: int = 4, blocks: int = 2048):
+    nbytes = src.numel() * src.element_size()
+    _check("qoq_stream_read", lib().qoq_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink"), unroll, blocks,
+                                                    _stream(src)))
 
 
 def mfma_probe(a: torch.Tensor, b: torch.Tensor):

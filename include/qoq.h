@@ -105,8 +105,8 @@ int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, siz
  * matrix-core products, INT32 accumulation, fp16 output):
  *   out[m,n] = fp16( float(acc[m,n]) * (float(s_X[m]) * float(s_W[n])) )
  * qx_i8 [M,K] int8 (16-byte aligned), s_x_fp16 [M], packed_w / group_meta / s_w_fp16
- * as written by qoq_quantize_pack_weights for the same N, K; out_fp16 [M,N]
- * row-major fp16 (4-byte aligned).  workspace may be NULL when
+ * as written by qoq_quantize_pack_weights for the same N, K (packed_w and group_meta
+ * 16-byte aligned); out_fp16 [M,N] row-major fp16 (16-byte aligned).  workspace may be NULL when
  * qoq_gemm_workspace_bytes reports 0.
  * Errors: INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
 int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w,
@@ -115,7 +115,8 @@ int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w,
                   size_t workspace_bytes, void *stream);
 
 /* Same main loop as qoq_w4a8_gemm with an INT32 epilogue: acc_i32 [M,N] row-major
- * receives the exact integer accumulators (for bit-exact verification).
+ * (16-byte aligned) receives the exact integer accumulators (for bit-exact
+ * verification).
  * Errors: as qoq_w4a8_gemm. */
 int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group_meta,
                       int32_t *acc_i32, int64_t M, int64_t N, int64_t K, int32_t group,
@@ -151,11 +152,23 @@ int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
  * size.  Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, void *stream);
 
+/* MFMA-only throughput kernel: `blocks` workgroups of 4 waves, each wave running
+ * `iters` rounds of 8 independent v_mfma_i32_16x16x64_i8 on register operands
+ * (32768 INT8 ops each).  Measures the practical INT8 matrix-core ceiling; `sink`
+ * (4 bytes, device) is written only in a case that does not occur.
+ * Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_mfma_peak(int iters, int blocks, void *sink, void *stream);
+
 /* One v_mfma_i32_16x16x64_i8 on a single wave: lane l supplies 16 A bytes at
  * a_frag + 16*l and 16 B bytes at b_frag + 16*l and receives its 4 INT32 results at
  * d_frag + 16*l.  Used to pin the operand and result lane layout.
  * Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_mfma_probe(const void *a_frag, const void *b_frag, void *d_frag, void *stream);
+
+/* One v_mfma_i32_32x32x32_i8 on a single wave: lane l supplies 16 A bytes at
+ * a_frag + 16*l and 16 B bytes at b_frag + 16*l and receives its 16 INT32 results at
+ * d_frag + 64*l.  Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_mfma_probe32(const void *a_frag, const void *b_frag, void *d_frag, void *stream);
 
 #ifdef __cplusplus
 }

@@ -110,7 +110,9 @@ def test_gemm_validation(L):
     assert f(*args(sx=NUL)) == INVALID
     assert f(*args(qx=ODD)) == ALIGNMENT
     assert f(*args(pw=ODD)) == ALIGNMENT
+    assert f(*args(md=ctypes.c_void_p(0x10002))) == ALIGNMENT
     assert f(*args(out=ODD)) == ALIGNMENT
+    assert f(*args(out=ctypes.c_void_p(0x10008))) == ALIGNMENT
     assert f(*args(K=139648 + 128)) == UNSUPPORTED
     g = L.qoq_w4a8_gemm_i32
     assert g(FAKE, FAKE, FAKE, NUL, 4, 32, 256, 128, NUL, 0, NUL) == INVALID
@@ -124,7 +126,11 @@ def test_diag_validation(L):
     assert L.qoq_stream_read(FAKE, 32, NUL, 4, 8, NUL) == INVALID
     assert L.qoq_stream_read(FAKE, 17, FAKE, 4, 8, NUL) == INVALID
     assert L.qoq_stream_read(ODD, 32, FAKE, 4, 8, NUL) == ALIGNMENT
+    assert L.qoq_mfma_peak(0, 8, FAKE, NUL) == INVALID
+    assert L.qoq_mfma_peak(8, 8, ODD, NUL) == ALIGNMENT
     assert L.qoq_mfma_probe(NUL, FAKE, FAKE, NUL) == INVALID
+    assert L.qoq_mfma_probe32(FAKE, NUL, FAKE, NUL) == INVALID
+    assert L.qoq_mfma_probe32(FAKE, FAKE, ODD, NUL) == ALIGNMENT
     assert L.qoq_mfma_probe(ODD, FAKE, FAKE, NUL) == ALIGNMENT
     assert L.qoq_dequantize_packed(FAKE, FAKE, 32, 100, 128, FAKE, NUL) == INVALID
     assert L.qoq_dequantize_packed(ODD, FAKE, 32, 256, 128, FAKE, NUL) == ALIGNMENT

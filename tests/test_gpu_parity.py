@@ -68,6 +68,31 @@ def test_mfma_probe_layout(gpu):
             assert d[l, i] == D[4 * (l // 16) + i, l % 16]
 
 
+def test_mfma32_probe_layout(gpu):
+    """v_mfma_i32_32x32x32_i8: lane l supplies row (l % 32) of A and column (l % 32)
+    of B as 16 bytes of k = 16*(l // 32) .. +15; register r of lane l holds
+    D[8*(r // 4) + 4*(l // 32) + r % 4][l % 32]."""
+    say("mfma32 probe")
+    rng = np.random.default_rng(6)
+    A = rng.integers(-128, 128, (32, 32)).astype(np.int8)     # rows x k
+    B = rng.integers(-128, 128, (32, 32)).astype(np.int8)     # k x cols
+    a = np.zeros((64, 16), np.int8)
+    b = np.zeros((64, 16), np.int8)
+    for l in range(64):
+        a[l] = A[l % 32, 16 * (l // 32): 16 * (l // 32) + 16]
+        b[l] = B[16 * (l // 32): 16 * (l // 32) + 16, l % 32]
+    d = host(qoq.mfma_probe32(to_dev(a, gpu), to_dev(b, gpu)))
+    D = A.astype(np.int64) @ B.astype(np.int64)
+    want = np.zeros((64, 16), np.int64)
+    for l in range(64):
+        for r in range(16):
+            want[l, r] = D[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32]
+    if not np.array_equal(d, want):
+        os.makedirs("gpurun_out", exist_ok=True)
+        np.savez("gpurun_out/mfma32_probe.npz", a=a, b=b, d=d, A=A, B=B)
+    assert np.array_equal(d, want)
+
+
 # ---------------------------------------------------------------------------
 # activation quantizer
 # ---------------------------------------------------------------------------

@@ -108,7 +108,7 @@ static int gemm_common(const void *qx_i8, const void *s_x_fp16, const void *pack
   if (M == 0) return QOQ_OK;
   if (!qx_i8 || !packed_w || !group_meta || !out) return QOQ_ERR_INVALID;
   if (out_kind == 0 && (!s_x_fp16 || !s_w_fp16)) return QOQ_ERR_INVALID;
-  if (!aligned(qx_i8, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 2) || !aligned(out, 4))
+  if (!aligned(qx_i8, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 16) || !aligned(out, 16))
     return QOQ_ERR_ALIGNMENT;
   if (out_kind == 0 && (!aligned(s_x_fp16, 2) || !aligned(s_w_fp16, 2))) return QOQ_ERR_ALIGNMENT;
   qoq::launch_w4a8_gemm(qx_i8, s_x_fp16, packed_w, group_meta, s_w_fp16, out, out_kind, M, N, K,
@@ -160,6 +160,20 @@ int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int b
   if (!aligned(src, 16) || !aligned(sink, 4)) return QOQ_ERR_ALIGNMENT;
   if (bytes == 0) return QOQ_OK;
   qoq::launch_stream_read(src, bytes, sink, unroll, blocks, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_mfma_peak(int iters, int blocks, void *sink, void *stream) {
+  if (iters <= 0 || blocks <= 0 || !sink) return QOQ_ERR_INVALID;
+  if (!aligned(sink, 4)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_mfma_peak(iters, blocks, sink, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_mfma_probe32(const void *a_frag, const void *b_frag, void *d_frag, void *stream) {
+  if (!a_frag || !b_frag || !d_frag) return QOQ_ERR_INVALID;
+  if (!aligned(a_frag, 16) || !aligned(b_frag, 16) || !aligned(d_frag, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_mfma_probe32(a_frag, b_frag, d_frag, as_stream(stream));
   return launch_status();
 }
 

@@ -8,6 +8,7 @@
 namespace qoq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;       // weights per (output channel, group)
@@ -144,6 +145,10 @@ __device__ __forceinline__ void dequant_lane(uint4 p, GroupConsts g, v4i &b_lo, 
 
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16i mfma32x32x32(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 }  // namespace qoq

@@ -86,10 +86,46 @@ void launch_stream_read(const void *src, size_t bytes, void *sink, int unroll, i
     hipLaunchKernelGGL(stream_read_kernel<1>, g, b, 0, stream, s, n16, k);
 }
 
+// MFMA-only loop: each wave runs `iters` rounds of 8 independent
+// v_mfma_i32_16x16x64_i8 chains on register operands (the practical INT8 matrix
+// throughput); the accumulators are folded and stored only in a case that does not
+// occur for the operands used, so the work cannot be dropped
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, int seed, int *__restrict__ sink) {
+  v4i a = {seed, seed + 1, seed + 2, seed + 3};
+  v4i b = {seed ^ 0x5a5a5a5a, seed + 7, seed - 3, seed * 5};
+  v4i acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4i{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = mfma16x16x64(a, b, acc[i]);
+  }
+  int x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x ^= acc[i][0] ^ acc[i][1] ^ acc[i][2] ^ acc[i][3];
+  if (x == 0x7fffffff) sink[0] = x;
+}
+
+void launch_mfma_peak(int iters, int blocks, void *sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, iters, 3,
+                     static_cast<int *>(sink));
+}
+
 __global__ __launch_bounds__(64) void mfma_probe_kernel(const v4i *__restrict__ a, const v4i *__restrict__ b,
                                                         v4i *__restrict__ d) {
   const int l = threadIdx.x;
   d[l] = mfma16x16x64(a[l], b[l], v4i{0, 0, 0, 0});
+}
+
+__global__ __launch_bounds__(64) void mfma_probe32_kernel(const v4i *__restrict__ a, const v4i *__restrict__ b,
+                                                          v16i *__restrict__ d) {
+  const int l = threadIdx.x;
+  d[l] = mfma32x32x32(a[l], b[l], v16i{});
+}
+
+void launch_mfma_probe32(const void *a, const void *b, void *d, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe32_kernel, dim3(1), dim3(64), 0, stream, static_cast<const v4i *>(a),
+                     static_cast<const v4i *>(b), static_cast<v16i *>(d));
 }
 
 void launch_mfma_probe(const void *a, const void *b, void *d, hipStream_t stream) {

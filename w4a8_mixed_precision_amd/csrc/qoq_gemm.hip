@@ -22,6 +22,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace qoq {
 
 namespace {
@@ -339,23 +341,696 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const int8_t *__restric
 }
 
 // ---------------------------------------------------------------------------
+// Large-M regime on the 32x32x32 INT8 MFMA (the shape that sustains the matrix
+// cores with few independent accumulators).  Same structure as the kernel above:
+// four waves side by side along N, each owning 32*TN columns (TN pairs of strips)
+// and all BM = 32*TM rows; A staged through LDS, double buffered; B dequantized
+// once, by its owner wave, in registers.
+//   32x32x32 operands: lane l supplies row / column (l % 32) and the 16 bytes
+//   k = 16*(l / 32) .. +15 of a 32-wide k block.  From the packed layout a lane of
+//   tile column tn reads, for its column (strip s0 + 2*tn + (l % 32) / 16, c = l % 16),
+//   slot h = l / 32 (low nibbles: k block 0, high nibbles: k block 2) and slot
+//   h = 2 + l / 32 (k blocks 1 and 3): two 16-byte loads per lane per group.
+//   Result: register r of lane l holds D[8*(r / 4) + 4*(l / 32) + r % 4][l % 32].
+// ---------------------------------------------------------------------------
+// Epilogue of the 32x32x32 kernels.  fp16: each 32-row block of a wave's tile goes
+// through a wave-private LDS scratch (32 rows x 32*TN fp16, rows padded by 16 bytes)
+// so the global writes are 16-byte row segments (whole cache lines) instead of
+// 2-byte scattered stores; INT32 (verification path): direct stores.
+// lds_wave: this wave's scratch, at least 32 * (64*TN + 16) bytes, free to use.
+template <int TM, int TN, int OUT>
+__device__ __forceinline__ void epilogue32(const v16i (&acc)[TM][TN], int8_t *__restrict__ lds_wave, int lane,
+                                           int m0, int n0, int M, int N, const __half *__restrict__ sx,
+                                           const __half *__restrict__ sw, void *__restrict__ out) {
+  const int c32 = lane & 31, hi = lane >> 5;
+  if (OUT == 1) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int n = n0 + 32 * tn + c32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 32 * tm + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (m < M) static_cast<int *>(out)[static_cast<size_t>(m) * N + n] = acc[tm][tn][r];
+        }
+    }
+    return;
+  }
+  constexpr int ROW = 64 * TN + 16;                  // bytes per staged row
+  constexpr int SEGS = 4 * TN;                       // 16-byte segments per row
+  float swn[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) swn[tn] = __half2float(sw[min(n0 + 32 * tn + c32, N - 1)]);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float sxm = __half2float(sx[min(m0 + 32 * tm + lr, M - 1)]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        *reinterpret_cast<__half *>(lds_wave + lr * ROW + 2 * (32 * tn + c32)) =
+            mul_round_half(static_cast<float>(acc[tm][tn][r]), sxm * swn[tn]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int e = lane; e < 32 * SEGS; e += 64) {
+      const int lr = e / SEGS, sg = e % SEGS;
+      const int m = m0 + 32 * tm + lr, n = n0 + 8 * sg;
+      const uint4 v = *reinterpret_cast<const uint4 *>(lds_wave + lr * ROW + 16 * sg);
+      if (m < M && n < N) *reinterpret_cast<uint4 *>(static_cast<__half *>(out) + static_cast<size_t>(m) * N + n) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <int TM, int TN, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(const int8_t *__restrict__ qx,
+                                                        const __half *__restrict__ sx,
+                                                        const uint4 *__restrict__ packed,
+                                                        const uint16_t *__restrict__ meta,
+                                                        const __half *__restrict__ sw, void *__restrict__ out, int M,
+                                                        int N, int K) {
+  constexpr int BM = 32 * TM;
+  constexpr int CH = BM * 8 / 256;           // 16-byte A chunks per thread per group
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, hi = lane >> 5;
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int nx = (NS + 8 * TN - 1) / (8 * TN);
+  const int ny = (M + BM - 1) / BM;
+  int tx, ty;
+  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  const int m0 = ty * BM;
+  const int s0 = (tx * 4 + wave) * 2 * TN;   // first strip of this wave
+
+  // A staging: chunk e = tid + 256*c -> row e / 8, 16-byte column e % 8
+  const int8_t *ag[CH];
+  bool agv[CH];
+  int alds[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = tid + 256 * c;
+    const int r = e >> 3, cc = e & 7;
+    agv[c] = (m0 + r) < M;
+    ag[c] = qx + static_cast<size_t>(agv[c] ? m0 + r : 0) * K + 16 * cc;
+    alds[c] = r * kLdsRow + 16 * cc;
+  }
+  // B: per tile column, this lane's strip (clamped; columns past N are dropped at the store)
+  size_t bchunk[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    bchunk[tn] = static_cast<size_t>(min(s0 + 2 * tn + (c32 >> 4), NS - 1)) * G;
+  const int slot0 = 16 * hi + (lane & 15), slot1 = 16 * (2 + hi) + (lane & 15);
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
+
+  const v4i zero4 = {0, 0, 0, 0};
+  v4i ar[CH];
+  uint4 p0[TN], p1[TN];
+  unsigned md[TN];
+
+#pragma unroll
+  for (int c = 0; c < CH; ++c) ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c]) : zero4;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    p0[tn] = packed[bchunk[tn] * 64 + slot0];
+    p1[tn] = packed[bchunk[tn] * 64 + slot1];
+    md[tn] = meta[bchunk[tn] * 16 + (lane & 15)];
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[0][alds[c]]) = ar[c];
+  __syncthreads();
+
+  const int arow = c32 * kLdsRow + 16 * hi;
+  for (int j = 0; j < G; ++j) {
+    const int buf = j & 1;
+    const bool more = (j + 1) < G;
+    uint4 q0[TN], q1[TN];
+    unsigned mdn[TN];
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c] + 128 * (j + 1)) : zero4;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const size_t ch = bchunk[tn] + j + 1;
+        q0[tn] = packed[ch * 64 + slot0];
+        q1[tn] = packed[ch * 64 + slot1];
+        mdn[tn] = meta[ch * 16 + (lane & 15)];
+      }
+    }
+    v4i b[4][TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const GroupConsts g = group_consts(md[tn]);
+      dequant_lane(p0[tn], g, b[0][tn], b[2][tn]);
+      dequant_lane(p1[tn], g, b[1][tn], b[3][tn]);
+    }
+    const int8_t *abuf = &As[buf][arow];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const v4i a = *reinterpret_cast<const v4i *>(abuf + tm * 32 * kLdsRow + 32 * kb);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(a, b[kb][tn], acc[tm][tn]);
+      }
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[buf ^ 1][alds[c]]) = ar[c];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        p0[tn] = q0[tn];
+        p1[tn] = q1[tn];
+        md[tn] = mdn[tn];
+      }
+    }
+    __syncthreads();
+  }
+
+  // the A buffers are free now (the loop ended with a barrier): 4 wave scratches
+  static_assert(4 * 32 * (64 * TN + 16) <= 2 * BM * kLdsRow, "epilogue scratch exceeds the A buffers");
+  epilogue32<TM, TN, OUT>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+}
+
+// ---------------------------------------------------------------------------
+// Large-M regime with a two-group register prefetch (32x32x32 INT8 MFMA).  Same
+// ownership and LDS layout as gemm_wide_kernel.  A prefetched value is never
+// copied between registers (a copy must wait for the load): the loop is unrolled
+// by two and uses two register sets, so group j+2's A chunks and packed codes land
+// in the set group j just released and are consumed in place two groups later.
+// Per group j (set q = j & 1): dequantize B(j) from set q; issue the loads of
+// group j+2 into set q; MFMAs of group j from LDS buffer q; write A(j+1) (set 1-q,
+// loaded a group earlier) into LDS buffer 1-q; barrier.  Group indices past the
+// end clamp to the last group (redundant in-bounds loads, never used).
+// ---------------------------------------------------------------------------
+template <int CH, int TN>
+struct W2Set {
+  v4i a[CH];
+  uint4 p0[TN], p1[TN];
+  unsigned md[TN];
+};
+
+template <int CH, int TN>
+__device__ __forceinline__ void w2_load(W2Set<CH, TN> &S, const int8_t *const (&ag)[CH], const uint4 *__restrict__ packed,
+                                        const uint16_t *__restrict__ meta, const unsigned (&boff)[TN],
+                                        const unsigned (&moff)[TN], int j) {
+#pragma unroll
+  for (int c = 0; c < CH; ++c) S.a[c] = *reinterpret_cast<const v4i *>(ag[c] + 128 * j);
+  const uint4 *pj = packed + static_cast<size_t>(j) * 64;
+  const uint16_t *mj = meta + static_cast<size_t>(j) * 16;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    S.p0[tn] = pj[boff[tn]];
+    S.p1[tn] = pj[boff[tn] + 32];
+    S.md[tn] = mj[moff[tn]];
+  }
+}
+
+template <int TM, int TN, int CH, int Q>
+__device__ __forceinline__ void w2_step(int j, int G, W2Set<CH, TN> &cur, W2Set<CH, TN> &oth, int8_t (*As)[32 * TM * kLdsRow],
+                                        const int (&alds)[CH], int arow, const int8_t *const (&ag)[CH],
+                                        const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                        const unsigned (&boff)[TN], const unsigned (&moff)[TN],
+                                        v16i (&acc)[TM][TN]) {
+  v4i b[4][TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const GroupConsts g = group_consts(cur.md[tn]);
+    dequant_lane(cur.p0[tn], g, b[0][tn], b[2][tn]);
+    dequant_lane(cur.p1[tn], g, b[1][tn], b[3][tn]);
+  }
+  // cur's A chunks went to LDS a group ago and its codes are consumed: reuse it.
+  // The scheduling fences keep these loads at the top of the group and the LDS
+  // writes at its end, so each load has two groups of work to land in.
+  __builtin_amdgcn_sched_barrier(0);
+  w2_load<CH, TN>(cur, ag, packed, meta, boff, moff, min(j + 2, G - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  const int8_t *abuf = &As[Q][arow];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const v4i a = *reinterpret_cast<const v4i *>(abuf + tm * 32 * kLdsRow + 32 * kb);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(a, b[kb][tn], acc[tm][tn]);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[Q ^ 1][alds[c]]) = oth.a[c];
+  __syncthreads();
+}
+
+template <int TM, int TN, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__restrict__ qx,
+                                                            const __half *__restrict__ sx,
+                                                            const uint4 *__restrict__ packed,
+                                                            const uint16_t *__restrict__ meta,
+                                                            const __half *__restrict__ sw, void *__restrict__ out,
+                                                            int M, int N, int K) {
+  constexpr int BM = 32 * TM;
+  constexpr int CH = BM * 8 / 256;
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, hi = lane >> 5;
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int nx = (NS + 8 * TN - 1) / (8 * TN);
+  const int ny = (M + BM - 1) / BM;
+  int tx, ty;
+  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  const int m0 = ty * BM;
+  const int s0 = (tx * 4 + wave) * 2 * TN;
+
+  // A staging: chunk e = tid + 256*c -> row e / 8, 16-byte column e % 8 (rows past M
+  // re-read row M-1; their results are never stored)
+  const int8_t *ag[CH];
+  int alds[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = tid + 256 * c;
+    const int r = e >> 3, cc = e & 7;
+    ag[c] = qx + static_cast<size_t>(min(m0 + r, M - 1)) * K + 16 * cc;
+    alds[c] = r * kLdsRow + 16 * cc;
+  }
+  unsigned boff[TN], moff[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const unsigned strip = static_cast<unsigned>(min(s0 + 2 * tn + (c32 >> 4), NS - 1));
+    boff[tn] = strip * static_cast<unsigned>(G) * 64u + 16u * hi + (lane & 15);
+    moff[tn] = strip * static_cast<unsigned>(G) * 16u + (lane & 15);
+  }
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
+
+  W2Set<CH, TN> s0set, s1set;
+  w2_load<CH, TN>(s0set, ag, packed, meta, boff, moff, 0);
+  w2_load<CH, TN>(s1set, ag, packed, meta, boff, moff, min(1, G - 1));
+#pragma unroll
+  for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[0][alds[c]]) = s0set.a[c];
+  __syncthreads();
+
+  const int arow = c32 * kLdsRow + 16 * hi;
+  int j = 0;
+  for (; j + 1 < G; j += 2) {
+    w2_step<TM, TN, CH, 0>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+    w2_step<TM, TN, CH, 1>(j + 1, G, s1set, s0set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+  }
+  if (j < G) w2_step<TM, TN, CH, 0>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+
+  static_assert(4 * 32 * (64 * TN + 16) <= 2 * BM * kLdsRow, "epilogue scratch exceeds the A buffers");
+  epilogue32<TM, TN, OUT>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+}
+
+// ---------------------------------------------------------------------------
+// Large-M regime, pipelined (32x32x32 INT8 MFMA).  Same ownership as above (four
+// waves side by side along N, each dequantizing only its own columns), with every
+// global read of the main loop done by asynchronous global -> LDS copies
+// (global_load_lds) into an S-stage ring, so no vector register waits on memory:
+//  * stage = A tile (BM rows x 128 bytes; the 16-byte chunks of row r stored at
+//    position chunk ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 bytes per cycle
+//    over 64 banks, two 128-byte rows per bank row, so the 16 rows one phase of an
+//    A-operand read touches land in 16 distinct bank groups) + per wave the packed
+//    chunks of its 2*TN strips (1 KB each, verbatim) + their metadata (one
+//    256-byte copy, 32 bytes per strip).
+//  * every iteration issues the copies of one group (group indices past the end
+//    clamp to the last group: redundant in-bounds copies nobody reads), so the
+//    number of copies issued after a given group is a constant and each wave can
+//    wait for exactly the groups it needs (vmcnt), then meet the others at one
+//    barrier per group.
+//  * at iteration j groups j and j+1 are resident: the MFMAs of group j (weights
+//    dequantized in the previous iteration) and the dequantization of group j+1
+//    are independent, so the two can be interleaved.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima): gfx9 encoding
+#define QOQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+template <int TM, int TN>
+struct PipeLayout {
+  static constexpr int BM = 32 * TM;
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_WAVE = 2 * TN * 1024;        // packed chunks of one wave
+  static constexpr int M_WAVE = 256;                  // metadata copy of one wave
+  static constexpr int B_OFF = A_BYTES;
+  static constexpr int M_OFF = A_BYTES + 4 * B_WAVE;
+  static constexpr int STAGE = M_OFF + 4 * M_WAVE;
+  static constexpr int VM = TM + 2 * TN + 1;          // copies per wave per group
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void pipe_dequant(const int8_t *__restrict__ stage, int wave, int lane,
+                                             v4i (&b)[4][TN]) {
+  using Lay = PipeLayout<TM, TN>;
+  const int8_t *bw = stage + Lay::B_OFF + wave * Lay::B_WAVE;
+  const uint16_t *mw = reinterpret_cast<const uint16_t *>(stage + Lay::M_OFF + wave * Lay::M_WAVE);
+  const int c32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int sl = 2 * tn + (c32 >> 4);                 // local strip of this lane's column
+    const uint4 p0 = *reinterpret_cast<const uint4 *>(bw + sl * 1024 + 16 * (16 * hi + (lane & 15)));
+    const uint4 p1 = *reinterpret_cast<const uint4 *>(bw + sl * 1024 + 16 * (32 + 16 * hi + (lane & 15)));
+    const GroupConsts g = group_consts(mw[sl * 16 + (lane & 15)]);
+    dequant_lane(p0, g, b[0][tn], b[2][tn]);
+    dequant_lane(p1, g, b[1][tn], b[3][tn]);
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void pipe_mfma(const int8_t *__restrict__ stage, int lane, const v4i (&b)[4][TN],
+                                          v16i (&acc)[TM][TN]) {
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int row = 32 * tm + r;
+      const v4i a = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * kb + hi) ^ ((row >> 1) & 7)));
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(a, b[kb][tn], acc[tm][tn]);
+    }
+}
+
+template <int TM, int TN, int S, int OCC, int OUT>
+__global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(const int8_t *__restrict__ qx,
+                                                           const __half *__restrict__ sx,
+                                                           const uint4 *__restrict__ packed,
+                                                           const uint16_t *__restrict__ meta,
+                                                           const __half *__restrict__ sw, void *__restrict__ out,
+                                                           int M, int N, int K) {
+  using Lay = PipeLayout<TM, TN>;
+  static_assert(S >= 3, "groups j and j+1 must be resident while j+S-1 is copied");
+  constexpr int BM = Lay::BM;
+  extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int nx = (NS + 8 * TN - 1) / (8 * TN);
+  const int ny = (M + BM - 1) / BM;
+  int tx, ty;
+  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  const int m0 = ty * BM;
+  const int s0 = (tx * 4 + wave) * 2 * TN;   // first strip of this wave
+
+  // A copies: wave w moves rows 8*(w*TM + i) .. +7; lane l lands at position l & 7
+  // of row 8*(w*TM + i) + (l >> 3), so it reads chunk ((l & 7) ^ ((row >> 1) & 7))
+  // of that row (rows past M re-read row M-1; their results are never stored)
+  const int8_t *asrc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = 8 * (wave * TM + i) + (lane >> 3);
+    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
+  // B copies: one 1 KB chunk per strip (lane l copies slot l); strips past N repeat
+  // the last strip (results dropped at the store)
+  const uint4 *bsrc[2 * TN];
+#pragma unroll
+  for (int t = 0; t < 2 * TN; ++t)
+    bsrc[t] = packed + static_cast<size_t>(min(s0 + t, NS - 1)) * G * 64 + lane;
+  // metadata: lanes 8t .. 8t+7 copy the 32 bytes of strip t (t < 2*TN); the other
+  // lanes repeat strip 0
+  const int mt_strip = (lane >> 3) < 2 * TN ? (lane >> 3) : 0;
+  const unsigned *msrc = reinterpret_cast<const unsigned *>(meta + static_cast<size_t>(min(s0 + mt_strip, NS - 1)) *
+                                                                       G * 16) + (lane & 7);
+
+  auto issue = [&](int j, int stage) {
+    int8_t *st = lds + stage * Lay::STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(asrc[i] + 128 * j), (lds_void_t *)(st + 1024 * (wave * TM + i)),
+                                       16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2 * TN; ++t)
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(bsrc[t] + static_cast<size_t>(j) * 64),
+                                       (lds_void_t *)(st + Lay::B_OFF + wave * Lay::B_WAVE + 1024 * t), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(msrc + static_cast<size_t>(j) * 8),
+                                     (lds_void_t *)(st + Lay::M_OFF + wave * Lay::M_WAVE), 4, 0, 0);
+  };
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
+
+  // prologue: groups 0 .. S-2 in order (the same per-group sequence as the loop)
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(min(st, G - 1), st);
+  v4i bc[4][TN], bn[4][TN];
+  QOQ_WAIT_VMCNT(Lay::VM * (S - 2));           // group 0 resident
+  __builtin_amdgcn_s_barrier();
+  pipe_dequant<TM, TN>(lds, wave, lane, bc);
+
+  for (int j = 0; j < G; ++j) {
+    // groups j and j+1 resident: copies of S-3 later groups may still be in flight
+    QOQ_WAIT_VMCNT(Lay::VM * (S - 3));
+    __builtin_amdgcn_s_barrier();
+    // stage (j+S-1) % S == (j-1) % S: everyone finished reading it before the barrier
+    issue(min(j + S - 1, G - 1), (j + S - 1) % S);
+    pipe_dequant<TM, TN>(lds + ((j + 1) % S) * Lay::STAGE, wave, lane, bn);
+    pipe_mfma<TM, TN>(lds + (j % S) * Lay::STAGE, lane, bc, acc);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) bc[kb][tn] = bn[kb][tn];
+  }
+  QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
+  __syncthreads();                              // every wave is done with the ring
+  static_assert(4 * 32 * (64 * TN + 16) <= S * Lay::STAGE, "epilogue scratch exceeds the ring");
+  epilogue32<TM, TN, OUT>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+}
+
+template <int TM, int TN, int S>
+constexpr int pipe_lds_bytes() {
+  return S * PipeLayout<TM, TN>::STAGE;
+}
+
+// ---------------------------------------------------------------------------
+// Large-M regime, A by copy engine and B by two register sets (32x32x32 MFMA).
+// Four waves side by side along N as above.  A (BM rows x 128 per group) is copied
+// global -> LDS with global_load_lds into a 3-stage ring (chunks of row r at
+// position chunk ^ ((r >> 1) & 7), bank-conflict free for 16-lane phases), so it
+// costs no registers and no LDS-write instructions.  The packed codes of group j+2
+// are loaded into the register set group j just consumed (loop unrolled by two; a
+// prefetched register is never copied, so the compiler can wait for exactly the
+// loads it needs).  A fragments are read one k block ahead of the MFMAs that use
+// them.  Per group j: dequantize B(j); copy A(j+2) and load B(j+2); MFMAs of j;
+// wait for A(j+1)'s copies; barrier.
+// ---------------------------------------------------------------------------
+template <int TN>
+struct DBSet {
+  uint4 p0[TN], p1[TN];
+  unsigned md[TN];
+};
+
+template <int TM, int TN, int Q>
+__device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *__restrict__ lds,
+                                          const int8_t *const (&asrc)[TM], int wave, int lane,
+                                          const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                          const unsigned (&boff)[TN], const unsigned (&moff)[TN],
+                                          v16i (&acc)[TM][TN]) {
+  constexpr int STAGE = 32 * TM * 128;
+  // dequantize this group's codes (set Q, loaded two groups ago)
+  v4i b[4][TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const GroupConsts g = group_consts(cur.md[tn]);
+    dequant_lane(cur.p0[tn], g, b[0][tn], b[2][tn]);
+    dequant_lane(cur.p1[tn], g, b[1][tn], b[3][tn]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // group j+2: A copies into ring stage (j+2) % 3 (held group j-1, finished before
+  // the last barrier), then the codes into the set just consumed
+  {
+    const int jn = min(j + 2, G - 1);
+    int8_t *st = lds + ((j + 2) % 3) * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(asrc[i] + 128 * jn), (lds_void_t *)(st + 1024 * (wave * TM + i)),
+                                       16, 0, 0);
+    const uint4 *pj = packed + static_cast<size_t>(jn) * 64;
+    const uint16_t *mj = meta + static_cast<size_t>(jn) * 16;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      cur.p0[tn] = pj[boff[tn]];
+      cur.p1[tn] = pj[boff[tn] + 32];
+      cur.md[tn] = mj[moff[tn]];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // MFMAs of group j, A fragments read one k block ahead
+  const int8_t *stage = lds + (j % 3) * STAGE;
+  const int r = lane & 31, hi = lane >> 5;
+  v4i af[2][TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int row = 32 * tm + r;
+    af[0][tm] = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((0 + hi) ^ ((row >> 1) & 7)));
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb + 1 < 4) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int row = 32 * tm + r;
+        af[(kb + 1) & 1][tm] =
+            *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * (kb + 1) + hi) ^ ((row >> 1) & 7)));
+      }
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(af[kb & 1][tm], b[kb][tn], acc[tm][tn]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // A(j+1) was copied one group ago; since then: B(j+1) (3*TN loads), this group's
+  // copies (TM) and B(j+2) (3*TN)
+  QOQ_WAIT_VMCNT(6 * TN + TM);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TM, int TN, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restrict__ qx,
+                                                           const __half *__restrict__ sx,
+                                                           const uint4 *__restrict__ packed,
+                                                           const uint16_t *__restrict__ meta,
+                                                           const __half *__restrict__ sw, void *__restrict__ out,
+                                                           int M, int N, int K) {
+  constexpr int BM = 32 * TM;
+  constexpr int STAGE = BM * 128;
+  __shared__ __attribute__((aligned(1024))) int8_t lds[3 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, hi = lane >> 5;
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int nx = (NS + 8 * TN - 1) / (8 * TN);
+  const int ny = (M + BM - 1) / BM;
+  int tx, ty;
+  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  const int m0 = ty * BM;
+  const int s0 = (tx * 4 + wave) * 2 * TN;
+
+  const int8_t *asrc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = 8 * (wave * TM + i) + (lane >> 3);
+    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
+  unsigned boff[TN], moff[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const unsigned strip = static_cast<unsigned>(min(s0 + 2 * tn + (c32 >> 4), NS - 1));
+    boff[tn] = strip * static_cast<unsigned>(G) * 64u + 16u * hi + (lane & 15);
+    moff[tn] = strip * static_cast<unsigned>(G) * 16u + (lane & 15);
+  }
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
+
+  // prologue: A(0), A(1) copies; B(0), B(1) into the two sets
+  DBSet<TN> set0, set1;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int jg = min(g, G - 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(asrc[i] + 128 * jg),
+                                       (lds_void_t *)(lds + g * STAGE + 1024 * (wave * TM + i)), 16, 0, 0);
+  }
+  {
+    const uint16_t *m1 = meta + static_cast<size_t>(min(1, G - 1)) * 16;
+    const uint4 *p1 = packed + static_cast<size_t>(min(1, G - 1)) * 64;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      set0.p0[tn] = packed[boff[tn]];
+      set0.p1[tn] = packed[boff[tn] + 32];
+      set0.md[tn] = meta[moff[tn]];
+    }
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      set1.p0[tn] = p1[boff[tn]];
+      set1.p1[tn] = p1[boff[tn] + 32];
+      set1.md[tn] = m1[moff[tn]];
+    }
+  }
+  // A(0): issued before A(1) (TM copies) and both B sets (6*TN loads)
+  QOQ_WAIT_VMCNT(TM + 6 * TN);
+  __builtin_amdgcn_s_barrier();
+
+  int j = 0;
+  for (; j + 1 < G; j += 2) {
+    dma2_step<TM, TN, 0>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+    dma2_step<TM, TN, 1>(j + 1, G, set1, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+  }
+  if (j < G) dma2_step<TM, TN, 0>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+  QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
+  __syncthreads();
+  static_assert(4 * 32 * (64 * TN + 16) <= 3 * STAGE, "epilogue scratch exceeds the ring");
+  epilogue32<TM, TN, OUT>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+}
+
+// ---------------------------------------------------------------------------
 // planning: which kernel and launch shape for (M, N, K)
 // ---------------------------------------------------------------------------
 typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const uint16_t *, const __half *,
                            void *, int, int, int);
 
 struct Config {
-  int kind;                 // 0 skinny, 1 tiled
-  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    tiled: TM, TN, -, -
+  int kind;                 // 0 skinny, 1 tiled (16x16x64), 2 wide (32x32x32), 3 pipelined
+  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    tiled / wide: TM, TN    pipelined: TM, TN, S
   GemmKernel k[2];          // fp16 epilogue, INT32 epilogue
   const char *name;
+  int lds;                  // dynamic LDS bytes
 };
 
 #define QOQ_SKINNY(MT, NBW, W, U)                                                                   \
   {0, MT, NBW, W, U, {gemm_skinny_kernel<MT, NBW, W, U, 0>, gemm_skinny_kernel<MT, NBW, W, U, 1>}, \
-   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U},
+   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U, 0},
 #define QOQ_TILED(TM, TN) \
-  {1, TM, TN, 0, 0, {gemm_tiled_kernel<TM, TN, 0>, gemm_tiled_kernel<TM, TN, 1>}, "tiled_tm" #TM "_tn" #TN},
+  {1, TM, TN, 0, 0, {gemm_tiled_kernel<TM, TN, 0>, gemm_tiled_kernel<TM, TN, 1>}, "tiled_tm" #TM "_tn" #TN, 0},
+#define QOQ_PIPE(TM, TN, S, OCC)                                                                     \
+  {3, TM, TN, S, OCC, {gemm_pipe_kernel<TM, TN, S, OCC, 0>, gemm_pipe_kernel<TM, TN, S, OCC, 1>},      \
+   "pipe_tm" #TM "_tn" #TN "_s" #S "_o" #OCC, pipe_lds_bytes<TM, TN, S>()},
+#define QOQ_DMA2(TM, TN) \
+  {5, TM, TN, 0, 0, {gemm_dma2_kernel<TM, TN, 0>, gemm_dma2_kernel<TM, TN, 1>}, "dma2_tm" #TM "_tn" #TN, 0},
+#define QOQ_WIDE2(TM, TN) \
+  {4, TM, TN, 0, 0, {gemm_wide2_kernel<TM, TN, 0>, gemm_wide2_kernel<TM, TN, 1>}, "wide2_tm" #TM "_tn" #TN, 0},
+#define QOQ_WIDE(TM, TN) \
+  {2, TM, TN, 0, 0, {gemm_wide_kernel<TM, TN, 0>, gemm_wide_kernel<TM, TN, 1>}, "wide_tm" #TM "_tn" #TN, 0},
 
 const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
@@ -364,13 +1039,19 @@ const Config kConfigs[] = {
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(3, 2, 8, 2)
     QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(4, 2, 8, 1)
     QOQ_TILED(4, 2) QOQ_TILED(4, 4) QOQ_TILED(8, 2) QOQ_TILED(8, 4) QOQ_TILED(16, 2)
+    QOQ_WIDE(2, 1) QOQ_WIDE(2, 2) QOQ_WIDE(4, 1) QOQ_WIDE(4, 2) QOQ_WIDE(8, 1)
+    QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1) QOQ_WIDE2(4, 2) QOQ_WIDE2(8, 1)
+    QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
+    QOQ_PIPE(4, 2, 4, 1) QOQ_PIPE(4, 2, 3, 1) QOQ_PIPE(2, 2, 3, 2) QOQ_PIPE(4, 1, 3, 2) QOQ_PIPE(2, 1, 3, 3)
+    QOQ_PIPE(2, 1, 4, 2) QOQ_PIPE(4, 1, 4, 1)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 const Config *find_config(int kind, int a, int b, int c, int d) {
   for (int i = 0; i < kNumConfigs; ++i) {
     const Config &cf = kConfigs[i];
-    if (cf.kind == kind && cf.a == a && cf.b == b && (kind == 1 || (cf.c == c && cf.d == d))) return &cf;
+    if (cf.kind == kind && cf.a == a && cf.b == b && (kind != 0 && kind != 3 || (cf.c == c && cf.d == d)))
+      return &cf;
   }
   return nullptr;
 }
@@ -412,9 +1093,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
         cfg = find_config(0, mt, 2, 8, 2);
       }
     } else {
-      // 128 x 128 workgroup tiles; 64-row tiles when that is needed for >= 512 tiles
-      const int64_t tiles128 = ((NS + 7) / 8) * ((M + 127) / 128);
-      cfg = tiles128 >= 512 ? find_config(1, 8, 2, 0, 0) : find_config(1, 4, 2, 0, 0);
+      // 128 x 256 workgroup tiles (A by copy engine) when there are enough of them
+      // to fill the chip; otherwise 64 x 128 tiles (four times as many)
+      const int64_t tiles_big = ((NS + 15) / 16) * ((M + 127) / 128);
+      cfg = tiles_big >= 384 ? find_config(5, 4, 2, 0, 0) : find_config(4, 2, 1, 0, 0);
     }
   }
   if (!cfg) cfg = find_config(0, 1, 1, 8, 2);   // present in kConfigs; never reached by the rules above
@@ -424,9 +1106,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     const int mt = cfg->a, nbw = cfg->b, waves = cfg->c;
     p.grid = dim3(static_cast<unsigned>((NS + nbw - 1) / nbw), static_cast<unsigned>((M + 16 * mt - 1) / (16 * mt)));
     p.block = dim3(64 * waves);
-  } else {
+  } else if (cfg->kind == 1) {
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 4 * tn - 1) / (4 * tn), ny = (M + 16 * tm - 1) / (16 * tm);
+    p.grid = dim3(static_cast<unsigned>(nx * ny));
+    p.block = dim3(256);
+  } else {   // wide and pipelined: 32-row blocks, 4 waves x 2*TN strips
+    const int tm = cfg->a, tn = cfg->b;
+    const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
     p.grid = dim3(static_cast<unsigned>(nx * ny));
     p.block = dim3(256);
   }
@@ -435,10 +1122,24 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+// Kernels whose LDS ring exceeds the default dynamic-LDS limit are granted their
+// size once per process (HIP keeps the attribute per kernel for the device).
+std::once_flag g_lds_once[kNumConfigs][2];
+
+void ensure_lds_attribute(const Config *cfg, int out_kind) {
+  if (cfg->lds <= 65536) return;
+  const int idx = static_cast<int>(cfg - kConfigs);
+  std::call_once(g_lds_once[idx][out_kind], [cfg, out_kind] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(cfg->k[out_kind]),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, cfg->lds);
+  });
+}
+
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
                       void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const Plan p = make_plan(M, N, K);
-  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
+  ensure_lds_attribute(p.cfg, out_kind);
+  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
                      static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), out,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));

@@ -44,6 +44,8 @@ _SIGNATURES = {
     "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "qoq_stream_copy": ([_c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
     "qoq_mfma_probe": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_mfma_probe32": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_mfma_peak": ([ctypes.c_int, ctypes.c_int, _c_vp, _c_vp], ctypes.c_int),
     "qoq_stream_read": ([_c_vp, _c_sz, _c_vp, ctypes.c_int, ctypes.c_int, _c_vp], ctypes.c_int),
 }
 
@@ -233,6 +235,10 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, unroll: int = 4, blocks: 
                                                     _stream(src)))
 
 
+def mfma_peak(iters: int, blocks: int, sink: torch.Tensor):
+    _check("qoq_mfma_peak", lib().qoq_mfma_peak(iters, blocks, _dev(sink, "sink"), _stream(sink)))
+
+
 def mfma_probe(a: torch.Tensor, b: torch.Tensor):
     """a, b int8 [64, 16] per-lane operand bytes -> d int32 [64, 4] per-lane results."""
     if a.shape != (64, 16) or b.shape != (64, 16):
@@ -240,6 +246,16 @@ def mfma_probe(a: torch.Tensor, b: torch.Tensor):
     d = torch.empty((64, 4), dtype=torch.int32, device=a.device)
     _check("qoq_mfma_probe", lib().qoq_mfma_probe(_dev(a, "a", torch.int8), _dev(b, "b", torch.int8),
                                                   _dev(d, "d", torch.int32), _stream(a)))
+    return d
+
+
+def mfma_probe32(a: torch.Tensor, b: torch.Tensor):
+    """a, b int8 [64, 16] per-lane operand bytes -> d int32 [64, 16] per-lane results."""
+    if a.shape != (64, 16) or b.shape != (64, 16):
+        raise ValueError("a and b must be int8 [64, 16]")
+    d = torch.empty((64, 16), dtype=torch.int32, device=a.device)
+    _check("qoq_mfma_probe32", lib().qoq_mfma_probe32(_dev(a, "a", torch.int8), _dev(b, "b", torch.int8),
+                                                      _dev(d, "d", torch.int32), _stream(a)))
     return d
 
 

@@ -65,18 +65,28 @@ class Case:
         self.out = torch.empty((M, L.N), dtype=torch.float16, device=dev)
         self.ops = wl.algorithmic_ops(M, L.N, L.K)
         self.bytes = wl.algorithmic_bytes(M, L.N, L.K)
+        self.ws = None
         self.i = 0
+
+    def workspace(self, q):
+        """The split-K workspace this case's plan needs (grown outside graph capture:
+        capture() runs fn once before capturing)."""
+        need = q.gemm_workspace_bytes(self.M, self.L.N, self.L.K)
+        if need and (self.ws is None or self.ws.numel() < need):
+            import torch
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.x.device)
+        return self.ws if need else None
 
     def step(self, q):
         p, m, s = self.sets[self.i % len(self.sets)]
         self.i += 1
         q.quantize_activations(self.x, out=(self.qx, self.sx))
-        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out)
+        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
 
     def gemm_only(self, q):
         p, m, s = self.sets[self.i % len(self.sets)]
         self.i += 1
-        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out)
+        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
 
     def quant_only(self, q):
         q.quantize_activations(self.x, out=(self.qx, self.sx))

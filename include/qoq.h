@@ -95,8 +95,15 @@ int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t 
 int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_i8,
                              void *s_x_fp16, void *stream);
 
-/* Workspace the GEMM entry points need for this problem (currently 0 for every
- * shape: split-K partial sums are reduced on chip).  Errors: INVALID, UNSUPPORTED. */
+/* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
+ * It is non-zero when the plan splits the K groups of each output tile over several
+ * workgroups ("QServe：把 W4A8KV4 ..." review §3.2: split-k when the batch is small;
+ * here for any shape whose output tiles alone would leave compute units idle):
+ * splits x M x N INT32 partial sums, written by the GEMM kernel and summed by a second
+ * kernel that applies the epilogue (both enqueued on `stream`).  The workspace is
+ * caller-owned device memory, 16-byte aligned, needs no initialization and holds
+ * nothing between calls; calls that may run concurrently need separate workspaces.
+ * Errors: INVALID, UNSUPPORTED. */
 int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes);
 
 /* W4A8 per-group GEMM with the fp16 epilogue ("QServe ..." summary, per-group
@@ -106,8 +113,9 @@ int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, siz
  *   out[m,n] = fp16( float(acc[m,n]) * (float(s_X[m]) * float(s_W[n])) )
  * qx_i8 [M,K] int8 (16-byte aligned), s_x_fp16 [M], packed_w / group_meta / s_w_fp16
  * as written by qoq_quantize_pack_weights for the same N, K (packed_w and group_meta
- * 16-byte aligned); out_fp16 [M,N] row-major fp16 (16-byte aligned).  workspace may be NULL when
- * qoq_gemm_workspace_bytes reports 0.
+ * 16-byte aligned); out_fp16 [M,N] row-major fp16 (16-byte aligned).  workspace: see
+ * qoq_gemm_workspace_bytes (may be NULL when that reports 0; WORKSPACE when it is
+ * NULL or smaller than reported, ALIGNMENT when not 16-byte aligned).
  * Errors: INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
 int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w,
                   const void *group_meta, const void *s_w_fp16, void *out_fp16, int64_t M,
@@ -125,6 +133,12 @@ int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group
 /* Name of the kernel configuration qoq_w4a8_gemm launches for this shape (static
  * string, "invalid" for a shape the GEMM rejects).  Used to match profiler output. */
 const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K);
+
+/* Split-K factor of that plan (1 = no split; > 1 = workgroups per output tile, which
+ * then needs the workspace), or a negative qoq_status for a shape the GEMM rejects
+ * (INVALID also for M == 0).  QOQ_GEMM_SPLITS=<n> in the environment forces n
+ * (clamped to [1, min(16, K/128)]) for the kernels that support split-K. */
+int qoq_gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 
 /* Name of the index-th kernel configuration the library contains (0-based), NULL past
  * the last.  Setting the environment variable QOQ_GEMM_CONFIG to one of these names

@@ -69,11 +69,48 @@ def test_plan_defined_for_every_shape(regime, monkeypatch):
         assert qoq.gemm_plan(77, 6144, 4096) == name
 
 
+def test_split_plan_and_workspace(monkeypatch):
+    """Split-K plans: factor, workspace size (splits x M x N INT32 partial sums),
+    and the override."""
+    # down projection at M = 256: 128 x 128 tiles, 2 x 32 = 64 of them -> 8 splits
+    assert qoq.gemm_plan(256, 4096, 14336) == "dma2_tm4_tn1"
+    sp = qoq.gemm_plan_splits(256, 4096, 14336)
+    assert sp == 8
+    assert qoq.gemm_workspace_bytes(256, 4096, 14336) == sp * 256 * 4096 * 4
+    assert qoq.gemm_plan_splits(1, 6144, 4096) == 1 and qoq.gemm_workspace_bytes(1, 6144, 4096) == 0
+    assert qoq.gemm_workspace_bytes(0, 6144, 4096) == 0
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "dma2_tm4_tn2")
+    for want, K in [(3, 4096), (16, 4096), (2, 256), (1, 128)]:
+        monkeypatch.setenv("QOQ_GEMM_SPLITS", str(want))
+        assert qoq.gemm_plan_splits(300, 1024, K) == min(want, K // 128)
+    monkeypatch.setenv("QOQ_GEMM_SPLITS", "1")
+    assert qoq.gemm_workspace_bytes(300, 1024, 4096) == 0
+    monkeypatch.setenv("QOQ_GEMM_CONFIG", "skinny_mt1_nb1_w8_u2")   # no split-K support
+    monkeypatch.setenv("QOQ_GEMM_SPLITS", "8")
+    assert qoq.gemm_plan_splits(300, 1024, 4096) == 1
+    with pytest.raises(qoq.QoQError):
+        qoq.gemm_plan_splits(0, 1024, 4096)
+
+
+def test_workspace_validation(L):
+    """Shapes whose plan splits K need the workspace: NULL or short -> WORKSPACE,
+    not 16-byte aligned -> ALIGNMENT (checked before any launch)."""
+    M, N, K = 256, 4096, 14336
+    need = qoq.gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    f = L.qoq_w4a8_gemm
+    a = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, 128)
+    assert f(*a, NUL, 0, NUL) == WORKSPACE
+    assert f(*a, FAKE, need - 1, NUL) == WORKSPACE
+    assert f(*a, ctypes.c_void_p(0x10008), need, NUL) == ALIGNMENT
+    g = L.qoq_w4a8_gemm_i32
+    assert g(FAKE, FAKE, FAKE, FAKE, M, N, K, 128, NUL, 0, NUL) == WORKSPACE
+
+
 def test_workspace_and_plan():
     assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
     assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
     assert qoq.gemm_plan(4096, 28672, 4096) == "dma2_tm4_tn2"
-    assert qoq.gemm_plan(256, 4096, 14336) == "wide2_tm2_tn1"
     assert qoq.gemm_plan(1, 17, 4096) == "invalid"
     assert qoq.gemm_plan(0, 16, 128) == "invalid"
 

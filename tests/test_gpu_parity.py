@@ -234,11 +234,13 @@ def test_dequant_matches_oracle_layer(gpu):
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
-def _gemm_full(dev, x16, w16, regime=None, config=None):
+def _gemm_full(dev, x16, w16, regime=None, config=None, splits=None):
     if regime:
         os.environ["QOQ_GEMM_REGIME"] = regime
     if config:
         os.environ["QOQ_GEMM_CONFIG"] = config
+    if splits:
+        os.environ["QOQ_GEMM_SPLITS"] = str(splits)
     try:
         N = w16.shape[0]
         packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, dev))
@@ -249,6 +251,7 @@ def _gemm_full(dev, x16, w16, regime=None, config=None):
     finally:
         os.environ.pop("QOQ_GEMM_REGIME", None)
         os.environ.pop("QOQ_GEMM_CONFIG", None)
+        os.environ.pop("QOQ_GEMM_SPLITS", None)
 
 
 SMALL_SHAPES = [  # (M, N, K): tiles, ragged tails and the degenerate sizes
@@ -289,6 +292,71 @@ def test_every_config_exact(gpu, config):
         acc, out = _gemm_full(gpu, x16, w16, config=config)
         assert np.array_equal(acc, r["acc"])
         check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def _split_configs():
+    return [c for c in _all_configs() if c.startswith(("wide2", "dma2"))]
+
+
+@pytest.mark.parametrize("config", _split_configs())
+@pytest.mark.parametrize("splits", [2, 3, 7, 16])
+def test_split_k_exact(gpu, config, splits):
+    """Split-K forced on the kernels that support it: uneven group ranges (7 splits
+    of 16 groups), one group per split (16), ragged M and N; INT32 bit-exact and
+    fp16 to the oracle."""
+    for (M, N, K) in [(70, 272, 2048), (129, 528, 1920), (5, 16, 2048)]:
+        say(f"gemm split-K config={config} splits={splits} M={M} N={N} K={K}")
+        os.environ["QOQ_GEMM_CONFIG"] = config
+        os.environ["QOQ_GEMM_SPLITS"] = str(splits)
+        try:
+            assert qoq.gemm_plan_splits(M, N, K) == min(splits, K // 128)
+            assert qoq.gemm_workspace_bytes(M, N, K) == min(splits, K // 128) * M * N * 4
+        finally:
+            os.environ.pop("QOQ_GEMM_CONFIG", None)
+            os.environ.pop("QOQ_GEMM_SPLITS", None)
+        rng = np.random.default_rng(M * 3 + N + K + splits)
+        x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+        r = o.w4a8_reference(x16, w16)
+        acc, out = _gemm_full(gpu, x16, w16, config=config, splits=splits)
+        assert np.array_equal(acc, r["acc"])
+        check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_split_k_workspace_reuse(gpu):
+    """One caller-owned workspace, filled with garbage first (it needs no
+    initialization), serving calls of different shapes and split factors back to
+    back, twice over."""
+    say("gemm split-K workspace reuse")
+    cases = [(129, 528, 1920, 5), (70, 272, 2048, 16), (300, 160, 1024, 2), (129, 528, 1920, 3)]
+    need = 0
+    for (M, N, K, sp) in cases:
+        os.environ["QOQ_GEMM_CONFIG"] = "wide2_tm2_tn1"
+        os.environ["QOQ_GEMM_SPLITS"] = str(sp)
+        try:
+            need = max(need, qoq.gemm_workspace_bytes(M, N, K))
+        finally:
+            os.environ.pop("QOQ_GEMM_CONFIG", None)
+            os.environ.pop("QOQ_GEMM_SPLITS", None)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=gpu)
+    for rep in range(2):
+        for (M, N, K, sp) in cases:
+            rng = np.random.default_rng(M + N + K + sp)
+            x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+            w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+            r = o.w4a8_reference(x16, w16)
+            packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+            qx, s_x = qoq.quantize_activations(to_dev(x16, gpu))
+            os.environ["QOQ_GEMM_CONFIG"] = "wide2_tm2_tn1"
+            os.environ["QOQ_GEMM_SPLITS"] = str(sp)
+            try:
+                acc = qoq.w4a8_gemm_i32(qx, packed, meta, N, workspace=ws)
+                out = qoq.w4a8_gemm(qx, s_x, packed, meta, s_w, N, workspace=ws)
+            finally:
+                os.environ.pop("QOQ_GEMM_CONFIG", None)
+                os.environ.pop("QOQ_GEMM_SPLITS", None)
+            assert np.array_equal(host(acc), r["acc"]), (rep, M, N, K, sp)
+            check_fp16(host(out), r["acc"], r["s_x"], r["s_w"])
 
 
 def test_gemm_tiny_config_exact(gpu):

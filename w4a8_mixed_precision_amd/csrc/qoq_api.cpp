@@ -94,15 +94,13 @@ int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, siz
   int st = check_gemm(M, N, K, group);
   if (st != QOQ_OK) return st;
   if (!bytes) return QOQ_ERR_INVALID;
-  *bytes = 0;
+  *bytes = M == 0 ? 0 : qoq::gemm_workspace_need(M, N, K);
   return QOQ_OK;
 }
 
 static int gemm_common(const void *qx_i8, const void *s_x_fp16, const void *packed_w, const void *group_meta,
                        const void *s_w_fp16, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
                        int32_t group, void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;   // no shape needs a workspace (checked against 0 below)
   int st = check_gemm(M, N, K, group);
   if (st != QOQ_OK) return st;
   if (M == 0) return QOQ_OK;
@@ -111,7 +109,12 @@ static int gemm_common(const void *qx_i8, const void *s_x_fp16, const void *pack
   if (!aligned(qx_i8, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 16) || !aligned(out, 16))
     return QOQ_ERR_ALIGNMENT;
   if (out_kind == 0 && (!aligned(s_x_fp16, 2) || !aligned(s_w_fp16, 2))) return QOQ_ERR_ALIGNMENT;
-  qoq::launch_w4a8_gemm(qx_i8, s_x_fp16, packed_w, group_meta, s_w_fp16, out, out_kind, M, N, K,
+  const size_t need = qoq::gemm_workspace_need(M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return QOQ_ERR_ALIGNMENT;
+  }
+  qoq::launch_w4a8_gemm(qx_i8, s_x_fp16, packed_w, group_meta, s_w_fp16, out, out_kind, M, N, K, workspace,
                         as_stream(stream));
   return launch_status();
 }
@@ -133,6 +136,13 @@ int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group
 const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K) {
   if (check_gemm(M, N, K, 128) != QOQ_OK || M == 0) return "invalid";
   return qoq::gemm_plan_name(M, N, K);
+}
+
+int qoq_gemm_plan_splits(int64_t M, int64_t N, int64_t K) {
+  const int st = check_gemm(M, N, K, 128);
+  if (st != QOQ_OK) return st;
+  if (M == 0) return QOQ_ERR_INVALID;
+  return qoq::gemm_plan_splits(M, N, K);
 }
 
 const char *qoq_gemm_config_name(int index) { return qoq::gemm_config_name(index); }

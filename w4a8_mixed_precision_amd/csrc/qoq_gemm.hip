@@ -22,6 +22,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace qoq {
@@ -92,7 +93,7 @@ template <int MT, int NBW, int WAVES, int U, int OUT>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, void *__restrict__ out, int M, int N,
-    int K) {
+    int K, int, int *) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = K >> 7;
@@ -197,10 +198,14 @@ constexpr int kLdsRow = 144;   // bytes per staged A row (128 + 16 padding)
 constexpr int kXcds = 8;
 constexpr int kTileGroupRows = 8;
 
-__device__ __forceinline__ void tile_coords(int bid, int nx, int ny, int &x, int &y) {
-  const int total = nx * ny;
-  int t = bid;
-  if (total % kXcds == 0) t = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+// workgroup id -> position in an order where each XCD owns a contiguous range
+__device__ __forceinline__ int xcd_order(int bid, int total) {
+  return total % kXcds == 0 ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
+}
+
+// position -> tile (x = column tile, y = row tile), walking kTileGroupRows row
+// tiles at a time
+__device__ __forceinline__ void tile_walk(int t, int nx, int ny, int &x, int &y) {
   const int group = kTileGroupRows * nx;
   const int g = t / group;
   const int first = g * kTileGroupRows;
@@ -210,13 +215,34 @@ __device__ __forceinline__ void tile_coords(int bid, int nx, int ny, int &x, int
   x = r / rows;
 }
 
+__device__ __forceinline__ void tile_coords(int bid, int nx, int ny, int &x, int &y) {
+  tile_walk(xcd_order(bid, nx * ny), nx, ny, x, y);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K.  When the output tiles alone would leave compute units idle (few tiles,
+// long K), the K groups of every tile are divided among `splits` workgroups:
+// split s takes groups [s*G/splits, (s+1)*G/splits) and stores its INT32 partial
+// tile, row-major, into slice s of the workspace (splits x M x N INT32).  A second
+// kernel (split_reduce_kernel) adds the slices (exact integer sums) and applies the
+// epilogue; the kernel boundary orders the two, so no workgroup waits on another.
+// Workgroups are ordered split-major within each XCD's contiguous range, so the
+// tiles resident on one XCD read the same K range of A and of the weights.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split_coords(int bid, int nx, int ny, int splits, int &x, int &y, int &split) {
+  const int tiles = nx * ny;
+  const int t = xcd_order(bid, tiles * splits);
+  split = t / tiles;
+  tile_walk(t - split * tiles, nx, ny, x, y);
+}
+
 template <int TM, int TN, int OUT>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const int8_t *__restrict__ qx,
                                                          const __half *__restrict__ sx,
                                                          const uint4 *__restrict__ packed,
                                                          const uint16_t *__restrict__ meta,
                                                          const __half *__restrict__ sw, void *__restrict__ out,
-                                                         int M, int N, int K) {
+                                                         int M, int N, int K, int, int *) {
   constexpr int BM = 16 * TM;
   constexpr int CH = BM * 8 / 256;           // 16-byte A chunks per thread per group
   static_assert(CH >= 1, "tile too small");
@@ -416,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(const int8_t *__restr
                                                         const uint4 *__restrict__ packed,
                                                         const uint16_t *__restrict__ meta,
                                                         const __half *__restrict__ sw, void *__restrict__ out, int M,
-                                                        int N, int K) {
+                                                        int N, int K, int, int *) {
   constexpr int BM = 32 * TM;
   constexpr int CH = BM * 8 / 256;           // 16-byte A chunks per thread per group
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
@@ -602,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
                                                             const uint4 *__restrict__ packed,
                                                             const uint16_t *__restrict__ meta,
                                                             const __half *__restrict__ sw, void *__restrict__ out,
-                                                            int M, int N, int K) {
+                                                            int M, int N, int K, int splits, int *__restrict__ ws) {
   constexpr int BM = 32 * TM;
   constexpr int CH = BM * 8 / 256;
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
@@ -611,12 +637,14 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, hi = lane >> 5;
-  const int G = K >> 7;
+  const int Gs = K >> 7;
   const int NS = N >> 4;
   const int nx = (NS + 8 * TN - 1) / (8 * TN);
   const int ny = (M + BM - 1) / BM;
-  int tx, ty;
-  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  int tx, ty, split;
+  split_coords(blockIdx.x, nx, ny, splits, tx, ty, split);
+  const int g0 = split * Gs / splits;
+  const int G = (split + 1) * Gs / splits - g0;   // groups of this split (>= 1)
   const int m0 = ty * BM;
   const int s0 = (tx * 4 + wave) * 2 * TN;
 
@@ -628,15 +656,15 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
   for (int c = 0; c < CH; ++c) {
     const int e = tid + 256 * c;
     const int r = e >> 3, cc = e & 7;
-    ag[c] = qx + static_cast<size_t>(min(m0 + r, M - 1)) * K + 16 * cc;
+    ag[c] = qx + static_cast<size_t>(min(m0 + r, M - 1)) * K + 128 * g0 + 16 * cc;
     alds[c] = r * kLdsRow + 16 * cc;
   }
   unsigned boff[TN], moff[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
     const unsigned strip = static_cast<unsigned>(min(s0 + 2 * tn + (c32 >> 4), NS - 1));
-    boff[tn] = strip * static_cast<unsigned>(G) * 64u + 16u * hi + (lane & 15);
-    moff[tn] = strip * static_cast<unsigned>(G) * 16u + (lane & 15);
+    boff[tn] = (strip * static_cast<unsigned>(Gs) + g0) * 64u + 16u * hi + (lane & 15);
+    moff[tn] = (strip * static_cast<unsigned>(Gs) + g0) * 16u + (lane & 15);
   }
 
   v16i acc[TM][TN];
@@ -661,6 +689,11 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
   if (j < G) w2_step<TM, TN, CH, 0>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
 
   static_assert(4 * 32 * (64 * TN + 16) <= 2 * BM * kLdsRow, "epilogue scratch exceeds the A buffers");
+  if (splits > 1) {   // partial sums of this split -> workspace slice
+    epilogue32<TM, TN, 1>(acc, nullptr, lane, m0, 16 * s0, M, N, nullptr, nullptr,
+                          ws + static_cast<size_t>(split) * M * N);
+    return;
+  }
   epilogue32<TM, TN, OUT>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
 }
 
@@ -741,7 +774,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(const int8_t *__res
                                                            const uint4 *__restrict__ packed,
                                                            const uint16_t *__restrict__ meta,
                                                            const __half *__restrict__ sw, void *__restrict__ out,
-                                                           int M, int N, int K) {
+                                                           int M, int N, int K, int, int *) {
   using Lay = PipeLayout<TM, TN>;
   static_assert(S >= 3, "groups j and j+1 must be resident while j+S-1 is copied");
   constexpr int BM = Lay::BM;
@@ -923,7 +956,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
                                                            const uint4 *__restrict__ packed,
                                                            const uint16_t *__restrict__ meta,
                                                            const __half *__restrict__ sw, void *__restrict__ out,
-                                                           int M, int N, int K) {
+                                                           int M, int N, int K, int splits, int *__restrict__ ws) {
   constexpr int BM = 32 * TM;
   constexpr int STAGE = BM * 128;
   __shared__ __attribute__((aligned(1024))) int8_t lds[3 * STAGE];
@@ -932,12 +965,14 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, hi = lane >> 5;
-  const int G = K >> 7;
+  const int Gs = K >> 7;
   const int NS = N >> 4;
   const int nx = (NS + 8 * TN - 1) / (8 * TN);
   const int ny = (M + BM - 1) / BM;
-  int tx, ty;
-  tile_coords(blockIdx.x, nx, ny, tx, ty);
+  int tx, ty, split;
+  split_coords(blockIdx.x, nx, ny, splits, tx, ty, split);
+  const int g0 = split * Gs / splits;
+  const int G = (split + 1) * Gs / splits - g0;   // groups of this split (>= 1)
   const int m0 = ty * BM;
   const int s0 = (tx * 4 + wave) * 2 * TN;
 
@@ -945,14 +980,14 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = 8 * (wave * TM + i) + (lane >> 3);
-    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 128 * g0 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
   }
   unsigned boff[TN], moff[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
     const unsigned strip = static_cast<unsigned>(min(s0 + 2 * tn + (c32 >> 4), NS - 1));
-    boff[tn] = strip * static_cast<unsigned>(G) * 64u + 16u * hi + (lane & 15);
-    moff[tn] = strip * static_cast<unsigned>(G) * 16u + (lane & 15);
+    boff[tn] = (strip * static_cast<unsigned>(Gs) + g0) * 64u + 16u * hi + (lane & 15);
+    moff[tn] = (strip * static_cast<unsigned>(Gs) + g0) * 16u + (lane & 15);
   }
 
   v16i acc[TM][TN];
@@ -1000,14 +1035,52 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
   QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
   __syncthreads();
   static_assert(4 * 32 * (64 * TN + 16) <= 3 * STAGE, "epilogue scratch exceeds the ring");
+  if (splits > 1) {   // partial sums of this split -> workspace slice
+    epilogue32<TM, TN, 1>(acc, nullptr, lane, m0, 16 * s0, M, N, nullptr, nullptr,
+                          ws + static_cast<size_t>(split) * M * N);
+    return;
+  }
   epilogue32<TM, TN, OUT>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+}
+
+// ---------------------------------------------------------------------------
+// Second pass of split-K: out[m, n] = epilogue(sum_s part[s][m][n]).  Each thread
+// takes 8 consecutive columns of one row (N % 16 == 0, so they never cross a row):
+// two 16-byte loads per slice, one 16-byte fp16 store (or two INT32 stores).
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const int *__restrict__ part, int splits, int M, int N,
+                                                           const __half *__restrict__ sx,
+                                                           const __half *__restrict__ sw, void *__restrict__ out) {
+  const size_t MN = static_cast<size_t>(M) * N;
+  const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e >= MN) return;
+  v4i lo = *reinterpret_cast<const v4i *>(part + e);
+  v4i hi = *reinterpret_cast<const v4i *>(part + e + 4);
+  for (int s = 1; s < splits; ++s) {
+    const int *p = part + static_cast<size_t>(s) * MN + e;
+    lo += *reinterpret_cast<const v4i *>(p);
+    hi += *reinterpret_cast<const v4i *>(p + 4);
+  }
+  if (OUT == 1) {
+    *reinterpret_cast<v4i *>(static_cast<int *>(out) + e) = lo;
+    *reinterpret_cast<v4i *>(static_cast<int *>(out) + e + 4) = hi;
+    return;
+  }
+  const int m = static_cast<int>(e / N), n = static_cast<int>(e % N);
+  const float sxm = __half2float(sx[m]);
+  const int acc[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  __align__(16) __half h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = mul_round_half(static_cast<float>(acc[i]), sxm * __half2float(sw[n + i]));
+  *reinterpret_cast<uint4 *>(static_cast<__half *>(out) + e) = *reinterpret_cast<const uint4 *>(h);
 }
 
 // ---------------------------------------------------------------------------
 // planning: which kernel and launch shape for (M, N, K)
 // ---------------------------------------------------------------------------
 typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const uint16_t *, const __half *,
-                           void *, int, int, int);
+                           void *, int, int, int, int, int *);
 
 struct Config {
   int kind;                 // 0 skinny, 1 tiled (16x16x64), 2 wide (32x32x32), 3 pipelined
@@ -1059,7 +1132,26 @@ const Config *find_config(int kind, int a, int b, int c, int d) {
 struct Plan {
   const Config *cfg;
   dim3 grid, block;
+  int splits;           // split-K factor (kinds 4 and 5 only)
+  size_t ws_bytes;      // workspace the launch needs (0 without split-K)
 };
+
+// Split-K factor: about kTargetWorkgroups workgroups (two per compute unit), each
+// split keeping at least kMinSplitGroups groups of 128 so the loop prologue stays
+// amortized.
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kMinSplitGroups = 4;
+constexpr int64_t kMaxSplits = 16;
+
+int choose_splits(int64_t tiles, int64_t G) {
+  int64_t s = (kTargetWorkgroups + tiles / 2) / tiles;   // rounded
+  if (const char *f = getenv("QOQ_GEMM_SPLITS")) {        // measurement override
+    const long v = strtol(f, nullptr, 10);
+    if (v >= 1) return static_cast<int>(std::min<int64_t>(std::min<int64_t>(v, kMaxSplits), G));
+  }
+  s = std::min<int64_t>(s, std::max<int64_t>(1, G / kMinSplitGroups));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits)));
+}
 
 Plan make_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t NS = N / 16;
@@ -1071,9 +1163,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     for (int i = 0; i < kNumConfigs; ++i)
       if (strcmp(kConfigs[i].name, name) == 0) cfg = &kConfigs[i];
   }
+  const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
+  const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
+  bool split_k = true;   // may the plan split K (kinds 4 and 5)
   if (!cfg) {
     const char *force = getenv("QOQ_GEMM_REGIME");
-    bool tiled = M > 64;
+    // 49..64 tokens on a wide layer: 64-row MFMA tiles beat the split-K-by-wave
+    // skinny kernel (the weights are read once either way)
+    bool tiled = M > 64 || (M > 48 && NS >= 1024);
     if (force && force[0] == 's') tiled = false;
     if (force && force[0] == 't') tiled = true;
     if (!tiled) {
@@ -1093,15 +1190,30 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
         cfg = find_config(0, mt, 2, 8, 2);
       }
     } else {
-      // 128 x 256 workgroup tiles (A by copy engine) when there are enough of them
-      // to fill the chip; otherwise 64 x 128 tiles (four times as many)
-      const int64_t tiles_big = ((NS + 15) / 16) * ((M + 127) / 128);
-      cfg = tiles_big >= 384 ? find_config(5, 4, 2, 0, 0) : find_config(4, 2, 1, 0, 0);
+      // measured on MI355X over the layer shapes of the workloads: the largest tile
+      // that still gives enough workgroups to fill the chip; when no tile size does
+      // (few columns, long K), split K over about 512 workgroups
+      split_k = true;
+      if (t256 >= 384) {
+        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256
+        split_k = false;
+      } else if (t128 >= 320) {
+        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128
+        split_k = false;
+      } else if (M <= 64) {
+        cfg = find_config(5, 2, 1, 0, 0);       // 64 x 128, split K
+      } else if (t256 >= 96) {
+        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, split K
+      } else {
+        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128, split K
+      }
     }
   }
   if (!cfg) cfg = find_config(0, 1, 1, 8, 2);   // present in kConfigs; never reached by the rules above
   Plan p;
   p.cfg = cfg;
+  p.splits = 1;
+  p.ws_bytes = 0;
   if (cfg->kind == 0) {
     const int mt = cfg->a, nbw = cfg->b, waves = cfg->c;
     p.grid = dim3(static_cast<unsigned>((NS + nbw - 1) / nbw), static_cast<unsigned>((M + 16 * mt - 1) / (16 * mt)));
@@ -1114,7 +1226,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
   } else {   // wide and pipelined: 32-row blocks, 4 waves x 2*TN strips
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
-    p.grid = dim3(static_cast<unsigned>(nx * ny));
+    const int64_t tiles = nx * ny;
+    if ((cfg->kind == 4 || cfg->kind == 5) && (split_k || getenv("QOQ_GEMM_SPLITS"))) {
+      p.splits = choose_splits(tiles, G);
+      if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
+    }
+    p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
     p.block = dim3(256);
   }
   return p;
@@ -1136,14 +1253,30 @@ void ensure_lds_attribute(const Config *cfg, int out_kind) {
 }
 
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
-                      void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                      void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
   const Plan p = make_plan(M, N, K);
   ensure_lds_attribute(p.cfg, out_kind);
   hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
                      static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), out,
-                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.splits,
+                     static_cast<int *>(p.splits > 1 ? ws : nullptr));
+  if (p.splits > 1) {
+    const size_t threads = static_cast<size_t>(M) * N / 8;
+    const dim3 g(static_cast<unsigned>((threads + 255) / 256));
+    if (out_kind == 0)
+      hipLaunchKernelGGL(split_reduce_kernel<0>, g, dim3(256), 0, st, static_cast<const int *>(ws), p.splits,
+                         static_cast<int>(M), static_cast<int>(N), static_cast<const __half *>(sx),
+                         static_cast<const __half *>(sw), out);
+    else
+      hipLaunchKernelGGL(split_reduce_kernel<1>, g, dim3(256), 0, st, static_cast<const int *>(ws), p.splits,
+                         static_cast<int>(M), static_cast<int>(N), nullptr, nullptr, out);
+  }
 }
+
+size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).ws_bytes; }
+
+int gemm_plan_splits(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).splits; }
 
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).cfg->name; }
 

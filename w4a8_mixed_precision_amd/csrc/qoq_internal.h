@@ -13,10 +13,13 @@ void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, 
 void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *packed, void *meta,
                                   void *sw, hipStream_t stream);
 
-// GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators
+// GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators; ws holds at least
+// gemm_workspace_need(M, N, K) bytes (may be null when that is 0)
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta,
-                      const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
+                      const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws,
                       hipStream_t stream);
+size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K);
+int gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
 const char *gemm_config_name(int index);
 

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
                           ctypes.c_int),
     "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_gemm_plan_splits": ([_c_i64, _c_i64, _c_i64], ctypes.c_int),
     "qoq_gemm_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "qoq_stream_copy": ([_c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
@@ -107,8 +108,9 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _ptr_or_null(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+def _dev_tensor(t, name: str):
+    _dev(t, name)
+    return t
 
 
 # ---------------------------------------------------------------------------
@@ -129,6 +131,13 @@ def gemm_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
 
 def gemm_plan(M: int, N: int, K: int) -> str:
     return lib().qoq_gemm_plan(M, N, K).decode()
+
+
+def gemm_plan_splits(M: int, N: int, K: int) -> int:
+    v = lib().qoq_gemm_plan_splits(M, N, K)
+    if v < 0:
+        raise QoQError("qoq_gemm_plan_splits", v)
+    return v
 
 
 def gemm_configs() -> list:
@@ -182,17 +191,47 @@ def quantize_activations(x: torch.Tensor, out=None):
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
+# Split-K workspaces, one per (device, stream), grown when a shape needs more.
+_workspaces = {}
+
+
+def workspace_for(qx: torch.Tensor, M: int, N: int, K: int, group: int = GROUP):
+    """The cached workspace of qx's device and current stream, sized for (M, N, K)
+    (None when the plan needs none)."""
+    need = gemm_workspace_bytes(M, N, K, group)
+    if need == 0:
+        return None
+    key = (qx.device.index, torch.cuda.current_stream(qx.device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the split-K workspace for this shape does not exist yet and cannot be "
+                               "allocated during graph capture: call once before capturing or pass workspace=")
+        ws = torch.empty(max(need, 2 * ws.numel() if ws is not None else 0), dtype=torch.uint8, device=qx.device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _workspace_args(workspace, qx, M, N, K, group):
+    if workspace is None:
+        workspace = workspace_for(qx, M, N, K, group)
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def w4a8_gemm(qx, s_x, packed, meta, s_w, N: int, out=None, group: int = GROUP, workspace=None):
-    """out fp16 [M, N] = fp16(acc * (s_x[m] * s_w[n]))."""
+    """out fp16 [M, N] = fp16(acc * (s_x[m] * s_w[n])).  workspace: None = the cached
+    one of this device and stream (see qoq_gemm_workspace_bytes for the contract)."""
     M, K = qx.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=qx.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, group)
     _check("qoq_w4a8_gemm",
            lib().qoq_w4a8_gemm(_dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
                                _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
                                _dev(s_w, "s_w", torch.float16), _dev(out, "out", torch.float16), M, N, K, group,
-                               _ptr_or_null(workspace), ws_bytes, _stream(qx)))
+                               ws_ptr, ws_bytes, _stream(qx)))
     return out
 
 
@@ -201,11 +240,11 @@ def w4a8_gemm_i32(qx, packed, meta, N: int, out=None, group: int = GROUP, worksp
     M, K = qx.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=qx.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, group)
     _check("qoq_w4a8_gemm_i32",
            lib().qoq_w4a8_gemm_i32(_dev(qx, "qx", torch.int8), _dev(packed, "packed", torch.uint8),
                                    _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K, group,
-                                   _ptr_or_null(workspace), ws_bytes, _stream(qx)))
+                                   ws_ptr, ws_bytes, _stream(qx)))
     return out
 
 

@@ -50,7 +50,7 @@ def test_weight_buffer_sizes():
 def test_config_names():
     names = qoq.gemm_configs()
     assert len(names) >= 4 and len(set(names)) == len(names)
-    assert any(n.startswith("skinny") for n in names) and any(n.startswith("tiled") for n in names)
+    assert any(n.startswith("skinny") for n in names) and any(n.startswith("dma2") for n in names)
     assert qoq.gemm_plan(1, 6144, 4096) in names
 
 

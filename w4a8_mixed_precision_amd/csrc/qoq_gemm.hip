@@ -23,7 +23,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 
 namespace qoq {
 
@@ -180,19 +179,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large-M regime (many tokens: INT8 MFMA throughput is the bound).
-//   workgroup = 4 waves side by side along N: wave w owns TN strips (16*TN output
-//   columns) and all BM = 16*TM rows of the tile, so every weight is dequantized by
-//   exactly one wave and stays in that wave's registers (no LDS traffic for B).
-//   One K step = one group of 128.  The A tile (BM x 128 INT8) is staged through
-//   LDS, double buffered, and read by all four waves; its rows are padded to 144
-//   bytes so the rows a 16-lane phase reads fall in distinct banks.  The next
-//   group's A chunks and packed weights are fetched into registers before the
-//   current group is consumed.
+// Large-M regime (many tokens: INT8 MFMA throughput is the bound), on the 32x32x32
+// INT8 MFMA (the shape that sustains the matrix cores with few accumulators).
+//   workgroup = 4 waves side by side along N: wave w owns 32*TN output columns (TN
+//   pairs of 16-column strips) and all BM = 32*TM rows of the tile, so every weight
+//   is dequantized by exactly one wave and stays in its registers.  One K step =
+//   one group of 128; the A tile (BM x 128 INT8) is staged through LDS and read by
+//   all four waves.
+//   32x32x32 operands: lane l supplies row / column (l % 32) and the 16 bytes
+//   k = 16*(l / 32) .. +15 of a 32-wide k block.  From the packed layout a lane of
+//   tile column tn reads, for its column (strip s0 + 2*tn + (l % 32) / 16, c = l % 16),
+//   slot h = l / 32 (low nibbles: k block 0, high nibbles: k block 2) and slot
+//   h = 2 + l / 32 (k blocks 1 and 3): two 16-byte loads per lane per group.
+//   Result: register r of lane l holds D[8*(r / 4) + 4*(l / 32) + r % 4][l % 32].
 //   Tile order: the grid is 1-D.  Workgroup b runs on XCD b % 8, so ids are first
 //   renumbered to give each XCD a contiguous range of tiles, then ranges are walked
-//   GY row-tiles at a time (row index fastest), so the workgroups resident on one
-//   XCD cover a compact block of rows x columns and share both operands in its L2.
+//   kTileGroupRows row-tiles at a time (row index fastest), so the workgroups
+//   resident on one XCD cover a compact block of rows x columns and share both
+//   operands in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kLdsRow = 144;   // bytes per staged A row (128 + 16 padding)
 constexpr int kXcds = 8;
@@ -236,148 +240,6 @@ __device__ __forceinline__ void split_coords(int bid, int nx, int ny, int splits
   tile_walk(t - split * tiles, nx, ny, x, y);
 }
 
-template <int TM, int TN, int OUT>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const int8_t *__restrict__ qx,
-                                                         const __half *__restrict__ sx,
-                                                         const uint4 *__restrict__ packed,
-                                                         const uint16_t *__restrict__ meta,
-                                                         const __half *__restrict__ sw, void *__restrict__ out,
-                                                         int M, int N, int K, int, int *) {
-  constexpr int BM = 16 * TM;
-  constexpr int CH = BM * 8 / 256;           // 16-byte A chunks per thread per group
-  static_assert(CH >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15, kq = lane >> 4;
-  const int G = K >> 7;
-  const int NS = N >> 4;
-  const int nx = (NS + 4 * TN - 1) / (4 * TN);
-  const int ny = (M + BM - 1) / BM;
-  int tx, ty;
-  tile_coords(blockIdx.x, nx, ny, tx, ty);
-  const int m0 = ty * BM;
-  const int strip0 = tx * (4 * TN) + wave * TN;
-
-  // A staging: chunk e = tid + 256*c -> row e / 8, 16-byte column e % 8
-  const int8_t *ag[CH];
-  bool agv[CH];
-  int alds[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e = tid + 256 * c;
-    const int r = e >> 3, cc = e & 7;
-    agv[c] = (m0 + r) < M;
-    ag[c] = qx + static_cast<size_t>(agv[c] ? m0 + r : 0) * K + 16 * cc;
-    alds[c] = r * kLdsRow + 16 * cc;
-  }
-  const uint4 *pb[TN];
-  const uint16_t *mb[TN];
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int s = min(strip0 + tn, NS - 1);   // strips past the end repeat the last; dropped at store
-    pb[tn] = packed + static_cast<size_t>(s) * G * 64 + lane;
-    mb[tn] = meta + static_cast<size_t>(s) * G * 16 + col;
-  }
-
-  v4i acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v4i{0, 0, 0, 0};
-
-  const v4i zero4 = {0, 0, 0, 0};
-  v4i ar[CH];
-  uint4 p[TN];
-  unsigned md[TN];
-
-  // prologue: group 0 into LDS buffer 0 and registers
-#pragma unroll
-  for (int c = 0; c < CH; ++c) ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c]) : zero4;
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    p[tn] = pb[tn][0];
-    md[tn] = mb[tn][0];
-  }
-#pragma unroll
-  for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[0][alds[c]]) = ar[c];
-  __syncthreads();
-
-  const int arow = col * kLdsRow + 16 * kq;
-  for (int j = 0; j < G; ++j) {
-    const int buf = j & 1;
-    const bool more = (j + 1) < G;
-    uint4 pn[TN];
-    unsigned mdn[TN];
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c] + 128 * (j + 1)) : zero4;
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        pn[tn] = pb[tn][static_cast<size_t>(j + 1) * 64];
-        mdn[tn] = mb[tn][static_cast<size_t>(j + 1) * 16];
-      }
-    }
-    v4i b0[TN], b1[TN];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) dequant_lane(p[tn], group_consts(md[tn]), b0[tn], b1[tn]);
-    const int8_t *abuf = &As[buf][arow];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const v4i a0 = *reinterpret_cast<const v4i *>(abuf + tm * 16 * kLdsRow);
-      const v4i a1 = *reinterpret_cast<const v4i *>(abuf + tm * 16 * kLdsRow + 64);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        acc[tm][tn] = mfma16x16x64(a0, b0[tn], acc[tm][tn]);
-        acc[tm][tn] = mfma16x16x64(a1, b1[tn], acc[tm][tn]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[buf ^ 1][alds[c]]) = ar[c];
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        p[tn] = pn[tn];
-        md[tn] = mdn[tn];
-      }
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int strip = strip0 + tn;
-    if (strip >= NS) continue;
-    const int n = strip * 16 + col;
-    const float swn = (OUT == 0) ? __half2float(sw[n]) : 0.0f;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 16 * tm + 4 * kq + i;
-        if (m < M) {
-          const float scale = (OUT == 0) ? __half2float(sx[m]) * swn : 0.0f;
-          store_result(out, OUT, static_cast<size_t>(m) * N + n, acc[tm][tn][i], scale);
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Large-M regime on the 32x32x32 INT8 MFMA (the shape that sustains the matrix
-// cores with few independent accumulators).  Same structure as the kernel above:
-// four waves side by side along N, each owning 32*TN columns (TN pairs of strips)
-// and all BM = 32*TM rows; A staged through LDS, double buffered; B dequantized
-// once, by its owner wave, in registers.
-//   32x32x32 operands: lane l supplies row / column (l % 32) and the 16 bytes
-//   k = 16*(l / 32) .. +15 of a 32-wide k block.  From the packed layout a lane of
-//   tile column tn reads, for its column (strip s0 + 2*tn + (l % 32) / 16, c = l % 16),
-//   slot h = l / 32 (low nibbles: k block 0, high nibbles: k block 2) and slot
-//   h = 2 + l / 32 (k blocks 1 and 3): two 16-byte loads per lane per group.
-//   Result: register r of lane l holds D[8*(r / 4) + 4*(l / 32) + r % 4][l % 32].
 // ---------------------------------------------------------------------------
 // Epilogue of the 32x32x32 kernels.  fp16: each 32-row block of a wave's tile goes
 // through a wave-private LDS scratch (32 rows x 32*TN fp16, rows padded by 16 bytes)
@@ -436,127 +298,10 @@ __device__ __forceinline__ void epilogue32(const v16i (&acc)[TM][TN], int8_t *__
   }
 }
 
-template <int TM, int TN, int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(const int8_t *__restrict__ qx,
-                                                        const __half *__restrict__ sx,
-                                                        const uint4 *__restrict__ packed,
-                                                        const uint16_t *__restrict__ meta,
-                                                        const __half *__restrict__ sw, void *__restrict__ out, int M,
-                                                        int N, int K, int, int *) {
-  constexpr int BM = 32 * TM;
-  constexpr int CH = BM * 8 / 256;           // 16-byte A chunks per thread per group
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31, hi = lane >> 5;
-  const int G = K >> 7;
-  const int NS = N >> 4;
-  const int nx = (NS + 8 * TN - 1) / (8 * TN);
-  const int ny = (M + BM - 1) / BM;
-  int tx, ty;
-  tile_coords(blockIdx.x, nx, ny, tx, ty);
-  const int m0 = ty * BM;
-  const int s0 = (tx * 4 + wave) * 2 * TN;   // first strip of this wave
-
-  // A staging: chunk e = tid + 256*c -> row e / 8, 16-byte column e % 8
-  const int8_t *ag[CH];
-  bool agv[CH];
-  int alds[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e = tid + 256 * c;
-    const int r = e >> 3, cc = e & 7;
-    agv[c] = (m0 + r) < M;
-    ag[c] = qx + static_cast<size_t>(agv[c] ? m0 + r : 0) * K + 16 * cc;
-    alds[c] = r * kLdsRow + 16 * cc;
-  }
-  // B: per tile column, this lane's strip (clamped; columns past N are dropped at the store)
-  size_t bchunk[TN];
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn)
-    bchunk[tn] = static_cast<size_t>(min(s0 + 2 * tn + (c32 >> 4), NS - 1)) * G;
-  const int slot0 = 16 * hi + (lane & 15), slot1 = 16 * (2 + hi) + (lane & 15);
-
-  v16i acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
-
-  const v4i zero4 = {0, 0, 0, 0};
-  v4i ar[CH];
-  uint4 p0[TN], p1[TN];
-  unsigned md[TN];
-
-#pragma unroll
-  for (int c = 0; c < CH; ++c) ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c]) : zero4;
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    p0[tn] = packed[bchunk[tn] * 64 + slot0];
-    p1[tn] = packed[bchunk[tn] * 64 + slot1];
-    md[tn] = meta[bchunk[tn] * 16 + (lane & 15)];
-  }
-#pragma unroll
-  for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[0][alds[c]]) = ar[c];
-  __syncthreads();
-
-  const int arow = c32 * kLdsRow + 16 * hi;
-  for (int j = 0; j < G; ++j) {
-    const int buf = j & 1;
-    const bool more = (j + 1) < G;
-    uint4 q0[TN], q1[TN];
-    unsigned mdn[TN];
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        ar[c] = agv[c] ? *reinterpret_cast<const v4i *>(ag[c] + 128 * (j + 1)) : zero4;
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const size_t ch = bchunk[tn] + j + 1;
-        q0[tn] = packed[ch * 64 + slot0];
-        q1[tn] = packed[ch * 64 + slot1];
-        mdn[tn] = meta[ch * 16 + (lane & 15)];
-      }
-    }
-    v4i b[4][TN];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const GroupConsts g = group_consts(md[tn]);
-      dequant_lane(p0[tn], g, b[0][tn], b[2][tn]);
-      dequant_lane(p1[tn], g, b[1][tn], b[3][tn]);
-    }
-    const int8_t *abuf = &As[buf][arow];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const v4i a = *reinterpret_cast<const v4i *>(abuf + tm * 32 * kLdsRow + 32 * kb);
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(a, b[kb][tn], acc[tm][tn]);
-      }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[buf ^ 1][alds[c]]) = ar[c];
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        p0[tn] = q0[tn];
-        p1[tn] = q1[tn];
-        md[tn] = mdn[tn];
-      }
-    }
-    __syncthreads();
-  }
-
-  // the A buffers are free now (the loop ended with a barrier): 4 wave scratches
-  static_assert(4 * 32 * (64 * TN + 16) <= 2 * BM * kLdsRow, "epilogue scratch exceeds the A buffers");
-  epilogue32<TM, TN, OUT>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
-}
-
 // ---------------------------------------------------------------------------
-// Large-M regime with a two-group register prefetch (32x32x32 INT8 MFMA).  Same
-// ownership and LDS layout as gemm_wide_kernel.  A prefetched value is never
+// Large-M regime, A staged by the waves, two-group register prefetch.  The A tile
+// is double buffered in LDS with rows padded to kLdsRow = 144 bytes, so the rows a
+// 16-lane phase reads fall in distinct banks.  A prefetched value is never
 // copied between registers (a copy must wait for the load): the loop is unrolled
 // by two and uses two register sets, so group j+2's A chunks and packed codes land
 // in the set group j just released and are consumed in place two groups later.
@@ -698,24 +443,8 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Large-M regime, pipelined (32x32x32 INT8 MFMA).  Same ownership as above (four
-// waves side by side along N, each dequantizing only its own columns), with every
-// global read of the main loop done by asynchronous global -> LDS copies
-// (global_load_lds) into an S-stage ring, so no vector register waits on memory:
-//  * stage = A tile (BM rows x 128 bytes; the 16-byte chunks of row r stored at
-//    position chunk ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 bytes per cycle
-//    over 64 banks, two 128-byte rows per bank row, so the 16 rows one phase of an
-//    A-operand read touches land in 16 distinct bank groups) + per wave the packed
-//    chunks of its 2*TN strips (1 KB each, verbatim) + their metadata (one
-//    256-byte copy, 32 bytes per strip).
-//  * every iteration issues the copies of one group (group indices past the end
-//    clamp to the last group: redundant in-bounds copies nobody reads), so the
-//    number of copies issued after a given group is a constant and each wave can
-//    wait for exactly the groups it needs (vmcnt), then meet the others at one
-//    barrier per group.
-//  * at iteration j groups j and j+1 are resident: the MFMAs of group j (weights
-//    dequantized in the previous iteration) and the dequantization of group j+1
-//    are independent, so the two can be interleaved.
+// Copy-engine helpers: global -> LDS copies (global_load_lds) count in vmcnt like
+// loads, so a wave waits for the copies it needs with a vmcnt-only wait.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -723,154 +452,14 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima): gfx9 encoding
 #define QOQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-template <int TM, int TN>
-struct PipeLayout {
-  static constexpr int BM = 32 * TM;
-  static constexpr int A_BYTES = BM * 128;
-  static constexpr int B_WAVE = 2 * TN * 1024;        // packed chunks of one wave
-  static constexpr int M_WAVE = 256;                  // metadata copy of one wave
-  static constexpr int B_OFF = A_BYTES;
-  static constexpr int M_OFF = A_BYTES + 4 * B_WAVE;
-  static constexpr int STAGE = M_OFF + 4 * M_WAVE;
-  static constexpr int VM = TM + 2 * TN + 1;          // copies per wave per group
-};
-
-template <int TM, int TN>
-__device__ __forceinline__ void pipe_dequant(const int8_t *__restrict__ stage, int wave, int lane,
-                                             v4i (&b)[4][TN]) {
-  using Lay = PipeLayout<TM, TN>;
-  const int8_t *bw = stage + Lay::B_OFF + wave * Lay::B_WAVE;
-  const uint16_t *mw = reinterpret_cast<const uint16_t *>(stage + Lay::M_OFF + wave * Lay::M_WAVE);
-  const int c32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int sl = 2 * tn + (c32 >> 4);                 // local strip of this lane's column
-    const uint4 p0 = *reinterpret_cast<const uint4 *>(bw + sl * 1024 + 16 * (16 * hi + (lane & 15)));
-    const uint4 p1 = *reinterpret_cast<const uint4 *>(bw + sl * 1024 + 16 * (32 + 16 * hi + (lane & 15)));
-    const GroupConsts g = group_consts(mw[sl * 16 + (lane & 15)]);
-    dequant_lane(p0, g, b[0][tn], b[2][tn]);
-    dequant_lane(p1, g, b[1][tn], b[3][tn]);
-  }
-}
-
-template <int TM, int TN>
-__device__ __forceinline__ void pipe_mfma(const int8_t *__restrict__ stage, int lane, const v4i (&b)[4][TN],
-                                          v16i (&acc)[TM][TN]) {
-  const int r = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int row = 32 * tm + r;
-      const v4i a = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * kb + hi) ^ ((row >> 1) & 7)));
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(a, b[kb][tn], acc[tm][tn]);
-    }
-}
-
-template <int TM, int TN, int S, int OCC, int OUT>
-__global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(const int8_t *__restrict__ qx,
-                                                           const __half *__restrict__ sx,
-                                                           const uint4 *__restrict__ packed,
-                                                           const uint16_t *__restrict__ meta,
-                                                           const __half *__restrict__ sw, void *__restrict__ out,
-                                                           int M, int N, int K, int, int *) {
-  using Lay = PipeLayout<TM, TN>;
-  static_assert(S >= 3, "groups j and j+1 must be resident while j+S-1 is copied");
-  constexpr int BM = Lay::BM;
-  extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = K >> 7;
-  const int NS = N >> 4;
-  const int nx = (NS + 8 * TN - 1) / (8 * TN);
-  const int ny = (M + BM - 1) / BM;
-  int tx, ty;
-  tile_coords(blockIdx.x, nx, ny, tx, ty);
-  const int m0 = ty * BM;
-  const int s0 = (tx * 4 + wave) * 2 * TN;   // first strip of this wave
-
-  // A copies: wave w moves rows 8*(w*TM + i) .. +7; lane l lands at position l & 7
-  // of row 8*(w*TM + i) + (l >> 3), so it reads chunk ((l & 7) ^ ((row >> 1) & 7))
-  // of that row (rows past M re-read row M-1; their results are never stored)
-  const int8_t *asrc[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = 8 * (wave * TM + i) + (lane >> 3);
-    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
-  }
-  // B copies: one 1 KB chunk per strip (lane l copies slot l); strips past N repeat
-  // the last strip (results dropped at the store)
-  const uint4 *bsrc[2 * TN];
-#pragma unroll
-  for (int t = 0; t < 2 * TN; ++t)
-    bsrc[t] = packed + static_cast<size_t>(min(s0 + t, NS - 1)) * G * 64 + lane;
-  // metadata: lanes 8t .. 8t+7 copy the 32 bytes of strip t (t < 2*TN); the other
-  // lanes repeat strip 0
-  const int mt_strip = (lane >> 3) < 2 * TN ? (lane >> 3) : 0;
-  const unsigned *msrc = reinterpret_cast<const unsigned *>(meta + static_cast<size_t>(min(s0 + mt_strip, NS - 1)) *
-                                                                       G * 16) + (lane & 7);
-
-  auto issue = [&](int j, int stage) {
-    int8_t *st = lds + stage * Lay::STAGE;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(asrc[i] + 128 * j), (lds_void_t *)(st + 1024 * (wave * TM + i)),
-                                       16, 0, 0);
-#pragma unroll
-    for (int t = 0; t < 2 * TN; ++t)
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(bsrc[t] + static_cast<size_t>(j) * 64),
-                                       (lds_void_t *)(st + Lay::B_OFF + wave * Lay::B_WAVE + 1024 * t), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(msrc + static_cast<size_t>(j) * 8),
-                                     (lds_void_t *)(st + Lay::M_OFF + wave * Lay::M_WAVE), 4, 0, 0);
-  };
-
-  v16i acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
-
-  // prologue: groups 0 .. S-2 in order (the same per-group sequence as the loop)
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(min(st, G - 1), st);
-  v4i bc[4][TN], bn[4][TN];
-  QOQ_WAIT_VMCNT(Lay::VM * (S - 2));           // group 0 resident
-  __builtin_amdgcn_s_barrier();
-  pipe_dequant<TM, TN>(lds, wave, lane, bc);
-
-  for (int j = 0; j < G; ++j) {
-    // groups j and j+1 resident: copies of S-3 later groups may still be in flight
-    QOQ_WAIT_VMCNT(Lay::VM * (S - 3));
-    __builtin_amdgcn_s_barrier();
-    // stage (j+S-1) % S == (j-1) % S: everyone finished reading it before the barrier
-    issue(min(j + S - 1, G - 1), (j + S - 1) % S);
-    pipe_dequant<TM, TN>(lds + ((j + 1) % S) * Lay::STAGE, wave, lane, bn);
-    pipe_mfma<TM, TN>(lds + (j % S) * Lay::STAGE, lane, bc, acc);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) bc[kb][tn] = bn[kb][tn];
-  }
-  QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
-  __syncthreads();                              // every wave is done with the ring
-  static_assert(4 * 32 * (64 * TN + 16) <= S * Lay::STAGE, "epilogue scratch exceeds the ring");
-  epilogue32<TM, TN, OUT>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
-}
-
-template <int TM, int TN, int S>
-constexpr int pipe_lds_bytes() {
-  return S * PipeLayout<TM, TN>::STAGE;
-}
-
 // ---------------------------------------------------------------------------
 // Large-M regime, A by copy engine and B by two register sets (32x32x32 MFMA).
 // Four waves side by side along N as above.  A (BM rows x 128 per group) is copied
-// global -> LDS with global_load_lds into a 3-stage ring (chunks of row r at
-// position chunk ^ ((r >> 1) & 7), bank-conflict free for 16-lane phases), so it
-// costs no registers and no LDS-write instructions.  The packed codes of group j+2
+// global -> LDS with global_load_lds into a 3-stage ring, so it costs no registers
+// and no LDS-write instructions.  The 16-byte chunks of row r are stored at
+// position chunk ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 bytes per cycle
+// over 64 banks, two 128-byte rows per bank row, so the 16 rows one phase of an
+// A-operand read touches land in 16 distinct bank groups.  The packed codes of group j+2
 // are loaded into the register set group j just consumed (loop unrolled by two; a
 // prefetched register is never copied, so the compiler can wait for exactly the
 // loads it needs).  A fragments are read one k block ahead of the MFMAs that use
@@ -898,6 +487,15 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
     dequant_lane(cur.p0[tn], g, b[0][tn], b[2][tn]);
     dequant_lane(cur.p1[tn], g, b[1][tn], b[3][tn]);
   }
+  // The codes die here.  The empty volatile asm consumes every dequantized value,
+  // so instruction selection cannot move any of the dequantization below the loads
+  // that refill the same set; otherwise the allocator keeps old and new codes in
+  // different registers and copies them at the loop edge, which makes the wave wait
+  // for those loads there.
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) asm volatile("" ::"v"(b[kb][tn]));
   __builtin_amdgcn_sched_barrier(0);
   // group j+2: A copies into ring stage (j+2) % 3 (held group j-1, finished before
   // the last barrier), then the codes into the set just consumed
@@ -1083,27 +681,19 @@ typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const 
                            void *, int, int, int, int, int *);
 
 struct Config {
-  int kind;                 // 0 skinny, 1 tiled (16x16x64), 2 wide (32x32x32), 3 pipelined
-  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    tiled / wide: TM, TN    pipelined: TM, TN, S
+  int kind;                 // 0 skinny, 4 wide2, 5 dma2
+  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    wide2 / dma2: TM, TN (c = d = 0)
   GemmKernel k[2];          // fp16 epilogue, INT32 epilogue
   const char *name;
-  int lds;                  // dynamic LDS bytes
 };
 
 #define QOQ_SKINNY(MT, NBW, W, U)                                                                   \
   {0, MT, NBW, W, U, {gemm_skinny_kernel<MT, NBW, W, U, 0>, gemm_skinny_kernel<MT, NBW, W, U, 1>}, \
-   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U, 0},
-#define QOQ_TILED(TM, TN) \
-  {1, TM, TN, 0, 0, {gemm_tiled_kernel<TM, TN, 0>, gemm_tiled_kernel<TM, TN, 1>}, "tiled_tm" #TM "_tn" #TN, 0},
-#define QOQ_PIPE(TM, TN, S, OCC)                                                                     \
-  {3, TM, TN, S, OCC, {gemm_pipe_kernel<TM, TN, S, OCC, 0>, gemm_pipe_kernel<TM, TN, S, OCC, 1>},      \
-   "pipe_tm" #TM "_tn" #TN "_s" #S "_o" #OCC, pipe_lds_bytes<TM, TN, S>()},
-#define QOQ_DMA2(TM, TN) \
-  {5, TM, TN, 0, 0, {gemm_dma2_kernel<TM, TN, 0>, gemm_dma2_kernel<TM, TN, 1>}, "dma2_tm" #TM "_tn" #TN, 0},
+   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U},
 #define QOQ_WIDE2(TM, TN) \
-  {4, TM, TN, 0, 0, {gemm_wide2_kernel<TM, TN, 0>, gemm_wide2_kernel<TM, TN, 1>}, "wide2_tm" #TM "_tn" #TN, 0},
-#define QOQ_WIDE(TM, TN) \
-  {2, TM, TN, 0, 0, {gemm_wide_kernel<TM, TN, 0>, gemm_wide_kernel<TM, TN, 1>}, "wide_tm" #TM "_tn" #TN, 0},
+  {4, TM, TN, 0, 0, {gemm_wide2_kernel<TM, TN, 0>, gemm_wide2_kernel<TM, TN, 1>}, "wide2_tm" #TM "_tn" #TN},
+#define QOQ_DMA2(TM, TN) \
+  {5, TM, TN, 0, 0, {gemm_dma2_kernel<TM, TN, 0>, gemm_dma2_kernel<TM, TN, 1>}, "dma2_tm" #TM "_tn" #TN},
 
 const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
@@ -1111,19 +701,15 @@ const Config kConfigs[] = {
     QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(3, 2, 8, 2)
     QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(4, 2, 8, 1)
-    QOQ_TILED(4, 2) QOQ_TILED(4, 4) QOQ_TILED(8, 2) QOQ_TILED(8, 4) QOQ_TILED(16, 2)
-    QOQ_WIDE(2, 1) QOQ_WIDE(2, 2) QOQ_WIDE(4, 1) QOQ_WIDE(4, 2) QOQ_WIDE(8, 1)
-    QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1) QOQ_WIDE2(4, 2) QOQ_WIDE2(8, 1)
+    QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
-    QOQ_PIPE(4, 2, 4, 1) QOQ_PIPE(4, 2, 3, 1) QOQ_PIPE(2, 2, 3, 2) QOQ_PIPE(4, 1, 3, 2) QOQ_PIPE(2, 1, 3, 3)
-    QOQ_PIPE(2, 1, 4, 2) QOQ_PIPE(4, 1, 4, 1)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 const Config *find_config(int kind, int a, int b, int c, int d) {
   for (int i = 0; i < kNumConfigs; ++i) {
     const Config &cf = kConfigs[i];
-    if (cf.kind == kind && cf.a == a && cf.b == b && (kind != 0 && kind != 3 || (cf.c == c && cf.d == d)))
+    if (cf.kind == kind && cf.a == a && cf.b == b && cf.c == c && cf.d == d)
       return &cf;
   }
   return nullptr;
@@ -1218,16 +804,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     const int mt = cfg->a, nbw = cfg->b, waves = cfg->c;
     p.grid = dim3(static_cast<unsigned>((NS + nbw - 1) / nbw), static_cast<unsigned>((M + 16 * mt - 1) / (16 * mt)));
     p.block = dim3(64 * waves);
-  } else if (cfg->kind == 1) {
-    const int tm = cfg->a, tn = cfg->b;
-    const int64_t nx = (NS + 4 * tn - 1) / (4 * tn), ny = (M + 16 * tm - 1) / (16 * tm);
-    p.grid = dim3(static_cast<unsigned>(nx * ny));
-    p.block = dim3(256);
-  } else {   // wide and pipelined: 32-row blocks, 4 waves x 2*TN strips
+  } else {   // wide2 / dma2: 32-row blocks, 4 waves x 2*TN strips
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
     const int64_t tiles = nx * ny;
-    if ((cfg->kind == 4 || cfg->kind == 5) && (split_k || getenv("QOQ_GEMM_SPLITS"))) {
+    if (split_k || getenv("QOQ_GEMM_SPLITS")) {
       p.splits = choose_splits(tiles, G);
       if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     }
@@ -1239,24 +820,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-// Kernels whose LDS ring exceeds the default dynamic-LDS limit are granted their
-// size once per process (HIP keeps the attribute per kernel for the device).
-std::once_flag g_lds_once[kNumConfigs][2];
-
-void ensure_lds_attribute(const Config *cfg, int out_kind) {
-  if (cfg->lds <= 65536) return;
-  const int idx = static_cast<int>(cfg - kConfigs);
-  std::call_once(g_lds_once[idx][out_kind], [cfg, out_kind] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(cfg->k[out_kind]),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, cfg->lds);
-  });
-}
-
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
                       void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
   const Plan p = make_plan(M, N, K);
-  ensure_lds_attribute(p.cfg, out_kind);
-  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
+  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
                      static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), out,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.splits,

@@ -110,7 +110,9 @@ def test_workspace_validation(L):
 def test_workspace_and_plan():
     assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
     assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
-    assert qoq.gemm_plan(4096, 28672, 4096) == "dma2_tm4_tn2"
+    assert qoq.gemm_plan(4096, 28672, 4096) == "sd_as2"
+    assert qoq.gemm_plan(4096, 4096, 14336) == "sd_as2"
+    assert qoq.gemm_plan(1024, 4096, 14336) == "dma2_tm4_tn2"
     assert qoq.gemm_plan(1, 17, 4096) == "invalid"
     assert qoq.gemm_plan(0, 16, 128) == "invalid"
 

@@ -295,7 +295,7 @@ def test_every_config_exact(gpu, config):
 
 
 def _split_configs():
-    return [c for c in _all_configs() if c.startswith(("wide2", "dma2"))]
+    return [c for c in _all_configs() if c.startswith(("wide2", "dma2", "sd_"))]
 
 
 @pytest.mark.parametrize("config", _split_configs())

@@ -23,6 +23,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace qoq {
 
@@ -451,6 +452,8 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima): gfx9 encoding
 #define QOQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+// lgkmcnt(0) only (LDS writes of this wave done; vmcnt and expcnt at their maxima)
+#define QOQ_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 // ---------------------------------------------------------------------------
 // Large-M regime, A by copy engine and B by two register sets (32x32x32 MFMA).
@@ -642,6 +645,219 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
 }
 
 // ---------------------------------------------------------------------------
+// Large-M regime, shared dequantization (32x32x32 INT8 MFMA).  The dequantization
+// work per MFMA falls with the number of rows that reuse each dequantized weight;
+// the register budget of two waves per SIMD caps a wave's tile, so here the rows
+// are spread over waves and the weights are dequantized once per workgroup and
+// shared through LDS:
+//   workgroup = 8 waves (two per SIMD), tile 256 rows x 256 columns; wave w
+//   computes rows 64*(w & 3) .. +63 and columns 128*(w >> 2) .. +127 (TM = 2,
+//   TN = 4) and dequantizes column block w (32 columns, two strips) for the whole
+//   workgroup, writing its B fragments to LDS in MFMA operand order
+//   (bbuf[block][k block][lane], 16 bytes each: every read and write is 64 lanes x
+//   16 contiguous bytes).
+//   A (256 x 128 per group) comes by copy engine into an AS-stage ring with the
+//   row-pair XOR swizzle; each wave reads only its own 64 rows.
+//   Per group j: dequantize j+1 (codes loaded two groups earlier) into B buffer
+//   (j+1) & 1; copy A(j+AS-1) and load the codes of j+3 into the register set just
+//   consumed; MFMAs of j from A stage j % AS and B buffer j & 1; wait for A(j+1);
+//   barrier (which also publishes B(j+1)).
+// ---------------------------------------------------------------------------
+constexpr int kSdStageA = 256 * 128;             // A bytes per stage
+constexpr int kSdBufB = 8 * 4 * 1024;            // dequantized B bytes per group
+
+template <int AS>
+constexpr int sd_lds_bytes() {
+  return AS * kSdStageA + 2 * kSdBufB;
+}
+
+struct SdCodes {
+  uint4 p0, p1;
+  unsigned md;
+};
+
+__device__ __forceinline__ void sd_load_codes(SdCodes &c, const uint4 *__restrict__ packed,
+                                              const uint16_t *__restrict__ meta, unsigned boff, unsigned moff,
+                                              int j) {
+  const uint4 *pj = packed + static_cast<size_t>(j) * 64;
+  c.p0 = pj[boff];
+  c.p1 = pj[boff + 32];
+  c.md = meta[static_cast<size_t>(j) * 16 + moff];
+}
+
+template <int AS>
+__device__ __forceinline__ void sd_copy_a(int j, int8_t *__restrict__ lds, const int8_t *const (&asrc)[4],
+                                          int wave) {
+  int8_t *st = lds + (j % AS) * kSdStageA;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(asrc[i] + 128 * j), (lds_void_t *)(st + 1024 * (wave * 4 + i)),
+                                     16, 0, 0);
+}
+
+template <int Q>
+__device__ __forceinline__ void sd_dequant(int8_t *__restrict__ bbuf, int wave, int lane, const SdCodes &cur) {
+  const GroupConsts g = group_consts(cur.md);
+  v4i b[4];
+  dequant_lane(cur.p0, g, b[0], b[2]);
+  dequant_lane(cur.p1, g, b[1], b[3]);
+  int8_t *dst = bbuf + (Q ^ 1) * kSdBufB + wave * 4096 + 16 * lane;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
+}
+
+template <int AS, int Q>
+__device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, int wave, int lane,
+                                        v16i (&acc)[2][4]) {
+  const int8_t *stage = lds + (j % AS) * kSdStageA;
+  const int8_t *bj = lds + AS * kSdStageA + Q * kSdBufB + (wave >> 2) * 4 * 4096 + 16 * lane;
+  const int r = lane & 31, hi = lane >> 5;
+  const int rbase = 64 * (wave & 3);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    v4i a[2], bf[4];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = rbase + 32 * tm + r;
+      a[tm] = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * kb + hi) ^ ((row >> 1) & 7)));
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096 + 1024 * kb);
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32x32x32(a[tm], bf[tn], acc[tm][tn]);
+  }
+}
+
+// One group.  Waves w and w + 4 share a SIMD and meet at the same barriers, so
+// they run the step's two phases in opposite orders (MF = MFMAs first for waves
+// 4..7): while one dequantizes (vector ALU) the other issues MFMAs, and the two
+// units work side by side.
+template <int AS, int Q, bool MF>
+__device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, int wave, int lane,
+                                        const int8_t *const (&asrc)[4], SdCodes &cur,
+                                        const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                        unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
+  int8_t *bbuf = lds + AS * kSdStageA;
+  if constexpr (MF) {
+    sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // group j+1 is dequantized from this set (loaded two groups ago) into B buffer
+  // (j+1) & 1, which every wave finished reading before the last barrier; then the
+  // set is refilled with group j+3's codes and group j+AS-1's A copies are issued
+  // (its stage held group j-1)
+  sd_dequant<Q>(bbuf, wave, lane, cur);
+  __builtin_amdgcn_sched_barrier(0);
+  sd_copy_a<AS>(min(j + AS - 1, G - 1), lds, asrc, wave);
+  sd_load_codes(cur, packed, meta, boff, moff, min(j + 3, G - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!MF) {
+    sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // A(j+1) must be resident.  AS == 3: it was copied one step ago and since then
+  // the codes of j+2 (3 loads), this step's 4 copies and 3 loads were issued;
+  // AS == 2: it is this step's copies, followed only by this step's 3 loads.
+  QOQ_WAIT_VMCNT(AS == 3 ? 10 : 3);
+  QOQ_WAIT_LGKMCNT0();                          // this wave's B(j+1) fragments are in LDS
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int AS, bool MF>
+__device__ __forceinline__ void sd_loop(int G, int8_t *__restrict__ lds, int wave, int lane,
+                                        const int8_t *const (&asrc)[4], SdCodes &set0, SdCodes &set1,
+                                        const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                        unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
+  int j = 0;
+  for (; j + 1 < G; j += 2) {
+    sd_step<AS, 0, MF>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF>(j + 1, G, lds, wave, lane, asrc, set0, packed, meta, boff, moff, acc);
+  }
+  if (j < G) sd_step<AS, 0, MF>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
+}
+
+template <int AS, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restrict__ qx,
+                                                        const __half *__restrict__ sx,
+                                                        const uint4 *__restrict__ packed,
+                                                        const uint16_t *__restrict__ meta,
+                                                        const __half *__restrict__ sw, void *__restrict__ out,
+                                                        int M, int N, int K, int splits, int *__restrict__ ws) {
+  static_assert(AS == 2 || AS == 3, "two or three A stages");
+  extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, hi = lane >> 5;
+  const int Gs = K >> 7;
+  const int NS = N >> 4;
+  const int nx = (NS + 15) / 16;
+  const int ny = (M + 255) / 256;
+  int tx, ty, split;
+  split_coords(blockIdx.x, nx, ny, splits, tx, ty, split);
+  const int g0 = split * Gs / splits;
+  const int G = (split + 1) * Gs / splits - g0;   // groups of this split (>= 1)
+  const int m0 = ty * 256;
+
+  // A copies: wave w moves rows 8*(4w + i) .. +7 of the 256-row stage
+  const int8_t *asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (wave * 4 + i) + (lane >> 3);
+    asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 128 * g0 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
+  // codes of column block `wave`: strip 16*tx + 2*wave + (c32 >> 4), slots 16*hi + c
+  // (k blocks 0, 2) and 32 + 16*hi + c (k blocks 1, 3); strips past N repeat the last
+  const unsigned strip = static_cast<unsigned>(min(16 * tx + 2 * wave + (c32 >> 4), NS - 1));
+  const unsigned boff = (strip * static_cast<unsigned>(Gs) + g0) * 64u + 16u * hi + (lane & 15);
+  const unsigned moff = (strip * static_cast<unsigned>(Gs) + g0) * 16u + (lane & 15);
+
+  v16i acc[2][4];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = v16i{};
+
+  // prologue: A(0) .. A(AS-2); codes 0 and 1; dequantize group 0 into B buffer 0;
+  // codes of group 2 into the set just consumed
+  for (int g = 0; g < AS - 1; ++g) sd_copy_a<AS>(min(g, G - 1), lds, asrc, wave);
+  SdCodes set0, set1;
+  sd_load_codes(set0, packed, meta, boff, moff, 0);
+  sd_load_codes(set1, packed, meta, boff, moff, min(1, G - 1));
+  {
+    const GroupConsts g = group_consts(set0.md);
+    v4i b[4];
+    dequant_lane(set0.p0, g, b[0], b[2]);
+    dequant_lane(set0.p1, g, b[1], b[3]);
+    int8_t *dst = lds + AS * kSdStageA + wave * 4096 + 16 * lane;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
+  }
+  sd_load_codes(set0, packed, meta, boff, moff, min(2, G - 1));
+  QOQ_WAIT_VMCNT(0);
+  __syncthreads();
+
+  if (wave < 4)
+    sd_loop<AS, false>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+  else
+    sd_loop<AS, true>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+  QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
+  __syncthreads();
+  const int wm0 = m0 + 64 * (wave & 3);
+  const int wn0 = 16 * (16 * tx + 8 * (wave >> 2));   // first column of this wave
+  if (splits > 1) {                             // partial sums of this split -> workspace slice
+    epilogue32<2, 4, 1>(acc, nullptr, lane, wm0, wn0, M, N, nullptr, nullptr,
+                        ws + static_cast<size_t>(split) * M * N);
+    return;
+  }
+  static_assert(8 * 32 * (64 * 4 + 16) <= sd_lds_bytes<AS>(), "epilogue scratch exceeds the LDS in use");
+  epilogue32<2, 4, OUT>(acc, lds + wave * 32 * (64 * 4 + 16), lane, wm0, wn0, M, N, sx, sw, out);
+}
+
+// ---------------------------------------------------------------------------
 // Second pass of split-K: out[m, n] = epilogue(sum_s part[s][m][n]).  Each thread
 // takes 8 consecutive columns of one row (N % 16 == 0, so they never cross a row):
 // two 16-byte loads per slice, one 16-byte fp16 store (or two INT32 stores).
@@ -681,10 +897,11 @@ typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const 
                            void *, int, int, int, int, int *);
 
 struct Config {
-  int kind;                 // 0 skinny, 4 wide2, 5 dma2
-  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    wide2 / dma2: TM, TN (c = d = 0)
+  int kind;                 // 0 skinny, 4 wide2, 5 dma2, 6 shared dequantization
+  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    wide2 / dma2: TM, TN    sd: A stages
   GemmKernel k[2];          // fp16 epilogue, INT32 epilogue
   const char *name;
+  int lds = 0;              // dynamic LDS bytes
 };
 
 #define QOQ_SKINNY(MT, NBW, W, U)                                                                   \
@@ -694,6 +911,7 @@ struct Config {
   {4, TM, TN, 0, 0, {gemm_wide2_kernel<TM, TN, 0>, gemm_wide2_kernel<TM, TN, 1>}, "wide2_tm" #TM "_tn" #TN},
 #define QOQ_DMA2(TM, TN) \
   {5, TM, TN, 0, 0, {gemm_dma2_kernel<TM, TN, 0>, gemm_dma2_kernel<TM, TN, 1>}, "dma2_tm" #TM "_tn" #TN},
+#define QOQ_SD(AS) {6, AS, 0, 0, 0, {gemm_sd_kernel<AS, 0>, gemm_sd_kernel<AS, 1>}, "sd_as" #AS, sd_lds_bytes<AS>()},
 
 const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
@@ -703,6 +921,7 @@ const Config kConfigs[] = {
     QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(4, 2, 8, 1)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
+    QOQ_SD(2) QOQ_SD(3)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -751,6 +970,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
+  const int64_t tsd = ((NS + 15) / 16) * ((M + 255) / 256);    // 256 x 256 tiles
   bool split_k = true;   // may the plan split K (kinds 4 and 5)
   if (!cfg) {
     const char *force = getenv("QOQ_GEMM_REGIME");
@@ -777,10 +997,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
       }
     } else {
       // measured on MI355X over the layer shapes of the workloads: the largest tile
-      // that still gives enough workgroups to fill the chip; when no tile size does
-      // (few columns, long K), split K over about 512 workgroups
+      // that still gives enough workgroups to fill the chip (256 x 256 tiles share
+      // each dequantized weight over 256 rows); when no tile size does (few
+      // columns, long K), split K over about 512 workgroups
       split_k = true;
-      if (t256 >= 384) {
+      if (tsd >= 256) {
+        cfg = find_config(6, 2, 0, 0, 0);       // 256 x 256, shared dequantization
+        split_k = false;
+      } else if (t256 >= 384) {
         cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256
         split_k = false;
       } else if (t128 >= 320) {
@@ -804,6 +1028,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     const int mt = cfg->a, nbw = cfg->b, waves = cfg->c;
     p.grid = dim3(static_cast<unsigned>((NS + nbw - 1) / nbw), static_cast<unsigned>((M + 16 * mt - 1) / (16 * mt)));
     p.block = dim3(64 * waves);
+  } else if (cfg->kind == 6) {   // 256 x 256 tiles, 8 waves
+    const int64_t tiles = ((NS + 15) / 16) * ((M + 255) / 256);
+    if (split_k || getenv("QOQ_GEMM_SPLITS")) {
+      p.splits = choose_splits(tiles, G);
+      if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
+    }
+    p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
+    p.block = dim3(512);
   } else {   // wide2 / dma2: 32-row blocks, 4 waves x 2*TN strips
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
@@ -820,10 +1052,24 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+// Kernels with more than 64 KB of dynamic LDS are granted their size once per
+// process (the attribute is kept per kernel).
+std::once_flag g_lds_once[kNumConfigs][2];
+
+void ensure_lds_attribute(const Config *cfg, int out_kind) {
+  if (cfg->lds <= 65536) return;
+  const int idx = static_cast<int>(cfg - kConfigs);
+  std::call_once(g_lds_once[idx][out_kind], [cfg, out_kind] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(cfg->k[out_kind]),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, cfg->lds);
+  });
+}
+
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
                       void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
   const Plan p = make_plan(M, N, K);
-  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
+  ensure_lds_attribute(p.cfg, out_kind);
+  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
                      static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), out,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.splits,

@@ -130,6 +130,38 @@ int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group
                       int32_t *acc_i32, int64_t M, int64_t N, int64_t K, int32_t group,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace in bytes qoq_w4a8_linear needs for this problem: 0 when the fused
+ * kernel serves it (M <= 16 and K <= 8192), otherwise room for qx (M*K bytes) and
+ * s_X (2*M bytes), each rounded up to 256 bytes, plus qoq_gemm_workspace_bytes.
+ * Errors: INVALID, UNSUPPORTED. */
+int qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes);
+
+/* The runtime step in one call: per-token activation quantization followed by the
+ * W4A8 GEMM with its fp16 epilogue — the same arithmetic, codes, scales and fp16
+ * results as qoq_quantize_activations + qoq_w4a8_gemm ("QServe ..." summary: the
+ * activation quantization is fused into the kernel that feeds the GEMM, so it costs
+ * no pass of its own).  For M <= 16 and K <= 8192 one kernel does both: each
+ * workgroup quantizes the token rows into LDS and runs the GEMM on them.
+ * x_fp16 [M,K] row-major fp16 (16-byte aligned); packed_w / group_meta / s_w_fp16 as
+ * for qoq_w4a8_gemm; out_fp16 [M,N] (16-byte aligned); s_x_fp16: NULL, or [M] fp16
+ * that receives the token scales.  workspace: caller-owned device memory of
+ * qoq_linear_workspace_bytes (may be NULL when that is 0), 256-byte aligned, no
+ * initialization needed; calls that may run concurrently need separate workspaces.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
+int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_meta,
+                    const void *s_w_fp16, void *out_fp16, void *s_x_fp16, int64_t M, int64_t N,
+                    int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Name of the kernel configuration qoq_w4a8_linear uses for this shape: a fused
+ * configuration, or the qoq_gemm_plan name when it quantizes and multiplies in two
+ * kernels ("invalid" for a shape it rejects).  QOQ_LINEAR_CONFIG=<fused name> or
+ * "unfused" in the environment forces the choice where the shape allows it. */
+const char *qoq_linear_plan(int64_t M, int64_t N, int64_t K);
+
+/* Name of the index-th fused linear configuration, NULL past the last. */
+const char *qoq_linear_config_name(int index);
+
 /* Name of the kernel configuration qoq_w4a8_gemm launches for this shape (static
  * string, "invalid" for a shape the GEMM rejects).  Used to match profiler output. */
 const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K);

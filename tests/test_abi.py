@@ -181,3 +181,52 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((4, 256), dtype=torch.float16)
     with pytest.raises(TypeError):
         qoq.quantize_activations(x)
+
+
+def test_linear_plan_and_workspace(monkeypatch):
+    """Fused linear for a few tokens and K <= 8192 (no workspace); two kernels
+    otherwise, with room for qx and s_X before the GEMM's own workspace."""
+    fused = qoq.linear_configs()
+    assert len(fused) >= 2
+    assert qoq.linear_plan(1, 6144, 4096) in fused
+    assert qoq.linear_plan(8, 512, 512) in fused
+    assert qoq.linear_workspace_bytes(1, 6144, 4096) == 0
+    assert qoq.linear_plan(1, 59136, 8192) == qoq.gemm_plan(1, 59136, 8192)     # too much repeated work
+    assert qoq.linear_plan(16, 6144, 4096) == qoq.gemm_plan(16, 6144, 4096)
+    assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_plan(17, 6144, 4096)
+    assert qoq.linear_plan(1, 4096, 14336) == qoq.gemm_plan(1, 4096, 14336)   # K beyond the fused limit
+    r256 = lambda v: (v + 255) // 256 * 256
+    for M, N, K in [(17, 6144, 4096), (256, 4096, 14336), (1, 4096, 14336), (64, 28672, 4096)]:
+        assert qoq.linear_workspace_bytes(M, N, K) == r256(M * K) + r256(2 * M) + qoq.gemm_workspace_bytes(M, N, K)
+    assert qoq.linear_workspace_bytes(0, 6144, 4096) == 0
+    assert qoq.linear_plan(0, 6144, 4096) == "invalid"
+    monkeypatch.setenv("QOQ_LINEAR_CONFIG", "unfused")
+    assert qoq.linear_plan(1, 6144, 4096) == qoq.gemm_plan(1, 6144, 4096)
+    assert qoq.linear_workspace_bytes(1, 6144, 4096) == 4096 + 256
+    for name in fused:                             # forced: any shape the kernel can hold
+        monkeypatch.setenv("QOQ_LINEAR_CONFIG", name)
+        assert qoq.linear_plan(4, 6144, 4096) == name
+        assert qoq.linear_plan(8, 6144, 2048) == name
+        assert qoq.linear_plan(1, 59136, 8192) == name
+        assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_plan(17, 6144, 4096)
+
+
+def test_linear_validation(L):
+    f = L.qoq_w4a8_linear
+    a = lambda x=FAKE, pw=FAKE, md=FAKE, sw=FAKE, out=FAKE, sx=NUL, M=4, N=32, K=256, g=128, ws=NUL, wb=0: (
+        x, pw, md, sw, out, sx, M, N, K, g, ws, wb, NUL)
+    assert f(*a(g=64)) == UNSUPPORTED
+    assert f(*a(N=40)) == INVALID
+    assert f(*a(K=200)) == INVALID
+    assert f(*a(M=-1)) == INVALID
+    assert f(*a(M=0, x=NUL, out=NUL)) == OK
+    assert f(*a(x=NUL)) == INVALID
+    assert f(*a(sw=NUL)) == INVALID
+    assert f(*a(x=ODD)) == ALIGNMENT
+    assert f(*a(out=ctypes.c_void_p(0x10008))) == ALIGNMENT
+    assert f(*a(sx=ODD)) == ALIGNMENT
+    M, N, K = 64, 6144, 4096                      # two kernels: needs the workspace
+    need = qoq.linear_workspace_bytes(M, N, K)
+    assert f(*a(M=M, N=N, K=K)) == WORKSPACE
+    assert f(*a(M=M, N=N, K=K, ws=FAKE, wb=need - 1)) == WORKSPACE
+    assert f(*a(M=M, N=N, K=K, ws=ctypes.c_void_p(0x10010), wb=need)) == ALIGNMENT

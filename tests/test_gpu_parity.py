@@ -445,3 +445,71 @@ def test_regimes_agree_on_layer(gpu):
     a1, _ = _gemm_full(gpu, x16, w16, "skinny")
     a2, _ = _gemm_full(gpu, x16, w16, "tiled")
     assert np.array_equal(a1, a2)
+
+
+# ---------------------------------------------------------------------------
+# linear = quantize + GEMM in one call (fused kernel for few tokens)
+# ---------------------------------------------------------------------------
+def _linear(dev, x16, packed, meta, s_w, N, config=None):
+    if config:
+        os.environ["QOQ_LINEAR_CONFIG"] = config
+    try:
+        x = to_dev(x16, dev)
+        s_x = torch.empty(x16.shape[0], dtype=torch.float16, device=dev)
+        out = qoq.w4a8_linear(x, packed, meta, s_w, N, s_x=s_x)
+        return host(out), host(s_x)
+    finally:
+        os.environ.pop("QOQ_LINEAR_CONFIG", None)
+
+
+def _linear_configs():
+    try:
+        return qoq.linear_configs() + ["unfused"]
+    except Exception:
+        return []
+
+
+@pytest.mark.parametrize("config", _linear_configs())
+def test_linear_matches_two_step_and_oracle(gpu, config):
+    """Every linear configuration forced: fp16 output bit-equal to quantize +
+    GEMM through the separate entry points, token scales equal to the
+    quantizer's, and the fp16 output to the oracle; ragged N, K from one group to
+    the fused limit, M from 1 to 16, and two-kernel shapes (M > 16, K > 8192)."""
+    shapes = [(1, 16, 128), (3, 80, 1152), (8, 272, 4096), (16, 48, 8192), (16, 528, 640), (13, 6144, 4096),
+              (17, 80, 1152), (2, 32, 8320), (40, 272, 256)]
+    for (M, N, K) in shapes:
+        say(f"linear config={config} M={M} N={N} K={K} plan={qoq.linear_plan(M, N, K)}")
+        rng = np.random.default_rng(M * 31 + N + K)
+        x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        x16[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+        if M > 2:
+            x16[1] = 0                                   # an all-zero token: s_X = 0, codes 0
+        w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+        packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+        out, sx = _linear(gpu, x16, packed, meta, s_w, N, config)
+        qx_d, sx_d = qoq.quantize_activations(to_dev(x16, gpu))
+        ref = host(qoq.w4a8_gemm(qx_d, sx_d, packed, meta, s_w, N))
+        assert np.array_equal(out.view(np.uint16), ref.view(np.uint16)), (M, N, K)
+        assert np.array_equal(sx.view(np.uint16), host(sx_d).view(np.uint16))
+        r = o.w4a8_reference(x16, w16)
+        check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_linear_layers_sampled(gpu):
+    """The headline decode shapes at full size through the linear entry point, in
+    the launch configuration the library picks, on sampled columns."""
+    L = wl.find("llama3_8b_qkv")
+    w16 = _layer_weights(L.name)
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    for M in L.Ms:
+        say(f"linear {L.name} M={M} plan={qoq.linear_plan(M, L.N, L.K)}")
+        x16 = wl.activations_fp16(L, M)
+        out, sx = _linear(gpu, x16, packed, meta, s_w, L.N)
+        rng = np.random.default_rng(M)
+        cols = np.unique(np.r_[0:16, L.N - 16:L.N, rng.integers(0, L.N, 200)])
+        q0, sw = o.quantize_weights_level0(w16[cols])
+        q, z, s = o.quantize_weights_level1(q0)
+        qx, sxo = o.quantize_activations(x16)
+        want = o.contract(qx, o.dequantize_level1(q, z, s))
+        check_fp16(out[:, cols], want, sxo, sw)
+        assert np.array_equal(sx.view(np.uint16), sxo.view(np.uint16))

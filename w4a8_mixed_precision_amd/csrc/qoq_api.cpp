@@ -138,6 +138,43 @@ const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K) {
   return qoq::gemm_plan_name(M, N, K);
 }
 
+int qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
+  int st = check_gemm(M, N, K, group);
+  if (st != QOQ_OK) return st;
+  if (!bytes) return QOQ_ERR_INVALID;
+  if (M > kMaxDim || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  *bytes = M == 0 ? 0 : qoq::linear_workspace_need(M, N, K);
+  return QOQ_OK;
+}
+
+int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_meta, const void *s_w_fp16,
+                    void *out_fp16, void *s_x_fp16, int64_t M, int64_t N, int64_t K, int32_t group,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_gemm(M, N, K, group);
+  if (st != QOQ_OK) return st;
+  if (M > kMaxDim || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !packed_w || !group_meta || !s_w_fp16 || !out_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 16) || !aligned(out_fp16, 16) ||
+      !aligned(s_w_fp16, 2) || !aligned(s_x_fp16, 2))
+    return QOQ_ERR_ALIGNMENT;
+  const size_t need = qoq::linear_workspace_need(M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QOQ_ERR_ALIGNMENT;
+  }
+  qoq::launch_w4a8_linear(x_fp16, packed_w, group_meta, s_w_fp16, out_fp16, s_x_fp16, M, N, K, workspace,
+                          as_stream(stream));
+  return launch_status();
+}
+
+const char *qoq_linear_plan(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm(M, N, K, 128) != QOQ_OK || M == 0) return "invalid";
+  return qoq::linear_plan_name(M, N, K);
+}
+
+const char *qoq_linear_config_name(int index) { return qoq::linear_config_name(index); }
+
 int qoq_gemm_plan_splits(int64_t M, int64_t N, int64_t K) {
   const int st = check_gemm(M, N, K, 128);
   if (st != QOQ_OK) return st;

@@ -62,6 +62,21 @@ __device__ __forceinline__ int sym_code(float x, float s, float qmax) {
   return static_cast<int>(r);
 }
 
+// 8 fp16 activations (one 16-byte chunk) -> 8 INT8 codes with scale s
+__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s) {
+  unsigned w[4] = {v.x, v.y, v.z, v.w};
+  unsigned out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = half_bits_to_float(w[i] & 0xffffu);
+    float hi = half_bits_to_float(w[i] >> 16);
+    unsigned q0 = static_cast<unsigned>(sym_code(lo, s, kXQmax)) & 0xffu;
+    unsigned q1 = static_cast<unsigned>(sym_code(hi, s, kXQmax)) & 0xffu;
+    out[i >> 1] |= (q0 | (q1 << 8)) << (16 * (i & 1));
+  }
+  return make_uint2(out[0], out[1]);
+}
+
 // ---------------------------------------------------------------------------
 // wave-wide reductions (wave64)
 // ---------------------------------------------------------------------------

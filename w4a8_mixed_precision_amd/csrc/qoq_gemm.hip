@@ -180,6 +180,157 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Few tokens with the activation quantization fused in (the linear entry point,
+// few rows x K).  The workgroup quantizes the token rows itself, with the routines
+// of the standalone quantizer (per-token absmax, fp16 scale, codes), so codes and
+// scales are identical to it, into LDS rows of K + 16 bytes (the 16-byte skew puts
+// the 16 rows one A-fragment read touches in distinct banks), while its first batch
+// of packed weights is in flight; then the skinny main loop runs with A fragments
+// read from LDS.  All threads share the quantization (row absmax by LDS atomics).
+// Every workgroup repeats it, so the fused kernel serves only shapes where that
+// costs less than a launch of its own.  Rows past M are never stored.
+// LDS: 16 fp32 token scales, then M code rows; the same space holds the partial
+// sums of the waves once the main loop is done.
+// ---------------------------------------------------------------------------
+constexpr int kXqMaxK = 8192;                   // LDS: 16 code rows of K + 16 bytes
+constexpr int kXqPerThread = 8;                 // chunks per thread: M * K / 8 <= 8 * threads
+
+template <int NBW, int U>
+struct SkinnyWBatch {
+  uint4 p[U][NBW];
+  unsigned md[U][NBW];
+};
+
+template <int NBW, int WAVES, int U>
+__device__ __forceinline__ void skinny_wload(SkinnyWBatch<NBW, U> &B, int b, int ngroups, int wave,
+                                             const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                             int strip0, int NS, int G, int lane) {
+  const int col = lane & 15;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = b * U + u;
+    const bool ok = t < ngroups;
+    const int j = wave + WAVES * t;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
+      B.p[u][nb] = ok ? packed[chunk * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+      B.md[u][nb] = ok ? static_cast<unsigned>(meta[chunk * 16 + col]) : 0u;
+    }
+  }
+}
+
+template <int NBW, int WAVES, int U>
+constexpr int skinny_xq_red_bytes() {
+  return WAVES * NBW * 4 * 64 * 4;
+}
+
+template <int NBW, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
+    const __half *__restrict__ x, __half *__restrict__ sx_out, const uint4 *__restrict__ packed,
+    const uint16_t *__restrict__ meta, const __half *__restrict__ sw, __half *__restrict__ out, int M, int N,
+    int K) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  float *sxl = reinterpret_cast<float *>(lds);
+  int8_t *qa = lds + 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+  const int strip0 = blockIdx.x * NBW;
+  const int pitch = K + 16;
+
+  const int ngroups = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
+  const int nbatch = (ngroups + U - 1) / U;
+  SkinnyWBatch<NBW, U> cur, nxt;
+  if (nbatch > 0) skinny_wload<NBW, WAVES, U>(cur, 0, ngroups, wave, packed, meta, strip0, NS, G, lane);
+
+  // per-token quantization of the M rows into LDS, shared by all threads: chunk c
+  // (8 halves) of the M x K/8 chunks goes to thread c mod T, kept in registers
+  // between the absmax and the quantization (M * K / 8 <= kXqPerThread * T)
+  constexpr int T = 64 * WAVES;
+  const int nchunk = K >> 3;
+  const int total = M * nchunk;
+  unsigned *rowmax = reinterpret_cast<unsigned *>(lds);          // 16 words, then reused for scales
+  if (threadIdx.x < 16) rowmax[threadIdx.x] = 0u;
+  __syncthreads();
+  uint4 v[kXqPerThread];
+#pragma unroll
+  for (int i = 0; i < kXqPerThread; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + T * i;
+    if (c < total) {
+      const int r = c / nchunk;
+      v[i] = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(r) * K)[c - r * nchunk];
+      atomicMax(&rowmax[r], absmax_bits8(v[i], 0u));
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < static_cast<unsigned>(M)) {
+    const __half sh = sym_scale(rowmax[threadIdx.x], static_cast<float>(kXQmax));
+    if (blockIdx.x == 0 && sx_out) sx_out[threadIdx.x] = sh;
+    sxl[threadIdx.x] = __half2float(sh);                        // overwrites this row's max
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kXqPerThread; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + T * i;
+    if (c < total) {
+      const int r = c / nchunk;
+      *reinterpret_cast<uint2 *>(qa + r * pitch + 8 * (c - r * nchunk)) = quant_chunk8(v[i], sxl[r]);
+    }
+  }
+  __syncthreads();
+
+  v4i acc[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) acc[nb] = v4i{0, 0, 0, 0};
+  const int8_t *arow = qa + min(col, M - 1) * pitch + 16 * kq;   // rows past M repeat row M-1 (never stored)
+  for (int b = 0; b < nbatch; ++b) {
+    if (b + 1 < nbatch) skinny_wload<NBW, WAVES, U>(nxt, b + 1, ngroups, wave, packed, meta, strip0, NS, G, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = b * U + u;
+      const int j = wave + WAVES * min(t, ngroups - 1);       // slots past the end hold zero codes
+      const v4i a0 = *reinterpret_cast<const v4i *>(arow + 128 * j);
+      const v4i a1 = *reinterpret_cast<const v4i *>(arow + 128 * j + 64);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        v4i b0, b1;
+        dequant_lane(cur.p[u][nb], group_consts(cur.md[u][nb]), b0, b1);
+        acc[nb] = mfma16x16x64(a0, b0, acc[nb]);
+        acc[nb] = mfma16x16x64(a1, b1, acc[nb]);
+      }
+    }
+    if (b + 1 < nbatch) cur = nxt;
+  }
+
+  // partial sums of the waves, added through LDS (the code rows are done with)
+  __syncthreads();
+  int *red = reinterpret_cast<int *>(lds + 64);
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * NBW + nb) * 4 + i) * 64 + lane] = acc[nb][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NBW * 256; e += 64 * WAVES) {
+    const int ln = e & 63;
+    const int ti = e >> 6;                        // nb * 4 + i
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[(w * NBW * 4 + ti) * 64 + ln];
+    const int nb = ti >> 2, i = ti & 3;
+    const int m = 4 * (ln >> 4) + i;
+    const int strip = strip0 + nb;
+    if (m < M && strip < NS) {
+      const int n = strip * 16 + (ln & 15);
+      out[static_cast<size_t>(m) * N + n] = mul_round_half(static_cast<float>(sum), sxl[m] * __half2float(sw[n]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Large-M regime (many tokens: INT8 MFMA throughput is the bound), on the 32x32x32
 // INT8 MFMA (the shape that sustains the matrix cores with few accumulators).
 //   workgroup = 4 waves side by side along N: wave w owns 32*TN output columns (TN
@@ -1092,6 +1243,99 @@ size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K) { return make_plan(M
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).splits; }
 
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).cfg->name; }
+
+// ---------------------------------------------------------------------------
+// linear = per-token quantization + GEMM.  M <= 16 and K <= 8192: one fused kernel;
+// otherwise the standalone quantizer writes qx / s_X into the workspace and the
+// GEMM plan runs on them.
+// ---------------------------------------------------------------------------
+typedef void (*XqKernel)(const __half *, __half *, const uint4 *, const uint16_t *, const __half *, __half *, int,
+                         int, int);
+
+struct XqConfig {
+  int nbw, waves;
+  XqKernel k;
+  const char *name;
+  int red;                  // LDS bytes of the partial-sum reduction
+};
+
+#define QOQ_XQ(NBW, W, U)                                                                              \
+  {NBW, W, gemm_skinny_xq_kernel<NBW, W, U>, "skinny_xq_nb" #NBW "_w" #W "_u" #U, \
+   skinny_xq_red_bytes<NBW, W, U>()},
+
+const XqConfig kXqConfigs[] = {QOQ_XQ(1, 16, 2) QOQ_XQ(2, 16, 2) QOQ_XQ(1, 8, 2) QOQ_XQ(2, 8, 2)};
+constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);
+std::once_flag g_xq_once[kNumXq];
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+constexpr int64_t kXqMaxM = 8;              // measured: beyond a few rows the repeated
+constexpr int64_t kXqMaxRepeat = 6 << 20;    // quantization costs more than a launch
+
+bool xq_fits(const XqConfig *c, int64_t M, int64_t K) { return M * (K / 8) <= int64_t{kXqPerThread} * 64 * c->waves; }
+
+// measurement override: QOQ_LINEAR_CONFIG=<fused configuration name> | unfused
+const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
+  if (M > 16 || K > kXqMaxK) return nullptr;      // the kernel's own limits (16 LDS code rows)
+  const char *force = getenv("QOQ_LINEAR_CONFIG");
+  if (force) {
+    if (strcmp(force, "unfused") == 0) return nullptr;
+    for (int i = 0; i < kNumXq; ++i)
+      if (strcmp(kXqConfigs[i].name, force) == 0) return xq_fits(&kXqConfigs[i], M, K) ? &kXqConfigs[i] : nullptr;
+  }
+  if (M > kXqMaxM) return nullptr;
+  // measured on MI355X: two strips per workgroup, 8 waves on wide layers; fused only
+  // while the quantization every workgroup repeats (workgroups x M x K elements)
+  // stays small
+  const int64_t NS = N / 16;
+  const XqConfig *c = NS >= 640 ? &kXqConfigs[3] : &kXqConfigs[1];
+  if ((NS + c->nbw - 1) / c->nbw * M * K > kXqMaxRepeat) return nullptr;
+  return xq_fits(c, M, K) ? c : nullptr;
+}
+
+
+
+int xq_lds_bytes(const XqConfig *c, int64_t M, int64_t K) {
+  return 64 + std::max(static_cast<int>(M * (K + 16)), c->red);
+}
+
+size_t linear_workspace_need(int64_t M, int64_t N, int64_t K) {
+  if (xq_plan(M, N, K)) return 0;
+  return align256(static_cast<size_t>(M) * K) + align256(2 * static_cast<size_t>(M)) + gemm_workspace_need(M, N, K);
+}
+
+const char *linear_plan_name(int64_t M, int64_t N, int64_t K) {
+  const XqConfig *c = xq_plan(M, N, K);
+  return c ? c->name : gemm_plan_name(M, N, K);
+}
+
+void launch_w4a8_linear(const void *x, const void *packed, const void *meta, const void *sw, void *out, void *sx_out,
+                        int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
+  if (const XqConfig *c = xq_plan(M, N, K)) {
+    const int idx = static_cast<int>(c - kXqConfigs);
+    const int lds = xq_lds_bytes(c, M, K);
+    std::call_once(g_xq_once[idx], [c] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(c->k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                64 + 16 * (kXqMaxK + 16));
+    });
+    const int64_t NS = N / 16;
+    hipLaunchKernelGGL(c->k, dim3(static_cast<unsigned>((NS + c->nbw - 1) / c->nbw)), dim3(64 * c->waves), lds, st,
+                       static_cast<const __half *>(x), static_cast<__half *>(sx_out),
+                       static_cast<const uint4 *>(packed), static_cast<const uint16_t *>(meta),
+                       static_cast<const __half *>(sw), static_cast<__half *>(out), static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(K));
+    return;
+  }
+  int8_t *qx = static_cast<int8_t *>(ws);
+  void *sx = sx_out ? sx_out : static_cast<void *>(qx + align256(static_cast<size_t>(M) * K));
+  void *gws = qx + align256(static_cast<size_t>(M) * K) + align256(2 * static_cast<size_t>(M));
+  launch_quantize_activations(x, M, K, qx, sx, st);
+  launch_w4a8_gemm(qx, sx, packed, meta, sw, out, 0, M, N, K, gws, st);
+}
+
+const char *linear_config_name(int index) {
+  return (index >= 0 && index < kNumXq) ? kXqConfigs[index].name : nullptr;
+}
 
 const char *gemm_config_name(int index) {
   return (index >= 0 && index < kNumConfigs) ? kConfigs[index].name : nullptr;

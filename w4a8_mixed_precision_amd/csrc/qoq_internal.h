@@ -21,6 +21,14 @@ void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const 
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K);
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
+
+// linear = quantize + GEMM (fused kernel when M <= 16 and K <= 8192); ws holds at
+// least linear_workspace_need(M, N, K) bytes, 256-byte aligned
+void launch_w4a8_linear(const void *x, const void *packed, const void *meta, const void *sw, void *out,
+                        void *sx_out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream);
+size_t linear_workspace_need(int64_t M, int64_t N, int64_t K);
+const char *linear_plan_name(int64_t M, int64_t N, int64_t K);
+const char *linear_config_name(int index);
 const char *gemm_config_name(int index);
 
 void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, int64_t K, void *w_i8,

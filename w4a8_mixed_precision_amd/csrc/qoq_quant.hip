@@ -20,20 +20,6 @@ namespace qoq {
 constexpr int kActThreads = 256;
 constexpr int kActChunks = 16;   // 16 x 8 halves x 256 threads = rows up to K = 32768
 
-__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s) {
-  unsigned w[4] = {v.x, v.y, v.z, v.w};
-  unsigned out[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo = half_bits_to_float(w[i] & 0xffffu);
-    float hi = half_bits_to_float(w[i] >> 16);
-    unsigned q0 = static_cast<unsigned>(sym_code(lo, s, kXQmax)) & 0xffu;
-    unsigned q1 = static_cast<unsigned>(sym_code(hi, s, kXQmax)) & 0xffu;
-    out[i >> 1] |= (q0 | (q1 << 8)) << (16 * (i & 1));
-  }
-  return make_uint2(out[0], out[1]);
-}
-
 __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half *__restrict__ x, int K,
                                                                    int8_t *__restrict__ qx,
                                                                    __half *__restrict__ sx) {

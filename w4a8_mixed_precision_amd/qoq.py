@@ -40,6 +40,11 @@ _SIGNATURES = {
     "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
                           ctypes.c_int),
     "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_linear_workspace_bytes": ([_c_i64, _c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "qoq_w4a8_linear": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz,
+                         _c_vp], ctypes.c_int),
+    "qoq_linear_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_linear_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_gemm_plan_splits": ([_c_i64, _c_i64, _c_i64], ctypes.c_int),
     "qoq_gemm_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
@@ -299,8 +304,63 @@ def mfma_probe32(a: torch.Tensor, b: torch.Tensor):
 
 
 # ---------------------------------------------------------------------------
-# convenience: the runtime path in one call (two launches)
+# the runtime step in one call: quantize + GEMM (one fused kernel for few tokens)
 # ---------------------------------------------------------------------------
-def w4a8_linear(x: torch.Tensor, packed, meta, s_w, N: int):
-    qx, s_x = quantize_activations(x)
-    return w4a8_gemm(qx, s_x, packed, meta, s_w, N)
+def linear_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    v = _c_sz()
+    _check("qoq_linear_workspace_bytes", lib().qoq_linear_workspace_bytes(M, N, K, group, ctypes.byref(v)))
+    return v.value
+
+
+def linear_plan(M: int, N: int, K: int) -> str:
+    return lib().qoq_linear_plan(M, N, K).decode()
+
+
+def linear_configs() -> list:
+    """Names of the fused linear configurations."""
+    out, i = [], 0
+    while True:
+        n = lib().qoq_linear_config_name(i)
+        if n is None:
+            return out
+        out.append(n.decode())
+        i += 1
+
+
+_linear_workspaces = {}
+
+
+def linear_workspace_for(x: torch.Tensor, M: int, N: int, K: int, group: int = GROUP):
+    """Cached workspace of x's device and current stream for (M, N, K), or None."""
+    need = linear_workspace_bytes(M, N, K, group)
+    if need == 0:
+        return None
+    key = (x.device.index, torch.cuda.current_stream(x.device).cuda_stream)
+    ws = _linear_workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the linear workspace for this shape does not exist yet and cannot be "
+                               "allocated during graph capture: call once before capturing or pass workspace=")
+        ws = torch.empty(max(need, 2 * ws.numel() if ws is not None else 0), dtype=torch.uint8, device=x.device)
+        _linear_workspaces[key] = ws
+    return ws
+
+
+def w4a8_linear(x: torch.Tensor, packed, meta, s_w, N: int, out=None, s_x=None, group: int = GROUP,
+                workspace=None):
+    """out fp16 [M, N] = quantize(x) then the W4A8 GEMM, in one library call.
+    s_x: optional fp16 [M] tensor that receives the token scales."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = linear_workspace_for(_dev_tensor(x, "x"), M, N, K, group)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    sx_ptr = _dev(s_x, "s_x", torch.float16) if s_x is not None else ctypes.c_void_p(0)
+    _check("qoq_w4a8_linear",
+           lib().qoq_w4a8_linear(_dev(x, "x", torch.float16), _dev(packed, "packed", torch.uint8),
+                                 _dev(meta, "meta", torch.int16), _dev(s_w, "s_w", torch.float16),
+                                 _dev(out, "out", torch.float16), sx_ptr, M, N, K, group, ws_ptr, ws_bytes,
+                                 _stream(x)))
+    return out

@@ -1,4 +1,5 @@
-"""CPU oracle for the QoQ W4A8 per-group GEMM.  TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the QoQ W4A8 GEMM (per-group, and the per-channel variant).
+TEST INFRASTRUCTURE ONLY.
 
 This module is the plain, slow, obviously-correct statement of what the GPU path
 computes.  Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
@@ -35,6 +36,14 @@ R5  Level-0 scale s_W = fp16(absmax / 119) (protective range), computed as an IE
 R6  Activations: per-token symmetric INT8 in [-127, 127], s_X = fp16(absmax / 127).
 R7  Epilogue: out = fp16( float32(acc) * (float32(s_X[m]) * float32(s_W[n])) ).
 R8  An all-zero row (or a scale that rounds to fp16 zero) quantizes to code 0.
+R9  Per-channel variant (the format without groups): per output channel asymmetric
+    UINT4 with an integer UINT4 zero and an fp16 scale s_W = fp16((max - min) / 15)
+    over the channel's range widened to contain 0 (R4), fp32 subtract and divide,
+    code q = clamp(z + rne(w / s_W), 0, 15) (R2), z = clamp(rne(-min / s_W), 0, 15).
+R10 Its epilogue term t_X x (z_W ⊙ s_W) takes t_X over the quantized activations,
+    t[m] = sum_k qx[m, k] (so s_X t is the row sum of X_hat = Q_X s_X): the epilogue
+    is then an exact rearrangement of sum_k X_hat W_hat, and the GEMM result is the
+    plain integer contraction sum_k qx (q - z) with the fp16 epilogue of R7.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
 the worked example printed on the pages, exhaustive bound sweeps of the protective
@@ -198,8 +207,8 @@ def epilogue(acc: np.ndarray, s_x16: np.ndarray, s_w16: np.ndarray) -> np.ndarra
 #       meta[(b * G + j) * 16 + c] = s_u8[n, j] | z[n, j] << 8       (uint16)
 #       s_W stays fp16 [N] in natural order.
 # ---------------------------------------------------------------------------
-def pack_weights(q_u4: np.ndarray, z: np.ndarray, s_u8: np.ndarray):
-    """-> (packed uint8 [N*K/2], meta uint16 [N*K/128])."""
+def pack_codes(q_u4: np.ndarray) -> np.ndarray:
+    """UINT4 codes [N, K] -> packed uint8 [N*K/2] in the order above."""
     q = np.asarray(q_u4, dtype=np.uint16)
     n_total, k_total = q.shape
     if n_total % 16 or k_total % GROUP:
@@ -213,7 +222,14 @@ def pack_weights(q_u4: np.ndarray, z: np.ndarray, s_u8: np.ndarray):
     b = off // (1024 * g_total)
     n = 16 * b + c
     k_lo = GROUP * j + 16 * h + i
-    packed = (q[n, k_lo] | (q[n, k_lo + 64] << 4)).astype(np.uint8)
+    return (q[n, k_lo] | (q[n, k_lo + 64] << 4)).astype(np.uint8)
+
+
+def pack_weights(q_u4: np.ndarray, z: np.ndarray, s_u8: np.ndarray):
+    """-> (packed uint8 [N*K/2], meta uint16 [N*K/128])."""
+    packed = pack_codes(q_u4)
+    n_total, k_total = np.asarray(q_u4).shape
+    g_total = k_total // GROUP
 
     moff = np.arange(n_total * g_total, dtype=np.int64)
     mc = moff % 16
@@ -247,4 +263,59 @@ def w4a8_reference(x16: np.ndarray, w16: np.ndarray):
     return {
         "q_s8": q_s8, "s_w": s_w, "q_u4": q_u4, "z": z, "s_u8": s_u8, "w_hat": w_hat,
         "qx": qx, "s_x": s_x, "acc": acc, "ref32": ref32, "out": ref32.astype(np.float16),
+    }
+
+
+# ---------------------------------------------------------------------------
+# O8  per-channel W4A8 (the format without groups): per output channel asymmetric
+#     UINT4 with an integer zero and an fp16 scale
+#     [QServe summary] "整数量化": Q = round(X/s + z), s = (Xmax - Xmin)/(qmax - qmin),
+#     z = round(qmin - Xmin/s), here with one (s, z) per output channel ("逐通道W4A8
+#     GEMM中的快速反量化": the zero point is per channel, so it can leave the main
+#     loop); [Inference chapter] §4.1 asymmetric quantizer; readings R1, R2, R4, R8, R9.
+# ---------------------------------------------------------------------------
+def quantize_weights_per_channel(w16: np.ndarray):
+    """W fp16 [N, K] -> (q_u4 uint8 [N, K], z uint8 [N], s_W fp16 [N])."""
+    w = np.asarray(w16, dtype=np.float16).astype(np.float32)
+    lo = np.minimum(w.min(axis=1), np.float32(0))                   # R4
+    hi = np.maximum(w.max(axis=1), np.float32(0))
+    s_w = ((hi - lo) / np.float32(U4_MAX)).astype(np.float16)     # fp32 subtract, divide; RNE
+    sw = s_w.astype(np.float32)
+    q = np.zeros(w.shape, dtype=np.uint8)
+    z = np.zeros(w.shape[0], dtype=np.uint8)
+    rows = np.nonzero(sw != 0)[0]                                  # R8
+    if rows.size:
+        zr = np.clip(np.rint(-lo[rows] / sw[rows]), 0, U4_MAX)     # z = round(qmin - Xmin/s)
+        qr = np.clip(zr[:, None] + np.rint(w[rows] / sw[rows, None]), 0, U4_MAX)   # R2
+        z[rows] = zr.astype(np.uint8)
+        q[rows] = qr.astype(np.uint8)
+    return q, z, s_w
+
+
+def dequantize_per_channel(q_u4: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """-> (q - z) int16 [N, K], the weight in units of its channel scale s_W."""
+    return np.asarray(q_u4, dtype=np.int16) - np.asarray(z, dtype=np.int16)[:, None]
+
+
+# ---------------------------------------------------------------------------
+# O9  t[m] = sum_k qx[m, k], the activation row sum of the per-channel epilogue
+#     [QServe summary] "逐通道W4A8 GEMM中的快速反量化": the second term becomes
+#     t_X x (z_W ⊙ s_W) with t_X = X 1_k, precomputed by the preceding memory-bound
+#     kernel; reading R10 (over the quantized activations).
+# ---------------------------------------------------------------------------
+def activation_row_sums(qx: np.ndarray) -> np.ndarray:
+    return np.asarray(qx, dtype=np.int64).sum(axis=1).astype(np.int32)
+
+
+def w4a8_pc_reference(x16: np.ndarray, w16: np.ndarray):
+    """Every intermediate of the per-channel path for X fp16 [M,K], W fp16 [N,K].
+    acc = sum_k qx (q - z) (exact), out = fp16(acc * (s_X * s_W)) (R7, R10)."""
+    q_u4, z, s_w = quantize_weights_per_channel(w16)
+    w_hat = dequantize_per_channel(q_u4, z)
+    qx, s_x = quantize_activations(x16)
+    acc = contract(qx, w_hat)
+    ref32 = epilogue_fp32(acc, s_x, s_w)
+    return {
+        "q_u4": q_u4, "z": z, "s_w": s_w, "w_hat": w_hat, "qx": qx, "s_x": s_x,
+        "t": activation_row_sums(qx), "acc": acc, "ref32": ref32, "out": ref32.astype(np.float16),
     }

@@ -368,3 +368,112 @@ def test_generator_is_seeded():
     # outlier channels: about 2% of weight columns and 1% of activation columns are large
     big = (np.abs(a.astype(np.float32)).max(axis=0) > 0.15).sum()
     assert 5 <= big <= 20
+
+
+# ---------------------------------------------------------------------------
+# per-channel variant (readings R9, R10)
+# ---------------------------------------------------------------------------
+def _exact_pc_quant(row):
+    """Per-channel asymmetric UINT4 of one fp16 row by exact rational arithmetic
+    (IEEE fp32 subtract / divide and the fp16 scale rounding done on Fractions)."""
+    vals = [Fraction(float(v)) for v in row]
+    lo = min(min(vals), Fraction(0))
+    hi = max(max(vals), Fraction(0))
+    diff = round_float(hi - lo, FP32)
+    s = round_float(round_float(diff / 15, FP32), FP16)
+    if s == 0:
+        return [0] * len(vals), 0, s
+    z = max(0, min(15, rne_int(round_float(-lo / s, FP32))))
+    q = [max(0, min(15, z + rne_int(round_float(v / s, FP32)))) for v in vals]
+    return q, z, s
+
+
+def test_per_channel_exact_rational():
+    rng = np.random.default_rng(11)
+    rows = [(rng.standard_normal(128) * sc).astype(np.float16) for sc in (1e-3, 0.02, 1.0, 40.0)]
+    rows.append(np.abs(rng.standard_normal(128) * 0.1).astype(np.float16))        # all >= 0: z = 0
+    rows.append(-np.abs(rng.standard_normal(128) * 0.1).astype(np.float16))       # all <= 0: z = 15
+    rows.append((rng.standard_normal(128) * 3e-6).astype(np.float16))             # subnormal scale
+    rows.append(np.zeros(128, np.float16))                                          # R8
+    w = np.stack(rows)
+    q, z, s = o.quantize_weights_per_channel(w)
+    for r in range(w.shape[0]):
+        qe, ze, se = _exact_pc_quant(w[r])
+        assert Fraction(float(s[r])) == se
+        assert int(z[r]) == ze
+        assert q[r].tolist() == qe
+    assert int(z[4]) == 0 and int(z[5]) == 15
+    assert float(s[7]) == 0 and not q[7].any() and int(z[7]) == 0
+
+
+@pytest.mark.parametrize("z0,e", [(0, 6), (7, 3), (15, 10), (4, 14)])
+def test_per_channel_lossless_rows(z0, e):
+    """Rows on the grid (k - z0) * 2^-e using all 16 codes: the scale, zero and codes
+    are recovered exactly and the reconstruction is lossless."""
+    rng = np.random.default_rng(z0 + e)
+    k = rng.integers(0, 16, (3, 256))
+    k[:, 0], k[:, 1] = 0, 15
+    w = ((k - z0) * 2.0 ** -e).astype(np.float16)
+    q, z, s = o.quantize_weights_per_channel(w)
+    assert np.all(s.astype(np.float64) == 2.0 ** -e)
+    assert np.all(z == z0)
+    assert np.array_equal(q, k.astype(np.uint8))
+    w_hat = o.dequantize_per_channel(q, z).astype(np.float64) * s.astype(np.float64)[:, None]
+    assert np.array_equal(w_hat, w.astype(np.float64))
+
+
+def test_per_channel_error_bound():
+    """|(q - z) s - w| <= s/2 (plus the fp32 division's half-ulp) for every element
+    that does not clamp; a clamp can only fire at the top of the range and then
+    costs at most one step: the zero makes the bottom of the range code 0 exactly."""
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((64, 512)) * rng.uniform(1e-3, 10, (64, 1))).astype(np.float16)
+    q, z, s = o.quantize_weights_per_channel(w)
+    wf = w.astype(np.float64)
+    sf = s.astype(np.float64)[:, None]
+    err = np.abs((q.astype(np.float64) - z.astype(np.float64)[:, None]) * sf - wf)
+    unclamped = z.astype(np.int64)[:, None] + np.rint(w.astype(np.float32) / s.astype(np.float32)[:, None]) <= 15
+    assert np.all(err[unclamped] <= sf.repeat(512, 1)[unclamped] * (0.5 + 2.0 ** -20))
+    assert np.all(err <= sf * 1.01)
+    assert np.all(q[np.arange(64), np.argmin(np.minimum(w, 0), axis=1)] == 0) or np.all(w.min(axis=1) >= 0)
+
+
+def test_per_channel_matches_pages_affine_formula():
+    """Away from exact ties, q = clip(round(w/s + z), 0, 15) with the pages' formula
+    in fp64 gives the same codes as R2's z + rne(w/s)."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((32, 384)) * 0.05).astype(np.float16)
+    q, z, s = o.quantize_weights_per_channel(w)
+    ref = np.clip(np.rint(w.astype(np.float64) / s.astype(np.float64)[:, None] + z[:, None]), 0, 15)
+    assert np.array_equal(q, ref.astype(np.uint8))
+
+
+@pytest.mark.parametrize("j", [-3, 2])
+def test_per_channel_power_of_two_invariance(j):
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float16)
+    q1, z1, s1 = o.quantize_weights_per_channel(w)
+    q2, z2, s2 = o.quantize_weights_per_channel((w.astype(np.float32) * 2.0 ** j).astype(np.float16))
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(s2.astype(np.float64), s1.astype(np.float64) * 2.0 ** j)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 16, 256), (5, 32, 128)])
+def test_per_channel_contraction_brute_force(M, N, K):
+    """Pure-Python sums: acc = sum_k qx (q - z), and the pages' rearrangement
+    sum_k qx q - z t with t = sum_k qx gives the same integers; the fp16 output is
+    the fp32 product of acc and the two scales, rounded once."""
+    rng = np.random.default_rng(M * 100 + N + K)
+    x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+    w16 = (rng.standard_normal((N, K)) * 0.05).astype(np.float16)
+    r = o.w4a8_pc_reference(x16, w16)
+    qx, q, z = r["qx"].tolist(), r["q_u4"].tolist(), r["z"].tolist()
+    for m in range(M):
+        t = sum(qx[m])
+        assert t == int(r["t"][m])
+        for n in range(N):
+            direct = sum(qx[m][k] * (q[n][k] - z[n]) for k in range(K))
+            split = sum(qx[m][k] * q[n][k] for k in range(K)) - z[n] * t
+            assert direct == split == int(r["acc"][m, n])
+            exact = Fraction(direct) * Fraction(float(r["s_x"][m])) * Fraction(float(r["s_w"][n]))
+            assert float(r["out"][m, n]) == float(round_float(round_float(exact, FP32), FP16))

@@ -24,7 +24,8 @@
  *     launched and no output is touched.  No C++ exception crosses this interface.
  *   - The library holds no mutable global state; calls are thread-safe.  Calls on
  *     different streams that write the same output race, as any GPU work does.
- *   - Only group == 128 is supported (QOQ_ERR_UNSUPPORTED otherwise).
+ *   - group == 128 (per-group weights); group == 0 selects per-channel weights where
+ *     a call documents it.  Anything else: QOQ_ERR_UNSUPPORTED.
  *   - Shapes: N % 16 == 0, K % 128 == 0, 0 < K <= 139648 (keeps every INT32
  *     accumulator exact: 127 * 121 * K < 2^31), M >= 0 (M == 0 is a no-op).
  *   - Inputs must be finite; behaviour for inf/NaN inputs is unspecified.
@@ -59,15 +60,18 @@ typedef enum {
   QOQ_ERR_HIP = -5           /* the HIP runtime reported an error at launch */
 } qoq_status;
 
-/* Library ABI version (increments when a signature or the storage layout changes). */
+/* Library ABI version (increments when a signature, an entry point or the storage
+ * layout changes; 2 adds the per-channel variant and the linear entry point). */
 int qoq_version(void);
 
 /* Human-readable text of a qoq_status value; never NULL, static storage. */
 const char *qoq_status_string(int status);
 
 /* Sizes in bytes of the three buffers qoq_quantize_pack_weights writes for W [N,K]:
- * packed_w = N*K/2, group_meta = 2*N*K/128, s_w = 2*N.  Any output pointer may be
- * NULL.  Errors: INVALID for bad N/K, UNSUPPORTED for group != 128. */
+ * group 128: packed_w = N*K/2, group_meta = 2*N*K/128, s_w = 2*N;
+ * group 0 (per-channel weights): packed_w = N*K/2, group_meta = N (the zeros, one
+ * byte per output channel), s_w = 2*N.  Any output pointer may be NULL.
+ * Errors: INVALID for bad N/K, UNSUPPORTED for any other group. */
 int qoq_weight_buffer_sizes(int64_t N, int64_t K, int32_t group, size_t *packed_w_bytes,
                             size_t *group_meta_bytes, size_t *s_w_bytes);
 
@@ -84,6 +88,16 @@ int qoq_weight_buffer_sizes(int64_t N, int64_t K, int32_t group, size_t *packed_
 int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t group,
                               void *packed_w, void *group_meta, void *s_w_fp16, void *stream);
 
+/* group == 0 selects the per-channel format (the W4A8 variant without groups, whose
+ * zero point leaves the main loop: "QServe ..." summary, per-channel fast
+ * dequantization; integer quantization with a zero point, one per channel):
+ *   lo = min(0, min_k W[n,k]), hi = max(0, max_k W[n,k])   (fp32)
+ *   s_W[n] = fp16((hi - lo) / 15)                          (fp32 subtract and divide)
+ *   z[n]   = clamp(rint(-lo / s_W), 0, 15),  q = clamp(z + rint(W / s_W), 0, 15)
+ *   (a row whose s_W is 0: q = 0, z = 0)
+ * packed_w: the codes in the same storage layout as above; group_meta receives the
+ * zeros (uint8 [N], no alignment requirement); s_w_fp16 [N]. */
+
 /* Per-token symmetric INT8 activation quantization (the activation side of the
  * epilogue scale s_W x s_X, "QServe ..." summary; symmetric quantizer of
  * "01 inference papers and experiments" §4.1):
@@ -94,6 +108,13 @@ int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t 
  * Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_i8,
                              void *s_x_fp16, void *stream);
+
+/* qoq_quantize_activations plus the per-token code sums of the per-channel epilogue:
+ * t_x[m] = sum_k qx[m, k] (INT32 [M], 4-byte aligned; the "t_X" of the per-channel
+ * epilogue term t_X x (z_W ⊙ s_W), taken over the quantized activations so the
+ * epilogue is exact).  Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_quantize_activations_rowsum(const void *x_fp16, int64_t M, int64_t K, void *qx_i8,
+                                    void *s_x_fp16, int32_t *t_x, void *stream);
 
 /* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
  * It is non-zero when the plan splits the K groups of each output tile over several
@@ -129,6 +150,24 @@ int qoq_w4a8_gemm(const void *qx_i8, const void *s_x_fp16, const void *packed_w,
 int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group_meta,
                       int32_t *acc_i32, int64_t M, int64_t N, int64_t K, int32_t group,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* W4A8 GEMM on per-channel weights ("QServe ..." summary, per-channel fast
+ * dequantization: O = (Q_X Q_W) ⊙ (s_W x s_X) - t_X x (z_W ⊙ s_W); the main loop
+ * multiplies the raw UINT4 codes, the zero point is applied in the epilogue):
+ *   acc[m,n] = sum_k qx[m,k] * q[n,k] - z[n] * t_x[m]   (= sum_k qx (q - z), exact)
+ *   out[m,n] = fp16( float(acc) * (float(s_X[m]) * float(s_W[n])) )
+ * packed_w / zeros / s_w_fp16 as written by qoq_quantize_pack_weights with group 0;
+ * t_x from qoq_quantize_activations_rowsum; other buffers, the workspace (the size
+ * qoq_gemm_workspace_bytes reports for the shape) and errors as for qoq_w4a8_gemm. */
+int qoq_w4a8_gemm_pc(const void *qx_i8, const void *s_x_fp16, const int32_t *t_x,
+                     const void *packed_w, const void *zeros, const void *s_w_fp16,
+                     void *out_fp16, int64_t M, int64_t N, int64_t K, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* The same with the INT32 epilogue: acc_i32 [M,N] receives acc exactly. */
+int qoq_w4a8_gemm_pc_i32(const void *qx_i8, const int32_t *t_x, const void *packed_w,
+                         const void *zeros, int32_t *acc_i32, int64_t M, int64_t N, int64_t K,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace in bytes qoq_w4a8_linear needs for this problem: 0 when the fused
  * kernel serves it (M <= 16 and K <= 8192), otherwise room for qx (M*K bytes) and

@@ -110,8 +110,8 @@ def test_workspace_validation(L):
 def test_workspace_and_plan():
     assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
     assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
-    assert qoq.gemm_plan(4096, 28672, 4096) == "sd_as2"
-    assert qoq.gemm_plan(4096, 4096, 14336) == "sd_as2"
+    assert qoq.gemm_plan(4096, 28672, 4096) == "dma2_tm4_tn2"
+    assert qoq.gemm_plan(256, 28672, 4096) == "wide2_tm4_tn1"
     assert qoq.gemm_plan(1024, 4096, 14336) == "dma2_tm4_tn2"
     assert qoq.gemm_plan(1, 17, 4096) == "invalid"
     assert qoq.gemm_plan(0, 16, 128) == "invalid"
@@ -230,3 +230,27 @@ def test_linear_validation(L):
     assert f(*a(M=M, N=N, K=K)) == WORKSPACE
     assert f(*a(M=M, N=N, K=K, ws=FAKE, wb=need - 1)) == WORKSPACE
     assert f(*a(M=M, N=N, K=K, ws=ctypes.c_void_p(0x10010), wb=need)) == ALIGNMENT
+
+
+def test_per_channel_sizes_and_validation(L):
+    s = qoq.weight_buffer_sizes(6144, 4096, group=0)
+    assert s == {"packed_w": 6144 * 4096 // 2, "group_meta": 6144, "s_w": 6144 * 2}
+    f = L.qoq_quantize_pack_weights
+    assert f(FAKE, 32, 256, 0, FAKE, ODD, FAKE, NUL) != ALIGNMENT    # zeros: bytes, any address
+    r = L.qoq_quantize_activations_rowsum
+    assert r(FAKE, 4, 256, FAKE, FAKE, NUL, NUL) == INVALID
+    assert r(FAKE, 4, 256, FAKE, FAKE, ctypes.c_void_p(0x10002), NUL) == ALIGNMENT
+    assert r(NUL, 0, 256, NUL, NUL, NUL, NUL) == OK
+    g = L.qoq_w4a8_gemm_pc
+    a = lambda qx=FAKE, sx=FAKE, t=FAKE, pw=FAKE, z=FAKE, sw=FAKE, out=FAKE, M=4, N=32, K=256: (
+        qx, sx, t, pw, z, sw, out, M, N, K, NUL, 0, NUL)
+    assert g(*a(t=NUL)) == INVALID
+    assert g(*a(z=NUL)) == INVALID
+    assert g(*a(t=ctypes.c_void_p(0x10002))) == ALIGNMENT
+    assert g(*a(N=40)) == INVALID
+    assert g(*a(M=0, qx=NUL, out=NUL)) == OK
+    M, N, K = 256, 4096, 14336                    # split-K plan: needs the workspace
+    assert g(*a(M=M, N=N, K=K)) == WORKSPACE
+    h = L.qoq_w4a8_gemm_pc_i32
+    assert h(FAKE, FAKE, FAKE, NUL, FAKE, 4, 32, 256, NUL, 0, NUL) == INVALID
+    assert qoq.gemm_workspace_bytes(M, N, K, group=0) == qoq.gemm_workspace_bytes(M, N, K)

@@ -21,17 +21,18 @@ int launch_status() {
   return e == hipSuccess ? QOQ_OK : QOQ_ERR_HIP;
 }
 
-// shape rules shared by the weight and GEMM calls
-int check_nk(int64_t N, int64_t K, int32_t group) {
-  if (group != 128) return QOQ_ERR_UNSUPPORTED;
+// shape rules shared by the weight and GEMM calls; group 0 = per-channel weights
+// (accepted by the calls that document it)
+int check_nk(int64_t N, int64_t K, int32_t group, bool allow_pc = false) {
+  if (group != 128 && !(allow_pc && group == 0)) return QOQ_ERR_UNSUPPORTED;
   if (N <= 0 || K <= 0 || N % 16 != 0 || K % 128 != 0) return QOQ_ERR_INVALID;
   if (K > kMaxK) return QOQ_ERR_UNSUPPORTED;
   if (N > kMaxDim || N * K / 2 > kMaxDim * 8) return QOQ_ERR_UNSUPPORTED;
   return QOQ_OK;
 }
 
-int check_gemm(int64_t M, int64_t N, int64_t K, int32_t group) {
-  int st = check_nk(N, K, group);
+int check_gemm(int64_t M, int64_t N, int64_t K, int32_t group, bool allow_pc = false) {
+  int st = check_nk(N, K, group, allow_pc);
   if (st != QOQ_OK) return st;
   if (M < 0) return QOQ_ERR_INVALID;
   if (M > kMaxDim) return QOQ_ERR_UNSUPPORTED;
@@ -44,13 +45,13 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int32_t group) {
 
 extern "C" {
 
-int qoq_version(void) { return 1; }
+int qoq_version(void) { return 2; }
 
 const char *qoq_status_string(int status) {
   switch (status) {
     case QOQ_OK: return "ok";
     case QOQ_ERR_INVALID: return "invalid argument (null pointer or shape not allowed)";
-    case QOQ_ERR_UNSUPPORTED: return "unsupported configuration (group != 128 or size beyond limits)";
+    case QOQ_ERR_UNSUPPORTED: return "unsupported configuration (group not allowed here or size beyond limits)";
     case QOQ_ERR_ALIGNMENT: return "pointer alignment requirement not met";
     case QOQ_ERR_WORKSPACE: return "workspace smaller than required";
     case QOQ_ERR_HIP: return "HIP runtime error at launch";
@@ -60,22 +61,27 @@ const char *qoq_status_string(int status) {
 
 int qoq_weight_buffer_sizes(int64_t N, int64_t K, int32_t group, size_t *packed_w_bytes,
                             size_t *group_meta_bytes, size_t *s_w_bytes) {
-  int st = check_nk(N, K, group);
+  int st = check_nk(N, K, group, true);
   if (st != QOQ_OK) return st;
   if (packed_w_bytes) *packed_w_bytes = static_cast<size_t>(N) * static_cast<size_t>(K) / 2;
-  if (group_meta_bytes) *group_meta_bytes = static_cast<size_t>(N) * static_cast<size_t>(K / 128) * 2;
+  if (group_meta_bytes)
+    *group_meta_bytes = group == 0 ? static_cast<size_t>(N) : static_cast<size_t>(N) * static_cast<size_t>(K / 128) * 2;
   if (s_w_bytes) *s_w_bytes = static_cast<size_t>(N) * 2;
   return QOQ_OK;
 }
 
 int qoq_quantize_pack_weights(const void *w_fp16, int64_t N, int64_t K, int32_t group, void *packed_w,
                               void *group_meta, void *s_w_fp16, void *stream) {
-  int st = check_nk(N, K, group);
+  int st = check_nk(N, K, group, true);
   if (st != QOQ_OK) return st;
   if (!w_fp16 || !packed_w || !group_meta || !s_w_fp16) return QOQ_ERR_INVALID;
-  if (!aligned(w_fp16, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 2) || !aligned(s_w_fp16, 2))
+  if (!aligned(w_fp16, 16) || !aligned(packed_w, 16) || !aligned(group_meta, group == 0 ? 1 : 2) ||
+      !aligned(s_w_fp16, 2))
     return QOQ_ERR_ALIGNMENT;
-  qoq::launch_quantize_pack_weights(w_fp16, N, K, packed_w, group_meta, s_w_fp16, as_stream(stream));
+  if (group == 0)
+    qoq::launch_quantize_pack_weights_pc(w_fp16, N, K, packed_w, group_meta, s_w_fp16, as_stream(stream));
+  else
+    qoq::launch_quantize_pack_weights(w_fp16, N, K, packed_w, group_meta, s_w_fp16, as_stream(stream));
   return launch_status();
 }
 
@@ -90,8 +96,55 @@ int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_
   return launch_status();
 }
 
+int qoq_quantize_activations_rowsum(const void *x_fp16, int64_t M, int64_t K, void *qx_i8, void *s_x_fp16,
+                                    int32_t *t_x, void *stream) {
+  if (M < 0 || K <= 0 || K % 8 != 0) return QOQ_ERR_INVALID;
+  if (M > kMaxDim || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !qx_i8 || !s_x_fp16 || !t_x) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(qx_i8, 16) || !aligned(s_x_fp16, 2) || !aligned(t_x, 4))
+    return QOQ_ERR_ALIGNMENT;
+  qoq::launch_quantize_activations_rowsum(x_fp16, M, K, qx_i8, s_x_fp16, t_x, as_stream(stream));
+  return launch_status();
+}
+
+static int gemm_pc_common(const void *qx_i8, const void *s_x_fp16, const int32_t *t_x, const void *packed_w,
+                          const void *zeros, const void *s_w_fp16, void *out, int out_kind, int64_t M, int64_t N,
+                          int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_gemm(M, N, K, 128);
+  if (st != QOQ_OK) return st;
+  if (M == 0) return QOQ_OK;
+  if (!qx_i8 || !t_x || !packed_w || !zeros || !out) return QOQ_ERR_INVALID;
+  if (out_kind == 0 && (!s_x_fp16 || !s_w_fp16)) return QOQ_ERR_INVALID;
+  if (!aligned(qx_i8, 16) || !aligned(packed_w, 16) || !aligned(out, 16) || !aligned(t_x, 4))
+    return QOQ_ERR_ALIGNMENT;
+  if (out_kind == 0 && (!aligned(s_x_fp16, 2) || !aligned(s_w_fp16, 2))) return QOQ_ERR_ALIGNMENT;
+  const size_t need = qoq::gemm_workspace_need(M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return QOQ_ERR_ALIGNMENT;
+  }
+  qoq::launch_w4a8_gemm_pc(qx_i8, s_x_fp16, t_x, packed_w, zeros, s_w_fp16, out, out_kind, M, N, K, workspace,
+                           as_stream(stream));
+  return launch_status();
+}
+
+int qoq_w4a8_gemm_pc(const void *qx_i8, const void *s_x_fp16, const int32_t *t_x, const void *packed_w,
+                     const void *zeros, const void *s_w_fp16, void *out_fp16, int64_t M, int64_t N, int64_t K,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return gemm_pc_common(qx_i8, s_x_fp16, t_x, packed_w, zeros, s_w_fp16, out_fp16, 0, M, N, K, workspace,
+                        workspace_bytes, stream);
+}
+
+int qoq_w4a8_gemm_pc_i32(const void *qx_i8, const int32_t *t_x, const void *packed_w, const void *zeros,
+                         int32_t *acc_i32, int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  return gemm_pc_common(qx_i8, nullptr, t_x, packed_w, zeros, nullptr, acc_i32, 1, M, N, K, workspace,
+                        workspace_bytes, stream);
+}
+
 int qoq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes) {
-  int st = check_gemm(M, N, K, group);
+  int st = check_gemm(M, N, K, group, true);
   if (st != QOQ_OK) return st;
   if (!bytes) return QOQ_ERR_INVALID;
   *bytes = M == 0 ? 0 : qoq::gemm_workspace_need(M, N, K);

@@ -158,6 +158,29 @@ __device__ __forceinline__ void dequant_lane(uint4 p, GroupConsts g, v4i &b_lo, 
   }
 }
 
+// Per-channel variant: the UINT4 codes themselves are the B operand (0..15 fit an
+// INT8 lane); the zero point is applied in the epilogue as z * t.  Unpacking only:
+// AND / SHIFT / AND per 8 codes ("QServe ..." summary, per-channel fast
+// dequantization: three logic operations per register).
+__device__ __forceinline__ void unpack_lane(uint4 p, v4i &b_lo, v4i &b_hi) {
+  unsigned w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    b_lo[r] = static_cast<int>(w[r] & 0x0f0f0f0fu);
+    b_hi[r] = static_cast<int>((w[r] >> 4) & 0x0f0f0f0fu);
+  }
+}
+
+// B operand of one lane: dequantized INT8 weights (per-group, PC = false) or the
+// raw codes (per-channel, PC = true)
+template <bool PC>
+__device__ __forceinline__ void weights_lane(uint4 p, unsigned meta16, v4i &b_lo, v4i &b_hi) {
+  if constexpr (PC)
+    unpack_lane(p, b_lo, b_hi);
+  else
+    dequant_lane(p, group_consts(meta16), b_lo, b_hi);
+}
+
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -59,7 +59,7 @@ struct SkinnyBatch {
 
 // Issues every load of batch b (groups t = b*U .. b*U+U-1 of this wave).  Only
 // scalars come in, so no pointer array can end up in private (scratch) memory.
-template <int MT, int NBW, int WAVES, int U>
+template <int MT, int NBW, int WAVES, int U, bool PC>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, int ngroups, int wave,
                                             const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                             const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
@@ -76,7 +76,7 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, i
       // strips past the end repeat the last one; their results are dropped at the store
       const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
       B.p[u][nb] = ok ? packed[chunk * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
-      B.md[u][nb] = ok ? static_cast<unsigned>(meta[chunk * 16 + col]) : 0u;
+      B.md[u][nb] = (!PC && ok) ? static_cast<unsigned>(meta[chunk * 16 + col]) : 0u;
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -89,10 +89,11 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, i
   }
 }
 
-template <int MT, int NBW, int WAVES, int U, int OUT>
+template <int MT, int NBW, int WAVES, int U, int OUT, bool PC>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
-    const uint16_t *__restrict__ meta, const __half *__restrict__ sw, void *__restrict__ out, int M, int N,
+    const uint16_t *__restrict__ meta, const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
+    const int *__restrict__ trow, void *__restrict__ out, int M, int N,
     int K, int, int *) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -114,16 +115,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
   SkinnyBatch<MT, NBW, U> cur, nxt;
   if (nbatch > 0)
-    skinny_load<MT, NBW, WAVES, U>(cur, 0, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
+    skinny_load<MT, NBW, WAVES, U, PC>(cur, 0, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
   for (int b = 0; b < nbatch; ++b) {
     if (b + 1 < nbatch)
-      skinny_load<MT, NBW, WAVES, U>(nxt, b + 1, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
+      skinny_load<MT, NBW, WAVES, U, PC>(nxt, b + 1, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         v4i b0, b1;
-        dequant_lane(cur.p[u][nb], group_consts(cur.md[u][nb]), b0, b1);
+        weights_lane<PC>(cur.p[u][nb], cur.md[u][nb], b0, b1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           acc[mt][nb] = mfma16x16x64(cur.a0[u][mt], b0, acc[mt][nb]);
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         const int n = strip * 16 + (ln & 15);
         float scale = 0.0f;
         if (OUT == 0) scale = __half2float(sx[m]) * __half2float(sw[n]);
+        if (PC) sum -= static_cast<int>(zp[n]) * trow[m];
         store_result(out, OUT, static_cast<size_t>(m) * N + n, sum, scale);
       }
     }
@@ -173,7 +175,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             const int n = strip * 16 + col;
             float scale = 0.0f;
             if (OUT == 0) scale = __half2float(sx[m]) * __half2float(sw[n]);
-            store_result(out, OUT, static_cast<size_t>(m) * N + n, acc[mt][nb][i], scale);
+            const int v = acc[mt][nb][i] - (PC ? static_cast<int>(zp[n]) * trow[m] : 0);
+            store_result(out, OUT, static_cast<size_t>(m) * N + n, v, scale);
           }
         }
   }
@@ -398,11 +401,18 @@ __device__ __forceinline__ void split_coords(int bid, int nx, int ny, int splits
 // so the global writes are 16-byte row segments (whole cache lines) instead of
 // 2-byte scattered stores; INT32 (verification path): direct stores.
 // lds_wave: this wave's scratch, at least 32 * (64*TN + 16) bytes, free to use.
-template <int TM, int TN, int OUT>
+// PC (per-channel weights): acc - z[n] * t[m] first (the zero point, moved out of
+// the main loop; "QServe ..." summary, per-channel fast dequantization).
+template <int TM, int TN, int OUT, bool PC = false>
 __device__ __forceinline__ void epilogue32(const v16i (&acc)[TM][TN], int8_t *__restrict__ lds_wave, int lane,
                                            int m0, int n0, int M, int N, const __half *__restrict__ sx,
-                                           const __half *__restrict__ sw, void *__restrict__ out) {
+                                           const __half *__restrict__ sw, void *__restrict__ out,
+                                           const uint8_t *__restrict__ zp = nullptr,
+                                           const int *__restrict__ trow = nullptr) {
   const int c32 = lane & 31, hi = lane >> 5;
+  int zn[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) zn[tn] = PC ? static_cast<int>(zp[min(n0 + 32 * tn + c32, N - 1)]) : 0;
   if (OUT == 1) {
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
@@ -413,7 +423,8 @@ __device__ __forceinline__ void epilogue32(const v16i (&acc)[TM][TN], int8_t *__
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 32 * tm + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (m < M) static_cast<int *>(out)[static_cast<size_t>(m) * N + n] = acc[tm][tn][r];
+          if (m < M)
+            static_cast<int *>(out)[static_cast<size_t>(m) * N + n] = acc[tm][tn][r] - (PC ? zn[tn] * trow[m] : 0);
         }
     }
     return;
@@ -428,11 +439,13 @@ __device__ __forceinline__ void epilogue32(const v16i (&acc)[TM][TN], int8_t *__
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int lr = 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float sxm = __half2float(sx[min(m0 + 32 * tm + lr, M - 1)]);
+      const int mrow = min(m0 + 32 * tm + lr, M - 1);
+      const float sxm = __half2float(sx[mrow]);
+      const int tm_ = PC ? trow[mrow] : 0;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         *reinterpret_cast<__half *>(lds_wave + lr * ROW + 2 * (32 * tn + c32)) =
-            mul_round_half(static_cast<float>(acc[tm][tn][r]), sxm * swn[tn]);
+            mul_round_half(static_cast<float>(acc[tm][tn][r] - zn[tn] * tm_), sxm * swn[tn]);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -469,7 +482,7 @@ struct W2Set {
   unsigned md[TN];
 };
 
-template <int CH, int TN>
+template <int CH, int TN, bool PC>
 __device__ __forceinline__ void w2_load(W2Set<CH, TN> &S, const int8_t *const (&ag)[CH], const uint4 *__restrict__ packed,
                                         const uint16_t *__restrict__ meta, const unsigned (&boff)[TN],
                                         const unsigned (&moff)[TN], int j) {
@@ -481,11 +494,11 @@ __device__ __forceinline__ void w2_load(W2Set<CH, TN> &S, const int8_t *const (&
   for (int tn = 0; tn < TN; ++tn) {
     S.p0[tn] = pj[boff[tn]];
     S.p1[tn] = pj[boff[tn] + 32];
-    S.md[tn] = mj[moff[tn]];
+    S.md[tn] = PC ? 0u : mj[moff[tn]];
   }
 }
 
-template <int TM, int TN, int CH, int Q>
+template <int TM, int TN, int CH, int Q, bool PC>
 __device__ __forceinline__ void w2_step(int j, int G, W2Set<CH, TN> &cur, W2Set<CH, TN> &oth, int8_t (*As)[32 * TM * kLdsRow],
                                         const int (&alds)[CH], int arow, const int8_t *const (&ag)[CH],
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
@@ -494,15 +507,14 @@ __device__ __forceinline__ void w2_step(int j, int G, W2Set<CH, TN> &cur, W2Set<
   v4i b[4][TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    const GroupConsts g = group_consts(cur.md[tn]);
-    dequant_lane(cur.p0[tn], g, b[0][tn], b[2][tn]);
-    dequant_lane(cur.p1[tn], g, b[1][tn], b[3][tn]);
+    weights_lane<PC>(cur.p0[tn], cur.md[tn], b[0][tn], b[2][tn]);
+    weights_lane<PC>(cur.p1[tn], cur.md[tn], b[1][tn], b[3][tn]);
   }
   // cur's A chunks went to LDS a group ago and its codes are consumed: reuse it.
   // The scheduling fences keep these loads at the top of the group and the LDS
   // writes at its end, so each load has two groups of work to land in.
   __builtin_amdgcn_sched_barrier(0);
-  w2_load<CH, TN>(cur, ag, packed, meta, boff, moff, min(j + 2, G - 1));
+  w2_load<CH, TN, PC>(cur, ag, packed, meta, boff, moff, min(j + 2, G - 1));
   __builtin_amdgcn_sched_barrier(0);
   const int8_t *abuf = &As[Q][arow];
 #pragma unroll
@@ -519,12 +531,13 @@ __device__ __forceinline__ void w2_step(int j, int G, W2Set<CH, TN> &cur, W2Set<
   __syncthreads();
 }
 
-template <int TM, int TN, int OUT>
+template <int TM, int TN, int OUT, bool PC>
 __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__restrict__ qx,
                                                             const __half *__restrict__ sx,
                                                             const uint4 *__restrict__ packed,
                                                             const uint16_t *__restrict__ meta,
-                                                            const __half *__restrict__ sw, void *__restrict__ out,
+                                                            const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
+    const int *__restrict__ trow, void *__restrict__ out,
                                                             int M, int N, int K, int splits, int *__restrict__ ws) {
   constexpr int BM = 32 * TM;
   constexpr int CH = BM * 8 / 256;
@@ -571,8 +584,8 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16i{};
 
   W2Set<CH, TN> s0set, s1set;
-  w2_load<CH, TN>(s0set, ag, packed, meta, boff, moff, 0);
-  w2_load<CH, TN>(s1set, ag, packed, meta, boff, moff, min(1, G - 1));
+  w2_load<CH, TN, PC>(s0set, ag, packed, meta, boff, moff, 0);
+  w2_load<CH, TN, PC>(s1set, ag, packed, meta, boff, moff, min(1, G - 1));
 #pragma unroll
   for (int c = 0; c < CH; ++c) *reinterpret_cast<v4i *>(&As[0][alds[c]]) = s0set.a[c];
   __syncthreads();
@@ -580,10 +593,10 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
   const int arow = c32 * kLdsRow + 16 * hi;
   int j = 0;
   for (; j + 1 < G; j += 2) {
-    w2_step<TM, TN, CH, 0>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
-    w2_step<TM, TN, CH, 1>(j + 1, G, s1set, s0set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+    w2_step<TM, TN, CH, 0, PC>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+    w2_step<TM, TN, CH, 1, PC>(j + 1, G, s1set, s0set, As, alds, arow, ag, packed, meta, boff, moff, acc);
   }
-  if (j < G) w2_step<TM, TN, CH, 0>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
+  if (j < G) w2_step<TM, TN, CH, 0, PC>(j, G, s0set, s1set, As, alds, arow, ag, packed, meta, boff, moff, acc);
 
   static_assert(4 * 32 * (64 * TN + 16) <= 2 * BM * kLdsRow, "epilogue scratch exceeds the A buffers");
   if (splits > 1) {   // partial sums of this split -> workspace slice
@@ -591,7 +604,8 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
                           ws + static_cast<size_t>(split) * M * N);
     return;
   }
-  epilogue32<TM, TN, OUT>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+  epilogue32<TM, TN, OUT, PC>(acc, &As[0][0] + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out,
+                              zp, trow);
 }
 
 // ---------------------------------------------------------------------------
@@ -618,7 +632,9 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // prefetched register is never copied, so the compiler can wait for exactly the
 // loads it needs).  A fragments are read one k block ahead of the MFMAs that use
 // them.  Per group j: dequantize B(j); copy A(j+2) and load B(j+2); MFMAs of j;
-// wait for A(j+1)'s copies; barrier.
+// wait for A(j+1)'s copies; barrier.  The copies and the register loads both count
+// in vmcnt but do not retire in order with each other, so a wait for a copy counts
+// only the copies issued after it.
 // ---------------------------------------------------------------------------
 template <int TN>
 struct DBSet {
@@ -626,7 +642,7 @@ struct DBSet {
   unsigned md[TN];
 };
 
-template <int TM, int TN, int Q>
+template <int TM, int TN, int Q, bool PC>
 __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *__restrict__ lds,
                                           const int8_t *const (&asrc)[TM], int wave, int lane,
                                           const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
@@ -637,9 +653,8 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
   v4i b[4][TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    const GroupConsts g = group_consts(cur.md[tn]);
-    dequant_lane(cur.p0[tn], g, b[0][tn], b[2][tn]);
-    dequant_lane(cur.p1[tn], g, b[1][tn], b[3][tn]);
+    weights_lane<PC>(cur.p0[tn], cur.md[tn], b[0][tn], b[2][tn]);
+    weights_lane<PC>(cur.p1[tn], cur.md[tn], b[1][tn], b[3][tn]);
   }
   // The codes die here.  The empty volatile asm consumes every dequantized value,
   // so instruction selection cannot move any of the dequantization below the loads
@@ -666,7 +681,7 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
     for (int tn = 0; tn < TN; ++tn) {
       cur.p0[tn] = pj[boff[tn]];
       cur.p1[tn] = pj[boff[tn] + 32];
-      cur.md[tn] = mj[moff[tn]];
+      cur.md[tn] = PC ? 0u : mj[moff[tn]];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -695,19 +710,21 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
       for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(af[kb & 1][tm], b[kb][tn], acc[tm][tn]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A(j+1) was copied one group ago; since then: B(j+1) (3*TN loads), this group's
-  // copies (TM) and B(j+2) (3*TN)
-  QOQ_WAIT_VMCNT(6 * TN + TM);
+  // A(j+1) was copied one group ago.  Copies retire in order among themselves but
+  // not in order with register loads, so the count allows only the copies issued
+  // after A(j+1) (this group's TM) to be outstanding.
+  QOQ_WAIT_VMCNT(TM);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int TM, int TN, int OUT>
+template <int TM, int TN, int OUT, bool PC>
 __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restrict__ qx,
                                                            const __half *__restrict__ sx,
                                                            const uint4 *__restrict__ packed,
                                                            const uint16_t *__restrict__ meta,
-                                                           const __half *__restrict__ sw, void *__restrict__ out,
+                                                           const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
+    const int *__restrict__ trow, void *__restrict__ out,
                                                            int M, int N, int K, int splits, int *__restrict__ ws) {
   constexpr int BM = 32 * TM;
   constexpr int STAGE = BM * 128;
@@ -765,25 +782,25 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
     for (int tn = 0; tn < TN; ++tn) {
       set0.p0[tn] = packed[boff[tn]];
       set0.p1[tn] = packed[boff[tn] + 32];
-      set0.md[tn] = meta[moff[tn]];
+      set0.md[tn] = PC ? 0u : meta[moff[tn]];
     }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       set1.p0[tn] = p1[boff[tn]];
       set1.p1[tn] = p1[boff[tn] + 32];
-      set1.md[tn] = m1[moff[tn]];
+      set1.md[tn] = PC ? 0u : m1[moff[tn]];
     }
   }
-  // A(0): issued before A(1) (TM copies) and both B sets (6*TN loads)
-  QOQ_WAIT_VMCNT(TM + 6 * TN);
+  // A(0) resident (one wait for everything the prologue issued)
+  QOQ_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
 
   int j = 0;
   for (; j + 1 < G; j += 2) {
-    dma2_step<TM, TN, 0>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
-    dma2_step<TM, TN, 1>(j + 1, G, set1, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+    dma2_step<TM, TN, 0, PC>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+    dma2_step<TM, TN, 1, PC>(j + 1, G, set1, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
   }
-  if (j < G) dma2_step<TM, TN, 0>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
+  if (j < G) dma2_step<TM, TN, 0, PC>(j, G, set0, lds, asrc, wave, lane, packed, meta, boff, moff, acc);
   QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
   __syncthreads();
   static_assert(4 * 32 * (64 * TN + 16) <= 3 * STAGE, "epilogue scratch exceeds the ring");
@@ -792,7 +809,8 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
                           ws + static_cast<size_t>(split) * M * N);
     return;
   }
-  epilogue32<TM, TN, OUT>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out);
+  epilogue32<TM, TN, OUT, PC>(acc, lds + wave * 32 * (64 * TN + 16), lane, m0, 16 * s0, M, N, sx, sw, out, zp,
+                              trow);
 }
 
 // ---------------------------------------------------------------------------
@@ -827,13 +845,14 @@ struct SdCodes {
   unsigned md;
 };
 
+template <bool PC>
 __device__ __forceinline__ void sd_load_codes(SdCodes &c, const uint4 *__restrict__ packed,
                                               const uint16_t *__restrict__ meta, unsigned boff, unsigned moff,
                                               int j) {
   const uint4 *pj = packed + static_cast<size_t>(j) * 64;
   c.p0 = pj[boff];
   c.p1 = pj[boff + 32];
-  c.md = meta[static_cast<size_t>(j) * 16 + moff];
+  c.md = PC ? 0u : meta[static_cast<size_t>(j) * 16 + moff];
 }
 
 template <int AS>
@@ -846,12 +865,11 @@ __device__ __forceinline__ void sd_copy_a(int j, int8_t *__restrict__ lds, const
                                      16, 0, 0);
 }
 
-template <int Q>
+template <int Q, bool PC>
 __device__ __forceinline__ void sd_dequant(int8_t *__restrict__ bbuf, int wave, int lane, const SdCodes &cur) {
-  const GroupConsts g = group_consts(cur.md);
   v4i b[4];
-  dequant_lane(cur.p0, g, b[0], b[2]);
-  dequant_lane(cur.p1, g, b[1], b[3]);
+  weights_lane<PC>(cur.p0, cur.md, b[0], b[2]);
+  weights_lane<PC>(cur.p1, cur.md, b[1], b[3]);
   int8_t *dst = bbuf + (Q ^ 1) * kSdBufB + wave * 4096 + 16 * lane;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
@@ -885,7 +903,7 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
 // they run the step's two phases in opposite orders (MF = MFMAs first for waves
 // 4..7): while one dequantizes (vector ALU) the other issues MFMAs, and the two
 // units work side by side.
-template <int AS, int Q, bool MF>
+template <int AS, int Q, bool MF, bool PC>
 __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, int wave, int lane,
                                         const int8_t *const (&asrc)[4], SdCodes &cur,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
@@ -899,43 +917,45 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   // (j+1) & 1, which every wave finished reading before the last barrier; then the
   // set is refilled with group j+3's codes and group j+AS-1's A copies are issued
   // (its stage held group j-1)
-  sd_dequant<Q>(bbuf, wave, lane, cur);
+  sd_dequant<Q, PC>(bbuf, wave, lane, cur);
   __builtin_amdgcn_sched_barrier(0);
   sd_copy_a<AS>(min(j + AS - 1, G - 1), lds, asrc, wave);
-  sd_load_codes(cur, packed, meta, boff, moff, min(j + 3, G - 1));
+  sd_load_codes<PC>(cur, packed, meta, boff, moff, min(j + 3, G - 1));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!MF) {
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // A(j+1) must be resident.  AS == 3: it was copied one step ago and since then
-  // the codes of j+2 (3 loads), this step's 4 copies and 3 loads were issued;
-  // AS == 2: it is this step's copies, followed only by this step's 3 loads.
-  QOQ_WAIT_VMCNT(AS == 3 ? 10 : 3);
+  // A(j+1) must be resident.  Copies retire in order among themselves but not in
+  // order with register loads, so the count allows only the copies issued after
+  // A(j+1) to be outstanding: AS == 3, this step's 4 copies of A(j+2); AS == 2, none
+  // (A(j+1) is this step's copy).
+  QOQ_WAIT_VMCNT(AS == 3 ? 4 : 0);
   QOQ_WAIT_LGKMCNT0();                          // this wave's B(j+1) fragments are in LDS
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int AS, bool MF>
+template <int AS, bool MF, bool PC>
 __device__ __forceinline__ void sd_loop(int G, int8_t *__restrict__ lds, int wave, int lane,
                                         const int8_t *const (&asrc)[4], SdCodes &set0, SdCodes &set1,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                         unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
   int j = 0;
   for (; j + 1 < G; j += 2) {
-    sd_step<AS, 0, MF>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
-    sd_step<AS, 1, MF>(j + 1, G, lds, wave, lane, asrc, set0, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, set0, packed, meta, boff, moff, acc);
   }
-  if (j < G) sd_step<AS, 0, MF>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
+  if (j < G) sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
 }
 
-template <int AS, int OUT>
+template <int AS, int OUT, bool PC>
 __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restrict__ qx,
                                                         const __half *__restrict__ sx,
                                                         const uint4 *__restrict__ packed,
                                                         const uint16_t *__restrict__ meta,
-                                                        const __half *__restrict__ sw, void *__restrict__ out,
+                                                        const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
+    const int *__restrict__ trow, void *__restrict__ out,
                                                         int M, int N, int K, int splits, int *__restrict__ ws) {
   static_assert(AS == 2 || AS == 3, "two or three A stages");
   extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
@@ -976,25 +996,24 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
   // codes of group 2 into the set just consumed
   for (int g = 0; g < AS - 1; ++g) sd_copy_a<AS>(min(g, G - 1), lds, asrc, wave);
   SdCodes set0, set1;
-  sd_load_codes(set0, packed, meta, boff, moff, 0);
-  sd_load_codes(set1, packed, meta, boff, moff, min(1, G - 1));
+  sd_load_codes<PC>(set0, packed, meta, boff, moff, 0);
+  sd_load_codes<PC>(set1, packed, meta, boff, moff, min(1, G - 1));
   {
-    const GroupConsts g = group_consts(set0.md);
     v4i b[4];
-    dequant_lane(set0.p0, g, b[0], b[2]);
-    dequant_lane(set0.p1, g, b[1], b[3]);
+    weights_lane<PC>(set0.p0, set0.md, b[0], b[2]);
+    weights_lane<PC>(set0.p1, set0.md, b[1], b[3]);
     int8_t *dst = lds + AS * kSdStageA + wave * 4096 + 16 * lane;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
   }
-  sd_load_codes(set0, packed, meta, boff, moff, min(2, G - 1));
+  sd_load_codes<PC>(set0, packed, meta, boff, moff, min(2, G - 1));
   QOQ_WAIT_VMCNT(0);
   __syncthreads();
 
   if (wave < 4)
-    sd_loop<AS, false>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+    sd_loop<AS, false, PC>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
   else
-    sd_loop<AS, true>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+    sd_loop<AS, true, PC>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
   QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
   __syncthreads();
   const int wm0 = m0 + 64 * (wave & 3);
@@ -1005,7 +1024,7 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
     return;
   }
   static_assert(8 * 32 * (64 * 4 + 16) <= sd_lds_bytes<AS>(), "epilogue scratch exceeds the LDS in use");
-  epilogue32<2, 4, OUT>(acc, lds + wave * 32 * (64 * 4 + 16), lane, wm0, wn0, M, N, sx, sw, out);
+  epilogue32<2, 4, OUT, PC>(acc, lds + wave * 32 * (64 * 4 + 16), lane, wm0, wn0, M, N, sx, sw, out, zp, trow);
 }
 
 // ---------------------------------------------------------------------------
@@ -1013,10 +1032,12 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
 // takes 8 consecutive columns of one row (N % 16 == 0, so they never cross a row):
 // two 16-byte loads per slice, one 16-byte fp16 store (or two INT32 stores).
 // ---------------------------------------------------------------------------
-template <int OUT>
+template <int OUT, bool PC>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const int *__restrict__ part, int splits, int M, int N,
                                                            const __half *__restrict__ sx,
-                                                           const __half *__restrict__ sw, void *__restrict__ out) {
+                                                           const __half *__restrict__ sw,
+                                                           const uint8_t *__restrict__ zp,
+                                                           const int *__restrict__ trow, void *__restrict__ out) {
   const size_t MN = static_cast<size_t>(M) * N;
   const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
   if (e >= MN) return;
@@ -1027,12 +1048,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const int *__restrict
     lo += *reinterpret_cast<const v4i *>(p);
     hi += *reinterpret_cast<const v4i *>(p + 4);
   }
+  const int m = static_cast<int>(e / N), n = static_cast<int>(e % N);
+  if (PC) {                                    // zero point of the per-channel weights
+    const int t = trow[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] -= static_cast<int>(zp[n + i]) * t;
+      hi[i] -= static_cast<int>(zp[n + 4 + i]) * t;
+    }
+  }
   if (OUT == 1) {
     *reinterpret_cast<v4i *>(static_cast<int *>(out) + e) = lo;
     *reinterpret_cast<v4i *>(static_cast<int *>(out) + e + 4) = hi;
     return;
   }
-  const int m = static_cast<int>(e / N), n = static_cast<int>(e % N);
   const float sxm = __half2float(sx[m]);
   const int acc[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   __align__(16) __half h[8];
@@ -1045,24 +1074,22 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const int *__restrict
 // planning: which kernel and launch shape for (M, N, K)
 // ---------------------------------------------------------------------------
 typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const uint16_t *, const __half *,
-                           void *, int, int, int, int, int *);
+                           const uint8_t *, const int *, void *, int, int, int, int, int *);
 
 struct Config {
   int kind;                 // 0 skinny, 4 wide2, 5 dma2, 6 shared dequantization
   int a, b, c, d;           // skinny: MT, NBW, WAVES, U    wide2 / dma2: TM, TN    sd: A stages
-  GemmKernel k[2];          // fp16 epilogue, INT32 epilogue
+  GemmKernel k[2][2];       // [per-group, per-channel][fp16 epilogue, INT32 epilogue]
   const char *name;
   int lds = 0;              // dynamic LDS bytes
 };
 
-#define QOQ_SKINNY(MT, NBW, W, U)                                                                   \
-  {0, MT, NBW, W, U, {gemm_skinny_kernel<MT, NBW, W, U, 0>, gemm_skinny_kernel<MT, NBW, W, U, 1>}, \
-   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U},
-#define QOQ_WIDE2(TM, TN) \
-  {4, TM, TN, 0, 0, {gemm_wide2_kernel<TM, TN, 0>, gemm_wide2_kernel<TM, TN, 1>}, "wide2_tm" #TM "_tn" #TN},
-#define QOQ_DMA2(TM, TN) \
-  {5, TM, TN, 0, 0, {gemm_dma2_kernel<TM, TN, 0>, gemm_dma2_kernel<TM, TN, 1>}, "dma2_tm" #TM "_tn" #TN},
-#define QOQ_SD(AS) {6, AS, 0, 0, 0, {gemm_sd_kernel<AS, 0>, gemm_sd_kernel<AS, 1>}, "sd_as" #AS, sd_lds_bytes<AS>()},
+#define QOQ_K4(...) {{__VA_ARGS__, 0, false>, __VA_ARGS__, 1, false>}, {__VA_ARGS__, 0, true>, __VA_ARGS__, 1, true>}}
+#define QOQ_SKINNY(MT, NBW, W, U) \
+  {0, MT, NBW, W, U, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U), "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U},
+#define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
+#define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
+#define QOQ_SD(AS) {6, AS, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
 
 const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
@@ -1121,7 +1148,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
-  const int64_t tsd = ((NS + 15) / 16) * ((M + 255) / 256);    // 256 x 256 tiles
   bool split_k = true;   // may the plan split K (kinds 4 and 5)
   if (!cfg) {
     const char *force = getenv("QOQ_GEMM_REGIME");
@@ -1148,21 +1174,21 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
       }
     } else {
       // measured on MI355X over the layer shapes of the workloads: the largest tile
-      // that still gives enough workgroups to fill the chip (256 x 256 tiles share
-      // each dequantized weight over 256 rows); when no tile size does (few
-      // columns, long K), split K over about 512 workgroups
+      // that still gives enough workgroups to fill the chip; when no tile size does
+      // (few columns, long K), split K over about 512 workgroups
       split_k = true;
-      if (tsd >= 256) {
-        cfg = find_config(6, 2, 0, 0, 0);       // 256 x 256, shared dequantization
+      const int64_t t64 = ((NS + 7) / 8) * ((M + 63) / 64);   // 64 x 128 tiles
+      if (t256 >= 384) {
+        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, copy-engine A
         split_k = false;
-      } else if (t256 >= 384) {
-        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256
-        split_k = false;
+      } else if (t256 >= 192 && G >= 96) {
+        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, long K: split in two
       } else if (t128 >= 320) {
-        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128
+        cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, A staged by the waves
         split_k = false;
       } else if (M <= 64) {
-        cfg = find_config(5, 2, 1, 0, 0);       // 64 x 128, split K
+        cfg = find_config(4, 2, 1, 0, 0);       // 64 x 128
+        split_k = t64 < 192;
       } else if (t256 >= 96) {
         cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, split K
       } else {
@@ -1205,37 +1231,51 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 
 // Kernels with more than 64 KB of dynamic LDS are granted their size once per
 // process (the attribute is kept per kernel).
-std::once_flag g_lds_once[kNumConfigs][2];
+std::once_flag g_lds_once[kNumConfigs][2][2];
 
-void ensure_lds_attribute(const Config *cfg, int out_kind) {
+void ensure_lds_attribute(const Config *cfg, int pc, int out_kind) {
   if (cfg->lds <= 65536) return;
   const int idx = static_cast<int>(cfg - kConfigs);
-  std::call_once(g_lds_once[idx][out_kind], [cfg, out_kind] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(cfg->k[out_kind]),
+  std::call_once(g_lds_once[idx][pc][out_kind], [cfg, pc, out_kind] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(cfg->k[pc][out_kind]),
                               hipFuncAttributeMaxDynamicSharedMemorySize, cfg->lds);
   });
 }
 
-void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
-                      void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
+void launch_gemm_any(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
+                     const void *zp, const void *tx, void *out, int pc, int out_kind, int64_t M, int64_t N, int64_t K,
+                     void *ws, hipStream_t st) {
   const Plan p = make_plan(M, N, K);
-  ensure_lds_attribute(p.cfg, out_kind);
-  hipLaunchKernelGGL(p.cfg->k[out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
+  ensure_lds_attribute(p.cfg, pc, out_kind);
+  hipLaunchKernelGGL(p.cfg->k[pc][out_kind], p.grid, p.block, p.cfg->lds, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
-                     static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), out,
-                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.splits,
+                     static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw),
+                     static_cast<const uint8_t *>(zp), static_cast<const int *>(tx), out, static_cast<int>(M),
+                     static_cast<int>(N), static_cast<int>(K), p.splits,
                      static_cast<int *>(p.splits > 1 ? ws : nullptr));
   if (p.splits > 1) {
     const size_t threads = static_cast<size_t>(M) * N / 8;
     const dim3 g(static_cast<unsigned>((threads + 255) / 256));
-    if (out_kind == 0)
-      hipLaunchKernelGGL(split_reduce_kernel<0>, g, dim3(256), 0, st, static_cast<const int *>(ws), p.splits,
-                         static_cast<int>(M), static_cast<int>(N), static_cast<const __half *>(sx),
-                         static_cast<const __half *>(sw), out);
-    else
-      hipLaunchKernelGGL(split_reduce_kernel<1>, g, dim3(256), 0, st, static_cast<const int *>(ws), p.splits,
-                         static_cast<int>(M), static_cast<int>(N), nullptr, nullptr, out);
+    using RK = void (*)(const int *, int, int, int, const __half *, const __half *, const uint8_t *, const int *,
+                        void *);
+    const RK rk[2][2] = {{split_reduce_kernel<0, false>, split_reduce_kernel<1, false>},
+                         {split_reduce_kernel<0, true>, split_reduce_kernel<1, true>}};
+    hipLaunchKernelGGL(rk[pc][out_kind], g, dim3(256), 0, st, static_cast<const int *>(ws), p.splits,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<const __half *>(sx),
+                       static_cast<const __half *>(sw), static_cast<const uint8_t *>(zp),
+                       static_cast<const int *>(tx), out);
   }
+}
+
+void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
+                      void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t st) {
+  launch_gemm_any(qx, sx, packed, meta, sw, nullptr, nullptr, out, 0, out_kind, M, N, K, ws, st);
+}
+
+void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const void *packed, const void *zeros,
+                         const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws,
+                         hipStream_t st) {
+  launch_gemm_any(qx, sx, packed, nullptr, sw, zeros, tx, out, 1, out_kind, M, N, K, ws, st);
 }
 
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).ws_bytes; }

@@ -12,12 +12,21 @@ void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, 
                                  hipStream_t stream);
 void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *packed, void *meta,
                                   void *sw, hipStream_t stream);
+void launch_quantize_pack_weights_pc(const void *w, int64_t N, int64_t K, void *packed, void *zeros, void *sw,
+                                     hipStream_t stream);
+void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
+                                        hipStream_t stream);
 
 // GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators; ws holds at least
 // gemm_workspace_need(M, N, K) bytes (may be null when that is 0)
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta,
                       const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws,
                       hipStream_t stream);
+// per-channel weights: B = raw codes, epilogue acc - zeros[n] * tx[m] (same plans
+// and workspace as the per-group GEMM)
+void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const void *packed, const void *zeros,
+                         const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws,
+                         hipStream_t stream);
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K);
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);

@@ -20,10 +20,22 @@ namespace qoq {
 constexpr int kActThreads = 256;
 constexpr int kActChunks = 16;   // 16 x 8 halves x 256 threads = rows up to K = 32768
 
+// sum of the 8 signed codes of a chunk (v_dot4_i32_i8 against ones)
+__device__ __forceinline__ int code_sum8(uint2 q) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(q.x), 0x01010101, 0, false) +
+         __builtin_amdgcn_sdot4(static_cast<int>(q.y), 0x01010101, 0, false);
+}
+
+// ROWSUM: also t[row] = sum_k qx[row, k] (the activation term of the per-channel
+// epilogue, "QServe ..." summary, per-channel fast dequantization: t_X is computed
+// by the memory-bound kernel that precedes the GEMM)
+template <bool ROWSUM>
 __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half *__restrict__ x, int K,
                                                                    int8_t *__restrict__ qx,
-                                                                   __half *__restrict__ sx) {
+                                                                   __half *__restrict__ sx,
+                                                                   int *__restrict__ tx) {
   __shared__ unsigned red[kActThreads / 64];
+  __shared__ int tred[kActThreads / 64];
   const int row = blockIdx.x;
   const int nchunk = K >> 3;
   const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(row) * K);
@@ -52,20 +64,47 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
   const float s = __half2float(sh);
   if (threadIdx.x == 0) sx[row] = sh;
 
+  int tsum = 0;
 #pragma unroll
   for (int c = 0; c < kActChunks; ++c) {
     int idx = threadIdx.x + c * kActThreads;
-    if (idx < nchunk) qr[idx] = quant_chunk8(v[c], s);
+    if (idx < nchunk) {
+      const uint2 q = quant_chunk8(v[c], s);
+      qr[idx] = q;
+      if (ROWSUM) tsum += code_sum8(q);
+    }
   }
-  for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads)
-    qr[idx] = quant_chunk8(xr[idx], s);
+  for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads) {
+    const uint2 q = quant_chunk8(xr[idx], s);
+    qr[idx] = q;
+    if (ROWSUM) tsum += code_sum8(q);
+  }
+  if (ROWSUM) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tsum += __shfl_xor(tsum, off, 64);
+    if ((threadIdx.x & 63) == 0) tred[threadIdx.x >> 6] = tsum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int t = 0;
+#pragma unroll
+      for (int w = 0; w < kActThreads / 64; ++w) t += tred[w];
+      tx[row] = t;
+    }
+  }
 }
 
 void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, void *sx,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(quantize_act_kernel, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
+  hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
                      static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
-                     static_cast<__half *>(sx));
+                     static_cast<__half *>(sx), nullptr);
+}
+
+void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
+                                        hipStream_t stream) {
+  hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
+                     static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
+                     static_cast<__half *>(sx), static_cast<int *>(tx));
 }
 
 // ---------------------------------------------------------------------------
@@ -77,6 +116,23 @@ void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, 
 // codes of bytes i = 2l mod 16, i+1 in slot h = l / 8; lane l + 32 holds the
 // matching high-nibble codes (k + 64).
 // ---------------------------------------------------------------------------
+// Store one group's codes of channel c of strip b: lane l holds the codes of k = 2l,
+// 2l+1 of the group.  For l < 32 those are the low-nibble codes of bytes i = 2l mod
+// 16, i+1 in slot h = l / 8; lane l + 32 holds the matching high-nibble codes (k + 64).
+__device__ __forceinline__ void store_group_codes(unsigned u0, unsigned u1, int lane, uint8_t *__restrict__ packed,
+                                                  int b, int G, int j, int c) {
+  const unsigned two = u0 | (u1 << 8);                                  // low nibbles
+  const unsigned upper = static_cast<unsigned>(__shfl_down(static_cast<int>(two), 32, 64));
+  const unsigned bytes2 = two | (upper << 4);                           // valid for lane < 32
+  const unsigned next = static_cast<unsigned>(__shfl_down(static_cast<int>(bytes2), 1, 64));
+  if (lane < 32 && (lane & 1) == 0) {
+    const int h = lane >> 3;
+    const int i = (2 * lane) & 15;                                      // 0, 4, 8, 12
+    const size_t off = (static_cast<size_t>(b * G + j) * 64 + 16 * h + c) * 16 + i;
+    *reinterpret_cast<unsigned *>(packed + off) = (bytes2 & 0xffffu) | (next << 16);
+  }
+}
+
 __device__ __forceinline__ int w_code(unsigned half_bits, float s) {
   return sym_code(half_bits_to_float(half_bits), s, kWQmax);
 }
@@ -110,18 +166,75 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const __half *__restr
     int z = min(max(rne_div(-lo, su), 0), 15);
     unsigned u0 = static_cast<unsigned>(min(max(z + rne_div(q0, su), 0), 15));
     unsigned u1 = static_cast<unsigned>(min(max(z + rne_div(q1, su), 0), 15));
-    unsigned two = u0 | (u1 << 8);                                    // low nibbles
-    unsigned upper = static_cast<unsigned>(__shfl_down(static_cast<int>(two), 32, 64));
-    unsigned bytes2 = two | (upper << 4);                             // valid for lane < 32
-    unsigned next = static_cast<unsigned>(__shfl_down(static_cast<int>(bytes2), 1, 64));
-    if (lane < 32 && (lane & 1) == 0) {
-      const int h = lane >> 3;
-      const int i = (2 * lane) & 15;                                  // 0, 4, 8, 12
-      size_t off = (static_cast<size_t>(b * G + j) * 64 + 16 * h + c) * 16 + i;
-      *reinterpret_cast<unsigned *>(packed + off) = (bytes2 & 0xffffu) | (next << 16);
-    }
+    store_group_codes(u0, u1, lane, packed, b, G, j, c);
     if (lane == 0) meta[static_cast<size_t>(b * G + j) * 16 + c] = static_cast<uint16_t>(su | (z << 8));
   }
+}
+
+// ---------------------------------------------------------------------------
+// per-channel packer: one wave per output channel n.
+//   pass 1: min / max of the row (widened to contain 0) -> s_W[n] (fp16), z[n]
+//   pass 2: per group of 128 the codes q = clamp(z + rint(w / s_W), 0, 15), in the
+//           same storage layout as the per-group packer.
+// ("QServe ..." summary, integer quantization (asymmetric, zero point) with one
+// scale and zero per output channel; per-channel fast dequantization)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_weights_pc_kernel(const __half *__restrict__ w, int N, int K,
+                                                              uint8_t *__restrict__ packed,
+                                                              uint8_t *__restrict__ zeros,
+                                                              __half *__restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const __half *wr = w + static_cast<size_t>(n) * K;
+
+  float lo = 0.0f, hi = 0.0f;                                         // the range contains 0
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(wr + k);
+    const unsigned u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = half_bits_to_float(u[i] & 0xffffu), b = half_bits_to_float(u[i] >> 16);
+      lo = fminf(lo, fminf(a, b));
+      hi = fmaxf(hi, fmaxf(a, b));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+  }
+  float q = __fdiv_rn(hi - lo, 15.0f);
+  __asm__ volatile("" : "+v"(q));       // the fp32 quotient is rounded before narrowing
+  const __half sh = __float2half_rn(q);
+  const float s = __half2float(sh);
+  const int z = s == 0.0f ? 0 : static_cast<int>(fminf(fmaxf(rintf(__fdiv_rn(-lo, s)), 0.0f), 15.0f));
+  if (lane == 0) {
+    sw[n] = sh;
+    zeros[n] = static_cast<uint8_t>(z);
+  }
+
+  const int G = K / kGroup;
+  const int b = n >> 4, c = n & 15;
+  for (int j = 0; j < G; ++j) {
+    const unsigned pair = *reinterpret_cast<const unsigned *>(wr + kGroup * j + 2 * lane);
+    unsigned u[2] = {0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float r = rintf(__fdiv_rn(half_bits_to_float((pair >> (16 * e)) & 0xffffu), s));
+        u[e] = static_cast<unsigned>(fminf(fmaxf(static_cast<float>(z) + r, 0.0f), 15.0f));
+      }
+    }
+    store_group_codes(u[0], u[1], lane, packed, b, G, j, c);
+  }
+}
+
+void launch_quantize_pack_weights_pc(const void *w, int64_t N, int64_t K, void *packed, void *zeros, void *sw,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(pack_weights_pc_kernel, dim3(static_cast<unsigned>((N + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const __half *>(w), static_cast<int>(N), static_cast<int>(K),
+                     static_cast<uint8_t *>(packed), static_cast<uint8_t *>(zeros), static_cast<__half *>(sw));
 }
 
 void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *packed, void *meta, void *sw,

@@ -40,6 +40,11 @@ _SIGNATURES = {
     "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
                           ctypes.c_int),
     "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
+                          _c_vp], ctypes.c_int),
+    "qoq_w4a8_gemm_pc_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp],
+                             ctypes.c_int),
     "qoq_linear_workspace_bytes": ([_c_i64, _c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz)], ctypes.c_int),
     "qoq_w4a8_linear": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz,
                          _c_vp], ctypes.c_int),
@@ -160,18 +165,21 @@ def gemm_configs() -> list:
 # offline weight quantization + packing
 # ---------------------------------------------------------------------------
 def quantize_pack_weights(w: torch.Tensor, group: int = GROUP, out=None):
-    """W fp16 [N, K] -> (packed uint8 [N*K/2], meta int16 [N*K/128] (uint16 bits), s_w fp16 [N])."""
+    """W fp16 [N, K] -> (packed uint8 [N*K/2], meta, s_w fp16 [N]).
+    group 128: meta int16 [N*K/128] (uint16 bits); group 0 (per-channel): meta =
+    the zeros, uint8 [N]."""
     N, K = w.shape
     sizes = weight_buffer_sizes(N, K, group)
+    mdt = torch.uint8 if group == 0 else torch.int16
     if out is None:
         packed = torch.empty(sizes["packed_w"], dtype=torch.uint8, device=w.device)
-        meta = torch.empty(sizes["group_meta"] // 2, dtype=torch.int16, device=w.device)
+        meta = torch.empty(sizes["group_meta"] // (1 if group == 0 else 2), dtype=mdt, device=w.device)
         s_w = torch.empty(N, dtype=torch.float16, device=w.device)
     else:
         packed, meta, s_w = out
     _check("qoq_quantize_pack_weights",
            lib().qoq_quantize_pack_weights(_dev(w, "w", torch.float16), N, K, group,
-                                           _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
+                                           _dev(packed, "packed", torch.uint8), _dev(meta, "meta", mdt),
                                            _dev(s_w, "s_w", torch.float16), _stream(w)))
     return packed, meta, s_w
 
@@ -193,9 +201,52 @@ def quantize_activations(x: torch.Tensor, out=None):
     return qx, s_x
 
 
+def quantize_activations_rowsum(x: torch.Tensor, out=None):
+    """X fp16 [M, K] -> (qx int8 [M, K], s_x fp16 [M], t int32 [M] = sum_k qx)."""
+    M, K = x.shape
+    if out is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        s_x = torch.empty(M, dtype=torch.float16, device=x.device)
+        t = torch.empty(M, dtype=torch.int32, device=x.device)
+    else:
+        qx, s_x, t = out
+    _check("qoq_quantize_activations_rowsum",
+           lib().qoq_quantize_activations_rowsum(_dev(x, "x", torch.float16), M, K, _dev(qx, "qx", torch.int8),
+                                                 _dev(s_x, "s_x", torch.float16), _dev(t, "t", torch.int32),
+                                                 _stream(x)))
+    return qx, s_x, t
+
+
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
+def w4a8_gemm_pc(qx, s_x, t, packed, zeros, s_w, N: int, out=None, workspace=None):
+    """Per-channel weights: out fp16 [M, N] = fp16((sum qx q - z t) * (s_x * s_w))."""
+    M, K = qx.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=qx.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, GROUP)
+    _check("qoq_w4a8_gemm_pc",
+           lib().qoq_w4a8_gemm_pc(_dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
+                                  _dev(t, "t", torch.int32), _dev(packed, "packed", torch.uint8),
+                                  _dev(zeros, "zeros", torch.uint8), _dev(s_w, "s_w", torch.float16),
+                                  _dev(out, "out", torch.float16), M, N, K, ws_ptr, ws_bytes, _stream(qx)))
+    return out
+
+
+def w4a8_gemm_pc_i32(qx, t, packed, zeros, N: int, out=None, workspace=None):
+    """Per-channel weights: acc int32 [M, N] = sum_k qx (q - z), exact."""
+    M, K = qx.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=qx.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, GROUP)
+    _check("qoq_w4a8_gemm_pc_i32",
+           lib().qoq_w4a8_gemm_pc_i32(_dev(qx, "qx", torch.int8), _dev(t, "t", torch.int32),
+                                      _dev(packed, "packed", torch.uint8), _dev(zeros, "zeros", torch.uint8),
+                                      _dev(out, "acc", torch.int32), M, N, K, ws_ptr, ws_bytes, _stream(qx)))
+    return out
+
+
 # Split-K workspaces, one per (device, stream), grown when a shape needs more.
 _workspaces = {}
 

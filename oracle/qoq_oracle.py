@@ -36,14 +36,16 @@ R5  Level-0 scale s_W = fp16(absmax / 119) (protective range), computed as an IE
 R6  Activations: per-token symmetric INT8 in [-127, 127], s_X = fp16(absmax / 127).
 R7  Epilogue: out = fp16( float32(acc) * (float32(s_X[m]) * float32(s_W[n])) ).
 R8  An all-zero row (or a scale that rounds to fp16 zero) quantizes to code 0.
-R9  Per-channel variant (the format without groups): per output channel asymmetric
+R12 Per-channel variant (the format without groups): per output channel asymmetric
     UINT4 with an integer UINT4 zero and an fp16 scale s_W = fp16((max - min) / 15)
     over the channel's range widened to contain 0 (R4), fp32 subtract and divide,
     code q = clamp(z + rne(w / s_W), 0, 15) (R2), z = clamp(rne(-min / s_W), 0, 15).
-R10 Its epilogue term t_X x (z_W ⊙ s_W) takes t_X over the quantized activations,
+R13 Its epilogue term t_X x (z_W ⊙ s_W) takes t_X over the quantized activations,
     t[m] = sum_k qx[m, k] (so s_X t is the row sum of X_hat = Q_X s_X): the epilogue
     is then an exact rearrangement of sum_k X_hat W_hat, and the GEMM result is the
     plain integer contraction sum_k qx (q - z) with the fp16 epilogue of R7.
+(R9-R11 concern the protective-range bound, the level-1 equation and the unpack
+count; they are listed with the design notes.)
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
 the worked example printed on the pages, exhaustive bound sweeps of the protective
@@ -272,7 +274,7 @@ def w4a8_reference(x16: np.ndarray, w16: np.ndarray):
 #     [QServe summary] "整数量化": Q = round(X/s + z), s = (Xmax - Xmin)/(qmax - qmin),
 #     z = round(qmin - Xmin/s), here with one (s, z) per output channel ("逐通道W4A8
 #     GEMM中的快速反量化": the zero point is per channel, so it can leave the main
-#     loop); [Inference chapter] §4.1 asymmetric quantizer; readings R1, R2, R4, R8, R9.
+#     loop); [Inference chapter] §4.1 asymmetric quantizer; readings R1, R2, R4, R8, R12.
 # ---------------------------------------------------------------------------
 def quantize_weights_per_channel(w16: np.ndarray):
     """W fp16 [N, K] -> (q_u4 uint8 [N, K], z uint8 [N], s_W fp16 [N])."""
@@ -301,7 +303,7 @@ def dequantize_per_channel(q_u4: np.ndarray, z: np.ndarray) -> np.ndarray:
 # O9  t[m] = sum_k qx[m, k], the activation row sum of the per-channel epilogue
 #     [QServe summary] "逐通道W4A8 GEMM中的快速反量化": the second term becomes
 #     t_X x (z_W ⊙ s_W) with t_X = X 1_k, precomputed by the preceding memory-bound
-#     kernel; reading R10 (over the quantized activations).
+#     kernel; reading R13 (over the quantized activations).
 # ---------------------------------------------------------------------------
 def activation_row_sums(qx: np.ndarray) -> np.ndarray:
     return np.asarray(qx, dtype=np.int64).sum(axis=1).astype(np.int32)
@@ -309,7 +311,7 @@ def activation_row_sums(qx: np.ndarray) -> np.ndarray:
 
 def w4a8_pc_reference(x16: np.ndarray, w16: np.ndarray):
     """Every intermediate of the per-channel path for X fp16 [M,K], W fp16 [N,K].
-    acc = sum_k qx (q - z) (exact), out = fp16(acc * (s_X * s_W)) (R7, R10)."""
+    acc = sum_k qx (q - z) (exact), out = fp16(acc * (s_X * s_W)) (R7, R13)."""
     q_u4, z, s_w = quantize_weights_per_channel(w16)
     w_hat = dequantize_per_channel(q_u4, z)
     qx, s_x = quantize_activations(x16)

@@ -371,7 +371,7 @@ def test_generator_is_seeded():
 
 
 # ---------------------------------------------------------------------------
-# per-channel variant (readings R9, R10)
+# per-channel variant (readings R12, R13)
 # ---------------------------------------------------------------------------
 def _exact_pc_quant(row):
     """Per-channel asymmetric UINT4 of one fp16 row by exact rational arithmetic

@@ -12,7 +12,8 @@ dominant kernel (timed with HIP events on the stream the kernels run on) and the
 CPU oracle timed on the host cores.
 
 --sweep runs every layer shape / batch size of the workload registry and writes a
-table to gpurun_out/sweep.json (not the headline line).
+table to gpurun_out/sweep.json (not the headline line); with --format channel it
+measures the per-channel weight format instead (gpurun_out/sweep_channel.json).
 """
 
 from __future__ import annotations
@@ -47,24 +48,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-launches", type=int, default=200)
+    ap.add_argument("--format", choices=("group", "channel"), default="group",
+                    help="weight format: per-group g128 (default) or the per-channel variant")
     return ap.parse_args()
 
 
 class Case:
     """Resident, rotated buffers for one (layer, M)."""
 
-    def __init__(self, L, M, dev, packed_sets):
+    def __init__(self, L, M, dev, packed_sets, per_channel=False):
         import torch
         from w4a8_mixed_precision_amd import workloads as wl
         self.L, self.M = L, M
+        self.pc = per_channel
         self.sets = packed_sets
         x16 = wl.activations_fp16(L, M)
         self.x = torch.from_numpy(x16).to(dev)
         self.qx = torch.empty((M, L.K), dtype=torch.int8, device=dev)
         self.sx = torch.empty(M, dtype=torch.float16, device=dev)
+        self.tx = torch.empty(M, dtype=torch.int32, device=dev)
         self.out = torch.empty((M, L.N), dtype=torch.float16, device=dev)
         self.ops = wl.algorithmic_ops(M, L.N, L.K)
-        self.bytes = wl.algorithmic_bytes(M, L.N, L.K)
+        self.bytes = wl.algorithmic_bytes(M, L.N, L.K, per_channel)
         self.ws = None
         self.lws = None
         self.i = 0
@@ -88,6 +93,11 @@ class Case:
     def step(self, q):
         """The runtime path: quantize + GEMM in one library call (one fused kernel
         for few tokens, else the quantizer and the GEMM plan)."""
+        if self.pc:
+            # per-channel format: the quantizer (with code sums) and the GEMM
+            self.quant_only(q)
+            self.gemm_only(q)
+            return
         p, m, s = self.sets[self.i % len(self.sets)]
         self.i += 1
         q.w4a8_linear(self.x, p, m, s, self.L.N, out=self.out, workspace=self.linear_workspace(q))
@@ -95,25 +105,33 @@ class Case:
     def gemm_only(self, q):
         p, m, s = self.sets[self.i % len(self.sets)]
         self.i += 1
-        q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
+        if self.pc:
+            q.w4a8_gemm_pc(self.qx, self.sx, self.tx, p, m, s, self.L.N, out=self.out,
+                           workspace=self.workspace(q))
+        else:
+            q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
 
     def quant_only(self, q):
-        q.quantize_activations(self.x, out=(self.qx, self.sx))
+        if self.pc:
+            q.quantize_activations_rowsum(self.x, out=(self.qx, self.sx, self.tx))
+        else:
+            q.quantize_activations(self.x, out=(self.qx, self.sx))
 
 
-def packed_sets_for(L, dev, q, max_sets=128):
+def packed_sets_for(L, dev, q, max_sets=128, per_channel=False):
     """Pack the layer's weights once, then clone the packed buffers until the
-    rotation covers ROTATE_BYTES (at least 2 sets)."""
+    rotation covers ROTATE_BYTES (at least 2 sets).  Per-channel format: the second
+    buffer holds one zero byte per channel instead of the group metadata."""
     import torch
     from w4a8_mixed_precision_amd import workloads as wl
     w = torch.from_numpy(wl.weights_fp16(L)).to(dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    p, m, s = q.quantize_pack_weights(w)
+    p, m, s = q.quantize_pack_weights(w, group=0 if per_channel else 128)
     torch.cuda.synchronize()
     pack_s = time.perf_counter() - t0
     del w
-    wbytes = p.numel() + m.numel() * 2 + s.numel() * 2
+    wbytes = p.numel() + m.numel() * m.element_size() + s.numel() * 2
     n = max(2, min(max_sets, -(-ROTATE_BYTES // wbytes)))
     sets = [(p, m, s)] + [(p.clone(), m.clone(), s.clone()) for _ in range(n - 1)]
     torch.cuda.synchronize()
@@ -236,7 +254,8 @@ def run_case_metrics(c, q, torch, launches):
     b = c.bytes
     return {
         "M": c.M, "K": c.L.K, "N": c.L.N, "plan": q.gemm_plan(c.M, c.L.N, c.L.K),
-        "linear_plan": q.linear_plan(c.M, c.L.N, c.L.K), "linear_us": s * 1e6,
+        "linear_plan": "quant_rowsum+gemm_pc" if c.pc else q.linear_plan(c.M, c.L.N, c.L.K),
+        "linear_us": s * 1e6, "format": "channel" if c.pc else "group",
         "gemm_us": g * 1e6, "quant_us": a * 1e6,
         "TOPS": c.ops / g / 1e12,
         "weight_GBps": b["weight"] / g / 1e9,
@@ -258,13 +277,13 @@ def copy_ceiling(q, torch, dev, nbytes=1 << 30, reps=10):
     return {"bytes_per_launch": 2 * nbytes, "us": t * 1e6, "GBps": 2 * nbytes / t / 1e9}
 
 
-def sweep(q, torch, dev, launches):
+def sweep(q, torch, dev, launches, per_channel=False):
     from w4a8_mixed_precision_amd import workloads as wl
     rows = []
     for L in wl.LAYERS:
-        sets, pack_s = packed_sets_for(L, dev, q)
+        sets, pack_s = packed_sets_for(L, dev, q, per_channel=per_channel)
         for M in L.Ms:
-            c = Case(L, M, dev, sets)
+            c = Case(L, M, dev, sets, per_channel)
             for _ in range(3):
                 c.step(q)
             torch.cuda.synchronize()
@@ -276,7 +295,8 @@ def sweep(q, torch, dev, launches):
         del sets
         torch.cuda.empty_cache()
     os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "sweep.json"), "w") as f:
+    name = "sweep_channel.json" if per_channel else "sweep.json"
+    with open(os.path.join(ROOT, "gpurun_out", name), "w") as f:
         json.dump(rows, f, indent=1)
     return rows
 
@@ -297,8 +317,12 @@ def main():
     qoq.lib()
 
     if args.sweep:
-        sweep(qoq, torch, dev, args.kernel_launches)
+        sweep(qoq, torch, dev, args.kernel_launches, args.format == "channel")
         return
+    if args.format != "group":
+        print("the headline line measures the per-group format; use --format channel with --sweep",
+              file=sys.stderr)
+        sys.exit(2)
 
     L = wl.find(args.layer)
     Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else L.Ms

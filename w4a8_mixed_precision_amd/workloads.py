@@ -88,12 +88,18 @@ def activations_fp16(L: Layer, M: int, K: int | None = None) -> np.ndarray:
     return x.astype(np.float16)
 
 
-def algorithmic_bytes(M: int, N: int, K: int) -> dict:
+def algorithmic_bytes(M: int, N: int, K: int, per_channel: bool = False) -> dict:
     """Bytes the GEMM must move at least once: packed weights (4 bit), group metadata
     counted at its UINT4 zero + UINT8 scale size (1.5 B per group), fp16 channel
-    scales, INT8 activations, fp16 token scales and the fp16 output."""
-    weight = N * K // 2 + (3 * N * (K // GROUP)) // 2 + 2 * N
-    act = M * K + 2 * M
+    scales, INT8 activations, fp16 token scales and the fp16 output.  Per-channel
+    format: no group metadata, a UINT4 zero per channel (0.5 B) and an INT32 code sum
+    per token."""
+    if per_channel:
+        weight = N * K // 2 + N // 2 + 2 * N
+        act = M * K + 2 * M + 4 * M
+    else:
+        weight = N * K // 2 + (3 * N * (K // GROUP)) // 2 + 2 * N
+        act = M * K + 2 * M
     out = 2 * M * N
     return {"weight": weight, "act": act, "out": out, "total": weight + act + out}
 

@@ -68,6 +68,11 @@ class Case:
         self.sx = torch.empty(M, dtype=torch.float16, device=dev)
         self.tx = torch.empty(M, dtype=torch.int32, device=dev)
         self.out = torch.empty((M, L.N), dtype=torch.float16, device=dev)
+        # up to 64 tokens the linear step feeds the GEMM tiled codes; the GEMM and
+        # quantizer timings below use the same kernels
+        from w4a8_mixed_precision_amd import qoq
+        self.tiled = (not per_channel) and M <= qoq.TILED_MAX_M
+        self.qt = torch.empty(qoq.tiled_bytes(M, L.K), dtype=torch.int8, device=dev) if self.tiled else None
         self.ops = wl.algorithmic_ops(M, L.N, L.K)
         self.bytes = wl.algorithmic_bytes(M, L.N, L.K, per_channel)
         self.ws = None
@@ -108,12 +113,16 @@ class Case:
         if self.pc:
             q.w4a8_gemm_pc(self.qx, self.sx, self.tx, p, m, s, self.L.N, out=self.out,
                            workspace=self.workspace(q))
+        elif self.tiled:
+            q.w4a8_gemm_tiled(self.qt, self.sx, p, m, s, self.M, self.L.N, self.L.K, out=self.out)
         else:
             q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
 
     def quant_only(self, q):
         if self.pc:
             q.quantize_activations_rowsum(self.x, out=(self.qx, self.sx, self.tx))
+        elif self.tiled:
+            q.quantize_activations_tiled(self.x, out=(self.qt, self.sx))
         else:
             q.quantize_activations(self.x, out=(self.qx, self.sx))
 
@@ -253,7 +262,8 @@ def run_case_metrics(c, q, torch, launches):
     s = time_launches(lambda: c.step(q), launches, torch)
     b = c.bytes
     return {
-        "M": c.M, "K": c.L.K, "N": c.L.N, "plan": q.gemm_plan(c.M, c.L.N, c.L.K),
+        "M": c.M, "K": c.L.K, "N": c.L.N,
+        "plan": q.gemm_tiled_plan(c.M, c.L.N, c.L.K) + ":tiled" if c.tiled else q.gemm_plan(c.M, c.L.N, c.L.K),
         "linear_plan": "quant_rowsum+gemm_pc" if c.pc else q.linear_plan(c.M, c.L.N, c.L.K),
         "linear_us": s * 1e6, "format": "channel" if c.pc else "group",
         "gemm_us": g * 1e6, "quant_us": a * 1e6,

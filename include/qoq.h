@@ -116,6 +116,20 @@ int qoq_quantize_activations(const void *x_fp16, int64_t M, int64_t K, void *qx_
 int qoq_quantize_activations_rowsum(const void *x_fp16, int64_t M, int64_t K, void *qx_i8,
                                     void *s_x_fp16, int32_t *t_x, void *stream);
 
+/* qoq_quantize_activations with the codes in the tiled layout that the few-token
+ * GEMM reads (qoq_w4a8_gemm_tiled): the codes of rows 16*rb .. +15 and k = 64*kb ..
+ * +63 form a 1 KB block at byte (rb * K/64 + kb) * 1024, in which the 16 bytes
+ * k = 64*kb + 16*q .. +15 of row 16*rb + r sit at offset (16*q + r) * 16 — the order
+ * in which the 16x16x64 INT8 matrix instruction takes its A operand, one 16-byte
+ * load per lane.  This is the compute-order layout idea the pages apply to the
+ * weights ("QServe：把 W4A8KV4 ..." review §3.2), applied here to the activations by
+ * the kernel that produces them.  qx_tiled: round_up(M, 16) * K bytes, 16-byte
+ * aligned; the rows past M of the last block are not written (the GEMM does not
+ * read them).  s_x_fp16 as for qoq_quantize_activations.  M <= 64, K % 64 == 0.
+ * Errors: INVALID, UNSUPPORTED (M > 64), ALIGNMENT, HIP. */
+int qoq_quantize_activations_tiled(const void *x_fp16, int64_t M, int64_t K, void *qx_tiled,
+                                   void *s_x_fp16, void *stream);
+
 /* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
  * It is non-zero when the plan splits the K groups of each output tile over several
  * workgroups ("QServe：把 W4A8KV4 ..." review §3.2: split-k when the batch is small;
@@ -151,6 +165,22 @@ int qoq_w4a8_gemm_i32(const void *qx_i8, const void *packed_w, const void *group
                       int32_t *acc_i32, int64_t M, int64_t N, int64_t K, int32_t group,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* qoq_w4a8_gemm for M <= 64 with the activation codes in the tiled layout of
+ * qoq_quantize_activations_tiled: same arithmetic and results; the few-token
+ * kernels only (no split-K workspace).  Errors: as qoq_w4a8_gemm, UNSUPPORTED for
+ * M > 64. */
+int qoq_w4a8_gemm_tiled(const void *qx_tiled, const void *s_x_fp16, const void *packed_w,
+                        const void *group_meta, const void *s_w_fp16, void *out_fp16, int64_t M,
+                        int64_t N, int64_t K, void *stream);
+
+/* The same with the INT32 epilogue (exact accumulators, as qoq_w4a8_gemm_i32). */
+int qoq_w4a8_gemm_tiled_i32(const void *qx_tiled, const void *packed_w, const void *group_meta,
+                            int32_t *acc_i32, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Name of the configuration qoq_w4a8_gemm_tiled launches ("invalid" for a shape it
+ * rejects). */
+const char *qoq_gemm_tiled_plan(int64_t M, int64_t N, int64_t K);
+
 /* W4A8 GEMM on per-channel weights ("QServe ..." summary, per-channel fast
  * dequantization: O = (Q_X Q_W) ⊙ (s_W x s_X) - t_X x (z_W ⊙ s_W); the main loop
  * multiplies the raw UINT4 codes, the zero point is applied in the epilogue):
@@ -170,17 +200,20 @@ int qoq_w4a8_gemm_pc_i32(const void *qx_i8, const int32_t *t_x, const void *pack
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace in bytes qoq_w4a8_linear needs for this problem: 0 when the fused
- * kernel serves it (M <= 16 and K <= 8192), otherwise room for qx (M*K bytes) and
- * s_X (2*M bytes), each rounded up to 256 bytes, plus qoq_gemm_workspace_bytes.
- * Errors: INVALID, UNSUPPORTED. */
+ * kernel serves it (qoq_linear_plan names a fused configuration), otherwise room for
+ * the codes (M <= 64: round_up(M, 16)*K bytes, tiled; else M*K, row-major) and s_X
+ * (2*M bytes), each rounded up to 256 bytes, plus, for M > 64,
+ * qoq_gemm_workspace_bytes.  Errors: INVALID, UNSUPPORTED. */
 int qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, size_t *bytes);
 
 /* The runtime step in one call: per-token activation quantization followed by the
  * W4A8 GEMM with its fp16 epilogue — the same arithmetic, codes, scales and fp16
  * results as qoq_quantize_activations + qoq_w4a8_gemm ("QServe ..." summary: the
  * activation quantization is fused into the kernel that feeds the GEMM, so it costs
- * no pass of its own).  For M <= 16 and K <= 8192 one kernel does both: each
- * workgroup quantizes the token rows into LDS and runs the GEMM on them.
+ * no pass of its own).  For a few tokens (M <= 8, K <= 8192, see qoq_linear_plan)
+ * one kernel does both: each workgroup quantizes the token rows into LDS and runs the
+ * GEMM on them; up to 64 tokens the codes go through the tiled layout
+ * (qoq_quantize_activations_tiled + qoq_w4a8_gemm_tiled); beyond, row-major.
  * x_fp16 [M,K] row-major fp16 (16-byte aligned); packed_w / group_meta / s_w_fp16 as
  * for qoq_w4a8_gemm; out_fp16 [M,N] (16-byte aligned); s_x_fp16: NULL, or [M] fp16
  * that receives the token scales.  workspace: caller-owned device memory of
@@ -193,8 +226,8 @@ int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_
                     void *stream);
 
 /* Name of the kernel configuration qoq_w4a8_linear uses for this shape: a fused
- * configuration, or the qoq_gemm_plan name when it quantizes and multiplies in two
- * kernels ("invalid" for a shape it rejects).  QOQ_LINEAR_CONFIG=<fused name> or
+ * configuration, or the qoq_gemm_tiled_plan (M <= 64) / qoq_gemm_plan name when it
+ * quantizes and multiplies in two kernels ("invalid" for a shape it rejects).  QOQ_LINEAR_CONFIG=<fused name> or
  * "unfused" in the environment forces the choice where the shape allows it. */
 const char *qoq_linear_plan(int64_t M, int64_t N, int64_t K);
 

@@ -185,30 +185,59 @@ def test_binding_rejects_cpu_tensors():
 
 def test_linear_plan_and_workspace(monkeypatch):
     """Fused linear for a few tokens and K <= 8192 (no workspace); two kernels
-    otherwise, with room for qx and s_X before the GEMM's own workspace."""
+    otherwise: tiled codes (whole 16-row blocks) and s_X up to 64 tokens, row-major
+    codes, s_X and the GEMM's own workspace beyond."""
     fused = qoq.linear_configs()
     assert len(fused) >= 2
     assert qoq.linear_plan(1, 6144, 4096) in fused
     assert qoq.linear_plan(8, 512, 512) in fused
     assert qoq.linear_workspace_bytes(1, 6144, 4096) == 0
-    assert qoq.linear_plan(1, 59136, 8192) == qoq.gemm_plan(1, 59136, 8192)     # too much repeated work
-    assert qoq.linear_plan(16, 6144, 4096) == qoq.gemm_plan(16, 6144, 4096)
-    assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_plan(17, 6144, 4096)
-    assert qoq.linear_plan(1, 4096, 14336) == qoq.gemm_plan(1, 4096, 14336)   # K beyond the fused limit
+    assert qoq.linear_plan(1, 59136, 8192) == qoq.gemm_tiled_plan(1, 59136, 8192)     # too much repeated work
+    assert qoq.linear_plan(16, 6144, 4096) == qoq.gemm_tiled_plan(16, 6144, 4096)
+    assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
+    assert qoq.linear_plan(64, 28672, 4096) == qoq.gemm_tiled_plan(64, 28672, 4096)
+    assert qoq.linear_plan(65, 6144, 4096) == qoq.gemm_plan(65, 6144, 4096)
+    assert qoq.linear_plan(1, 4096, 14336) == qoq.gemm_tiled_plan(1, 4096, 14336)   # K beyond the fused limit
     r256 = lambda v: (v + 255) // 256 * 256
-    for M, N, K in [(17, 6144, 4096), (256, 4096, 14336), (1, 4096, 14336), (64, 28672, 4096)]:
+    for M, N, K in [(17, 6144, 4096), (1, 4096, 14336), (64, 28672, 4096)]:
+        assert qoq.linear_workspace_bytes(M, N, K) == r256((M + 15) // 16 * 16 * K) + r256(2 * M)
+    for M, N, K in [(65, 6144, 4096), (256, 4096, 14336)]:
         assert qoq.linear_workspace_bytes(M, N, K) == r256(M * K) + r256(2 * M) + qoq.gemm_workspace_bytes(M, N, K)
     assert qoq.linear_workspace_bytes(0, 6144, 4096) == 0
     assert qoq.linear_plan(0, 6144, 4096) == "invalid"
     monkeypatch.setenv("QOQ_LINEAR_CONFIG", "unfused")
-    assert qoq.linear_plan(1, 6144, 4096) == qoq.gemm_plan(1, 6144, 4096)
-    assert qoq.linear_workspace_bytes(1, 6144, 4096) == 4096 + 256
+    assert qoq.linear_plan(1, 6144, 4096) == qoq.gemm_tiled_plan(1, 6144, 4096)
+    assert qoq.linear_workspace_bytes(1, 6144, 4096) == 16 * 4096 + 256
     for name in fused:                             # forced: any shape the kernel can hold
         monkeypatch.setenv("QOQ_LINEAR_CONFIG", name)
         assert qoq.linear_plan(4, 6144, 4096) == name
         assert qoq.linear_plan(8, 6144, 2048) == name
         assert qoq.linear_plan(1, 59136, 8192) == name
-        assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_plan(17, 6144, 4096)
+        assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
+
+
+def test_tiled_plans_and_validation(L):
+    """The tiled-code GEMM runs few-token kernels only, up to 64 tokens."""
+    for M, N, K in [(1, 6144, 4096), (16, 6144, 4096), (64, 6144, 4096), (64, 28672, 4096), (33, 4096, 14336)]:
+        assert qoq.gemm_tiled_plan(M, N, K).startswith("skinny_")
+    assert qoq.gemm_tiled_plan(65, 6144, 4096) == "invalid"
+    assert qoq.gemm_tiled_plan(0, 6144, 4096) == "invalid"
+    assert qoq.tiled_bytes(1, 4096) == 16 * 4096 and qoq.tiled_bytes(17, 128) == 32 * 128
+    q = L.qoq_quantize_activations_tiled
+    assert q(FAKE, 65, 4096, FAKE, FAKE, NUL) == UNSUPPORTED
+    assert q(FAKE, 4, 96, FAKE, FAKE, NUL) == INVALID              # K % 64
+    assert q(FAKE, 0, 4096, NUL, NUL, NUL) == OK
+    assert q(FAKE, 4, 4096, NUL, FAKE, NUL) == INVALID
+    assert q(ODD, 4, 4096, FAKE, FAKE, NUL) == ALIGNMENT
+    g = L.qoq_w4a8_gemm_tiled
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65, 6144, 4096, NUL) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4000, NUL) == INVALID
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 6144, 4096, NUL) == OK
+    assert g(FAKE, NUL, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4096, NUL) == INVALID
+    assert g(ODD, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4096, NUL) == ALIGNMENT
+    gi = L.qoq_w4a8_gemm_tiled_i32
+    assert gi(FAKE, FAKE, FAKE, FAKE, 65, 6144, 4096, NUL) == UNSUPPORTED
+    assert gi(FAKE, FAKE, FAKE, ODD, 4, 6144, 4096, NUL) == ALIGNMENT
 
 
 def test_linear_validation(L):

@@ -181,6 +181,16 @@ __device__ __forceinline__ void weights_lane(uint4 p, unsigned meta16, v4i &b_lo
     dequant_lane(p, group_consts(meta16), b_lo, b_hi);
 }
 
+// Tiled activation codes (the few-token GEMM's A operand): the codes of a 16-row
+// block and a 64-wide k block are 1 KB, stored in the order the 16x16x64 INT8 MFMA
+// takes its A operand (lane l = 16*kq + r: row r, k = 16*kq .. +15), so that a
+// 16-byte load per lane reads a block as 1 KB of consecutive bytes.  Blocks are
+// row-block major: block (rb, kb) starts at (rb * K/64 + kb) * 1024.
+__host__ __device__ __forceinline__ size_t tiled_offset(int row, int k, int K) {
+  return ((static_cast<size_t>(row >> 4) * (K >> 6) + (k >> 6)) * 64 + ((k >> 4) & 3) * 16 + (row & 15)) * 16 +
+         (k & 15);
+}
+
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -42,13 +42,28 @@ __device__ __forceinline__ void store_result(void *out, int out_kind, size_t idx
 //   token rows, and its waves split the K groups round-robin (split-K): wave w
 //   takes groups w, w + WAVES, w + 2*WAVES, ...  A wave works through its groups in
 //   batches of U: every load of a batch (one 128-bit packed-code load per lane per
-//   strip, one 16-bit metadata load, the activation fragments) is issued before any
-//   of them is consumed, and the next batch is issued before the current one is
-//   computed, so each wave keeps up to 2*U KB of weights in flight per strip.
-//   Slots past the wave's last group are zero-filled: zero codes with zero
-//   metadata dequantize to 0 and add nothing.  Partial sums of the waves are added
-//   through LDS; the epilogue follows.
+//   strip, one metadata load, the activation fragments) is issued before any
+//   of them is consumed.  Batches live in a ring of R register sets: batch b + R - 1
+//   is issued before batch b is computed, so R - 1 batches are in flight while one
+//   is computed, and the wait for batch b leaves the later ones in flight.  The
+//   ring is indexed by compile-time slots (the loop is unrolled by R): a copy from
+//   one register set to another at the loop edge would wait for every load in
+//   flight.  Slots past the wave's last group get zero activations and add nothing.
+//   AT: the activation codes are in the tiled layout (tiled_offset), so each
+//   fragment load is 1 KB of consecutive bytes (row-major codes: 16 rows, 16 cache
+//   lines, per load).  Partial sums of the waves are added through LDS; the
+//   epilogue follows.
 // ---------------------------------------------------------------------------
+// The metadata word of column col of a chunk is loaded as the aligned 32-bit pair
+// (columns col & ~1, col | 1) and shifted at its use (meta_of): a 16-bit load is
+// widened right where it lands, and when that point is the merge after a
+// conditional load, the widening waits for every load issued before it.
+__device__ __forceinline__ unsigned meta_pair(const uint16_t *__restrict__ meta, size_t chunk, int col) {
+  return reinterpret_cast<const unsigned *>(meta)[chunk * 8 + (col >> 1)];
+}
+
+__device__ __forceinline__ unsigned meta_of(unsigned pair, int col) { return pair >> (16 * (col & 1)); }
+
 template <int MT, int NBW, int U>
 struct SkinnyBatch {
   uint4 p[U][NBW];
@@ -59,7 +74,7 @@ struct SkinnyBatch {
 
 // Issues every load of batch b (groups t = b*U .. b*U+U-1 of this wave).  Only
 // scalars come in, so no pointer array can end up in private (scratch) memory.
-template <int MT, int NBW, int WAVES, int U, bool PC>
+template <int MT, int NBW, int WAVES, int U, bool PC, bool AT>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, int ngroups, int wave,
                                             const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                             const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
@@ -70,26 +85,49 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, i
   for (int u = 0; u < U; ++u) {
     const int t = b * U + u;
     const bool ok = t < ngroups;
-    const int j = wave + WAVES * t;
+    // a slot past the wave's last group reloads its first group's weights (in
+    // bounds) and zero activations, so it adds nothing; the weight loads stay
+    // unconditional (a value merged from a conditional load is consumed at the
+    // merge, which would wait for every load issued before it)
+    const int j = wave + WAVES * (ok ? t : 0);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       // strips past the end repeat the last one; their results are dropped at the store
       const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
-      B.p[u][nb] = ok ? packed[chunk * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
-      B.md[u][nb] = (!PC && ok) ? static_cast<unsigned>(meta[chunk * 16 + col]) : 0u;
+      B.p[u][nb] = packed[chunk * 64 + lane];
+      B.md[u][nb] = PC ? 0u : meta_pair(meta, chunk, col);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = m0 + 16 * mt + col;
       const bool oka = ok && r < M;
-      const int8_t *a = qx + static_cast<size_t>(oka ? r : 0) * K + 128 * (ok ? j : 0) + 16 * kq;
+      // row-major codes: a lane reads 16 bytes of its own row (16 rows per load);
+      // tiled codes: the two 1 KB blocks (k blocks 2j, 2j + 1) of the row block
+      const int8_t *a = AT ? qx + ((static_cast<size_t>((m0 >> 4) + mt) * (K >> 6) + 2 * j) * 64 + lane) * 16
+                           : qx + static_cast<size_t>(oka ? r : 0) * K + 128 * j + 16 * kq;
       B.a0[u][mt] = oka ? *reinterpret_cast<const v4i *>(a) : zero4;
-      B.a1[u][mt] = oka ? *reinterpret_cast<const v4i *>(a + 64) : zero4;
+      B.a1[u][mt] = oka ? *reinterpret_cast<const v4i *>(a + (AT ? 1024 : 64)) : zero4;
     }
   }
 }
 
-template <int MT, int NBW, int WAVES, int U, int OUT, bool PC>
+template <int MT, int NBW, int U, bool PC>
+__device__ __forceinline__ void skinny_compute(const SkinnyBatch<MT, NBW, U> &B, v4i (&acc)[MT][NBW], int col) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      v4i b0, b1;
+      weights_lane<PC>(B.p[u][nb], meta_of(B.md[u][nb], col), b0, b1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][nb] = mfma16x16x64(B.a0[u][mt], b0, acc[mt][nb]);
+        acc[mt][nb] = mfma16x16x64(B.a1[u][mt], b1, acc[mt][nb]);
+      }
+    }
+}
+
+template <int MT, int NBW, int WAVES, int U, int R, int OUT, bool PC, bool AT = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
@@ -113,25 +151,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   const int ngroups = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;   // groups of this wave
   const int nbatch = (ngroups + U - 1) / U;
 
-  SkinnyBatch<MT, NBW, U> cur, nxt;
-  if (nbatch > 0)
-    skinny_load<MT, NBW, WAVES, U, PC>(cur, 0, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
-  for (int b = 0; b < nbatch; ++b) {
-    if (b + 1 < nbatch)
-      skinny_load<MT, NBW, WAVES, U, PC>(nxt, b + 1, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0, lane);
+  SkinnyBatch<MT, NBW, U> ring[R];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int r = 0; r < R - 1; ++r)
+    if (r < nbatch)
+      skinny_load<MT, NBW, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0,
+                                             lane);
+  for (int b0 = 0; b0 < nbatch; b0 += R) {
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        v4i b0, b1;
-        weights_lane<PC>(cur.p[u][nb], cur.md[u][nb], b0, b1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][nb] = mfma16x16x64(cur.a0[u][mt], b0, acc[mt][nb]);
-          acc[mt][nb] = mfma16x16x64(cur.a1[u][mt], b1, acc[mt][nb]);
-        }
-      }
-    if (b + 1 < nbatch) cur = nxt;
+    for (int r = 0; r < R; ++r) {
+      const int b = b0 + r;
+      if (b >= nbatch) break;
+      if (b + R - 1 < nbatch)
+        skinny_load<MT, NBW, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
+                                               strip0, NS, G, K, M, m0, lane);
+      skinny_compute<MT, NBW, U, PC>(ring[r], acc, col);
+    }
   }
 
   constexpr int T = MT * NBW;   // 16x16 tiles per wave
@@ -212,13 +247,12 @@ __device__ __forceinline__ void skinny_wload(SkinnyWBatch<NBW, U> &B, int b, int
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = b * U + u;
-    const bool ok = t < ngroups;
-    const int j = wave + WAVES * t;
+    const int j = wave + WAVES * (t < ngroups ? t : 0);   // past the end: in-bounds reload, zero activations
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
-      B.p[u][nb] = ok ? packed[chunk * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
-      B.md[u][nb] = ok ? static_cast<unsigned>(meta[chunk * 16 + col]) : 0u;
+      B.p[u][nb] = packed[chunk * 64 + lane];
+      B.md[u][nb] = meta_pair(meta, chunk, col);
     }
   }
 }
@@ -228,7 +262,7 @@ constexpr int skinny_xq_red_bytes() {
   return WAVES * NBW * 4 * 64 * 4;
 }
 
-template <int NBW, int WAVES, int U>
+template <int NBW, int WAVES, int U, int R>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
     const __half *__restrict__ x, __half *__restrict__ sx_out, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, __half *__restrict__ out, int M, int N,
@@ -247,8 +281,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
 
   const int ngroups = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
   const int nbatch = (ngroups + U - 1) / U;
-  SkinnyWBatch<NBW, U> cur, nxt;
-  if (nbatch > 0) skinny_wload<NBW, WAVES, U>(cur, 0, ngroups, wave, packed, meta, strip0, NS, G, lane);
+  // weight batches in a ring of R register sets, as in the skinny kernel
+  SkinnyWBatch<NBW, U> ring[R];
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r)
+    if (r < nbatch) skinny_wload<NBW, WAVES, U>(ring[r], r, ngroups, wave, packed, meta, strip0, NS, G, lane);
 
   // per-token quantization of the M rows into LDS, shared by all threads: chunk c
   // (8 halves) of the M x K/8 chunks goes to thread c mod T, kept in registers
@@ -261,13 +298,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
   __syncthreads();
   uint4 v[kXqPerThread];
 #pragma unroll
-  for (int i = 0; i < kXqPerThread; ++i) {
+  for (int i = 0; i < kXqPerThread; ++i) {      // every load first, so they are in flight together
     const int c = static_cast<int>(threadIdx.x) + T * i;
     if (c < total) {
       const int r = c / nchunk;
       v[i] = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(r) * K)[c - r * nchunk];
-      atomicMax(&rowmax[r], absmax_bits8(v[i], 0u));
     }
+  }
+#pragma unroll
+  for (int i = 0; i < kXqPerThread; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + T * i;
+    if (c < total) atomicMax(&rowmax[c / nchunk], absmax_bits8(v[i], 0u));
   }
   __syncthreads();
   if (threadIdx.x < static_cast<unsigned>(M)) {
@@ -290,23 +331,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) acc[nb] = v4i{0, 0, 0, 0};
   const int8_t *arow = qa + min(col, M - 1) * pitch + 16 * kq;   // rows past M repeat row M-1 (never stored)
-  for (int b = 0; b < nbatch; ++b) {
-    if (b + 1 < nbatch) skinny_wload<NBW, WAVES, U>(nxt, b + 1, ngroups, wave, packed, meta, strip0, NS, G, lane);
+  for (int b0 = 0; b0 < nbatch; b0 += R) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = b * U + u;
-      const int j = wave + WAVES * min(t, ngroups - 1);       // slots past the end hold zero codes
-      const v4i a0 = *reinterpret_cast<const v4i *>(arow + 128 * j);
-      const v4i a1 = *reinterpret_cast<const v4i *>(arow + 128 * j + 64);
+    for (int r = 0; r < R; ++r) {
+      const int b = b0 + r;
+      if (b >= nbatch) break;
+      if (b + R - 1 < nbatch)
+        skinny_wload<NBW, WAVES, U>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, strip0, NS, G,
+                                    lane);
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        v4i b0, b1;
-        dequant_lane(cur.p[u][nb], group_consts(cur.md[u][nb]), b0, b1);
-        acc[nb] = mfma16x16x64(a0, b0, acc[nb]);
-        acc[nb] = mfma16x16x64(a1, b1, acc[nb]);
+      for (int u = 0; u < U; ++u) {
+        const int t = b * U + u;
+        const bool ok = t < ngroups;                          // uniform: slots past the end add zero
+        const int j = wave + WAVES * (ok ? t : 0);
+        const v4i zero4 = {0, 0, 0, 0};
+        const v4i a0 = ok ? *reinterpret_cast<const v4i *>(arow + 128 * j) : zero4;
+        const v4i a1 = ok ? *reinterpret_cast<const v4i *>(arow + 128 * j + 64) : zero4;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          v4i w0, w1;
+          dequant_lane(ring[r].p[u][nb], group_consts(meta_of(ring[r].md[u][nb], col)), w0, w1);
+          acc[nb] = mfma16x16x64(a0, w0, acc[nb]);
+          acc[nb] = mfma16x16x64(a1, w1, acc[nb]);
+        }
       }
     }
-    if (b + 1 < nbatch) cur = nxt;
   }
 
   // partial sums of the waves, added through LDS (the code rows are done with)
@@ -1078,18 +1127,25 @@ typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const 
 
 struct Config {
   int kind;                 // 0 skinny, 4 wide2, 5 dma2, 6 shared dequantization
-  int a, b, c, d;           // skinny: MT, NBW, WAVES, U    wide2 / dma2: TM, TN    sd: A stages
+  int a, b, c, d, e;        // skinny: MT, NBW, WAVES, U, R    wide2 / dma2: TM, TN    sd: A stages
   GemmKernel k[2][2];       // [per-group, per-channel][fp16 epilogue, INT32 epilogue]
   const char *name;
   int lds = 0;              // dynamic LDS bytes
+  GemmKernel kt[2] = {nullptr, nullptr};   // skinny, per-group, tiled codes: [fp16, INT32]
 };
 
 #define QOQ_K4(...) {{__VA_ARGS__, 0, false>, __VA_ARGS__, 1, false>}, {__VA_ARGS__, 0, true>, __VA_ARGS__, 1, true>}}
-#define QOQ_SKINNY(MT, NBW, W, U) \
-  {0, MT, NBW, W, U, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U), "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U},
-#define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
-#define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
-#define QOQ_SD(AS) {6, AS, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
+// skinny names carry the ring depth only when it is not 2
+#define QOQ_KT(...) {__VA_ARGS__, 0, false, true>, __VA_ARGS__, 1, false, true>}
+#define QOQ_SKINNY(MT, NBW, W, U)                                                                      \
+  {0, MT, NBW, W, U, 2, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U, 2), "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U, \
+   0, QOQ_KT(gemm_skinny_kernel<MT, NBW, W, U, 2)},
+#define QOQ_SKINNY_R(MT, NBW, W, U, R)                                                      \
+  {0, MT, NBW, W, U, R, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U, R),                          \
+   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U "_r" #R, 0, QOQ_KT(gemm_skinny_kernel<MT, NBW, W, U, R)},
+#define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
+#define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
+#define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
 
 const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
@@ -1097,16 +1153,21 @@ const Config kConfigs[] = {
     QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(3, 2, 8, 2)
     QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(4, 2, 8, 1)
+    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(1, 1, 16, 2, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
+    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 1, 3)
+    QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
+    QOQ_SKINNY_R(4, 4, 8, 1, 3)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(2) QOQ_SD(3)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-const Config *find_config(int kind, int a, int b, int c, int d) {
+const Config *find_config(int kind, int a, int b, int c, int d, int e = 0) {
+  if (kind == 0 && e == 0) e = 2;
   for (int i = 0; i < kNumConfigs; ++i) {
     const Config &cf = kConfigs[i];
-    if (cf.kind == kind && cf.a == a && cf.b == b && cf.c == c && cf.d == d)
+    if (cf.kind == kind && cf.a == a && cf.b == b && cf.c == c && cf.d == d && cf.e == e)
       return &cf;
   }
   return nullptr;
@@ -1136,7 +1197,9 @@ int choose_splits(int64_t tiles, int64_t G) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits)));
 }
 
-Plan make_plan(int64_t M, int64_t N, int64_t K) {
+// tiled_a: the activation codes are in the tiled layout (M <= kTiledMaxM), which
+// only the few-token kernels read
+Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   const int64_t NS = N / 16;
   const int64_t G = K / 128;
   // measurement overrides (not needed for correct use): QOQ_GEMM_REGIME=skinny|tiled,
@@ -1144,7 +1207,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
   const Config *cfg = nullptr;
   if (const char *name = getenv("QOQ_GEMM_CONFIG")) {
     for (int i = 0; i < kNumConfigs; ++i)
-      if (strcmp(kConfigs[i].name, name) == 0) cfg = &kConfigs[i];
+      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kind == 0)) cfg = &kConfigs[i];
   }
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
@@ -1156,6 +1219,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     bool tiled = M > 64 || (M > 48 && NS >= 1024);
     if (force && force[0] == 's') tiled = false;
     if (force && force[0] == 't') tiled = true;
+    if (tiled_a) tiled = false;
     if (!tiled) {
       // measured on MI355X (config sweep over the layer shapes of the workloads):
       //  M <= 16: one 16-row block; wide layers with short K stream one strip per
@@ -1278,6 +1342,17 @@ void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const v
   launch_gemm_any(qx, sx, packed, nullptr, sw, zeros, tx, out, 1, out_kind, M, N, K, ws, st);
 }
 
+void launch_w4a8_gemm_tiled(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
+                            void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const Plan p = make_plan(M, N, K, true);
+  hipLaunchKernelGGL(p.cfg->kt[out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
+                     static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
+                     static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), nullptr, nullptr, out,
+                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), 1, nullptr);
+}
+
+const char *gemm_tiled_plan_name(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, true).cfg->name; }
+
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).ws_bytes; }
 
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).splits; }
@@ -1285,9 +1360,10 @@ int gemm_plan_splits(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).cfg->name; }
 
 // ---------------------------------------------------------------------------
-// linear = per-token quantization + GEMM.  M <= 16 and K <= 8192: one fused kernel;
-// otherwise the standalone quantizer writes qx / s_X into the workspace and the
-// GEMM plan runs on them.
+// linear = per-token quantization + GEMM.  A few tokens (xq_plan): one fused kernel;
+// otherwise the standalone quantizer writes the codes and s_X into the workspace
+// (tiled codes up to kTiledMaxM tokens, read by a few-token kernel; row-major codes
+// and the GEMM plan beyond).
 // ---------------------------------------------------------------------------
 typedef void (*XqKernel)(const __half *, __half *, const uint4 *, const uint16_t *, const __half *, __half *, int,
                          int, int);
@@ -1300,10 +1376,14 @@ struct XqConfig {
 };
 
 #define QOQ_XQ(NBW, W, U)                                                                              \
-  {NBW, W, gemm_skinny_xq_kernel<NBW, W, U>, "skinny_xq_nb" #NBW "_w" #W "_u" #U, \
+  {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, 2>, "skinny_xq_nb" #NBW "_w" #W "_u" #U, \
+   skinny_xq_red_bytes<NBW, W, U>()},
+#define QOQ_XQ_R(NBW, W, U, R)                                                                         \
+  {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, R>, "skinny_xq_nb" #NBW "_w" #W "_u" #U "_r" #R, \
    skinny_xq_red_bytes<NBW, W, U>()},
 
-const XqConfig kXqConfigs[] = {QOQ_XQ(1, 16, 2) QOQ_XQ(2, 16, 2) QOQ_XQ(1, 8, 2) QOQ_XQ(2, 8, 2)};
+const XqConfig kXqConfigs[] = {QOQ_XQ(1, 16, 2) QOQ_XQ(2, 16, 2) QOQ_XQ(1, 8, 2) QOQ_XQ(2, 8, 2)
+                               QOQ_XQ_R(2, 16, 2, 3) QOQ_XQ_R(2, 8, 2, 3)};
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);
 std::once_flag g_xq_once[kNumXq];
 
@@ -1339,14 +1419,24 @@ int xq_lds_bytes(const XqConfig *c, int64_t M, int64_t K) {
   return 64 + std::max(static_cast<int>(M * (K + 16)), c->red);
 }
 
+// Unfused linear: up to kTiledMaxM tokens the quantizer writes the tiled layout and
+// a few-token kernel reads it; beyond, row-major codes and the GEMM plan.
+bool linear_tiled(int64_t M) { return M <= kTiledMaxM; }
+
+size_t linear_qx_bytes(int64_t M, int64_t K) {
+  return align256(static_cast<size_t>(linear_tiled(M) ? (M + 15) / 16 * 16 : M) * K);
+}
+
 size_t linear_workspace_need(int64_t M, int64_t N, int64_t K) {
   if (xq_plan(M, N, K)) return 0;
-  return align256(static_cast<size_t>(M) * K) + align256(2 * static_cast<size_t>(M)) + gemm_workspace_need(M, N, K);
+  return linear_qx_bytes(M, K) + align256(2 * static_cast<size_t>(M)) +
+         (linear_tiled(M) ? 0 : gemm_workspace_need(M, N, K));
 }
 
 const char *linear_plan_name(int64_t M, int64_t N, int64_t K) {
   const XqConfig *c = xq_plan(M, N, K);
-  return c ? c->name : gemm_plan_name(M, N, K);
+  if (c) return c->name;
+  return linear_tiled(M) ? gemm_tiled_plan_name(M, N, K) : gemm_plan_name(M, N, K);
 }
 
 void launch_w4a8_linear(const void *x, const void *packed, const void *meta, const void *sw, void *out, void *sx_out,
@@ -1367,8 +1457,13 @@ void launch_w4a8_linear(const void *x, const void *packed, const void *meta, con
     return;
   }
   int8_t *qx = static_cast<int8_t *>(ws);
-  void *sx = sx_out ? sx_out : static_cast<void *>(qx + align256(static_cast<size_t>(M) * K));
-  void *gws = qx + align256(static_cast<size_t>(M) * K) + align256(2 * static_cast<size_t>(M));
+  void *sx = sx_out ? sx_out : static_cast<void *>(qx + linear_qx_bytes(M, K));
+  if (linear_tiled(M)) {
+    launch_quantize_activations_tiled(x, M, K, qx, sx, st);
+    launch_w4a8_gemm_tiled(qx, sx, packed, meta, sw, out, 0, M, N, K, st);
+    return;
+  }
+  void *gws = qx + linear_qx_bytes(M, K) + align256(2 * static_cast<size_t>(M));
   launch_quantize_activations(x, M, K, qx, sx, st);
   launch_w4a8_gemm(qx, sx, packed, meta, sw, out, 0, M, N, K, gws, st);
 }

@@ -14,6 +14,10 @@ void launch_quantize_pack_weights(const void *w, int64_t N, int64_t K, void *pac
                                   void *sw, hipStream_t stream);
 void launch_quantize_pack_weights_pc(const void *w, int64_t N, int64_t K, void *packed, void *zeros, void *sw,
                                      hipStream_t stream);
+// codes in the tiled layout of the few-token GEMM (tiled_offset in qoq_device.h);
+// qx holds round_up(M, 16) * K bytes, rows past M are not written
+void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void *qx, void *sx,
+                                       hipStream_t stream);
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream);
 
@@ -27,12 +31,18 @@ void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const 
 void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const void *packed, const void *zeros,
                          const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K, void *ws,
                          hipStream_t stream);
+// tiled activation codes (M <= kTiledMaxM): few-token kernels only, no workspace
+constexpr int64_t kTiledMaxM = 64;
+void launch_w4a8_gemm_tiled(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
+                            void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+const char *gemm_tiled_plan_name(int64_t M, int64_t N, int64_t K);
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K);
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
 
-// linear = quantize + GEMM (fused kernel when M <= 16 and K <= 8192); ws holds at
-// least linear_workspace_need(M, N, K) bytes, 256-byte aligned
+// linear = quantize + GEMM (fused kernel for a few tokens, tiled codes up to
+// kTiledMaxM tokens); ws holds at least linear_workspace_need(M, N, K) bytes,
+// 256-byte aligned
 void launch_w4a8_linear(const void *x, const void *packed, const void *meta, const void *sw, void *out,
                         void *sx_out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream);
 size_t linear_workspace_need(int64_t M, int64_t N, int64_t K);

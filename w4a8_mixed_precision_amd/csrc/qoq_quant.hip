@@ -29,7 +29,9 @@ __device__ __forceinline__ int code_sum8(uint2 q) {
 // ROWSUM: also t[row] = sum_k qx[row, k] (the activation term of the per-channel
 // epilogue, "QServe ..." summary, per-channel fast dequantization: t_X is computed
 // by the memory-bound kernel that precedes the GEMM)
-template <bool ROWSUM>
+// TILED: codes stored in the tiled layout of the few-token GEMM (tiled_offset)
+// instead of row-major.
+template <bool ROWSUM, bool TILED = false>
 __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half *__restrict__ x, int K,
                                                                    int8_t *__restrict__ qx,
                                                                    __half *__restrict__ sx,
@@ -41,16 +43,18 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
   const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(row) * K);
   uint2 *qr = reinterpret_cast<uint2 *>(qx + static_cast<size_t>(row) * K);
 
+  // every load is issued before any value is used, so they are in flight together
+  // (a use right after each load would wait for it, one memory latency per chunk);
+  // chunks past the row are zero and leave the maximum unchanged
   uint4 v[kActChunks];
-  unsigned amax = 0;
 #pragma unroll
   for (int c = 0; c < kActChunks; ++c) {
     int idx = threadIdx.x + c * kActThreads;
-    if (idx < nchunk) {
-      v[c] = xr[idx];
-      amax = absmax_bits8(v[c], amax);
-    }
+    v[c] = idx < nchunk ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
   }
+  unsigned amax = 0;
+#pragma unroll
+  for (int c = 0; c < kActChunks; ++c) amax = absmax_bits8(v[c], amax);
   for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads)
     amax = absmax_bits8(xr[idx], amax);
 
@@ -64,19 +68,25 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
   const float s = __half2float(sh);
   if (threadIdx.x == 0) sx[row] = sh;
 
+  auto store = [&](int idx, uint2 q) {
+    if (TILED)
+      *reinterpret_cast<uint2 *>(qx + tiled_offset(row, 8 * idx, K)) = q;
+    else
+      qr[idx] = q;
+  };
   int tsum = 0;
 #pragma unroll
   for (int c = 0; c < kActChunks; ++c) {
     int idx = threadIdx.x + c * kActThreads;
     if (idx < nchunk) {
       const uint2 q = quant_chunk8(v[c], s);
-      qr[idx] = q;
+      store(idx, q);
       if (ROWSUM) tsum += code_sum8(q);
     }
   }
   for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads) {
     const uint2 q = quant_chunk8(xr[idx], s);
-    qr[idx] = q;
+    store(idx, q);
     if (ROWSUM) tsum += code_sum8(q);
   }
   if (ROWSUM) {
@@ -97,6 +107,13 @@ void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, 
                                  hipStream_t stream) {
   hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
                      static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
+                     static_cast<__half *>(sx), nullptr);
+}
+
+void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void *qx, void *sx,
+                                       hipStream_t stream) {
+  hipLaunchKernelGGL((quantize_act_kernel<false, true>), dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0,
+                     stream, static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
                      static_cast<__half *>(sx), nullptr);
 }
 

@@ -40,6 +40,11 @@ _SIGNATURES = {
     "qoq_w4a8_gemm_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz, _c_vp],
                           ctypes.c_int),
     "qoq_gemm_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_quantize_activations_tiled": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_w4a8_gemm_tiled": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+                            ctypes.c_int),
+    "qoq_w4a8_gemm_tiled_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp], ctypes.c_int),
+    "qoq_gemm_tiled_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
     "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
                           _c_vp], ctypes.c_int),
@@ -201,6 +206,31 @@ def quantize_activations(x: torch.Tensor, out=None):
     return qx, s_x
 
 
+TILED_MAX_M = 64
+
+
+def tiled_bytes(M: int, K: int) -> int:
+    """Bytes of the tiled activation codes of M tokens (whole 16-row blocks)."""
+    return (M + 15) // 16 * 16 * K
+
+
+def quantize_activations_tiled(x: torch.Tensor, out=None):
+    """X fp16 [M, K] (M <= 64) -> (qx_tiled int8 [round_up(M, 16) * K] in the layout of
+    qoq_quantize_activations_tiled, s_x fp16 [M])."""
+    M, K = x.shape
+    if out is None:
+        qx = torch.empty(tiled_bytes(M, K), dtype=torch.int8, device=x.device)
+        s_x = torch.empty(M, dtype=torch.float16, device=x.device)
+    else:
+        qx, s_x = out
+    if qx.numel() < tiled_bytes(M, K):
+        raise ValueError(f"qx_tiled holds {qx.numel()} bytes, {tiled_bytes(M, K)} needed")
+    _check("qoq_quantize_activations_tiled",
+           lib().qoq_quantize_activations_tiled(_dev(x, "x", torch.float16), M, K, _dev(qx, "qx", torch.int8),
+                                                _dev(s_x, "s_x", torch.float16), _stream(x)))
+    return qx, s_x
+
+
 def quantize_activations_rowsum(x: torch.Tensor, out=None):
     """X fp16 [M, K] -> (qx int8 [M, K], s_x fp16 [M], t int32 [M] = sum_k qx)."""
     M, K = x.shape
@@ -302,6 +332,40 @@ def w4a8_gemm_i32(qx, packed, meta, N: int, out=None, group: int = GROUP, worksp
                                    _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K, group,
                                    ws_ptr, ws_bytes, _stream(qx)))
     return out
+
+
+def _check_tiled(qx, M, K):
+    if qx.numel() < tiled_bytes(M, K):
+        raise ValueError(f"qx_tiled holds {qx.numel()} bytes, {tiled_bytes(M, K)} needed")
+
+
+def w4a8_gemm_tiled(qx_tiled, s_x, packed, meta, s_w, M: int, N: int, K: int, out=None):
+    """qoq_w4a8_gemm on tiled activation codes (M <= 64): out fp16 [M, N]."""
+    _check_tiled(qx_tiled, M, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=qx_tiled.device)
+    _check("qoq_w4a8_gemm_tiled",
+           lib().qoq_w4a8_gemm_tiled(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(s_x, "s_x", torch.float16),
+                                     _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
+                                     _dev(s_w, "s_w", torch.float16), _dev(out, "out", torch.float16), M, N, K,
+                                     _stream(qx_tiled)))
+    return out
+
+
+def w4a8_gemm_tiled_i32(qx_tiled, packed, meta, M: int, N: int, K: int, out=None):
+    """Exact INT32 accumulators from tiled activation codes (M <= 64)."""
+    _check_tiled(qx_tiled, M, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=qx_tiled.device)
+    _check("qoq_w4a8_gemm_tiled_i32",
+           lib().qoq_w4a8_gemm_tiled_i32(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(packed, "packed", torch.uint8),
+                                         _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K,
+                                         _stream(qx_tiled)))
+    return out
+
+
+def gemm_tiled_plan(M: int, N: int, K: int) -> str:
+    return lib().qoq_gemm_tiled_plan(M, N, K).decode()
 
 
 # ---------------------------------------------------------------------------

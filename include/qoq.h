@@ -210,7 +210,7 @@ int qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, s
  * W4A8 GEMM with its fp16 epilogue — the same arithmetic, codes, scales and fp16
  * results as qoq_quantize_activations + qoq_w4a8_gemm ("QServe ..." summary: the
  * activation quantization is fused into the kernel that feeds the GEMM, so it costs
- * no pass of its own).  For a few tokens (M <= 8, K <= 8192, see qoq_linear_plan)
+ * no pass of its own).  For one or two tokens (M <= 2, K <= 8192, see qoq_linear_plan)
  * one kernel does both: each workgroup quantizes the token rows into LDS and runs the
  * GEMM on them; up to 64 tokens the codes go through the tiled layout
  * (qoq_quantize_activations_tiled + qoq_w4a8_gemm_tiled); beyond, row-major.

@@ -190,9 +190,11 @@ def test_linear_plan_and_workspace(monkeypatch):
     fused = qoq.linear_configs()
     assert len(fused) >= 2
     assert qoq.linear_plan(1, 6144, 4096) in fused
-    assert qoq.linear_plan(8, 512, 512) in fused
+    assert qoq.linear_plan(2, 512, 512) in fused
+    assert qoq.linear_plan(1, 59136, 8192) in fused
     assert qoq.linear_workspace_bytes(1, 6144, 4096) == 0
-    assert qoq.linear_plan(1, 59136, 8192) == qoq.gemm_tiled_plan(1, 59136, 8192)     # too much repeated work
+    assert qoq.linear_plan(3, 6144, 4096) == qoq.gemm_tiled_plan(3, 6144, 4096)
+    assert qoq.linear_plan(2, 131072, 8192) == qoq.gemm_tiled_plan(2, 131072, 8192)   # too much repeated work
     assert qoq.linear_plan(16, 6144, 4096) == qoq.gemm_tiled_plan(16, 6144, 4096)
     assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
     assert qoq.linear_plan(64, 28672, 4096) == qoq.gemm_tiled_plan(64, 28672, 4096)

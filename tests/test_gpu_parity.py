@@ -110,6 +110,19 @@ def _act_cases():
     x[4, :] = np.float16(-2.5)                                         # ties
     yield "edge_K40960", x
     yield "ragged_K136", (rng.standard_normal((3, 136)) * 2).astype(np.float16)
+    # exact half-integer quotients (ties to even) and values next to them: s = 1/8
+    # (absmax 15.875) and s = 3/128 (absmax 2.9765625), both exact in fp16
+    t = np.zeros((4, 512), np.float32)
+    n = np.arange(-127, 127)
+    t[0, :254] = (n + 0.5) / 8
+    t[0, 300] = 15.875
+    t[1, :254] = 3 * (2 * n + 1) / 256
+    t[1, 300] = 2.9765625
+    t[2] = t[0] + np.sign(t[0]) * 2.0 ** -10
+    t[2, 300] = 15.875
+    t[3] = t[1] - np.sign(t[1]) * 2.0 ** -11
+    t[3, 300] = 2.9765625
+    yield "ties_K512", t.astype(np.float16)
 
 
 @pytest.mark.parametrize("name,x", list(_act_cases()), ids=lambda v: v if isinstance(v, str) else "")

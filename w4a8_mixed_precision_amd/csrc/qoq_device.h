@@ -62,19 +62,55 @@ __device__ __forceinline__ int sym_code(float x, float s, float qmax) {
   return static_cast<int>(r);
 }
 
-// 8 fp16 activations (one 16-byte chunk) -> 8 INT8 codes with scale s
-__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s) {
-  unsigned w[4] = {v.x, v.y, v.z, v.w};
-  unsigned out[2] = {0u, 0u};
+// Activation codes for a row-constant scale s, with rcp = fp32(1 / s) (IEEE divide):
+// the same values as sym_code(x, s, 127), i.e. rint of the correctly rounded fp32
+// quotient, clamped.  q = fp32(x * rcp) is within |x/s| * 2^-22 of that quotient
+// (two roundings against one), far below 2^-12 for every |x/s| this scale allows
+// (under 2^8: s is at least about absmax / 190 even after fp16 subnormal rounding),
+// so rint(q) decides the same way unless q lies within 2^-12 of a half-integer;
+// those rare elements take the IEEE divide, in a branch the whole wave takes only
+// when one of its lanes needs it (a per-lane branch is turned into a divide for
+// every element plus a select).  Saves the divide sequence per element, which made
+// the quantizer vector-ALU bound.
+
+// fp32(1 / s) for quant_chunk8 (0 for s == 0, never used then)
+__device__ __forceinline__ float act_rcp(float s) { return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s); }
+
+// rint(q) clamped to [-127, 127], as an integer
+__device__ __forceinline__ int act_int(float q) {
+  return static_cast<int>(fminf(fmaxf(rintf(q), -static_cast<float>(kXQmax)), static_cast<float>(kXQmax)));
+}
+
+// distance of q from the nearest half-integer (v_fract: q - floor(q))
+__device__ __forceinline__ float half_gap(float q) { return fabsf(__builtin_amdgcn_fractf(q) - 0.5f); }
+
+// 8 fp16 activations (one 16-byte chunk) -> 8 INT8 codes with scale s (rcp = act_rcp(s))
+__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s, float rcp) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  float x[8], q[8];
+  float gap = 1.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo = half_bits_to_float(w[i] & 0xffffu);
-    float hi = half_bits_to_float(w[i] >> 16);
-    unsigned q0 = static_cast<unsigned>(sym_code(lo, s, kXQmax)) & 0xffu;
-    unsigned q1 = static_cast<unsigned>(sym_code(hi, s, kXQmax)) & 0xffu;
-    out[i >> 1] |= (q0 | (q1 << 8)) << (16 * (i & 1));
+  for (int i = 0; i < 8; ++i) {
+    x[i] = half_bits_to_float((w[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+    q[i] = x[i] * rcp;
+    gap = fminf(gap, half_gap(q[i]));
   }
-  return make_uint2(out[0], out[1]);
+  if (__ballot(gap < 0x1p-12f) != 0) {          // uniform: rare
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (half_gap(q[i]) < 0x1p-12f) q[i] = __fdiv_rn(x[i], s);
+  }
+  if (s == 0.0f) return make_uint2(0u, 0u);
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = act_int(q[i]);
+  // bytes 0 of c[0..3] and c[4..7] (v_perm_b32 selector: byte 4 of the first
+  // operand, byte 0 of the second, ...)
+  const unsigned lo01 = __builtin_amdgcn_perm(static_cast<unsigned>(c[1]), static_cast<unsigned>(c[0]), 0x0c0c0400u);
+  const unsigned lo23 = __builtin_amdgcn_perm(static_cast<unsigned>(c[3]), static_cast<unsigned>(c[2]), 0x04000c0cu);
+  const unsigned hi01 = __builtin_amdgcn_perm(static_cast<unsigned>(c[5]), static_cast<unsigned>(c[4]), 0x0c0c0400u);
+  const unsigned hi23 = __builtin_amdgcn_perm(static_cast<unsigned>(c[7]), static_cast<unsigned>(c[6]), 0x04000c0cu);
+  return make_uint2(lo01 | lo23, hi01 | hi23);
 }
 
 // ---------------------------------------------------------------------------

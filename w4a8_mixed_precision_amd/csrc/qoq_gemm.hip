@@ -227,10 +227,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 // read from LDS.  All threads share the quantization (row absmax by LDS atomics).
 // Every workgroup repeats it, so the fused kernel serves only shapes where that
 // costs less than a launch of its own.  Rows past M are never stored.
-// LDS: 16 fp32 token scales, then M code rows; the same space holds the partial
-// sums of the waves once the main loop is done.
+// LDS: 16 fp32 token scales and their reciprocals, then M code rows; the same space
+// holds the partial sums of the waves once the main loop is done.
 // ---------------------------------------------------------------------------
 constexpr int kXqMaxK = 8192;                   // LDS: 16 code rows of K + 16 bytes
+constexpr int kXqHead = 128;                    // LDS: 16 token scales and reciprocals
 constexpr int kXqPerThread = 8;                 // chunks per thread: M * K / 8 <= 8 * threads
 
 template <int NBW, int U>
@@ -268,8 +269,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, __half *__restrict__ out, int M, int N,
     int K) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
-  float *sxl = reinterpret_cast<float *>(lds);
-  int8_t *qa = lds + 64;
+  float *sxl = reinterpret_cast<float *>(lds);             // 16 token scales
+  float *rcpl = sxl + 16;                                   // their reciprocals (act_rcp)
+  int8_t *qa = lds + kXqHead;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = K >> 7;
@@ -315,6 +317,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
     const __half sh = sym_scale(rowmax[threadIdx.x], static_cast<float>(kXQmax));
     if (blockIdx.x == 0 && sx_out) sx_out[threadIdx.x] = sh;
     sxl[threadIdx.x] = __half2float(sh);                        // overwrites this row's max
+    rcpl[threadIdx.x] = act_rcp(__half2float(sh));
   }
   __syncthreads();
 #pragma unroll
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
     const int c = static_cast<int>(threadIdx.x) + T * i;
     if (c < total) {
       const int r = c / nchunk;
-      *reinterpret_cast<uint2 *>(qa + r * pitch + 8 * (c - r * nchunk)) = quant_chunk8(v[i], sxl[r]);
+      *reinterpret_cast<uint2 *>(qa + r * pitch + 8 * (c - r * nchunk)) = quant_chunk8(v[i], sxl[r], rcpl[r]);
     }
   }
   __syncthreads();
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
 
   // partial sums of the waves, added through LDS (the code rows are done with)
   __syncthreads();
-  int *red = reinterpret_cast<int *>(lds + 64);
+  int *red = reinterpret_cast<int *>(lds + kXqHead);
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -1389,8 +1392,8 @@ std::once_flag g_xq_once[kNumXq];
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-constexpr int64_t kXqMaxM = 8;              // measured: beyond a few rows the repeated
-constexpr int64_t kXqMaxRepeat = 6 << 20;    // quantization costs more than a launch
+constexpr int64_t kXqMaxM = 2;               // measured: beyond two rows the repeated
+constexpr int64_t kXqMaxRepeat = 32 << 20;    // quantization costs more than a launch
 
 bool xq_fits(const XqConfig *c, int64_t M, int64_t K) { return M * (K / 8) <= int64_t{kXqPerThread} * 64 * c->waves; }
 
@@ -1404,11 +1407,11 @@ const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
       if (strcmp(kXqConfigs[i].name, force) == 0) return xq_fits(&kXqConfigs[i], M, K) ? &kXqConfigs[i] : nullptr;
   }
   if (M > kXqMaxM) return nullptr;
-  // measured on MI355X: two strips per workgroup, 8 waves on wide layers; fused only
-  // while the quantization every workgroup repeats (workgroups x M x K elements)
-  // stays small
+  // measured on MI355X (decode layers of the workloads, M = 1, 2): two strips and 8
+  // waves per workgroup; fused only while the quantization every workgroup repeats
+  // (workgroups x M x K elements) stays bounded
   const int64_t NS = N / 16;
-  const XqConfig *c = NS >= 640 ? &kXqConfigs[3] : &kXqConfigs[1];
+  const XqConfig *c = &kXqConfigs[3];
   if ((NS + c->nbw - 1) / c->nbw * M * K > kXqMaxRepeat) return nullptr;
   return xq_fits(c, M, K) ? c : nullptr;
 }
@@ -1416,7 +1419,7 @@ const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
 
 
 int xq_lds_bytes(const XqConfig *c, int64_t M, int64_t K) {
-  return 64 + std::max(static_cast<int>(M * (K + 16)), c->red);
+  return kXqHead + std::max(static_cast<int>(M * (K + 16)), c->red);
 }
 
 // Unfused linear: up to kTiledMaxM tokens the quantizer writes the tiled layout and
@@ -1446,7 +1449,7 @@ void launch_w4a8_linear(const void *x, const void *packed, const void *meta, con
     const int lds = xq_lds_bytes(c, M, K);
     std::call_once(g_xq_once[idx], [c] {
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(c->k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                64 + 16 * (kXqMaxK + 16));
+                                kXqHead + 16 * (kXqMaxK + 16));
     });
     const int64_t NS = N / 16;
     hipLaunchKernelGGL(c->k, dim3(static_cast<unsigned>((NS + c->nbw - 1) / c->nbw)), dim3(64 * c->waves), lds, st,

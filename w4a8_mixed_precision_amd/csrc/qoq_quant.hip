@@ -10,12 +10,18 @@
 #include "qoq_device.h"
 #include "qoq_internal.h"
 
+#include <algorithm>
+
 namespace qoq {
 
 // ---------------------------------------------------------------------------
-// activation quantizer: one 256-thread workgroup per token row.  Each thread keeps
-// up to kActChunks 16-byte chunks of the row in registers so the row is read from
-// HBM once; longer rows re-read the remainder (L2-resident) in the second pass.
+// activation quantizer: 256-thread workgroups, gridDim.y of them per token row.
+// Each thread keeps up to kActChunks 16-byte chunks of the row in registers so the
+// row is read from HBM once; longer rows re-read the remainder (L2-resident) in the
+// second pass.  With few tokens a row is split over gridDim.y workgroups: each
+// reads the whole row for the maximum (the other reads hit L2) and quantizes and
+// stores only the register slots c with c % gridDim.y == blockIdx.y, so the work of
+// a long row is not left to one compute unit.
 // ---------------------------------------------------------------------------
 constexpr int kActThreads = 256;
 constexpr int kActChunks = 16;   // 16 x 8 halves x 256 threads = rows up to K = 32768
@@ -66,7 +72,9 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
 
   const __half sh = sym_scale(amax, static_cast<float>(kXQmax));
   const float s = __half2float(sh);
-  if (threadIdx.x == 0) sx[row] = sh;
+  const float rcp = act_rcp(s);
+  const int part = blockIdx.y, parts = gridDim.y;
+  if (threadIdx.x == 0 && part == 0) sx[row] = sh;
 
   auto store = [&](int idx, uint2 q) {
     if (TILED)
@@ -78,14 +86,15 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
 #pragma unroll
   for (int c = 0; c < kActChunks; ++c) {
     int idx = threadIdx.x + c * kActThreads;
-    if (idx < nchunk) {
-      const uint2 q = quant_chunk8(v[c], s);
+    if (idx < nchunk && c % parts == part) {
+      const uint2 q = quant_chunk8(v[c], s, rcp);
       store(idx, q);
       if (ROWSUM) tsum += code_sum8(q);
     }
   }
+  // the remainder of rows longer than the register budget (launched with one part)
   for (int idx = threadIdx.x + kActChunks * kActThreads; idx < nchunk; idx += kActThreads) {
-    const uint2 q = quant_chunk8(xr[idx], s);
+    const uint2 q = quant_chunk8(xr[idx], s, rcp);
     store(idx, q);
     if (ROWSUM) tsum += code_sum8(q);
   }
@@ -103,20 +112,29 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
   }
 }
 
+// workgroups per row: enough to give a few rows about 256 workgroups, at most one
+// per register slot in use; one when the row does not fit the registers
+unsigned row_parts(int64_t M, int64_t K) {
+  const int64_t slots = (K / 8 + kActThreads - 1) / kActThreads;
+  if (slots > kActChunks) return 1;
+  return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(slots, 256 / M)));
+}
+
 void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, void *sx,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
-                     static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
-                     static_cast<__half *>(sx), nullptr);
+  hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<unsigned>(M), row_parts(M, K)),
+                     dim3(kActThreads), 0, stream, static_cast<const __half *>(x), static_cast<int>(K),
+                     static_cast<int8_t *>(qx), static_cast<__half *>(sx), nullptr);
 }
 
 void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void *qx, void *sx,
                                        hipStream_t stream) {
-  hipLaunchKernelGGL((quantize_act_kernel<false, true>), dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0,
-                     stream, static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
-                     static_cast<__half *>(sx), nullptr);
+  hipLaunchKernelGGL((quantize_act_kernel<false, true>), dim3(static_cast<unsigned>(M), row_parts(M, K)),
+                     dim3(kActThreads), 0, stream, static_cast<const __half *>(x), static_cast<int>(K),
+                     static_cast<int8_t *>(qx), static_cast<__half *>(sx), nullptr);
 }
 
+// one part per row: the code sum needs every code of the row
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream) {
   hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,

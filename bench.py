@@ -77,6 +77,7 @@ class Case:
         self.bytes = wl.algorithmic_bytes(M, L.N, L.K, per_channel)
         self.ws = None
         self.lws = None
+        self.prod = None
         self.i = 0
 
     def workspace(self, q):
@@ -117,6 +118,32 @@ class Case:
             q.w4a8_gemm_tiled(self.qt, self.sx, p, m, s, self.M, self.L.N, self.L.K, out=self.out)
         else:
             q.w4a8_gemm(self.qx, self.sx, p, m, s, self.L.N, out=self.out, workspace=self.workspace(q))
+
+    def producer(self, q):
+        """The kernel that would feed this GEMM with the quantization fused in: RMSNorm
+        + quantization before QKV / gate+up (K = hidden size), SiLU(gate) * up +
+        quantization before the down projection (K = intermediate size); same code
+        layout as the linear step."""
+        import torch
+        if self.prod is None:
+            if self.L.name.startswith(("llama3_8b_down", "qwen72b_down")):
+                gu = torch.cat([self.x, self.x.flip(1)], dim=1).contiguous()
+                self.prod = ("silu", gu)
+            else:
+                g = torch.ones(self.L.K, dtype=torch.float16, device=self.x.device)
+                self.prod = ("norm", g)
+        kind, t = self.prod
+        out = (self.qt if self.tiled else self.qx, self.sx, None)
+        if kind == "silu":
+            q.silu_mul_quantize(t[:, :self.L.K], t[:, self.L.K:], tiled=self.tiled, out=out)
+        else:
+            q.rmsnorm_quantize(self.x, t, 1e-5, tiled=self.tiled, out=out)
+
+    def producer_bytes(self):
+        M, K = self.M, self.L.K
+        if self.prod is not None and self.prod[0] == "silu":
+            return 4 * M * K + M * K + 2 * M
+        return 2 * M * K + 2 * K + M * K + 2 * M
 
     def quant_only(self, q):
         if self.pc:
@@ -260,6 +287,10 @@ def run_case_metrics(c, q, torch, launches):
     g = time_launches(lambda: c.gemm_only(q), launches, torch)
     a = time_launches(lambda: c.quant_only(q), launches, torch)
     s = time_launches(lambda: c.step(q), launches, torch)
+    pr = None
+    if not c.pc and c.L.K <= 32768:
+        c.producer(q)
+        pr = time_launches(lambda: c.producer(q), launches, torch)
     b = c.bytes
     return {
         "M": c.M, "K": c.L.K, "N": c.L.N,
@@ -274,6 +305,9 @@ def run_case_metrics(c, q, torch, launches):
         "mfma_frac": c.ops / g / 1e12 / INT8_PEAK_TOPS,
         "roofline_frac": max(b["total"] / (HBM_PEAK_GBPS * 1e9), c.ops / (INT8_PEAK_TOPS * 1e12)) / g,
         "quant_GBps": (3 * c.M * c.L.K + 2 * c.M) / a / 1e9,
+        "producer": None if pr is None else (c.prod[0] + "_quant"),
+        "producer_us": None if pr is None else pr * 1e6,
+        "producer_GBps": None if pr is None else c.producer_bytes() / pr / 1e9,
         "rotation_sets": len(c.sets),
     }
 

@@ -130,6 +130,36 @@ int qoq_quantize_activations_rowsum(const void *x_fp16, int64_t M, int64_t K, vo
 int qoq_quantize_activations_tiled(const void *x_fp16, int64_t M, int64_t K, void *qx_tiled,
                                    void *s_x_fp16, void *stream);
 
+/* The producers of the GEMM's INT8 activations with the quantization fused in
+ * ("QServe：把 W4A8KV4 ..." review, runtime precision mapping §3.2 and data path
+ * step 2: fused into the preceding normalization kernel for the QKV projection and
+ * the first FFN layer, into the preceding activation kernel for the second FFN
+ * layer).  Each forms the fp16 value the unfused pipeline would write, in
+ * registers, and quantizes it per token exactly as qoq_quantize_activations (same
+ * codes and s_X); t_x (NULL or INT32 [M], 4-byte aligned) also receives the code
+ * sums of qoq_quantize_activations_rowsum.
+ *   layout 0: qx row-major [M,K]; layout 1: the tiled layout of
+ *   qoq_quantize_activations_tiled (M <= 64, K % 64 == 0, round_up(M,16)*K bytes).
+ * K % 8 == 0 and K <= 32768 (one row in registers); qx 16-byte aligned, s_x_fp16 [M].
+ * Errors: INVALID, UNSUPPORTED (K > 32768; layout 1 with M > 64), ALIGNMENT, HIP. */
+
+/* RMSNorm (the normalization of the Llama / Qwen workloads) + quantization:
+ *   y = fp16(fp32(fp32(x * inv) * gamma)), inv = fp32(1 / fp32(sqrt(fp32(mean +
+ *   eps)))), mean = fp32(sum_k x^2 / K) with the sum in fp64 (IEEE operations).
+ * x_fp16 [M,K] row-major and gamma_fp16 [K], both 16-byte aligned; eps > 0. */
+int qoq_rmsnorm_quantize(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M,
+                         int64_t K, int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x,
+                         void *stream);
+
+/* SwiGLU activation + quantization: h = fp16(gate * up / (1 + exp(-gate))), the
+ * expression evaluated in fp64 and rounded once.  gate_fp16 and up_fp16: [M,K]
+ * with row stride ld elements (ld >= K, ld % 8 == 0; e.g. the two halves of a fused
+ * gate+up projection output [M, 2K]: gate = out, up = out + K, ld = 2K), 16-byte
+ * aligned. */
+int qoq_silu_mul_quantize(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M,
+                          int64_t K, int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x,
+                          void *stream);
+
 /* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
  * It is non-zero when the plan splits the K groups of each output tile over several
  * workgroups ("QServe：把 W4A8KV4 ..." review §3.2: split-k when the batch is small;

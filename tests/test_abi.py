@@ -285,3 +285,30 @@ def test_per_channel_sizes_and_validation(L):
     h = L.qoq_w4a8_gemm_pc_i32
     assert h(FAKE, FAKE, FAKE, NUL, FAKE, 4, 32, 256, NUL, 0, NUL) == INVALID
     assert qoq.gemm_workspace_bytes(M, N, K, group=0) == qoq.gemm_workspace_bytes(M, N, K)
+
+
+def test_fused_producer_validation(L):
+    """RMSNorm / SiLU*up + quantization: argument checks before any launch."""
+    r = L.qoq_rmsnorm_quantize
+    ok = dict(x=FAKE, g=FAKE, eps=1e-5, M=4, K=4096, lay=0, q=FAKE, s=FAKE, t=NUL)
+    call = lambda **kw: r(*[{**ok, **kw}[k] for k in ("x", "g", "eps", "M", "K", "lay", "q", "s", "t")], NUL)
+    assert call(M=0) == OK
+    assert call(eps=0.0) == INVALID and call(eps=-1.0) == INVALID
+    assert call(K=100) == INVALID                               # K % 8
+    assert call(K=32776) == UNSUPPORTED                         # one row in registers
+    assert call(lay=2) == INVALID
+    assert call(lay=1, K=4104) == INVALID                       # tiled: K % 64
+    assert call(lay=1, M=65) == UNSUPPORTED
+    assert call(x=NUL) == INVALID and call(q=NUL) == INVALID and call(s=NUL) == INVALID
+    assert call(x=ODD) == ALIGNMENT and call(g=ODD) == ALIGNMENT and call(q=ODD) == ALIGNMENT
+    assert call(t=ODD) == ALIGNMENT
+    f = L.qoq_silu_mul_quantize
+    ok2 = dict(gt=FAKE, up=FAKE, ld=8192, M=4, K=4096, lay=0, q=FAKE, s=FAKE, t=NUL)
+    call2 = lambda **kw: f(*[{**ok2, **kw}[k] for k in ("gt", "up", "ld", "M", "K", "lay", "q", "s", "t")], NUL)
+    assert call2(M=0) == OK
+    assert call2(ld=4000) == INVALID                            # ld < K
+    assert call2(ld=8196) == INVALID                            # ld % 8
+    assert call2(K=40000, ld=40000) == UNSUPPORTED
+    assert call2(lay=1, M=65) == UNSUPPORTED
+    assert call2(gt=NUL) == INVALID and call2(up=NUL) == INVALID
+    assert call2(gt=ODD) == ALIGNMENT and call2(up=ODD) == ALIGNMENT and call2(q=ODD) == ALIGNMENT

@@ -119,6 +119,40 @@ int qoq_quantize_activations_tiled(const void *x_fp16, int64_t M, int64_t K, voi
   return launch_status();
 }
 
+static int fused_common_checks(int64_t M, int64_t K, int32_t layout, const void *qx, const void *s_x,
+                               const int32_t *t_x) {
+  if (M < 0 || K <= 0 || K % 8 != 0 || (layout != 0 && layout != 1)) return QOQ_ERR_INVALID;
+  if (layout == 1 && K % 64 != 0) return QOQ_ERR_INVALID;
+  if (K > qoq::kFusedMaxK || M > kMaxDim || (layout == 1 && M > qoq::kTiledMaxM)) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!qx || !s_x) return QOQ_ERR_INVALID;
+  if (!aligned(qx, 16) || !aligned(s_x, 2) || (t_x && !aligned(t_x, 4))) return QOQ_ERR_ALIGNMENT;
+  return 1;   // proceed
+}
+
+int qoq_rmsnorm_quantize(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M, int64_t K,
+                         int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x, void *stream) {
+  if (!(eps > 0.0f) || eps > 1.0e30f) return QOQ_ERR_INVALID;
+  const int st = fused_common_checks(M, K, layout, qx, s_x_fp16, t_x);
+  if (st != 1) return st;
+  if (!x_fp16 || !gamma_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(gamma_fp16, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_rmsnorm_quantize(x_fp16, gamma_fp16, eps, M, K, layout, qx, s_x_fp16, t_x, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_silu_mul_quantize(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K,
+                          int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x, void *stream) {
+  if (ld < K || ld % 8 != 0) return QOQ_ERR_INVALID;
+  const int st = fused_common_checks(M, K, layout, qx, s_x_fp16, t_x);
+  if (st != 1) return st;
+  if (!gate_fp16 || !up_fp16) return QOQ_ERR_INVALID;
+  if (ld > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  if (!aligned(gate_fp16, 16) || !aligned(up_fp16, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_silu_mul_quantize(gate_fp16, up_fp16, ld, M, K, layout, qx, s_x_fp16, t_x, as_stream(stream));
+  return launch_status();
+}
+
 static int gemm_tiled_common(const void *qx_tiled, const void *s_x_fp16, const void *packed_w,
                              const void *group_meta, const void *s_w_fp16, void *out, int out_kind, int64_t M,
                              int64_t N, int64_t K, void *stream) {

@@ -21,6 +21,15 @@ void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream);
 
+// producers with the quantization fused in (tiled: codes in the tiled layout,
+// M <= kTiledMaxM); tx may be null (no code sums); K % 8 == 0, K <= kFusedMaxK;
+// gate / up rows have stride ld elements
+constexpr int64_t kFusedMaxK = 32768;
+void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_t M, int64_t K, int tiled,
+                             void *qx, void *sx, void *tx, hipStream_t stream);
+void launch_silu_mul_quantize(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, int tiled,
+                              void *qx, void *sx, void *tx, hipStream_t stream);
+
 // GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators; ws holds at least
 // gemm_workspace_need(M, N, K) bytes (may be null when that is 0)
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta,

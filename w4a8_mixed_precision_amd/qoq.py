@@ -45,6 +45,10 @@ _SIGNATURES = {
                             ctypes.c_int),
     "qoq_w4a8_gemm_tiled_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp], ctypes.c_int),
     "qoq_gemm_tiled_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_rmsnorm_quantize": ([_c_vp, _c_vp, ctypes.c_float, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp],
+                             ctypes.c_int),
+    "qoq_silu_mul_quantize": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp],
+                              ctypes.c_int),
     "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
                           _c_vp], ctypes.c_int),
@@ -229,6 +233,47 @@ def quantize_activations_tiled(x: torch.Tensor, out=None):
            lib().qoq_quantize_activations_tiled(_dev(x, "x", torch.float16), M, K, _dev(qx, "qx", torch.int8),
                                                 _dev(s_x, "s_x", torch.float16), _stream(x)))
     return qx, s_x
+
+
+def _fused_outputs(M, K, dev, tiled, rowsum, out):
+    if out is not None:
+        return out
+    qx = torch.empty(tiled_bytes(M, K) if tiled else (M, K), dtype=torch.int8, device=dev)
+    s_x = torch.empty(M, dtype=torch.float16, device=dev)
+    t = torch.empty(M, dtype=torch.int32, device=dev) if rowsum else None
+    return qx, s_x, t
+
+
+def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float, tiled: bool = False, rowsum: bool = False,
+                     out=None):
+    """RMSNorm + per-token INT8 quantization in one kernel: X fp16 [M, K], gamma fp16
+    [K] -> (qx, s_x fp16 [M], t int32 [M] or None); qx row-major [M, K] or tiled."""
+    M, K = x.shape
+    qx, s_x, t = _fused_outputs(M, K, x.device, tiled, rowsum, out)
+    _check("qoq_rmsnorm_quantize",
+           lib().qoq_rmsnorm_quantize(_dev(x, "x", torch.float16), _dev(gamma, "gamma", torch.float16), float(eps),
+                                      M, K, 1 if tiled else 0, _dev(qx, "qx", torch.int8),
+                                      _dev(s_x, "s_x", torch.float16),
+                                      None if t is None else _dev(t, "t", torch.int32), _stream(x)))
+    return qx, s_x, t
+
+
+def silu_mul_quantize(gate: torch.Tensor, up: torch.Tensor, tiled: bool = False, rowsum: bool = False, out=None):
+    """SiLU(gate) * up + per-token INT8 quantization in one kernel.  gate, up: fp16
+    [M, K] views with the same row stride (e.g. the halves of a gate+up output)."""
+    M, K = gate.shape
+    if up.shape != gate.shape or gate.stride(1) != 1 or up.stride(1) != 1 or gate.stride(0) != up.stride(0):
+        raise ValueError("gate and up must be [M, K] views with unit column stride and the same row stride")
+    qx, s_x, t = _fused_outputs(M, K, gate.device, tiled, rowsum, out)
+    for t_, n_ in ((gate, "gate"), (up, "up")):
+        if not isinstance(t_, torch.Tensor) or t_.device.type != "cuda" or t_.dtype != torch.float16:
+            raise TypeError(f"{n_} must be an fp16 HIP device tensor")
+    _check("qoq_silu_mul_quantize",
+           lib().qoq_silu_mul_quantize(ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(up.data_ptr()),
+                                       gate.stride(0), M, K, 1 if tiled else 0, _dev(qx, "qx", torch.int8),
+                                       _dev(s_x, "s_x", torch.float16),
+                                       None if t is None else _dev(t, "t", torch.int32), _stream(gate)))
+    return qx, s_x, t
 
 
 def quantize_activations_rowsum(x: torch.Tensor, out=None):

@@ -160,6 +160,14 @@ int qoq_silu_mul_quantize(const void *gate_fp16, const void *up_fp16, int64_t ld
                           int64_t K, int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x,
                           void *stream);
 
+/* The same kernels without the quantization (the unfused pipeline's normalization and
+ * activation kernels): the fp16 values the fused entry points quantize, [M,K]
+ * row-major fp16, 16-byte aligned.  Same arguments and errors otherwise. */
+int qoq_rmsnorm(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M, int64_t K,
+                void *y_fp16, void *stream);
+int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K,
+                 void *h_fp16, void *stream);
+
 /* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
  * It is non-zero when the plan splits the K groups of each output tile over several
  * workgroups ("QServe：把 W4A8KV4 ..." review §3.2: split-k when the batch is small;

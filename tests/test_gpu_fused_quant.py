@@ -126,3 +126,39 @@ def test_fused_layer_rows_sampled(gpu, name, M):
     assert np.array_equal(host(q)[rows], wq)
     assert np.array_equal(host(s)[rows].view(np.uint16), ws.view(np.uint16))
     assert np.array_equal(host(t)[rows].astype(np.int64), wt.astype(np.int64))
+
+
+def _all_finite_fp16():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return v[np.isfinite(v)]
+
+
+@pytest.mark.parametrize("u", [1.0, -0.3701171875, 3.125, 0.00099945068359375])
+def test_silu_mul_every_fp16_gate(gpu, u):
+    """The fp16 value of SiLU(gate) * up for every finite fp16 gate (63488 values),
+    bit for bit against the oracle's single rounding of the fp64 expression: pins
+    the fast fp32 path, its 2^-20 error band and the fp64 decision between the two
+    candidates."""
+    g = _all_finite_fp16()
+    K = 4096
+    n = (g.size + K - 1) // K * K
+    gg = np.zeros(n, np.float16)
+    gg[: g.size] = g
+    gg = gg.reshape(-1, K)
+    uu = np.full(gg.shape, u, np.float16)
+    say(f"silu_mul every fp16 gate, up={u}")
+    h = host(qoq.silu_mul(to_dev(gg, gpu), to_dev(uu, gpu)))
+    want = fq.silu_mul_fp16(gg, uu)
+    assert np.array_equal(h.view(np.uint16), want.view(np.uint16))
+
+
+def test_rmsnorm_fp16_values(gpu):
+    """The normalization's fp16 output itself, bit for bit, on rows of every scale."""
+    rng = np.random.default_rng(12)
+    for M, K in [(7, 4096), (3, 14336), (2, 29568), (5, 136)]:
+        x = (rng.standard_normal((M, K)) * rng.choice([1e-3, 1.0, 50.0], (M, 1))).astype(np.float16)
+        gamma = (1.0 + 0.3 * rng.standard_normal(K)).astype(np.float16)
+        say(f"rmsnorm fp16 M={M} K={K}")
+        y = host(qoq.rmsnorm(to_dev(x, gpu), to_dev(gamma, gpu), EPS))
+        assert np.array_equal(y.view(np.uint16), fq.rmsnorm_fp16(x, gamma, EPS).view(np.uint16))

@@ -153,6 +153,28 @@ int qoq_silu_mul_quantize(const void *gate_fp16, const void *up_fp16, int64_t ld
   return launch_status();
 }
 
+int qoq_rmsnorm(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M, int64_t K, void *y_fp16,
+                void *stream) {
+  if (!(eps > 0.0f) || eps > 1.0e30f || M < 0 || K <= 0 || K % 8 != 0) return QOQ_ERR_INVALID;
+  if (K > qoq::kFusedMaxK || M > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !gamma_fp16 || !y_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(gamma_fp16, 16) || !aligned(y_fp16, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_rmsnorm_quantize(x_fp16, gamma_fp16, eps, M, K, -1, y_fp16, nullptr, nullptr, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K, void *h_fp16,
+                 void *stream) {
+  if (M < 0 || K <= 0 || K % 8 != 0 || ld < K || ld % 8 != 0) return QOQ_ERR_INVALID;
+  if (K > qoq::kFusedMaxK || M > kMaxDim || ld > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!gate_fp16 || !up_fp16 || !h_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(gate_fp16, 16) || !aligned(up_fp16, 16) || !aligned(h_fp16, 16)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_silu_mul_quantize(gate_fp16, up_fp16, ld, M, K, -1, h_fp16, nullptr, nullptr, as_stream(stream));
+  return launch_status();
+}
+
 static int gemm_tiled_common(const void *qx_tiled, const void *s_x_fp16, const void *packed_w,
                              const void *group_meta, const void *s_w_fp16, void *out, int out_kind, int64_t M,
                              int64_t N, int64_t K, void *stream) {

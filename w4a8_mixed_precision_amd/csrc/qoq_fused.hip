@@ -24,8 +24,7 @@ namespace qoq {
 
 namespace {
 
-constexpr int kFThreads = 256;
-constexpr int kFChunks = 16;            // 16 chunks x 8 values x 256 threads: K <= 32768
+constexpr int kFThreads = 256;           // up to 16 chunks x 8 values x 256 threads: K <= 32768
 
 __device__ __forceinline__ double block_sum_f64(double v, double *red) {
 #pragma unroll
@@ -71,10 +70,24 @@ __device__ __forceinline__ void store_codes(int8_t *__restrict__ qx, int row, in
     reinterpret_cast<uint2 *>(qx + static_cast<size_t>(row) * K)[idx] = q;
 }
 
-// Quantize the fp16 values y (register chunks, fp16 bits) of one row, given their
-// maximum magnitude (fp16 bits): s_X, the codes of this part's slots, the code sum.
-template <bool TILED, bool ROWSUM>
-__device__ __forceinline__ void quantize_row(const uint4 (&y)[kFChunks], unsigned amax, int row, int K,
+// Quantize the fp16 values y (CH register chunks per thread, fp16 bits) of one row,
+// given their maximum magnitude (fp16 bits): s_X, the codes of this part's slots
+// (slot c of every thread belongs to part c % gridDim.y), the code sum.
+// The unfused pipeline's fp16 output instead (the value the fused kernels quantize):
+// row-major [M, K] fp16.
+template <int CH>
+__device__ __forceinline__ void store_row_fp16(const uint4 (&y)[CH], int row, int K, __half *__restrict__ out) {
+  const int nchunk = K >> 3;
+  uint4 *o = reinterpret_cast<uint4 *>(out + static_cast<size_t>(row) * K);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * kFThreads;
+    if (idx < nchunk) o[idx] = y[c];
+  }
+}
+
+template <int CH, bool TILED, bool ROWSUM>
+__device__ __forceinline__ void quantize_row(const uint4 (&y)[CH], unsigned amax, int row, int K,
                                              int8_t *__restrict__ qx, __half *__restrict__ sx,
                                              int *__restrict__ tx, int *ired) {
   const int nchunk = K >> 3;
@@ -85,7 +98,7 @@ __device__ __forceinline__ void quantize_row(const uint4 (&y)[kFChunks], unsigne
   if (threadIdx.x == 0 && part == 0) sx[row] = sh;
   int tsum = 0;
 #pragma unroll
-  for (int c = 0; c < kFChunks; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int idx = threadIdx.x + c * kFThreads;
     if (idx < nchunk && c % parts == part) {
       const uint2 q = quant_chunk8(y[c], s, rcp);
@@ -108,8 +121,10 @@ __device__ __forceinline__ unsigned pack_half2(__half lo, __half hi) {
 // ---------------------------------------------------------------------------
 // RMSNorm + quantization.  One row per blockIdx.x; gridDim.y workgroups share a
 // row (each recomputes the row's statistics and quantizes its share of the slots).
+// CH chunks of 8 values per thread hold the row (CH * 2048 >= K): the launcher
+// picks the smallest, so short rows leave registers for more waves.
 // ---------------------------------------------------------------------------
-template <bool TILED, bool ROWSUM>
+template <int CH, bool TILED, bool ROWSUM, bool OUT16 = false>
 __global__ __launch_bounds__(kFThreads) void rmsnorm_quant_kernel(const __half *__restrict__ x,
                                                                   const __half *__restrict__ gamma, float eps,
                                                                   int K, int8_t *__restrict__ qx,
@@ -121,34 +136,36 @@ __global__ __launch_bounds__(kFThreads) void rmsnorm_quant_kernel(const __half *
   const int nchunk = K >> 3;
   const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(row) * K);
   const uint4 *gr = reinterpret_cast<const uint4 *>(gamma);
-  uint4 v[kFChunks], g[kFChunks];
+  uint4 v[CH];
 #pragma unroll
-  for (int c = 0; c < kFChunks; ++c) {          // every load first: all in flight together
+  for (int c = 0; c < CH; ++c) {                 // every load first: all in flight together
     const int idx = threadIdx.x + c * kFThreads;
     v[c] = idx < nchunk ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
-    g[c] = idx < nchunk ? gr[idx] : make_uint4(0u, 0u, 0u, 0u);
   }
   double ss = 0.0;
 #pragma unroll
-  for (int c = 0; c < kFChunks; ++c) {
-    if (threadIdx.x + c * kFThreads >= nchunk) continue;   // past the row (whole slots skipped)
+  for (int c = 0; c < CH; ++c) {
     const unsigned w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double xv = static_cast<double>(half_bits_to_float((w[i >> 1] >> (16 * (i & 1))) & 0xffffu));
-      ss += xv * xv;                             // each square is exact in fp64
+      ss += xv * xv;                             // each square is exact in fp64; zero chunks add 0
     }
   }
   const double sum = block_sum_f64(ss, dred);
   const float mean = static_cast<float>(sum / static_cast<double>(K));
-  const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(mean, eps)));
+  // IEEE square root: __builtin_sqrtf is correctly rounded here (HIP's __fsqrt_rn
+  // maps to the approximate native instruction unless the library's rounded
+  // operations are selected, and differed in the last bit)
+  const float inv = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(mean, eps)));
 
   unsigned amax = 0;
 #pragma unroll
-  for (int c = 0; c < kFChunks; ++c) {
-    if (threadIdx.x + c * kFThreads >= nchunk) continue;
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * kFThreads;
+    const uint4 gc = idx < nchunk ? gr[idx] : make_uint4(0u, 0u, 0u, 0u);   // L2-resident, shared by rows
     const unsigned w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-    const unsigned gw[4] = {g[c].x, g[c].y, g[c].z, g[c].w};
+    const unsigned gw[4] = {gc.x, gc.y, gc.z, gc.w};
     unsigned o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -158,35 +175,56 @@ __global__ __launch_bounds__(kFThreads) void rmsnorm_quant_kernel(const __half *
       __asm__ volatile("" : "+v"(t0), "+v"(t1));   // fp32(x * inv) is rounded before the gamma product
       o[i] = pack_half2(mul_round_half(t0, g0), mul_round_half(t1, g1));
     }
-    v[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    v[c] = make_uint4(o[0], o[1], o[2], o[3]);   // past the row: x = 0, gamma = 0 -> 0
     amax = absmax_bits8(v[c], amax);
   }
+  if (OUT16) {                                   // qx carries the fp16 output
+    store_row_fp16<CH>(v, row, K, reinterpret_cast<__half *>(qx));
+    return;
+  }
   amax = block_max_u32(amax, ured);
-  quantize_row<TILED, ROWSUM>(v, amax, row, K, qx, sx, tx, ired);
+  quantize_row<CH, TILED, ROWSUM>(v, amax, row, K, qx, sx, tx, ired);
 }
 
 // ---------------------------------------------------------------------------
 // SiLU(gate) * up + quantization.  gate and up rows have stride ld (elements).
-// One workgroup per row (gridDim.y == 1): every value exactly (fp64) in
-// registers, then the quantization.  Several per row (gridDim.y > 1, few tokens):
-// the row maximum needs every value, the codes only this part's, so all values are
-// first formed in fp32 (within 2^-20 relative of the exact ones), the exact fp64
-// values are taken for the candidates of the maximum (fp32 magnitude within 2^-12
-// of the fp32 maximum) and for this part's slots.
+// h = fp16 of the exact gate * up / (1 + exp(-gate)).  Each value is first formed
+// in fp32, h32 = (gate * up) * rcp(1 + expf(-gate)): gate * up is exact (two 11-bit
+// significands) and the rest costs a few ulps, well under 2^-20 relative.  If
+// h32 - e and h32 + e (e = 2^-20 |h32|) round to the same fp16, so does the exact
+// value (rounding is monotone).  Otherwise the two fp16 candidates are adjacent
+// and the exact value is compared with their midpoint in fp64 (gate * up / (1 +
+// exp(-gate)) in fp64; for gate != 0 it is irrational, so it never equals the
+// midpoint), in a branch the wave takes only when one of its lanes needs it.  The
+// fp16 value is therefore RN16 of the fp64 expression, like the oracle's.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ __half silu_mul_exact(float gf, float uf) {
-  const double gd = static_cast<double>(gf), ud = static_cast<double>(uf);
-  const _Float16 h = static_cast<_Float16>(gd * ud / (1.0 + exp(-gd)));   // one rounding, fp64 -> fp16
-  return __ushort_as_half(__builtin_bit_cast(unsigned short, h));
-}
-
-// fp32 with the accurate expf (about 1 ulp) and an IEEE divide; gate * up is exact
-// in fp32 (two 11-bit significands): relative error well under 2^-20
 __device__ __forceinline__ float silu_mul_fast(float gf, float uf) {
-  return gf * uf / (1.0f + expf(-gf));
+  return (gf * uf) * __builtin_amdgcn_rcpf(1.0f + expf(-gf));
 }
 
-template <bool TILED, bool ROWSUM>
+// fp16 bits of RN16(h) for h within e of h32, or 0xffffffff when undecided
+__device__ __forceinline__ unsigned round_h16(float h32) {
+  const float e = fabsf(h32) * 0x1p-20f;
+  const unsigned lo = __half_as_ushort(__float2half_rn(h32 - e));
+  const unsigned hi = __half_as_ushort(__float2half_rn(h32 + e));
+  return lo == hi ? lo : 0xffffffffu;
+}
+
+// the undecided case: compare the fp64 value with the midpoint of the two
+// candidates RN16(h32 - e) < RN16(h32 + e)
+__device__ __noinline__ unsigned decide_h16(float gf, float uf, float h32) {
+  const float e = fabsf(h32) * 0x1p-20f;
+  const __half lo = __float2half_rn(h32 - e), hi = __float2half_rn(h32 + e);
+  const double mid = 0.5 * (static_cast<double>(__half2float(lo)) + static_cast<double>(__half2float(hi)));
+  const double gd = static_cast<double>(gf);
+  const double h = gd * static_cast<double>(uf) / (1.0 + exp(-gd));
+  const unsigned lb = __half_as_ushort(lo), hb = __half_as_ushort(hi);
+  if (h < mid) return lb;
+  if (h > mid) return hb;
+  return (lb & 1u) ? hb : lb;                      // a tie (only in principle): to even
+}
+
+template <int CH, bool TILED, bool ROWSUM, bool OUT16 = false>
 __global__ __launch_bounds__(kFThreads) void silu_mul_quant_kernel(const __half *__restrict__ gate,
                                                                    const __half *__restrict__ up, int ld, int K,
                                                                    int8_t *__restrict__ qx,
@@ -195,76 +233,48 @@ __global__ __launch_bounds__(kFThreads) void silu_mul_quant_kernel(const __half 
   __shared__ unsigned ured[kFThreads / 64];
   __shared__ int ired[kFThreads / 64];
   const int row = blockIdx.x;
-  const int part = blockIdx.y, parts = gridDim.y;
   const int nchunk = K >> 3;
   const uint4 *gr = reinterpret_cast<const uint4 *>(gate + static_cast<size_t>(row) * ld);
   const uint4 *ur = reinterpret_cast<const uint4 *>(up + static_cast<size_t>(row) * ld);
-  uint4 a[kFChunks], b[kFChunks];
+  uint4 a[CH], b[CH];
 #pragma unroll
-  for (int c = 0; c < kFChunks; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int idx = threadIdx.x + c * kFThreads;
     a[c] = idx < nchunk ? gr[idx] : make_uint4(0u, 0u, 0u, 0u);
     b[c] = idx < nchunk ? ur[idx] : make_uint4(0u, 0u, 0u, 0u);
   }
   unsigned amax = 0;
-  if (parts == 1) {
 #pragma unroll
-    for (int c = 0; c < kFChunks; ++c) {
-      if (threadIdx.x + c * kFThreads >= nchunk) continue;   // past the row (whole slots skipped)
-      const unsigned gw[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
-      const unsigned uw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
-      unsigned o[4];
+  for (int c = 0; c < CH; ++c) {
+    const unsigned gw[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
+    const unsigned uw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
+    float gf[8], uf[8], h[8];
+    unsigned r[8];
+    bool open = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = pack_half2(silu_mul_exact(half_bits_to_float(gw[i] & 0xffffu), half_bits_to_float(uw[i] & 0xffffu)),
-                          silu_mul_exact(half_bits_to_float(gw[i] >> 16), half_bits_to_float(uw[i] >> 16)));
-      a[c] = make_uint4(o[0], o[1], o[2], o[3]);
-      amax = absmax_bits8(a[c], amax);
+    for (int i = 0; i < 8; ++i) {
+      const unsigned sh = 16 * (i & 1);
+      gf[i] = half_bits_to_float((gw[i >> 1] >> sh) & 0xffffu);
+      uf[i] = half_bits_to_float((uw[i >> 1] >> sh) & 0xffffu);
+      h[i] = silu_mul_fast(gf[i], uf[i]);
+      r[i] = round_h16(h[i]);
+      open |= r[i] == 0xffffffffu;
     }
-    amax = block_max_u32(amax, ured);
-  } else {
-    float fmax = 0.0f;
+    if (__ballot(open) != 0) {                     // uniform: rare
 #pragma unroll
-    for (int c = 0; c < kFChunks; ++c) {
-      if (threadIdx.x + c * kFThreads >= nchunk) continue;
-      const unsigned gw[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
-      const unsigned uw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned sh = 16 * (i & 1);
-        fmax = fmaxf(fmax, fabsf(silu_mul_fast(half_bits_to_float((gw[i >> 1] >> sh) & 0xffffu),
-                                               half_bits_to_float((uw[i >> 1] >> sh) & 0xffffu))));
-      }
+      for (int i = 0; i < 8; ++i)
+        if (r[i] == 0xffffffffu) r[i] = decide_h16(gf[i], uf[i], h[i]);
     }
-    fmax = __uint_as_float(block_max_u32(__float_as_uint(fmax), ured));   // non-negative: bit order = value order
-    const float cut = fmax * (1.0f - 0x1p-12f);
-#pragma unroll
-    for (int c = 0; c < kFChunks; ++c) {
-      if (threadIdx.x + c * kFThreads >= nchunk) continue;
-      const unsigned gw[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
-      const unsigned uw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
-      const bool mine = c % parts == part;
-      unsigned o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned sh = 16 * (i & 1);
-        const float gf = half_bits_to_float((gw[i >> 1] >> sh) & 0xffffu);
-        const float uf = half_bits_to_float((uw[i >> 1] >> sh) & 0xffffu);
-        const bool cand = fabsf(silu_mul_fast(gf, uf)) >= cut;
-        if (mine || cand) {
-          const unsigned hb = __half_as_ushort(silu_mul_exact(gf, uf));
-          if (cand) amax = max(amax, hb & 0x7fffu);
-          o[i >> 1] |= hb << sh;
-        }
-      }
-      if (mine) a[c] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    amax = block_max_u32(amax, ured);
+    a[c] = make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+    amax = absmax_bits8(a[c], amax);               // past the row: gate = up = 0 -> 0
   }
-  quantize_row<TILED, ROWSUM>(a, amax, row, K, qx, sx, tx, ired);
+  if (OUT16) {
+    store_row_fp16<CH>(a, row, K, reinterpret_cast<__half *>(qx));
+    return;
+  }
+  amax = block_max_u32(amax, ured);
+  quantize_row<CH, TILED, ROWSUM>(a, amax, row, K, qx, sx, tx, ired);
 }
-
-}  // namespace
 
 // workgroups per row: as for the standalone quantizer (a few tokens spread a row
 // over up to one workgroup per register slot); one when the code sum is wanted
@@ -274,39 +284,85 @@ unsigned fused_row_parts(int64_t M, int64_t K, bool rowsum) {
   return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(slots, 256 / M)));
 }
 
+// register chunks per thread: the smallest power of two that holds the row
+int fused_chunks(int64_t K) {
+  const int64_t slots = (K / 8 + kFThreads - 1) / kFThreads;
+  int ch = 1;
+  while (ch < slots) ch *= 2;
+  return ch;
+}
+
+template <int CH>
+void launch_rmsnorm_ch(const __half *x, const __half *g, float eps, int K, bool tiled, int8_t *q, __half *s, int *t,
+                       dim3 grid, hipStream_t st, bool out16) {
+  if (out16) {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, false, false, true>), grid, dim3(kFThreads), 0, st, x, g, eps, K, q, s, t);
+    return;
+  }
+  if (tiled) {
+    if (t) hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, true, true>), grid, dim3(kFThreads), 0, st, x, g, eps, K, q, s, t);
+    else hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, true, false>), grid, dim3(kFThreads), 0, st, x, g, eps, K, q, s, t);
+  } else {
+    if (t) hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, false, true>), grid, dim3(kFThreads), 0, st, x, g, eps, K, q, s, t);
+    else hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, false, false>), grid, dim3(kFThreads), 0, st, x, g, eps, K, q, s, t);
+  }
+}
+
+template <int CH>
+void launch_silu_ch(const __half *g, const __half *u, int ld, int K, bool tiled, int8_t *q, __half *s, int *t,
+                    dim3 grid, hipStream_t st, bool out16) {
+  if (out16) {
+    hipLaunchKernelGGL((silu_mul_quant_kernel<CH, false, false, true>), grid, dim3(kFThreads), 0, st, g, u, ld, K, q, s, t);
+    return;
+  }
+  if (tiled) {
+    if (t) hipLaunchKernelGGL((silu_mul_quant_kernel<CH, true, true>), grid, dim3(kFThreads), 0, st, g, u, ld, K, q, s, t);
+    else hipLaunchKernelGGL((silu_mul_quant_kernel<CH, true, false>), grid, dim3(kFThreads), 0, st, g, u, ld, K, q, s, t);
+  } else {
+    if (t) hipLaunchKernelGGL((silu_mul_quant_kernel<CH, false, true>), grid, dim3(kFThreads), 0, st, g, u, ld, K, q, s, t);
+    else hipLaunchKernelGGL((silu_mul_quant_kernel<CH, false, false>), grid, dim3(kFThreads), 0, st, g, u, ld, K, q, s, t);
+  }
+}
+
+}  // namespace
+
+// tiled == -1: the fp16 output of the normalization itself into qx (no quantization)
 void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_t M, int64_t K, int tiled,
                              void *qx, void *sx, void *tx, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(M), fused_row_parts(M, K, tx != nullptr));
+  const bool out16 = tiled < 0;
+  const dim3 grid(static_cast<unsigned>(M), out16 ? 1u : fused_row_parts(M, K, tx != nullptr));
   const __half *xp = static_cast<const __half *>(x);
   const __half *gp = static_cast<const __half *>(gamma);
   int8_t *q = static_cast<int8_t *>(qx);
   __half *s = static_cast<__half *>(sx);
   int *t = static_cast<int *>(tx);
   const int k = static_cast<int>(K);
-  if (tiled) {
-    if (t) hipLaunchKernelGGL((rmsnorm_quant_kernel<true, true>), grid, dim3(kFThreads), 0, st, xp, gp, eps, k, q, s, t);
-    else hipLaunchKernelGGL((rmsnorm_quant_kernel<true, false>), grid, dim3(kFThreads), 0, st, xp, gp, eps, k, q, s, t);
-  } else {
-    if (t) hipLaunchKernelGGL((rmsnorm_quant_kernel<false, true>), grid, dim3(kFThreads), 0, st, xp, gp, eps, k, q, s, t);
-    else hipLaunchKernelGGL((rmsnorm_quant_kernel<false, false>), grid, dim3(kFThreads), 0, st, xp, gp, eps, k, q, s, t);
+  switch (fused_chunks(K)) {
+    case 1: launch_rmsnorm_ch<1>(xp, gp, eps, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 2: launch_rmsnorm_ch<2>(xp, gp, eps, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 4: launch_rmsnorm_ch<4>(xp, gp, eps, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 8: launch_rmsnorm_ch<8>(xp, gp, eps, k, tiled > 0, q, s, t, grid, st, out16); break;
+    default: launch_rmsnorm_ch<16>(xp, gp, eps, k, tiled > 0, q, s, t, grid, st, out16); break;
   }
 }
 
+// tiled == -1: the fp16 activation itself into qx (no quantization)
 void launch_silu_mul_quantize(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, int tiled,
                               void *qx, void *sx, void *tx, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(M), fused_row_parts(M, K, tx != nullptr));
+  const bool out16 = tiled < 0;
+  const dim3 grid(static_cast<unsigned>(M), out16 ? 1u : fused_row_parts(M, K, tx != nullptr));
   const __half *gp = static_cast<const __half *>(gate);
   const __half *up_ = static_cast<const __half *>(up);
   int8_t *q = static_cast<int8_t *>(qx);
   __half *s = static_cast<__half *>(sx);
   int *t = static_cast<int *>(tx);
   const int k = static_cast<int>(K), l = static_cast<int>(ld);
-  if (tiled) {
-    if (t) hipLaunchKernelGGL((silu_mul_quant_kernel<true, true>), grid, dim3(kFThreads), 0, st, gp, up_, l, k, q, s, t);
-    else hipLaunchKernelGGL((silu_mul_quant_kernel<true, false>), grid, dim3(kFThreads), 0, st, gp, up_, l, k, q, s, t);
-  } else {
-    if (t) hipLaunchKernelGGL((silu_mul_quant_kernel<false, true>), grid, dim3(kFThreads), 0, st, gp, up_, l, k, q, s, t);
-    else hipLaunchKernelGGL((silu_mul_quant_kernel<false, false>), grid, dim3(kFThreads), 0, st, gp, up_, l, k, q, s, t);
+  switch (fused_chunks(K)) {
+    case 1: launch_silu_ch<1>(gp, up_, l, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 2: launch_silu_ch<2>(gp, up_, l, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 4: launch_silu_ch<4>(gp, up_, l, k, tiled > 0, q, s, t, grid, st, out16); break;
+    case 8: launch_silu_ch<8>(gp, up_, l, k, tiled > 0, q, s, t, grid, st, out16); break;
+    default: launch_silu_ch<16>(gp, up_, l, k, tiled > 0, q, s, t, grid, st, out16); break;
   }
 }
 

@@ -21,8 +21,9 @@ void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream);
 
-// producers with the quantization fused in (tiled: codes in the tiled layout,
-// M <= kTiledMaxM); tx may be null (no code sums); K % 8 == 0, K <= kFusedMaxK;
+// producers with the quantization fused in (tiled 1: codes in the tiled layout,
+// M <= kTiledMaxM; 0: row-major; -1: no quantization, the fp16 value itself into
+// qx as [M, K] fp16); tx may be null (no code sums); K % 8 == 0, K <= kFusedMaxK;
 // gate / up rows have stride ld elements
 constexpr int64_t kFusedMaxK = 32768;
 void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_t M, int64_t K, int tiled,

@@ -49,6 +49,8 @@ _SIGNATURES = {
                              ctypes.c_int),
     "qoq_silu_mul_quantize": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp],
                               ctypes.c_int),
+    "qoq_rmsnorm": ([_c_vp, _c_vp, ctypes.c_float, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_silu_mul": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
     "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
                           _c_vp], ctypes.c_int),
@@ -274,6 +276,29 @@ def silu_mul_quantize(gate: torch.Tensor, up: torch.Tensor, tiled: bool = False,
                                        _dev(s_x, "s_x", torch.float16),
                                        None if t is None else _dev(t, "t", torch.int32), _stream(gate)))
     return qx, s_x, t
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out=None):
+    """The normalization alone: fp16 [M, K] (the value rmsnorm_quantize quantizes)."""
+    M, K = x.shape
+    y = torch.empty((M, K), dtype=torch.float16, device=x.device) if out is None else out
+    _check("qoq_rmsnorm", lib().qoq_rmsnorm(_dev(x, "x", torch.float16), _dev(gamma, "gamma", torch.float16),
+                                            float(eps), M, K, _dev(y, "y", torch.float16), _stream(x)))
+    return y
+
+
+def silu_mul(gate: torch.Tensor, up: torch.Tensor, out=None):
+    """SiLU(gate) * up alone: fp16 [M, K] (the value silu_mul_quantize quantizes)."""
+    M, K = gate.shape
+    if up.shape != gate.shape or gate.stride(1) != 1 or up.stride(1) != 1 or gate.stride(0) != up.stride(0):
+        raise ValueError("gate and up must be [M, K] views with unit column stride and the same row stride")
+    for t_, n_ in ((gate, "gate"), (up, "up")):
+        if not isinstance(t_, torch.Tensor) or t_.device.type != "cuda" or t_.dtype != torch.float16:
+            raise TypeError(f"{n_} must be an fp16 HIP device tensor")
+    h = torch.empty((M, K), dtype=torch.float16, device=gate.device) if out is None else out
+    _check("qoq_silu_mul", lib().qoq_silu_mul(ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(up.data_ptr()),
+                                              gate.stride(0), M, K, _dev(h, "h", torch.float16), _stream(gate)))
+    return h
 
 
 def quantize_activations_rowsum(x: torch.Tensor, out=None):

@@ -1,0 +1,142 @@
+"""Pins of the KV4 oracle (oracle/kv4_oracle.py): the per-head INT4 quantizer against
+exact rational arithmetic and its error bound, degenerate vectors, scale
+invariance; decode attention against closed forms and a pure-Python evaluation."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kv4_oracle as kv
+from tests.exact_float import FP16, FP32, round_float, rne_int
+
+
+def _quant_exact(x16):
+    """R17 by rationals: s = RN16(RN32(max - min) / 15 -> RN32), z = rne(RN32(-min / s)),
+    q = clamp(z + rne(RN32(x / s)), 0, 15)."""
+    xs = [Fraction(float(v)) for v in x16]
+    lo, hi = min(xs), max(xs)
+    rng32 = round_float(hi - lo, FP32)
+    if rng32 == 0:
+        s = round_float(abs(hi), FP16)
+    else:
+        s = round_float(round_float(rng32 / 15, FP32), FP16)
+    if s == 0:
+        return [0] * len(xs), s, 0
+    z = rne_int(round_float(-lo / s, FP32))
+    q = [min(max(z + rne_int(round_float(x / s, FP32)), 0), 15) for x in xs]
+    return q, s, z
+
+
+@pytest.mark.parametrize("scale", [1e-3, 0.7, 40.0])
+def test_kv_quantize_matches_exact_rationals(scale):
+    rng = np.random.default_rng(int(scale * 1000))
+    x = (rng.standard_normal((6, 128)) * scale).astype(np.float16)
+    x[1] = np.abs(x[1])                              # one-signed vectors: z <= 0 allowed
+    x[2] = -np.abs(x[2])
+    q, s, z = kv.kv_quantize(x)
+    for i in range(6):
+        wq, ws, wz = _quant_exact(x[i])
+        assert [int(v) for v in q[i]] == wq
+        assert Fraction(float(s[i])) == ws and float(z[i]) == wz
+
+
+def test_kv_quantize_error_bound():
+    """|x - (q - z) s| <= s / 2 (+ the fp16 rounding of s, relative 2^-11 of the
+    range) for every element; codes span [0, 15]."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((200, 128)) * rng.uniform(0.01, 10, (200, 1))).astype(np.float16)
+    q, s, z = kv.kv_quantize(x)
+    xd = (q.astype(np.float64) - z.astype(np.float64)[:, None]) * s.astype(np.float64)[:, None]
+    err = np.abs(xd - x.astype(np.float64))
+    span = (x.max(1) - x.min(1)).astype(np.float64)
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2 + span[:, None] * 2.0 ** -10)
+    assert q.max() == 15 and q.min() == 0
+
+
+def test_kv_quantize_degenerate_vectors():
+    x = np.zeros((3, 128), np.float16)
+    x[1] = 2.5
+    x[2] = -0.375
+    q, s, z = kv.kv_quantize(x)
+    back = kv.kv_dequantize(q, s, z)
+    assert np.array_equal(back.view(np.uint16) & 0x7fff, x.view(np.uint16) & 0x7fff)   # exact (sign of 0 aside)
+    assert float(s[0]) == 0 and float(z[0]) == 0 and not q[0].any()
+    assert float(s[1]) == 2.5 and float(z[1]) == -1 and np.all(q[1] == 0)
+    assert float(s[2]) == 0.375 and float(z[2]) == 1 and np.all(q[2] == 0)
+
+
+@pytest.mark.parametrize("j", [-5, 4])
+def test_kv_quantize_power_of_two_invariance(j):
+    rng = np.random.default_rng(j + 20)
+    x = rng.standard_normal((8, 128)).astype(np.float16)
+    q1, s1, z1 = kv.kv_quantize(x)
+    q2, s2, z2 = kv.kv_quantize((x.astype(np.float32) * 2.0 ** j).astype(np.float16))
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(s2.astype(np.float64), s1.astype(np.float64) * 2.0 ** j)
+
+
+def test_kv_dequantize_single_rounding():
+    q = np.array([[0, 15, 7, 3]], np.uint8)
+    s = np.array([0.1], np.float16)
+    z = np.array([-3.0], np.float16)
+    got = kv.kv_dequantize(q, s, z)[0].astype(np.float64)
+    for k in range(4):
+        exact = (Fraction(int(q[0, k])) + 3) * Fraction(float(s[0]))
+        assert got[k] == float(round_float(exact, FP16))
+
+
+def test_attention_uniform_keys_average_values():
+    """Equal keys: every score is the same, the output is the mean of the values."""
+    rng = np.random.default_rng(4)
+    S, HKV, D, H = 37, 2, 128, 8
+    K = np.repeat(rng.standard_normal((1, HKV, D)).astype(np.float16), S, 0)
+    V = rng.standard_normal((S, HKV, D)).astype(np.float16)
+    q = rng.standard_normal((H, D)).astype(np.float16)
+    o = kv.decode_attention(q, K, V, HKV).astype(np.float64)
+    for h in range(H):
+        assert np.allclose(o[h], V[:, h // 4, :].astype(np.float64).mean(0), atol=2e-3, rtol=2e-3)
+
+
+def test_attention_one_dominant_key():
+    """One key aligned with q and far larger than the rest: its value comes out."""
+    D = 128
+    q = np.zeros((1, D), np.float16)
+    q[0, 0] = 8.0
+    K = np.zeros((5, 1, D), np.float16)
+    K[3, 0, 0] = 200.0                                  # score 1600 / sqrt(128) ~ 141
+    V = np.arange(5 * D, dtype=np.float32).reshape(5, 1, D).astype(np.float16) / 64
+    o = kv.decode_attention(q, K, V, 1)
+    assert np.array_equal(o[0].view(np.uint16), V[3, 0].view(np.uint16))
+
+
+def test_attention_gqa_head_mapping():
+    """Head h reads KV head h // r: give each KV head distinct constant values."""
+    S, HKV, D, H = 9, 4, 128, 16
+    K = np.zeros((S, HKV, D), np.float16)
+    V = np.zeros((S, HKV, D), np.float16)
+    for g in range(HKV):
+        V[:, g, :] = g + 1
+    q = np.ones((H, D), np.float16)
+    o = kv.decode_attention(q, K, V, HKV)
+    for h in range(H):
+        assert np.all(o[h] == h // 4 + 1)
+
+
+def test_attention_brute_force_python():
+    """Pure-Python loops with math.exp on a small case."""
+    rng = np.random.default_rng(5)
+    S, HKV, D, H = 6, 2, 128, 4
+    q = rng.standard_normal((H, D)).astype(np.float16)
+    K = rng.standard_normal((S, HKV, D)).astype(np.float16)
+    V = rng.standard_normal((S, HKV, D)).astype(np.float16)
+    o = kv.decode_attention(q, K, V, HKV).astype(np.float64)
+    for h in range(H):
+        g = h // 2
+        sc = [sum(float(q[h, d]) * float(K[t, g, d]) for d in range(D)) / math.sqrt(D) for t in range(S)]
+        m = max(sc)
+        w = [math.exp(v - m) for v in sc]
+        tot = sum(w)
+        for d in range(0, D, 17):
+            ref = sum(w[t] * float(V[t, g, d]) for t in range(S)) / tot
+            assert abs(o[h, d] - ref) <= 2.0 ** -11 * abs(ref) + 1e-7

@@ -23,12 +23,13 @@ Readings (also listed with the design notes):
 
 R17 "Per-head dynamic" quantization is per token and per KV head: the D values of
     one head's key (or value) vector of one token share one (s, z).  UINT4 codes
-    (q_min = 0, q_max = 15); s = fp16(fp32(X_max - X_min) / 15) (fp32 IEEE, then
-    fp16, the stored value is the one used); z = rne(-X_min / s) (fp32), an integer
-    stored as fp16 (it may be negative: no range widening is needed because the
-    zero is a float); codes q = clamp(z + rne(x / s), 0, 15) (fp32 quotient,
-    reading R2 of the weights).  X_max == X_min: s = fp16(|X_max|) (0 for an
-    all-zero vector, then every code and z are 0), which reproduces the constant.
+    (q_min = 0, q_max = 15) over the vector's range widened to contain 0 (as the
+    weights' groups, reading R4: z then lies in [0, 15], so q - z is a small exact
+    integer in FP16 arithmetic; without it z = rne(-X_min / s) grows without bound
+    for one-signed vectors with a narrow range); s = fp16(fp32(hi - lo) / 15) (fp32
+    IEEE, then fp16; the stored value is the one used); z = rne(-lo / s) (fp32),
+    stored as fp16 (exact); codes q = clamp(z + rne(x / s), 0, 15) (fp32 quotient,
+    reading R2 of the weights).  An all-zero vector: s = 0, every code and z are 0.
 R18 The dequantized cache value is K_hat = fp16((q - z) * s): q - z is an exact
     small integer and the product is rounded once to fp16 (the pages' FP16 math).
 R19 Decode attention over the dequantized values is the plain definition, computed
@@ -51,12 +52,10 @@ def kv_quantize(x16: np.ndarray):
     """Per-vector asymmetric UINT4 (R17).  x16: fp16 [..., D] -> (codes uint8
     [..., D], s fp16 [...], z fp16 [...])."""
     x = np.asarray(x16, dtype=np.float16).astype(np.float32)
-    lo = x.min(axis=-1)
-    hi = x.max(axis=-1)
+    lo = np.minimum(x.min(axis=-1), np.float32(0))
+    hi = np.maximum(x.max(axis=-1), np.float32(0))
     rng = (hi - lo).astype(np.float32)
     s = (rng / np.float32(Q_MAX)).astype(np.float16)
-    flat = rng == 0
-    s = np.where(flat, np.abs(hi).astype(np.float16), s)
     s32 = s.astype(np.float32)
     safe = np.where(s32 == 0, np.float32(1), s32)
     z = np.where(s32 == 0, np.float32(0), np.rint(-lo / safe)).astype(np.float32)

@@ -12,15 +12,12 @@ from tests.exact_float import FP16, FP32, round_float, rne_int
 
 
 def _quant_exact(x16):
-    """R17 by rationals: s = RN16(RN32(max - min) / 15 -> RN32), z = rne(RN32(-min / s)),
-    q = clamp(z + rne(RN32(x / s)), 0, 15)."""
+    """R17 by rationals: lo = min(0, min x), hi = max(0, max x), s = RN16(RN32(RN32(hi
+    - lo) / 15)), z = rne(RN32(-lo / s)), q = clamp(z + rne(RN32(x / s)), 0, 15)."""
     xs = [Fraction(float(v)) for v in x16]
-    lo, hi = min(xs), max(xs)
+    lo, hi = min(min(xs), 0), max(max(xs), 0)
     rng32 = round_float(hi - lo, FP32)
-    if rng32 == 0:
-        s = round_float(abs(hi), FP16)
-    else:
-        s = round_float(round_float(rng32 / 15, FP32), FP16)
+    s = round_float(round_float(rng32 / 15, FP32), FP16)
     if s == 0:
         return [0] * len(xs), s, 0
     z = rne_int(round_float(-lo / s, FP32))
@@ -32,7 +29,7 @@ def _quant_exact(x16):
 def test_kv_quantize_matches_exact_rationals(scale):
     rng = np.random.default_rng(int(scale * 1000))
     x = (rng.standard_normal((6, 128)) * scale).astype(np.float16)
-    x[1] = np.abs(x[1])                              # one-signed vectors: z <= 0 allowed
+    x[1] = np.abs(x[1])                              # one-signed vectors: z = 0 / 15
     x[2] = -np.abs(x[2])
     q, s, z = kv.kv_quantize(x)
     for i in range(6):
@@ -43,27 +40,29 @@ def test_kv_quantize_matches_exact_rationals(scale):
 
 def test_kv_quantize_error_bound():
     """|x - (q - z) s| <= s / 2 (+ the fp16 rounding of s, relative 2^-11 of the
-    range) for every element; codes span [0, 15]."""
+    range) for every element; zeros in [0, 15]; codes span [0, 15]."""
     rng = np.random.default_rng(3)
     x = (rng.standard_normal((200, 128)) * rng.uniform(0.01, 10, (200, 1))).astype(np.float16)
+    x[::7] = np.abs(x[::7]) + np.float16(3)              # one-signed, offset away from 0
     q, s, z = kv.kv_quantize(x)
     xd = (q.astype(np.float64) - z.astype(np.float64)[:, None]) * s.astype(np.float64)[:, None]
     err = np.abs(xd - x.astype(np.float64))
-    span = (x.max(1) - x.min(1)).astype(np.float64)
+    span = (np.maximum(x.max(1), 0) - np.minimum(x.min(1), 0)).astype(np.float64)
     assert np.all(err <= s.astype(np.float64)[:, None] / 2 + span[:, None] * 2.0 ** -10)
     assert q.max() == 15 and q.min() == 0
+    assert np.all((z >= 0) & (z <= 15)) and np.array_equal(z, np.rint(z))
 
 
 def test_kv_quantize_degenerate_vectors():
     x = np.zeros((3, 128), np.float16)
-    x[1] = 2.5
-    x[2] = -0.375
+    x[1] = 2.5                                            # constant: lo = 0, s = 1/6, z = 0, q = 15
+    x[2, 7] = -0.375                                      # a single non-zero
     q, s, z = kv.kv_quantize(x)
-    back = kv.kv_dequantize(q, s, z)
-    assert np.array_equal(back.view(np.uint16) & 0x7fff, x.view(np.uint16) & 0x7fff)   # exact (sign of 0 aside)
-    assert float(s[0]) == 0 and float(z[0]) == 0 and not q[0].any()
-    assert float(s[1]) == 2.5 and float(z[1]) == -1 and np.all(q[1] == 0)
-    assert float(s[2]) == 0.375 and float(z[2]) == 1 and np.all(q[2] == 0)
+    back = kv.kv_dequantize(q, s, z).astype(np.float64)
+    assert float(s[0]) == 0 and float(z[0]) == 0 and not q[0].any() and not back[0].any()
+    assert float(z[1]) == 0 and np.all(q[1] == 15) and np.allclose(back[1], 2.5, rtol=2.0 ** -10)
+    assert float(z[2]) == 15 and q[2, 7] == 0 and np.all(np.delete(q[2], 7) == 15)
+    assert abs(back[2, 7] + 0.375) <= 2.0 ** -10 and not np.delete(back[2], 7).any()
 
 
 @pytest.mark.parametrize("j", [-5, 4])
@@ -79,10 +78,10 @@ def test_kv_quantize_power_of_two_invariance(j):
 def test_kv_dequantize_single_rounding():
     q = np.array([[0, 15, 7, 3]], np.uint8)
     s = np.array([0.1], np.float16)
-    z = np.array([-3.0], np.float16)
+    z = np.array([6.0], np.float16)
     got = kv.kv_dequantize(q, s, z)[0].astype(np.float64)
     for k in range(4):
-        exact = (Fraction(int(q[0, k])) + 3) * Fraction(float(s[0]))
+        exact = (Fraction(int(q[0, k])) - 6) * Fraction(float(s[0]))
         assert got[k] == float(round_float(exact, FP16))
 
 

@@ -168,6 +168,61 @@ int qoq_rmsnorm(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M
 int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K,
                  void *h_fp16, void *stream);
 
+/* ------------------------------------------------------------------------------
+ * KV4: paged, per-head dynamic INT4 KV cache and decode attention ("QServe: W4A8KV4
+ * ..." summary: attention o_h = softmax(q_h K_{h_KV}^T / sqrt(D)) V_{h_KV}, h_KV =
+ * h / r; asymmetric integer quantization; a paged KV cache keeping each head's FP16
+ * scale and zero inside the page right after its quantized features; KV4 attention
+ * in FP16.  "QServe：把 W4A8KV4 ..." review §3.2 and §4 steps 4-5.)
+ * Head dim 128, 64 tokens per page.  The pool is caller-owned device memory of
+ * num_pages x qoq_kv4_page_bytes bytes (16-byte aligned); a page holds, for each KV
+ * head, the K and V codes of its 64 token slots (in the operand order of the
+ * attention kernel's matrix instructions) followed by the fp16 K scales, K zeros, V
+ * scales and V zeros of the slots.  page_table: int32 [B, max_pages], the pool page
+ * of each 64-token span of each sequence (pages of different sequences distinct).
+ * num_pages: pages in the pool.  Positions, page ids and seq_lens are device data the
+ * host cannot check; the kernels guard them: the write skips a token whose position
+ * falls outside the table or whose page id lies outside [0, num_pages), the attention
+ * clamps page ids to that range and seq_lens to [1, max_len] (a bad table gives wrong
+ * values, never an access outside the buffers).
+ * ------------------------------------------------------------------------------ */
+
+/* Bytes of one page (all h_kv heads).  Errors: INVALID, UNSUPPORTED (head_dim != 128). */
+int qoq_kv4_page_bytes(int64_t h_kv, int64_t head_dim, size_t *bytes);
+
+/* KV write: quantize n_new new tokens per sequence into the cache.  k_new, v_new: fp16
+ * [B, n_new, h_kv, 128] (4-byte aligned); token i of sequence b goes to position
+ * positions[b] + i.  Per token and KV head, over the 128 values x with the range
+ * widened to contain 0 (lo = min(0, min x), hi = max(0, max x)): s = fp16(fp32(hi -
+ * lo) / 15), z = rne(-lo / s) in [0, 15], codes clamp(z + rne(x / s), 0, 15) (fp32
+ * IEEE quotients; s = 0 for an all-zero vector, codes and z 0); s and z stored as
+ * fp16.  One workgroup per (sequence, KV head) writes its tokens in order (a V byte
+ * holds two tokens); calls for the same pages must not overlap.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, HIP. */
+int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,
+                  int64_t head_dim, const int32_t *positions, const int32_t *page_table,
+                  int64_t max_pages, void *kv_pool, int64_t num_pages, void *stream);
+
+/* Workspace for qoq_kv4_decode_attention (0 when one workgroup per (sequence, KV
+ * head) covers the sequence): split partials, no initialization needed.
+ * Errors: INVALID, UNSUPPORTED. */
+int qoq_kv4_attention_workspace_bytes(int64_t B, int64_t h, int64_t h_kv, int64_t head_dim,
+                                      int64_t max_len, size_t *bytes);
+
+/* Decode attention of one new token per sequence over its cached tokens:
+ *   o[b, head] = softmax(q[b, head] . K_hat / sqrt(128)) V_hat over the seq_lens[b]
+ *   cached tokens of KV head head / (h / h_kv), K_hat = fp16((code - z) * s).
+ * q: fp16 [B, h, 128]; out: fp16 [B, h, 128] (16-byte aligned); seq_lens: int32 [B],
+ * 1 <= seq_lens[b] <= max_len <= 64 * max_pages; h % h_kv == 0, h / h_kv <= 16.
+ * Products on the matrix cores with FP16 inputs and FP32 accumulation; the
+ * softmax in FP32 with the probabilities rounded to FP16 for the second product.
+ * workspace: qoq_kv4_attention_workspace_bytes (WORKSPACE when smaller).
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
+int qoq_kv4_decode_attention(const void *q, const void *kv_pool, int64_t num_pages,
+                             const int32_t *page_table, int64_t max_pages, const int32_t *seq_lens,
+                             int64_t B, int64_t h, int64_t h_kv, int64_t head_dim, int64_t max_len,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace in bytes the GEMM entry points need for this problem (0 for M == 0).
  * It is non-zero when the plan splits the K groups of each output tile over several
  * workgroups ("QServe：把 W4A8KV4 ..." review §3.2: split-k when the batch is small;

@@ -312,3 +312,31 @@ def test_fused_producer_validation(L):
     assert call2(lay=1, M=65) == UNSUPPORTED
     assert call2(gt=NUL) == INVALID and call2(up=NUL) == INVALID
     assert call2(gt=ODD) == ALIGNMENT and call2(up=ODD) == ALIGNMENT and call2(q=ODD) == ALIGNMENT
+
+
+def test_kv4_validation(L):
+    """KV4 cache entry points: sizes, splits and argument checks before any launch."""
+    assert qoq.kv4_page_bytes(8) == 8 * 8704
+    with pytest.raises(qoq.QoQError) as e:
+        b = ctypes.c_size_t(0)
+        qoq._check("qoq_kv4_page_bytes", L.qoq_kv4_page_bytes(8, 64, ctypes.byref(b)))
+    assert e.value.status == UNSUPPORTED
+    assert qoq.kv4_attention_workspace_bytes(64, 32, 8, 1024) == 0          # 512 workgroups already
+    w = qoq.kv4_attention_workspace_bytes(1, 32, 8, 4096)                   # split over the sequence
+    assert w > 0 and w % (32 * 130 * 4) == 0 and w // (32 * 130 * 4) <= 32
+    wr = L.qoq_kv4_write
+    assert wr(FAKE, FAKE, 2, 1, 8, 64, FAKE, FAKE, 4, FAKE, 16, NUL) == UNSUPPORTED       # head dim
+    assert wr(FAKE, FAKE, 0, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == OK
+    assert wr(NUL, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == INVALID
+    assert wr(FAKE, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, ODD, 16, NUL) == ALIGNMENT
+    at = L.qoq_kv4_decode_attention
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(q=FAKE, pool=FAKE, np_=16, pt=FAKE, mp=4, sl=FAKE, B=2, h=32, hkv=8,
+                                                           hd=128, ml=256, out=FAKE, ws=NUL, wb=0, st=NUL).items()]
+    assert at(*args(h=30)) == INVALID                                       # h % h_kv
+    assert at(*args(h=256, hkv=8)) == UNSUPPORTED                           # group of 32 heads
+    assert at(*args(ml=257)) == INVALID                                     # beyond the page table
+    assert at(*args(hd=64)) == UNSUPPORTED
+    assert at(*args(B=0)) == OK
+    assert at(*args(out=ODD)) == ALIGNMENT
+    assert at(*args(B=1, ml=4096, mp=64)) == WORKSPACE                      # needs split partials
+    assert at(*args(np_=0)) == INVALID and wr(FAKE, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, FAKE, 0, NUL) == INVALID

@@ -1,0 +1,161 @@
+"""GPU parity of the KV4 path against the CPU oracle (oracle/kv4_oracle.py).
+
+KV write: codes, fp16 scales and zeros read back from the pages (their layout undone
+on the host from its documented definition, include/qoq.h and csrc/qoq_kv4.hip) are
+compared bit for bit with the oracle's quantization, for tokens written one at a
+time and many at once, on shuffled page tables.
+
+Decode attention: the output against the oracle's fp64 attention over the same
+dequantized cache, within |err| <= 2^-8 max|V_hat| + 2^-9 |ref|.  The kernel's
+arithmetic: FP16 products with FP32 accumulation (exact dequantized inputs), FP32
+softmax, probabilities rounded to FP16 for the second product (relative 2^-11 per
+weight, so at most 2^-11 max|V_hat| on the output), FP16 output (2^-11 |o|); the
+score accumulation adds a few 2^-24-relative terms.  The bound leaves a margin of
+about 2 over these.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv4_oracle as kv
+from w4a8_mixed_precision_amd import qoq
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+P = 64
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _layout_index(h_kv):
+    """Byte offsets (within a (page, head) section) and nibble of K and V codes for
+    every (slot t, dim d), from the documented page layout."""
+    t = np.arange(P)[:, None]
+    d = np.arange(D)[None, :]
+    blk, tt = t // 16, t % 16
+    kb = blk * 1024 + (16 * ((d % 16) // 4) + tt) * 16 + 2 * (d // 16) + (d % 4) // 2
+    kn = d % 2
+    qt, ti = tt // 4, tt % 4
+    vb = 4096 + blk * 1024 + (16 * qt + d % 16) * 16 + 2 * (d // 16) + ti // 2
+    vn = np.broadcast_to(ti % 2, vb.shape)
+    return kb, np.broadcast_to(kn, kb.shape), vb, vn
+
+
+def read_pages(pool, page_ids, h_kv, ntok):
+    """Host decode of the first ntok slots of the given pages (in sequence order):
+    (k codes, k s, k z, v codes, v s, v z) as [ntok, h_kv, D] / [ntok, h_kv]."""
+    pb = qoq.kv4_page_bytes(h_kv) // h_kv
+    kb, kn, vb, vn = _layout_index(h_kv)
+    out = [np.zeros((ntok, h_kv, D), np.uint8), np.zeros((ntok, h_kv), np.float16),
+           np.zeros((ntok, h_kv), np.float16), np.zeros((ntok, h_kv, D), np.uint8),
+           np.zeros((ntok, h_kv), np.float16), np.zeros((ntok, h_kv), np.float16)]
+    for i in range(ntok):
+        page, slot = page_ids[i // P], i % P
+        for g in range(h_kv):
+            sec = pool[(page * h_kv + g) * pb:(page * h_kv + g + 1) * pb]
+            out[0][i, g] = (sec[kb[slot]] >> (4 * kn[slot])) & 0xF
+            out[3][i, g] = (sec[vb[slot]] >> (4 * vn[slot])) & 0xF
+            st = sec[8192:8704].view(np.float16)
+            out[1][i, g], out[2][i, g], out[4][i, g], out[5][i, g] = st[slot], st[64 + slot], st[128 + slot], \
+                st[192 + slot]
+    return out
+
+
+def _pages(rng, B, max_pages, spare=3):
+    ids = rng.permutation(B * max_pages + spare)[: B * max_pages].astype(np.int32)
+    return ids.reshape(B, max_pages)
+
+
+def _kv(rng, n, h_kv, scale=1.0):
+    x = (rng.standard_normal((n, h_kv, D)) * scale).astype(np.float32)
+    x[:, :, rng.choice(D, 3, replace=False)] *= 8           # a few outlier channels per head
+    return x.astype(np.float16)
+
+
+def test_kv4_write_bit_exact(gpu):
+    rng = np.random.default_rng(1)
+    h_kv, B, max_pages = 4, 3, 3
+    pt = _pages(rng, B, max_pages)
+    npages = B * max_pages + 3
+    pool = torch.zeros(npages * qoq.kv4_page_bytes(h_kv), dtype=torch.uint8, device=gpu)
+    n_tot = 150
+    k = _kv(rng, B * n_tot, h_kv).reshape(B, n_tot, h_kv, D)
+    v = _kv(rng, B * n_tot, h_kv, 0.3).reshape(B, n_tot, h_kv, D)
+    k[0, 5] = 0                                             # an all-zero vector
+    v[1, 7] = np.abs(v[1, 7]) + np.float16(2)               # one-signed, away from 0
+    # tokens 0..36 at once, then one at a time up to 60, then 61..149 at once
+    spans = [(0, 37)] + [(i, i + 1) for i in range(37, 61)] + [(61, n_tot)]
+    dpt = to_dev(pt, gpu)
+    for a, e in spans:
+        say(f"kv4_write tokens {a}..{e - 1}")
+        qoq.kv4_write(to_dev(k[:, a:e], gpu), to_dev(v[:, a:e], gpu), to_dev(np.full(B, a, np.int32), gpu), dpt, pool)
+    poolh = host(pool)
+    for b in range(B):
+        kc, ks, kz, vc, vs, vz = read_pages(poolh, pt[b], h_kv, n_tot)
+        wq, ws, wz = kv.kv_quantize(k[b])
+        assert np.array_equal(kc, wq) and np.array_equal(ks.view(np.uint16), ws.view(np.uint16))
+        assert np.array_equal(kz.view(np.uint16), wz.view(np.uint16))
+        wq, ws, wz = kv.kv_quantize(v[b])
+        assert np.array_equal(vc, wq) and np.array_equal(vs.view(np.uint16), ws.view(np.uint16))
+        assert np.array_equal(vz.view(np.uint16), wz.view(np.uint16))
+
+
+def _run_attention(gpu, rng, lens, h, h_kv, kscale=1.0, vscale=1.0):
+    B = len(lens)
+    max_len = max(lens)
+    max_pages = (max_len + P - 1) // P
+    pt = _pages(rng, B, max_pages)
+    pool = torch.empty((pt.size + 3) * qoq.kv4_page_bytes(h_kv), dtype=torch.uint8, device=gpu)
+    pool.fill_(0xA5)                                        # unwritten slots hold garbage
+    dpt = to_dev(pt, gpu)
+    ks, vs = [], []
+    for b, n in enumerate(lens):
+        k = _kv(rng, n, h_kv, kscale)
+        v = _kv(rng, n, h_kv, vscale)
+        ks.append(k)
+        vs.append(v)
+        qoq.kv4_write(to_dev(k[None], gpu), to_dev(v[None], gpu), to_dev(np.zeros(1, np.int32), gpu), dpt[b:b + 1],
+                      pool)
+    q = (rng.standard_normal((B, h, D)) * 1.0).astype(np.float16)
+    o = host(qoq.kv4_decode_attention(to_dev(q, gpu), pool, dpt, to_dev(np.array(lens, np.int32), gpu), h_kv,
+                                      max_len))
+    for b in range(B):
+        ref = kv.attention_reference(q[b], ks[b], vs[b], h_kv).astype(np.float64)
+        vq, vs_, vz = kv.kv_quantize(vs[b])
+        vmax = np.abs(kv.kv_dequantize(vq, vs_, vz).astype(np.float64)).max()
+        err = np.abs(o[b].astype(np.float64) - ref)
+        bound = 2.0 ** -8 * vmax + 2.0 ** -9 * np.abs(ref)
+        assert np.all(err <= bound), (b, lens[b], float(err.max()), float(vmax))
+
+
+@pytest.mark.parametrize("lens,h,h_kv", [([1, 17, 64, 300], 32, 8), ([1000, 65], 64, 8), ([16, 15, 33], 8, 8),
+                                         ([4096], 32, 8), ([129] * 16, 32, 8)])
+def test_kv4_decode_attention(gpu, lens, h, h_kv):
+    say(f"kv4 attention lens={lens[:4]}{'...' if len(lens) > 4 else ''} h={h} h_kv={h_kv} "
+        f"splits={qoq.kv4_attention_workspace_bytes(len(lens), h, h_kv, max(lens)) > 0}")
+    _run_attention(gpu, np.random.default_rng(sum(lens) + h), lens, h, h_kv)
+
+
+def test_kv4_decode_attention_peaked_scores(gpu):
+    """Large keys: softmax dominated by a few tokens (scores of order 100)."""
+    say("kv4 attention peaked")
+    _run_attention(gpu, np.random.default_rng(9), [200, 70], 32, 8, kscale=6.0, vscale=3.0)
+
+
+def test_kv4_decode_attention_batch64(gpu):
+    """The decode shape of the throughput measurement, sampled sequences checked."""
+    rng = np.random.default_rng(10)
+    say("kv4 attention batch 64 x 1024")
+    _run_attention(gpu, rng, [1024] * 64, 32, 8)

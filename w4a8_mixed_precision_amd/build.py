@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libqoq.so")
 
-SOURCES = ["qoq_api.cpp", "qoq_quant.hip", "qoq_gemm.hip", "qoq_fused.hip", "qoq_diag.hip"]
+SOURCES = ["qoq_api.cpp", "qoq_quant.hip", "qoq_gemm.hip", "qoq_fused.hip", "qoq_kv4.hip", "qoq_diag.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -175,6 +175,70 @@ int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t
   return launch_status();
 }
 
+int qoq_kv4_page_bytes(int64_t h_kv, int64_t head_dim, size_t *bytes) {
+  if (h_kv <= 0 || !bytes) return QOQ_ERR_INVALID;
+  if (head_dim != 128 || h_kv > 1024) return QOQ_ERR_UNSUPPORTED;
+  *bytes = static_cast<size_t>(h_kv) * qoq::kKv4PageBytes;
+  return QOQ_OK;
+}
+
+int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv, int64_t head_dim,
+                  const int32_t *positions, const int32_t *page_table, int64_t max_pages, void *kv_pool,
+                  int64_t num_pages, void *stream) {
+  if (B < 0 || n_new < 0 || h_kv <= 0 || max_pages <= 0 || num_pages <= 0) return QOQ_ERR_INVALID;
+  if (num_pages > INT32_MAX || max_pages > (int64_t{1} << 24)) return QOQ_ERR_UNSUPPORTED;
+  if (head_dim != 128 || h_kv > 1024 || B > 65535 || n_new > (int64_t{1} << 20)) return QOQ_ERR_UNSUPPORTED;
+  if (B == 0 || n_new == 0) return QOQ_OK;
+  if (!k_new || !v_new || !positions || !page_table || !kv_pool) return QOQ_ERR_INVALID;
+  if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||
+      !aligned(kv_pool, 16))
+    return QOQ_ERR_ALIGNMENT;
+  qoq::launch_kv4_write(k_new, v_new, B, n_new, h_kv, positions, page_table, max_pages, num_pages, kv_pool,
+                        as_stream(stream));
+  return launch_status();
+}
+
+static int kv4_attn_checks(int64_t B, int64_t h, int64_t h_kv, int64_t head_dim, int64_t max_len, int64_t max_pages) {
+  if (B < 0 || h <= 0 || h_kv <= 0 || max_len <= 0 || max_pages <= 0 || h % h_kv != 0) return QOQ_ERR_INVALID;
+  if (head_dim != 128 || h / h_kv > 16 || B > 65535 || h_kv > 1024) return QOQ_ERR_UNSUPPORTED;
+  if (max_pages > (int64_t{1} << 24)) return QOQ_ERR_UNSUPPORTED;
+  if (max_len > max_pages * qoq::kKv4PageTokens) return QOQ_ERR_INVALID;
+  return QOQ_OK;
+}
+
+int qoq_kv4_attention_workspace_bytes(int64_t B, int64_t h, int64_t h_kv, int64_t head_dim, int64_t max_len,
+                                      size_t *bytes) {
+  const int st = kv4_attn_checks(B, h, h_kv, head_dim, max_len, (max_len + qoq::kKv4PageTokens - 1) /
+                                                                   qoq::kKv4PageTokens);
+  if (st != QOQ_OK) return st;
+  if (!bytes) return QOQ_ERR_INVALID;
+  *bytes = B == 0 ? 0 : qoq::kv4_workspace_need(B, h, h_kv, max_len);
+  return QOQ_OK;
+}
+
+int qoq_kv4_decode_attention(const void *q, const void *kv_pool, int64_t num_pages, const int32_t *page_table,
+                             int64_t max_pages, const int32_t *seq_lens, int64_t B, int64_t h, int64_t h_kv,
+                             int64_t head_dim, int64_t max_len, void *out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  const int st = kv4_attn_checks(B, h, h_kv, head_dim, max_len, max_pages);
+  if (st != QOQ_OK) return st;
+  if (num_pages <= 0) return QOQ_ERR_INVALID;
+  if (num_pages > INT32_MAX) return QOQ_ERR_UNSUPPORTED;
+  if (B == 0) return QOQ_OK;
+  if (!q || !kv_pool || !page_table || !seq_lens || !out) return QOQ_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(out, 16))
+    return QOQ_ERR_ALIGNMENT;
+  const size_t need = qoq::kv4_workspace_need(B, h, h_kv, max_len);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return QOQ_ERR_ALIGNMENT;
+  }
+  qoq::launch_kv4_attention(q, kv_pool, num_pages, page_table, max_pages, seq_lens, B, h, h_kv, max_len, out,
+                            workspace, as_stream(stream));
+  return launch_status();
+}
+
 static int gemm_tiled_common(const void *qx_tiled, const void *s_x_fp16, const void *packed_w,
                              const void *group_meta, const void *s_w_fp16, void *out, int out_kind, int64_t M,
                              int64_t N, int64_t K, void *stream) {

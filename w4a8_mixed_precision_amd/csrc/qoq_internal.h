@@ -31,6 +31,20 @@ void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_
 void launch_silu_mul_quantize(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, int tiled,
                               void *qx, void *sx, void *tx, hipStream_t stream);
 
+// KV4 cache (head dim 128, 64-token pages, the layout described in qoq_kv4.hip)
+constexpr int kKv4PageTokens = 64;
+constexpr int kKv4PageBytes = 8704;              // per (page, KV head): K, V codes + fp16 stats
+constexpr int64_t kKv4TargetWorkgroups = 512;
+constexpr int64_t kKv4MaxSplits = 32;
+int kv4_splits(int64_t B, int64_t h_kv, int64_t max_len);
+size_t kv4_workspace_need(int64_t B, int64_t h, int64_t h_kv, int64_t max_len);
+void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,
+                      const int *positions, const int *page_table, int64_t max_pages, int64_t num_pages, void *pool,
+                      hipStream_t stream);
+void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, const int *page_table,
+                          int64_t max_pages, const int *seq_lens, int64_t B, int64_t h, int64_t h_kv,
+                          int64_t max_len, void *out, void *ws, hipStream_t stream);
+
 // GEMM: out_kind 0 = fp16 epilogue, 1 = INT32 accumulators; ws holds at least
 // gemm_workspace_need(M, N, K) bytes (may be null when that is 0)
 void launch_w4a8_gemm(const void *qx, const void *sx, const void *packed, const void *meta,

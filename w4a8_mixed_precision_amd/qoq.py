@@ -51,6 +51,13 @@ _SIGNATURES = {
                               ctypes.c_int),
     "qoq_rmsnorm": ([_c_vp, _c_vp, ctypes.c_float, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
     "qoq_silu_mul": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_kv4_page_bytes": ([_c_i64, _c_i64, ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "qoq_kv4_write": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+                      ctypes.c_int),
+    "qoq_kv4_attention_workspace_bytes": ([_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)],
+                                          ctypes.c_int),
+    "qoq_kv4_decode_attention": ([_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                  _c_i64, _c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
     "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
                           _c_vp], ctypes.c_int),
@@ -299,6 +306,70 @@ def silu_mul(gate: torch.Tensor, up: torch.Tensor, out=None):
     _check("qoq_silu_mul", lib().qoq_silu_mul(ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(up.data_ptr()),
                                               gate.stride(0), M, K, _dev(h, "h", torch.float16), _stream(gate)))
     return h
+
+
+# ---------------------------------------------------------------------------
+# KV4 cache
+# ---------------------------------------------------------------------------
+KV4_PAGE_TOKENS = 64
+KV4_HEAD_DIM = 128
+
+
+def kv4_page_bytes(h_kv: int) -> int:
+    b = _c_sz(0)
+    _check("qoq_kv4_page_bytes", lib().qoq_kv4_page_bytes(h_kv, KV4_HEAD_DIM, ctypes.byref(b)))
+    return int(b.value)
+
+
+def _kv4_pool_pages(pool: torch.Tensor, h_kv: int) -> int:
+    pb = kv4_page_bytes(h_kv)
+    if pool.numel() % pb or pool.numel() == 0:
+        raise ValueError(f"kv4 pool: {pool.numel()} bytes is not a whole number of {pb}-byte pages")
+    return pool.numel() // pb
+
+
+def kv4_write(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor, page_table: torch.Tensor,
+              pool: torch.Tensor):
+    """k_new, v_new fp16 [B, n_new, h_kv, 128]; positions int32 [B]; page_table int32
+    [B, max_pages]; pool uint8 [num_pages * kv4_page_bytes(h_kv)]."""
+    B, n_new, h_kv, D = k_new.shape
+    if v_new.shape != k_new.shape or positions.numel() != B or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("kv4_write: shapes of k_new, v_new, positions, page_table disagree")
+    num_pages = _kv4_pool_pages(pool, h_kv)
+    _check("qoq_kv4_write",
+           lib().qoq_kv4_write(_dev(k_new, "k_new", torch.float16), _dev(v_new, "v_new", torch.float16), B, n_new,
+                               h_kv, D, _dev(positions, "positions", torch.int32),
+                               _dev(page_table, "page_table", torch.int32), page_table.shape[1],
+                               _dev(pool, "pool", torch.uint8), num_pages, _stream(k_new)))
+
+
+def kv4_attention_workspace_bytes(B: int, h: int, h_kv: int, max_len: int) -> int:
+    b = _c_sz(0)
+    _check("qoq_kv4_attention_workspace_bytes",
+           lib().qoq_kv4_attention_workspace_bytes(B, h, h_kv, KV4_HEAD_DIM, max_len, ctypes.byref(b)))
+    return int(b.value)
+
+
+def kv4_decode_attention(q: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                         h_kv: int, max_len: int, out=None, workspace=None):
+    """q fp16 [B, h, 128] -> o fp16 [B, h, 128] over the cached tokens."""
+    B, h, D = q.shape
+    if seq_lens.numel() != B or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("kv4_decode_attention: shapes of q, seq_lens, page_table disagree")
+    num_pages = _kv4_pool_pages(pool, h_kv)
+    if out is None:
+        out = torch.empty_like(q)
+    need = kv4_attention_workspace_bytes(B, h, h_kv, max_len)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace") if need else None
+    _check("qoq_kv4_decode_attention",
+           lib().qoq_kv4_decode_attention(_dev(q, "q", torch.float16), _dev(pool, "pool", torch.uint8), num_pages,
+                                          _dev(page_table, "page_table", torch.int32), page_table.shape[1],
+                                          _dev(seq_lens, "seq_lens", torch.int32), B, h, h_kv, D, max_len,
+                                          _dev(out, "out", torch.float16), ws, workspace.numel() if need else 0,
+                                          _stream(q)))
+    return out
 
 
 def quantize_activations_rowsum(x: torch.Tensor, out=None):

@@ -14,6 +14,8 @@ CPU oracle timed on the host cores.
 --sweep runs every layer shape / batch size of the workload registry and writes a
 table to gpurun_out/sweep.json (not the headline line); with --format channel it
 measures the per-channel weight format instead (gpurun_out/sweep_channel.json).
+--kv4 measures the INT4 KV cache path instead (decode attention and the KV write on
+the decode shapes of the registry, gpurun_out/kv4.json).
 """
 
 from __future__ import annotations
@@ -48,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-launches", type=int, default=200)
+    ap.add_argument("--kv4", action="store_true", help="measure the KV4 decode attention and KV write")
     ap.add_argument("--format", choices=("group", "channel"), default="group",
                     help="weight format: per-group g128 (default) or the per-channel variant")
     return ap.parse_args()
@@ -312,6 +315,87 @@ def run_case_metrics(c, q, torch, launches):
     }
 
 
+class KvCase:
+    """Resident KV4 cache for one decode shape, copied into disjoint page ranges until
+    the rotation covers ROTATE_BYTES (so the MALL and L2 do not serve the cache); each
+    call attends over the next copy."""
+
+    def __init__(self, S, dev, q):
+        import numpy as np
+        import torch
+        from w4a8_mixed_precision_amd import workloads as wl
+        self.S = S
+        P = wl.KV_PAGE_TOKENS
+        mp = -(-S.seq_len // P)
+        pb = q.kv4_page_bytes(S.h_kv)
+        set_pages = S.B * mp
+        set_bytes = set_pages * pb
+        self.nsets = max(2, -(-ROTATE_BYTES // set_bytes))
+        self.pool = torch.empty(self.nsets * set_bytes, dtype=torch.uint8, device=dev)
+        perm = np.random.default_rng(S.B * 7 + S.seq_len).permutation(set_pages).astype(np.int32).reshape(S.B, mp)
+        self.tables = [torch.from_numpy(perm + i * set_pages).to(dev) for i in range(self.nsets)]
+        base = self.pool[:set_bytes]
+        zero = torch.zeros(S.B, dtype=torch.int32, device=dev)
+        chunk = 4096                                   # tokens per write call while filling
+        for a in range(0, S.seq_len, chunk):
+            n = min(chunk, S.seq_len - a)
+            k = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 0)[a:a + n] for b in range(S.B)])).to(dev)
+            v = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 1)[a:a + n] for b in range(S.B)])).to(dev)
+            q.kv4_write(k, v, zero + a, self.tables[0], base)
+        for i in range(1, self.nsets):
+            self.pool[i * set_bytes:(i + 1) * set_bytes].copy_(base)
+        self.q = torch.from_numpy(wl.kv_queries_fp16(S)).to(dev)
+        self.lens = torch.full((S.B,), S.seq_len, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.q)
+        need = q.kv4_attention_workspace_bytes(S.B, S.h, S.h_kv, S.seq_len)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        # the decode-step write: one new token per sequence at position seq_len - 1
+        self.k1 = torch.from_numpy(np.stack([wl.kv_fp16(S, b, 1, 0)[0] for b in range(S.B)])[:, None]).to(dev)
+        self.v1 = torch.from_numpy(np.stack([wl.kv_fp16(S, b, 1, 1)[0] for b in range(S.B)])[:, None]).to(dev)
+        self.pos = torch.full((S.B,), S.seq_len - 1, dtype=torch.int32, device=dev)
+        self.bytes = wl.kv_attention_bytes(S.B, S.seq_len, S.h, S.h_kv)
+        self.flops = wl.kv_attention_flops(S.B, S.seq_len, S.h)
+        self.splits = need // (S.B * S.h * (wl.KV_HEAD_DIM + 2) * 4) if need else 1
+        self.i = 0
+
+    def attend(self, q):
+        t = self.tables[self.i % self.nsets]
+        self.i += 1
+        q.kv4_decode_attention(self.q, self.pool, t, self.lens, self.S.h_kv, self.S.seq_len, out=self.out,
+                               workspace=self.ws)
+
+    def write(self, q):
+        t = self.tables[self.i % self.nsets]
+        self.i += 1
+        q.kv4_write(self.k1, self.v1, self.pos, t, self.pool)
+
+
+def kv4_bench(q, torch, dev, launches):
+    from w4a8_mixed_precision_amd import workloads as wl
+    rows = []
+    for S in wl.KV_SHAPES:
+        c = KvCase(S, dev, q)
+        for _ in range(3):
+            c.attend(q)
+        torch.cuda.synchronize()
+        ta = time_launches(lambda: c.attend(q), launches, torch)
+        tw = time_launches(lambda: c.write(q), launches, torch)
+        r = {"shape": S.name, "B": S.B, "seq_len": S.seq_len, "h": S.h, "h_kv": S.h_kv, "splits": c.splits,
+             "attention_us": ta * 1e6, "bytes_per_launch": c.bytes, "GBps": c.bytes / ta / 1e9,
+             "hbm_frac": c.bytes / ta / 1e9 / HBM_PEAK_GBPS, "TFLOPs": c.flops / ta / 1e12,
+             "tokens_per_s": S.B * S.seq_len / ta,
+             "write_us": tw * 1e6, "write_bytes": S.B * S.h_kv * (4 * wl.KV_HEAD_DIM + wl.KV_TOKEN_HEAD_BYTES),
+             "rotation_sets": c.nsets}
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+        del c
+        torch.cuda.empty_cache()
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", "kv4.json"), "w") as f:
+        json.dump(rows, f, indent=1)
+    return rows
+
+
 def copy_ceiling(q, torch, dev, nbytes=1 << 30, reps=10):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -360,6 +444,9 @@ def main():
     dev = torch.device("cuda:0")
     qoq.lib()
 
+    if args.kv4:
+        kv4_bench(qoq, torch, dev, args.kernel_launches)
+        return
     if args.sweep:
         sweep(qoq, torch, dev, args.kernel_launches, args.format == "channel")
         return

@@ -323,7 +323,7 @@ def test_kv4_validation(L):
     assert e.value.status == UNSUPPORTED
     assert qoq.kv4_attention_workspace_bytes(64, 32, 8, 1024) == 0          # 512 workgroups already
     w = qoq.kv4_attention_workspace_bytes(1, 32, 8, 4096)                   # split over the sequence
-    assert w > 0 and w % (32 * 130 * 4) == 0 and w // (32 * 130 * 4) <= 32
+    assert w > 0 and w % (32 * 130 * 4) == 0 and w // (32 * 130 * 4) <= 64
     wr = L.qoq_kv4_write
     assert wr(FAKE, FAKE, 2, 1, 8, 64, FAKE, FAKE, 4, FAKE, 16, NUL) == UNSUPPORTED       # head dim
     assert wr(FAKE, FAKE, 0, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == OK

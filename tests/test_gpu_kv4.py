@@ -39,25 +39,35 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _layout_index(h_kv):
-    """Byte offsets (within a (page, head) section) and nibble of K and V codes for
-    every (slot t, dim d), from the documented page layout."""
+def _layout_index():
+    """Byte offset (within a (page, head) section) and bit shift of the K and V code
+    of every (slot t, dim d), from the documented page layout: 16-token block at
+    blk * 1024 (+ 4096 for V), lane slot 16 qd + t (K) or 16 qt + dd (V) at 16 bytes
+    each, word u, nibble k."""
     t = np.arange(P)[:, None]
     d = np.arange(D)[None, :]
     blk, tt = t // 16, t % 16
-    kb = blk * 1024 + (16 * ((d % 16) // 4) + tt) * 16 + 2 * (d // 16) + (d % 4) // 2
-    kn = d % 2
+    # K: dim d = 16 (2u + (k >> 1 & 1)) + 4 qd + 2 (k & 1) + (k >> 2)
+    j, r = d // 16, d % 16
+    qd, rr = r // 4, r % 4
+    u, kpar = j // 2, j % 2
+    k = 4 * (rr % 2) + (rr // 2) + 2 * kpar
+    kb = blk * 1024 + (16 * qd + tt) * 16 + 4 * u + k // 2
+    ksh = 4 * (k % 2)
+    # V: token 4 qt + 2 (k & 1) + (k >> 2) of dim 16 (2u + (k >> 1 & 1)) + dd
     qt, ti = tt // 4, tt % 4
-    vb = 4096 + blk * 1024 + (16 * qt + d % 16) * 16 + 2 * (d // 16) + ti // 2
-    vn = np.broadcast_to(ti % 2, vb.shape)
-    return kb, np.broadcast_to(kn, kb.shape), vb, vn
+    dd = d % 16
+    k = 4 * (ti % 2) + (ti // 2) + 2 * kpar
+    vb = 4096 + blk * 1024 + (16 * qt + dd) * 16 + 4 * u + k // 2
+    vsh = 4 * (k % 2)
+    return kb, np.broadcast_to(ksh, kb.shape), vb, np.broadcast_to(vsh, vb.shape)
 
 
 def read_pages(pool, page_ids, h_kv, ntok):
     """Host decode of the first ntok slots of the given pages (in sequence order):
     (k codes, k s, k z, v codes, v s, v z) as [ntok, h_kv, D] / [ntok, h_kv]."""
     pb = qoq.kv4_page_bytes(h_kv) // h_kv
-    kb, kn, vb, vn = _layout_index(h_kv)
+    kb, ksh, vb, vsh = _layout_index()
     out = [np.zeros((ntok, h_kv, D), np.uint8), np.zeros((ntok, h_kv), np.float16),
            np.zeros((ntok, h_kv), np.float16), np.zeros((ntok, h_kv, D), np.uint8),
            np.zeros((ntok, h_kv), np.float16), np.zeros((ntok, h_kv), np.float16)]
@@ -65,11 +75,12 @@ def read_pages(pool, page_ids, h_kv, ntok):
         page, slot = page_ids[i // P], i % P
         for g in range(h_kv):
             sec = pool[(page * h_kv + g) * pb:(page * h_kv + g + 1) * pb]
-            out[0][i, g] = (sec[kb[slot]] >> (4 * kn[slot])) & 0xF
-            out[3][i, g] = (sec[vb[slot]] >> (4 * vn[slot])) & 0xF
-            st = sec[8192:8704].view(np.float16)
-            out[1][i, g], out[2][i, g], out[4][i, g], out[5][i, g] = st[slot], st[64 + slot], st[128 + slot], \
-                st[192 + slot]
+            out[0][i, g] = (sec[kb[slot]] >> ksh[slot]) & 0xF
+            out[3][i, g] = (sec[vb[slot]] >> vsh[slot]) & 0xF
+            kst = sec[8192 + 4 * slot:8192 + 4 * slot + 4].view(np.float16)
+            vst = sec[8448 + 16 * (slot // 4):8448 + 16 * (slot // 4) + 16].view(np.float16)
+            out[1][i, g], out[2][i, g] = kst[0], kst[1]
+            out[4][i, g], out[5][i, g] = vst[slot % 4], vst[4 + slot % 4]
     return out
 
 

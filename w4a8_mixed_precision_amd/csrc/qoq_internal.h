@@ -34,8 +34,11 @@ void launch_silu_mul_quantize(const void *gate, const void *up, int64_t ld, int6
 // KV4 cache (head dim 128, 64-token pages, the layout described in qoq_kv4.hip)
 constexpr int kKv4PageTokens = 64;
 constexpr int kKv4PageBytes = 8704;              // per (page, KV head): K, V codes + fp16 stats
-constexpr int64_t kKv4TargetWorkgroups = 512;
-constexpr int64_t kKv4MaxSplits = 32;
+#ifndef QOQ_KV4_TARGET_WG
+#define QOQ_KV4_TARGET_WG 512
+#endif
+constexpr int64_t kKv4TargetWorkgroups = QOQ_KV4_TARGET_WG;
+constexpr int64_t kKv4MaxSplits = 64;
 int kv4_splits(int64_t B, int64_t h_kv, int64_t max_len);
 size_t kv4_workspace_need(int64_t B, int64_t h, int64_t h_kv, int64_t max_len);
 void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,

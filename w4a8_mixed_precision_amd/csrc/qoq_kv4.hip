@@ -11,28 +11,38 @@
 //
 // MI355X mapping (this library's own): both contractions run on the matrix cores
 // (v_mfma_f32_16x16x16_f16: FP16 inputs, FP32 accumulation); dequantization on the
-// vector ALU with packed FP16 (bias 1024 + code, exact subtraction of 1024 + z, one
-// rounded multiply by s: two packed operations per pair of values).  A wave works
-// on blocks of 16 tokens and keeps everything in registers:
+// vector ALU with packed FP16.  A wave works on blocks of 16 tokens and keeps
+// everything in registers:
 //   S^T = K_hat q^T      A = K_hat (16 tokens x 16 dims per k step), B = q^T
 //                        -> lane l holds head l % 16, tokens 4 (l / 16) + i
-//   online softmax per head (the lane's own head)
+//   online softmax per head (the lane's own head), base 2
 //   O^T += V_hat^T P^T   A = V_hat^T (16 dims x 16 tokens), B = P^T straight from
 //                        the softmax registers -> lane l holds head l % 16
 // so the cache is stored in the matrix instructions' operand order (below), one
 // 16-byte load per lane per 16-token block for K and one for V.
 //
-// Page layout (kPageTokens tokens, head dim 128): for page p and KV head g, kPageBytes
-// at (p * H_KV + g) * kPageBytes:
+// Dequantization of a pair of codes: the codes sit in nibbles k and k + 4 of a
+// 32-bit word, so one and-or with 0x000f000f (nibbles 0 and 4) or 0x00f000f0 (1 and
+// 5) against the fp16 bit pattern of 1024 or 64 (whose mantissa steps are 1 and 1/16)
+// gives the fp16 pair (base + c0, base + c1) exactly; nibbles 2, 6 and 3, 7 the same
+// after one shift by 8.  Then (base + c) - (base + z) = c - z exactly, and one
+// rounded multiply by s: K_hat = fp16((c - z) s).  Two packed FP16 operations per
+// pair of values after the extraction.
+//
+// Page layout (kPageTokens = 64 tokens, head dim 128): for page p and KV head g,
+// kPageBytes at (p * H_KV + g) * kPageBytes:
 //   [0, 4096)     K codes, 16-token block b at b * 1024; lane slot L = 16 qd + t
-//                 (token t of the block, dim quarter qd) at L * 16: byte 2j + e
-//                 holds dims 16 j + 4 qd + 2 e (low nibble) and + 1 (high nibble),
-//                 j = 0..7, e = 0, 1
+//                 (token t of the block, dim quarter qd) at L * 16; 32-bit word u
+//                 (u = 0..3) of the slot, nibble k (bits 4k..4k+3) holds dim
+//                 16 (2u + (k >> 1 & 1)) + 4 qd + 2 (k & 1) + (k >> 2)
 //   [4096, 8192)  V codes, block b at 4096 + b * 1024; lane slot L = 16 qt + dd
-//                 (token quarter qt, dim dd of a 16-dim block) at L * 16: byte
-//                 2 cb + e holds tokens 4 qt + 2 e (low) and + 1 (high) of dim
-//                 16 cb + dd, cb = 0..7
-//   [8192, 8704)  fp16 K scales [64], K zeros [64], V scales [64], V zeros [64]
+//                 (token quarter qt, dim dd of a 16-dim block) at L * 16; word u,
+//                 nibble k holds token 4 qt + 2 (k & 1) + (k >> 2) of dim
+//                 16 (2u + (k >> 1 & 1)) + dd
+//   [8192, 8448)  K statistics: token t at 8192 + 4t, fp16 scale (low half) and
+//                 fp16 zero (high half)
+//   [8448, 8704)  V statistics: tokens 4 qg .. 4 qg + 3 at 8448 + 16 qg, their four
+//                 fp16 scales then their four fp16 zeros
 #include "qoq_device.h"
 #include "qoq_internal.h"
 
@@ -52,30 +62,53 @@ constexpr int kD = 128;
 constexpr int kP = kKv4PageTokens;           // tokens per page (64)
 constexpr int kKCodes = 0;
 constexpr int kVCodes = kP * kD / 2;          // 4096
-constexpr int kKScale = 2 * kVCodes;          // 8192
-constexpr int kKZero = kKScale + 2 * kP;
-constexpr int kVScale = kKZero + 2 * kP;
-constexpr int kVZero = kVScale + 2 * kP;
-static_assert(kVZero + 2 * kP == kKv4PageBytes, "page layout");
+constexpr int kKStats = 2 * kVCodes;          // 8192: (scale, zero) per token
+constexpr int kVStats = kKStats + 4 * kP;     // 8448: 4 scales, 4 zeros per 4 tokens
+static_assert(kVStats + 4 * kP == kKv4PageBytes, "page layout");
 
 __device__ __forceinline__ f4 mfma_f16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ h2 bits_h2(unsigned u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ unsigned h2_bits(h2 v) { return __builtin_bit_cast(unsigned, v); }
 
-// two 4-bit codes (low, high nibble of byte b) -> fp16 pair (1024 + c0, 1024 + c1)
-__device__ __forceinline__ h2 biased_pair(unsigned b) {
-  return bits_h2((b & 0xfu) | ((b & 0xf0u) << 12) | 0x64006400u);
+constexpr unsigned kBase1024 = 0x64006400u, kBase64 = 0x54005400u;
+
+// The extraction masks live in registers so that (w & mask) | base is one
+// v_and_or_b32 (the base from a scalar register; one scalar operand per
+// instruction); as literals the compiler splits it into an and and an or.
+struct NibbleMasks {
+  unsigned lo, hi;
+};
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m;
+  __asm__ volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m.lo));
+  __asm__ volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(m.hi));
+  return m;
+}
+__device__ __forceinline__ unsigned and_or(unsigned w, unsigned mask, unsigned base) {
+  unsigned r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(mask), "s"(base));
+  return r;
+}
+// nibbles 0 and 4 of w -> (1024 + c0, 1024 + c4); nibbles 1 and 5 -> (64 + c1, 64 + c5)
+__device__ __forceinline__ h2 pair_lo(unsigned w, const NibbleMasks &nm) { return bits_h2(and_or(w, nm.lo, kBase1024)); }
+__device__ __forceinline__ h2 pair_hi(unsigned w, const NibbleMasks &nm) { return bits_h2(and_or(w, nm.hi, kBase64)); }
+
+// -(base + z) for a pair of fp16 zeros (exact: z is an integer in [0, 15])
+__device__ __forceinline__ h2 neg_biased(unsigned zz, unsigned base) {
+  const h2 v = bits_h2(zz) + bits_h2(base);
+  return bits_h2(__builtin_bit_cast(unsigned, v) ^ 0x80008000u);
 }
 
 // ---------------------------------------------------------------------------
 // KV write: one wave per (sequence, KV head); the new tokens of the sequence one
-// after another (the V bytes it touches hold two tokens, so one writer per page).
-// Lane l holds dims 2l, 2l + 1.  Quantization (per token and head): range widened
-// to contain 0, s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s), q = clamp(z +
-// rne(x / s), 0, 15), fp32 IEEE quotients; s and z stored as fp16.
+// after another.  Lane l quantizes dims 2l, 2l + 1.  Quantization (per token and
+// head): range widened to contain 0, s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s),
+// q = clamp(z + rne(x / s), 0, 15), fp32 IEEE quotients; s and z stored as fp16.
+// The codes go through LDS so that each 32-bit word of the page is written by one
+// lane: a K word holds one token (plain store), a V word four tokens (the lane that
+// owns the word updates its two nibbles of the token, for every token, in order).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
@@ -107,6 +140,8 @@ __device__ __forceinline__ void kv_quant2(float x0, float x1, unsigned &c0, unsi
   c1 = static_cast<unsigned>(fminf(fmaxf(z + rintf(__fdiv_rn(x1, s)), 0.0f), 15.0f));
 }
 
+__device__ __forceinline__ unsigned half_bits(__half h) { return __builtin_bit_cast(unsigned short, h); }
+
 // Positions and page ids are data the host cannot check: a token whose position
 // falls outside the page table, or whose page id lies outside the pool, is skipped
 // (a bad table gives wrong contents, never an access outside the buffers).
@@ -115,6 +150,7 @@ __global__ __launch_bounds__(64) void kv4_write_kernel(const __half *__restrict_
                                                        const int *__restrict__ positions,
                                                        const int *__restrict__ page_table, int max_pages,
                                                        int num_pages, uint8_t *__restrict__ pool) {
+  __shared__ uint8_t kcode[kD], vcode[kD];
   const int b = blockIdx.y, g = blockIdx.x, lane = threadIdx.x;
   const int d0 = 2 * lane;
   for (int i = 0; i < n_new; ++i) {
@@ -122,69 +158,185 @@ __global__ __launch_bounds__(64) void kv4_write_kernel(const __half *__restrict_
     if (pos < 0 || pos / kP >= max_pages) continue;
     const int page = page_table[static_cast<size_t>(b) * max_pages + pos / kP];
     if (page < 0 || page >= num_pages) continue;
-    const int slot = pos % kP;
+    const int slot = pos % kP, blk = slot >> 4, t = slot & 15;
     uint8_t *pg = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
     const size_t src = ((static_cast<size_t>(b) * n_new + i) * h_kv + g) * kD + d0;
     const unsigned kw = *reinterpret_cast<const unsigned *>(k_new + src);
     const unsigned vw = *reinterpret_cast<const unsigned *>(v_new + src);
     unsigned c0, c1;
-    __half sh, zh;
-    // K: dims d0, d0 + 1 share one byte
-    kv_quant2(half_bits_to_float(kw & 0xffffu), half_bits_to_float(kw >> 16), c0, c1, sh, zh);
-    {
-      const int blk = slot >> 4, t = slot & 15;
-      const int j = d0 >> 4, qd = (d0 & 15) >> 2, e = (d0 & 3) >> 1;
-      pg[kKCodes + blk * 1024 + (16 * qd + t) * 16 + 2 * j + e] = static_cast<uint8_t>(c0 | (c1 << 4));
-      if (lane == 0) {
-        reinterpret_cast<__half *>(pg + kKScale)[slot] = sh;
-        reinterpret_cast<__half *>(pg + kKZero)[slot] = zh;
-      }
-    }
-    // V: one nibble of each of two bytes (the other nibble is a neighbouring token)
-    kv_quant2(half_bits_to_float(vw & 0xffffu), half_bits_to_float(vw >> 16), c0, c1, sh, zh);
-    {
-      const int blk = slot >> 4, t = slot & 15;
-      const int qt = t >> 2, ti = t & 3, e = ti >> 1, hi = ti & 1;
+    __half ksh, kzh, vsh, vzh;
+    kv_quant2(half_bits_to_float(kw & 0xffffu), half_bits_to_float(kw >> 16), c0, c1, ksh, kzh);
+    kcode[d0] = static_cast<uint8_t>(c0);
+    kcode[d0 + 1] = static_cast<uint8_t>(c1);
+    kv_quant2(half_bits_to_float(vw & 0xffffu), half_bits_to_float(vw >> 16), c0, c1, vsh, vzh);
+    vcode[d0] = static_cast<uint8_t>(c0);
+    vcode[d0 + 1] = static_cast<uint8_t>(c1);
+    __syncthreads();
+    if (lane < 16) {                                   // K: word u of slot (qd, t), this token only
+      const int qd = lane >> 2, u = lane & 3;
+      unsigned w = 0;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int d = d0 + u;
-        const int cb = d >> 4, dd = d & 15;
-        uint8_t *p = pg + kVCodes + blk * 1024 + (16 * qt + dd) * 16 + 2 * cb + e;
-        const unsigned c = u ? c1 : c0;
-        const unsigned old = *p;
-        *p = static_cast<uint8_t>(hi ? ((old & 0x0fu) | (c << 4)) : ((old & 0xf0u) | c));
+      for (int k = 0; k < 8; ++k) {
+        const int d = 16 * (2 * u + ((k >> 1) & 1)) + 4 * qd + 2 * (k & 1) + (k >> 2);
+        w |= static_cast<unsigned>(kcode[d]) << (4 * k);
       }
-      if (lane == 0) {
-        reinterpret_cast<__half *>(pg + kVScale)[slot] = sh;
-        reinterpret_cast<__half *>(pg + kVZero)[slot] = zh;
-      }
+      *reinterpret_cast<unsigned *>(pg + kKCodes + blk * 1024 + (16 * qd + t) * 16 + 4 * u) = w;
     }
-    __syncthreads();                                   // the next token may share V bytes
+    {                                                  // V: word u of slot (qt, dd), two nibbles
+      const int dd = lane & 15, u = lane >> 4, qt = t >> 2, ti = t & 3;
+      const int k0 = 4 * (ti & 1) + (ti >> 1);         // nibble of dim 16 (2u) + dd; + 2 for 16 (2u + 1) + dd
+      unsigned *wp = reinterpret_cast<unsigned *>(pg + kVCodes + blk * 1024 + (16 * qt + dd) * 16 + 4 * u);
+      const unsigned keep = ~((0xfu << (4 * k0)) | (0xfu << (4 * k0 + 8)));
+      *wp = (*wp & keep) | (static_cast<unsigned>(vcode[32 * u + dd]) << (4 * k0)) |
+            (static_cast<unsigned>(vcode[32 * u + 16 + dd]) << (4 * k0 + 8));
+    }
+    if (lane == 0) {
+      *reinterpret_cast<unsigned *>(pg + kKStats + 4 * slot) = half_bits(ksh) | (half_bits(kzh) << 16);
+      __half *vst = reinterpret_cast<__half *>(pg + kVStats + 16 * (slot >> 2));
+      vst[slot & 3] = vsh;
+      vst[4 + (slot & 3)] = vzh;
+    }
+    __syncthreads();                                   // the staging bytes are reused by the next token
   }
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention.  Workgroup (split s, KV head g, sequence b), 4 waves; the split
-// covers 16-token blocks [s * bps, min(nblk, (s + 1) * bps)), wave w every 4th of
-// them.  Per wave: m, l (fp32, for the lane's head) and O^T (32 fp32 per lane).  The
-// waves merge through LDS; one split writes o directly, several write unnormalized
-// partials (O, m, l) that kv4_combine_kernel merges.
+// Decode attention.  Workgroup (split s, KV head g, sequence b), kAttnWaves waves;
+// the split covers 16-token blocks [s * bps, min(nblk, (s + 1) * bps)) (bps a
+// multiple of 4, so splits start on page boundaries), wave w every kAttnWaves-th
+// of them.  The page ids of a 64-page window sit one per lane and are read with
+// readlane; each wave keeps the next block's codes and statistics in flight while
+// it computes the current one (a two-slot ring).  Per wave: m, l (fp32, for the
+// lane's head, scores in base-2 units; l summed over the lane's own tokens until
+// the end) and O^T (32 fp32 per lane).  The running
+// maximum is raised only when a score exceeds it by more than 2^kLazy: in between
+// the weights exp2(score - m) stay below 2^kLazy, and the final division by l
+// (accumulated against the same m) is unchanged.  The waves merge through LDS; one
+// split writes o directly, several write unnormalized partials (O, m, l) that
+// kv4_combine_kernel merges.
 // ---------------------------------------------------------------------------
-constexpr int kAttnWaves = 4;
+#ifndef QOQ_KV4_WAVES
+#define QOQ_KV4_WAVES 4
+#endif
+constexpr int kAttnWaves = QOQ_KV4_WAVES;
+constexpr int kWindowBlocks = 4 * 64;              // blocks of the 64 pages one wave's lanes name
+constexpr float kLazy = 8.0f;
 
-struct AttnPartial {
-  float o[8][4];
-  float m, l;
+struct KvBlock {                                   // raw data of one 16-token block, one lane's share
+  uint4 kc, vc;                                    // K codes (token hl), V codes (tokens 4 quad + 0..3)
+  unsigned ks;                                     // fp16 scale | fp16 zero << 16 of K token hl
+  uint4 vs;                                        // fp16 scales (x, y), zeros (z, w) of V tokens 4 quad + 0..3
 };
 
-__global__ __launch_bounds__(64 * kAttnWaves) void kv4_attention_kernel(
+// Buffer loads: the (page, head) section is a buffer resource (its base in scalar
+// registers, its size as the range: a load past it returns zeros), the block
+// offset a scalar, the lane offsets constant vector registers; no per-block vector
+// address arithmetic.
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;           // raw 32-bit data format
+
+__device__ __forceinline__ uint4 as_uint4(u4v v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+__device__ __forceinline__ void load_block(KvBlock &r, const uint8_t *__restrict__ pool, int page, int h_kv, int g,
+                                           int blk, unsigned lane_off, unsigned ks_off, unsigned vs_off) {
+  const int pb = blk & 3;                          // block within the page
+  const uint8_t *sec = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sec), 0, kKv4PageBytes, kBufferWord3);
+  r.kc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kKCodes + pb * 1024, 0));
+  r.vc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kVCodes + pb * 1024, 0));
+  r.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, ks_off, kKStats + pb * 64, 0);
+  r.vs = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, vs_off, kVStats + pb * 64, 0));
+}
+
+// one block: scores S^T = K_hat q^T, online softmax update, O^T += V_hat^T P^T
+__device__ __forceinline__ void attend_block(const KvBlock &rb, int blk, int len, int hl, int quad, float c2,
+                                             const NibbleMasks &nm, const h4 (&qf)[8], float &m, float &l,
+                                             f4 (&o)[8]) {
+  const int tok0 = blk * 16;
+  const bool tail = tok0 + 16 > len;                   // wave-uniform: only a sequence's last block
+  unsigned kst = rb.ks;
+  uint4 vst = rb.vs;
+  // tokens past the sequence: scale and zero 0 -> dequantized 0, whatever the codes
+  if (tail) {
+    if (tok0 + hl >= len) kst = 0u;
+    const int valid = len - (tok0 + 4 * quad);        // how many of the lane's 4 V tokens exist
+    if (valid < 4) {
+      const unsigned keep01 = (valid > 0 ? 0xffffu : 0u) | (valid > 1 ? 0xffff0000u : 0u);
+      const unsigned keep23 = valid > 2 ? 0xffffu : 0u;
+      vst.x &= keep01;
+      vst.z &= keep01;
+      vst.y &= keep23;
+      vst.w &= keep23;
+    }
+  }
+  // K_hat fragments (token hl, one scale and zero for the lane)
+  const unsigned kz = (kst >> 16) * 0x10001u, ks = (kst & 0xffffu) * 0x10001u;
+  const h2 kb1024 = neg_biased(kz, kBase1024), kb64 = neg_biased(kz, kBase64), ks2 = bits_h2(ks);
+  const unsigned kw[4] = {rb.kc.x, rb.kc.y, rb.kc.z, rb.kc.w};
+  f4 st0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, st1 = st0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned w = kw[u], w8 = w >> 8;
+    const h2 a0 = (pair_lo(w, nm) + kb1024) * ks2, a1 = (pair_hi(w, nm) + kb64) * ks2;    // dims 16 (2u) + 4 quad + 0..3
+    const h2 b0 = (pair_lo(w8, nm) + kb1024) * ks2, b1 = (pair_hi(w8, nm) + kb64) * ks2;  // dims 16 (2u + 1) + ...
+    st0 = mfma_f16(h4{a0[0], a0[1], a1[0], a1[1]}, qf[2 * u], st0);
+    st1 = mfma_f16(h4{b0[0], b0[1], b1[0], b1[1]}, qf[2 * u + 1], st1);
+  }
+  // base-2 scores of the lane's head for tokens tok0 + 4 quad + i
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = (st0[i] + st1[i]) * c2;
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (tok0 + 4 * quad + i < len) ? sc[i] : -INFINITY;
+  }
+  const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  // m is the same in the 4 lanes of a head; it is raised (for every head of the wave
+  // at once) only when some score exceeds it by more than kLazy, m = -inf at first
+  if (__builtin_amdgcn_ballot_w64(lm > m + kLazy)) {
+    float bm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));             // finite: every block has a valid token
+    const float mn = fmaxf(m, bm);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+    m = mn;
+  }
+  // the lane's share of the denominator (its 4 tokens); summed over the 4 lanes at the end
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(sc[i] - m);
+    l += p[i];
+  }
+  const h4 pf = {static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1]), static_cast<_Float16>(p[2]),
+                 static_cast<_Float16>(p[3])};
+  // V_hat^T fragments (tokens 4 quad + 0, 1 and + 2, 3) and O^T += V_hat^T P^T
+  const h2 vs01 = bits_h2(vst.x), vs23 = bits_h2(vst.y);
+  const h2 vb01 = neg_biased(vst.z, kBase1024), vb23 = neg_biased(vst.w, kBase64);
+  const unsigned vw[4] = {rb.vc.x, rb.vc.y, rb.vc.z, rb.vc.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned w = vw[u], w8 = w >> 8;
+    const h2 a0 = (pair_lo(w, nm) + vb01) * vs01, a1 = (pair_hi(w, nm) + vb23) * vs23;    // dim 16 (2u) + l % 16
+    const h2 b0 = (pair_lo(w8, nm) + vb01) * vs01, b1 = (pair_hi(w8, nm) + vb23) * vs23;  // dim 16 (2u + 1) + l % 16
+    o[2 * u] = mfma_f16(h4{a0[0], a0[1], a1[0], a1[1]}, pf, o[2 * u]);
+    o[2 * u + 1] = mfma_f16(h4{b0[0], b0[1], b1[0], b1[1]}, pf, o[2 * u + 1]);
+  }
+}
+
+// at most 128 registers per lane: four waves per SIMD, no accumulation registers
+__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(4))) void kv4_attention_kernel(
     const __half *__restrict__ q, const uint8_t *__restrict__ pool, const int *__restrict__ page_table,
     int max_pages, int num_pages, const int *__restrict__ seq_lens, int max_len, int h, int h_kv, int bps,
-    float scale, __half *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+    float c2, __half *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml) {
   __shared__ float red[kAttnWaves][34][64];
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int splits = gridDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = h / h_kv;
   const int hl = lane & 15, quad = lane >> 4;
   const int len = min(max(seq_lens[b], 1), max_len);   // data: clamped to what the table covers
@@ -202,87 +354,44 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kv4_attention_kernel(
       qf[j] = __builtin_bit_cast(h4, w);
     }
   }
+  const NibbleMasks nm = nibble_masks();
   float m = -INFINITY, l = 0.0f;
   f4 o[8];
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) o[cb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int blk = blk0 + wave; blk < blk1; blk += kAttnWaves) {
-    const int tok0 = blk * 16;
-    const int page = min(max(page_table[static_cast<size_t>(b) * max_pages + tok0 / kP], 0), num_pages - 1);
-    const uint8_t *pg = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
-    const int pb = (tok0 % kP) >> 4;                  // block within the page
-    // loads: K fragment (token hl), V fragment (tokens 4 quad + 0..3), their stats
-    const uint4 kc = *reinterpret_cast<const uint4 *>(pg + kKCodes + pb * 1024 + lane * 16);
-    const uint4 vc = *reinterpret_cast<const uint4 *>(pg + kVCodes + pb * 1024 + lane * 16);
-    const int tk = pb * 16 + hl;                       // the lane's K token in the page
-    const int tv = pb * 16 + 4 * quad;                 // first of the lane's V tokens
-    unsigned ks = reinterpret_cast<const unsigned short *>(pg + kKScale)[tk];
-    unsigned kz = reinterpret_cast<const unsigned short *>(pg + kKZero)[tk];
-    uint2 vs = *reinterpret_cast<const uint2 *>(pg + kVScale + 2 * tv);
-    uint2 vz = *reinterpret_cast<const uint2 *>(pg + kVZero + 2 * tv);
-    // tokens past the sequence: scale and zero 0 -> dequantized 0, whatever the codes
-    if (tok0 + hl >= len) ks = kz = 0u;
-    {
-      const int valid = len - (tok0 + 4 * quad);        // how many of the 4 V tokens exist
-      if (valid < 4) {
-        const unsigned keep0 = valid > 0 ? 0xffffu : 0u, keep1 = valid > 1 ? 0xffff0000u : 0u;
-        const unsigned keep2 = valid > 2 ? 0xffffu : 0u;
-        vs.x &= keep0 | keep1;
-        vz.x &= keep0 | keep1;
-        vs.y &= keep2;
-        vz.y &= keep2;
-      }
-    }
-    // K_hat fragment: (1024 + c) - (1024 + z), times s (two packed ops per pair)
-    const h2 kbias = bits_h2((kz | (kz << 16)) ^ 0x80008000u) - bits_h2(0x64006400u);   // -z - 1024
-    const h2 ks2 = bits_h2(ks | (ks << 16));
-    const unsigned kw[4] = {kc.x, kc.y, kc.z, kc.w};
-    f4 st = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const unsigned w = kw[j >> 1] >> (16 * (j & 1));
-      const h2 p0 = (biased_pair(w & 0xffu) + kbias) * ks2;
-      const h2 p1 = (biased_pair((w >> 8) & 0xffu) + kbias) * ks2;
-      const h4 a = {p0[0], p0[1], p1[0], p1[1]};
-      st = mfma_f16(a, qf[j], st);
-    }
-    // scores of the lane's head for tokens tok0 + 4 quad + i; softmax update
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (tok0 + 4 * quad + i < len) ? st[i] * scale : -INFINITY;
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m, bm);                     // finite: every block has a valid token
-    const float alpha = expf(m - mn);                  // m = -inf at first: 0
-    float p[4], ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = expf(sc[i] - mn);
-      ps += p[i];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
-    m = mn;
-    const h4 pf = {static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1]), static_cast<_Float16>(p[2]),
-                   static_cast<_Float16>(p[3])};
-    // V_hat^T fragments and O^T += V_hat^T P^T
-    const h2 vs01 = bits_h2(vs.x), vs23 = bits_h2(vs.y);
-    const h2 vb01 = bits_h2(vz.x ^ 0x80008000u) - bits_h2(0x64006400u);
-    const h2 vb23 = bits_h2(vz.y ^ 0x80008000u) - bits_h2(0x64006400u);
-    const unsigned vw[4] = {vc.x, vc.y, vc.z, vc.w};
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const unsigned w = vw[cb >> 1] >> (16 * (cb & 1));
-      const h2 p0 = (biased_pair(w & 0xffu) + vb01) * vs01;
-      const h2 p1 = (biased_pair((w >> 8) & 0xffu) + vb23) * vs23;
-      const h4 a = {p0[0], p0[1], p1[0], p1[1]};
-      o[cb] = mfma_f16(a, pf, o[cb] * alpha);
+  const int *ptab = page_table + static_cast<size_t>(b) * max_pages;
+  const unsigned lane_off = 16u * lane, ks_off = 4u * hl, vs_off = 16u * quad;
+  for (int w0 = blk0; w0 < blk1; w0 += kWindowBlocks) {
+    const int wend = min(blk1, w0 + kWindowBlocks);
+    const int pg0 = w0 >> 2;                           // w0 is a page boundary
+    const int pi = pg0 + lane;
+    const int mypage = pi < max_pages ? min(max(ptab[pi], 0), num_pages - 1) : 0;
+    // Two blocks per trip, each slot of the ring loaded at one place.  The loads are
+    // unconditional (a block past the window reloads the window's last block, which
+    // is not used) so that the wait before each block counts only the loads issued
+    // before it, never the prefetch behind it.
+    const int last = wend - 1;
+    KvBlock ring0, ring1;
+    int blk = w0 + wave;
+    int ld = min(blk, last);
+    load_block(ring0, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
+                 vs_off);
+    for (; blk < wend; blk += 2 * kAttnWaves) {
+      ld = min(blk + kAttnWaves, last);
+      load_block(ring1, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
+                 vs_off);
+      attend_block(ring0, blk, len, hl, quad, c2, nm, qf, m, l, o);
+      ld = min(blk + 2 * kAttnWaves, last);
+      load_block(ring0, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
+                 vs_off);
+      if (blk + kAttnWaves < wend) attend_block(ring1, blk + kAttnWaves, len, hl, quad, c2, nm, qf, m, l, o);
     }
   }
 
+  // the head's denominator: the 4 lanes' shares
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
   // merge the waves: partials through LDS, wave 0 combines
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb)
@@ -299,7 +408,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kv4_attention_kernel(
 #pragma unroll
   for (int w = 0; w < kAttnWaves; ++w) {
     const float mw = red[w][32][lane];
-    f[w] = mw == -INFINITY ? 0.0f : expf(mw - mm);    // a wave with no block adds nothing
+    f[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mm);   // a wave with no block adds nothing
     ll += red[w][33][lane] * f[w];
   }
   const int head = g * r + hl;
@@ -341,8 +450,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kv4_attention_kernel(
   }
 }
 
-// o[b, head] = sum_s O_s exp(m_s - m) / sum_s l_s exp(m_s - m); a split with no
-// tokens has m = -inf and adds nothing
+// o[b, head] = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m) (base-2 maxima); a split
+// with no tokens has m = -inf and adds nothing
 __global__ __launch_bounds__(kD) void kv4_combine_kernel(const float *__restrict__ ws_o,
                                                          const float *__restrict__ ws_ml, int splits, int bh,
                                                          __half *__restrict__ out) {
@@ -354,7 +463,7 @@ __global__ __launch_bounds__(kD) void kv4_combine_kernel(const float *__restrict
     const size_t p = static_cast<size_t>(s) * bh + row;
     const float ms = ws_ml[2 * p];
     if (ms == -INFINITY) continue;
-    const float f = expf(ms - mm);
+    const float f = __builtin_amdgcn_exp2f(ms - mm);
     ll += ws_ml[2 * p + 1] * f;
     acc += ws_o[p * kD + d] * f;
   }
@@ -391,16 +500,17 @@ void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, co
                           int64_t max_len, void *out, void *ws, hipStream_t st) {
   const int splits = kv4_splits(B, h_kv, max_len);
   const int64_t nblk = (max_len + 15) / 16;
-  const int bps = static_cast<int>((nblk + splits - 1) / splits);
+  const int bps = static_cast<int>(((nblk + splits - 1) / splits + 3) / 4 * 4);   // whole pages per split
   float *wo = static_cast<float *>(ws);
   float *wml = splits > 1 ? wo + static_cast<size_t>(splits) * B * h * kD : nullptr;
-  const float scale = 1.0f / sqrtf(static_cast<float>(kD));
+  // scores in base 2: q . k / sqrt(128) * log2(e)
+  const float c2 = static_cast<float>(1.4426950408889634 / 11.313708498984761);
   hipLaunchKernelGGL(kv4_attention_kernel,
                      dim3(static_cast<unsigned>(splits), static_cast<unsigned>(h_kv), static_cast<unsigned>(B)),
                      dim3(64 * kAttnWaves), 0, st, static_cast<const __half *>(q),
                      static_cast<const uint8_t *>(pool), page_table, static_cast<int>(max_pages),
                      static_cast<int>(num_pages), seq_lens, static_cast<int>(max_len), static_cast<int>(h),
-                     static_cast<int>(h_kv), bps, scale, static_cast<__half *>(out), wo, wml);
+                     static_cast<int>(h_kv), bps, c2, static_cast<__half *>(out), wo, wml);
   if (splits > 1)
     hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(kD), 0, st, wo, wml, splits,
                        static_cast<int>(B * h), static_cast<__half *>(out));

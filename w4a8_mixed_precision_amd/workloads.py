@@ -106,3 +106,68 @@ def algorithmic_bytes(M: int, N: int, K: int, per_channel: bool = False) -> dict
 
 def algorithmic_ops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
+
+
+# KV4 decode attention shapes: one new token per sequence attending to its cache.
+# Llama-3-8B (32 query heads, 8 KV heads of 128), the Qwen-72B-class model (64 / 8)
+# and Llama-2-7B (32 / 32) at decode batch sizes and contexts of a serving mix (the
+# pages' throughput runs use 1024 input tokens; the long single sequence exercises
+# the split over the sequence).
+@dataclass(frozen=True)
+class KvShape:
+    name: str
+    B: int
+    seq_len: int
+    h: int
+    h_kv: int
+
+
+KV_SHAPES = (
+    KvShape("llama3_8b_b64_l1024", 64, 1024, 32, 8),
+    KvShape("llama3_8b_b256_l512", 256, 512, 32, 8),
+    KvShape("llama3_8b_b16_l4096", 16, 4096, 32, 8),
+    KvShape("llama3_8b_b1_l32768", 1, 32768, 32, 8),
+    KvShape("qwen72b_b64_l1024", 64, 1024, 64, 8),
+    # Llama-2-7B (32 heads, no grouping): the pages' KV4 attention breakdown runs 64
+    # requests of 1024 input tokens on this model
+    KvShape("llama2_7b_b64_l1024", 64, 1024, 32, 32),
+)
+
+KV_PAGE_TOKENS = 64
+KV_HEAD_DIM = 128
+# bytes per cached token per KV head: 128 K codes + 128 V codes at 4 bits, fp16
+# scale and zero for each of K and V
+KV_TOKEN_HEAD_BYTES = KV_HEAD_DIM + 8
+
+
+def find_kv(name: str) -> KvShape:
+    for s in KV_SHAPES:
+        if s.name == name:
+            return s
+    raise KeyError(name)
+
+
+def kv_fp16(S: KvShape, b: int, n: int, role: int, scale: float = 1.0) -> np.ndarray:
+    """Keys (role 0) or values (role 1) fp16 [n, h_kv, 128] for sequence b: N(0, scale)
+    with 3 outlier channels per head scaled x8 (the Key outliers the pages report)."""
+    r = _rng(5, b, 4 + role, n)
+    x = r.standard_normal((n, S.h_kv, KV_HEAD_DIM), dtype=np.float32) * np.float32(scale)
+    cols = _rng(5, 0, 6 + role, 0).choice(KV_HEAD_DIM, 3, replace=False)
+    x[:, :, cols] *= np.float32(8.0)
+    return x.astype(np.float16)
+
+
+def kv_queries_fp16(S: KvShape) -> np.ndarray:
+    return _rng(5, 0, 8, S.B).standard_normal((S.B, S.h, KV_HEAD_DIM), dtype=np.float32).astype(np.float16)
+
+
+def kv_attention_bytes(B: int, seq_len: int, h: int, h_kv: int) -> int:
+    """Bytes decode attention must move at least once: every cached token's codes and
+    statistics of every KV head, the fp16 queries and outputs, the page table entries
+    and lengths."""
+    pages = -(-seq_len // KV_PAGE_TOKENS)
+    return B * seq_len * h_kv * KV_TOKEN_HEAD_BYTES + 2 * 2 * B * h * KV_HEAD_DIM + 4 * B * pages + 4 * B
+
+
+def kv_attention_flops(B: int, seq_len: int, h: int) -> int:
+    return 2 * 2 * B * h * seq_len * KV_HEAD_DIM

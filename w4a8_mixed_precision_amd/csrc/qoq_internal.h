@@ -38,7 +38,10 @@ constexpr int kKv4PageBytes = 8704;              // per (page, KV head): K, V co
 #define QOQ_KV4_TARGET_WG 512
 #endif
 constexpr int64_t kKv4TargetWorkgroups = QOQ_KV4_TARGET_WG;
-constexpr int64_t kKv4MaxSplits = 64;
+#ifndef QOQ_KV4_MAX_SPLITS
+#define QOQ_KV4_MAX_SPLITS 64
+#endif
+constexpr int64_t kKv4MaxSplits = QOQ_KV4_MAX_SPLITS;
 int kv4_splits(int64_t B, int64_t h_kv, int64_t max_len);
 size_t kv4_workspace_need(int64_t B, int64_t h, int64_t h_kv, int64_t max_len);
 void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,

@@ -249,16 +249,17 @@ __device__ __forceinline__ void load_block(KvBlock &r, const uint8_t *__restrict
   r.vs = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, vs_off, kVStats + pb * 64, 0));
 }
 
-// one block: scores S^T = K_hat q^T, online softmax update, O^T += V_hat^T P^T
+// one block: scores S^T = K_hat q^T, online softmax update, O^T += V_hat^T P^T.
+// TAIL: the block ends past the sequence (the masked last block of a sequence).
+template <bool TAIL>
 __device__ __forceinline__ void attend_block(const KvBlock &rb, int blk, int len, int hl, int quad, float c2,
                                              const NibbleMasks &nm, const h4 (&qf)[8], float &m, float &l,
                                              f4 (&o)[8]) {
   const int tok0 = blk * 16;
-  const bool tail = tok0 + 16 > len;                   // wave-uniform: only a sequence's last block
   unsigned kst = rb.ks;
   uint4 vst = rb.vs;
   // tokens past the sequence: scale and zero 0 -> dequantized 0, whatever the codes
-  if (tail) {
+  if (TAIL) {
     if (tok0 + hl >= len) kst = 0u;
     const int valid = len - (tok0 + 4 * quad);        // how many of the lane's 4 V tokens exist
     if (valid < 4) {
@@ -287,7 +288,7 @@ __device__ __forceinline__ void attend_block(const KvBlock &rb, int blk, int len
   float sc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) sc[i] = (st0[i] + st1[i]) * c2;
-  if (tail) {
+  if (TAIL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = (tok0 + 4 * quad + i < len) ? sc[i] : -INFINITY;
   }
@@ -339,9 +340,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = h / h_kv;
   const int hl = lane & 15, quad = lane >> 4;
+  const int blk0 = s * bps;
+  // the first window's page ids (one per lane), requested before the length is known
+  const int *ptab = page_table + static_cast<size_t>(b) * max_pages;
+  const int first_pi = (blk0 >> 2) + lane;
+  const int first_page = first_pi < max_pages ? ptab[first_pi] : 0;
   const int len = min(max(seq_lens[b], 1), max_len);   // data: clamped to what the table covers
   const int nblk = (len + 15) >> 4;
-  const int blk0 = s * bps, blk1 = min(nblk, blk0 + bps);
+  const int blk1 = min(nblk, blk0 + bps);
 
   // q^T as the B operand of S^T = K_hat q^T: lane holds head hl, dims 16 j + 4 quad + 0..3
   h4 qf[8];
@@ -360,32 +366,49 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) o[cb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int *ptab = page_table + static_cast<size_t>(b) * max_pages;
   const unsigned lane_off = 16u * lane, ks_off = 4u * hl, vs_off = 16u * quad;
   for (int w0 = blk0; w0 < blk1; w0 += kWindowBlocks) {
     const int wend = min(blk1, w0 + kWindowBlocks);
     const int pg0 = w0 >> 2;                           // w0 is a page boundary
     const int pi = pg0 + lane;
-    const int mypage = pi < max_pages ? min(max(ptab[pi], 0), num_pages - 1) : 0;
-    // Two blocks per trip, each slot of the ring loaded at one place.  The loads are
-    // unconditional (a block past the window reloads the window's last block, which
-    // is not used) so that the wait before each block counts only the loads issued
-    // before it, never the prefetch behind it.
-    const int last = wend - 1;
-    KvBlock ring0, ring1;
-    int blk = w0 + wave;
-    int ld = min(blk, last);
-    load_block(ring0, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
-                 vs_off);
-    for (; blk < wend; blk += 2 * kAttnWaves) {
-      ld = min(blk + kAttnWaves, last);
-      load_block(ring1, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
-                 vs_off);
-      attend_block(ring0, blk, len, hl, quad, c2, nm, qf, m, l, o);
-      ld = min(blk + 2 * kAttnWaves, last);
-      load_block(ring0, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
-                 vs_off);
-      if (blk + kAttnWaves < wend) attend_block(ring1, blk + kAttnWaves, len, hl, quad, c2, nm, qf, m, l, o);
+    const int id = w0 == blk0 ? first_page : (pi < max_pages ? ptab[pi] : 0);
+    const int mypage = min(max(id, 0), num_pages - 1);
+    // Full blocks: three per trip, two blocks in flight ahead of the one computed.
+    // Inside the loop every load and every block is unconditional (a load past the
+    // range reloads its last block, which is not used), so the wait before each
+    // block counts only the loads issued before it, never the prefetches behind it.
+    const int wfull = min(wend, len >> 4);
+    if (w0 < wfull) {
+      const int last = wfull - 1;
+      KvBlock ring0, ring1, ring2;
+      auto fetch = [&](KvBlock &r, int bk) {
+        const int ld = min(bk, last);
+        load_block(r, pool, __builtin_amdgcn_readlane(mypage, (ld >> 2) - pg0), h_kv, g, ld, lane_off, ks_off,
+                   vs_off);
+      };
+      int blk = w0 + wave;
+      const int mine = blk < wfull ? (wfull - blk + kAttnWaves - 1) / kAttnWaves : 0;   // this wave's blocks
+      fetch(ring0, blk);
+      fetch(ring1, blk + kAttnWaves);
+      int i = 0;
+      for (; i + 3 <= mine; i += 3, blk += 3 * kAttnWaves) {
+        fetch(ring2, blk + 2 * kAttnWaves);
+        attend_block<false>(ring0, blk, len, hl, quad, c2, nm, qf, m, l, o);
+        fetch(ring0, blk + 3 * kAttnWaves);
+        attend_block<false>(ring1, blk + kAttnWaves, len, hl, quad, c2, nm, qf, m, l, o);
+        fetch(ring1, blk + 4 * kAttnWaves);
+        attend_block<false>(ring2, blk + 2 * kAttnWaves, len, hl, quad, c2, nm, qf, m, l, o);
+      }
+      // the last one or two (already in ring0, ring1)
+      if (i < mine) attend_block<false>(ring0, blk, len, hl, quad, c2, nm, qf, m, l, o);
+      if (i + 1 < mine) attend_block<false>(ring1, blk + kAttnWaves, len, hl, quad, c2, nm, qf, m, l, o);
+    }
+    // the sequence's partial last block, by the wave the interleaving gives it
+    const int tb = nblk - 1;
+    if ((len & 15) && tb >= w0 && tb < wend && (tb - w0) % kAttnWaves == wave) {
+      KvBlock rt;
+      load_block(rt, pool, __builtin_amdgcn_readlane(mypage, (tb >> 2) - pg0), h_kv, g, tb, lane_off, ks_off, vs_off);
+      attend_block<true>(rt, tb, len, hl, quad, c2, nm, qf, m, l, o);
     }
   }
 
@@ -451,23 +474,32 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 }
 
 // o[b, head] = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m) (base-2 maxima); a split
-// with no tokens has m = -inf and adds nothing
-__global__ __launch_bounds__(kD) void kv4_combine_kernel(const float *__restrict__ ws_o,
+// with no tokens has m = -inf, O = 0, l = 0 and adds nothing.  One wave per (b, head):
+// the maxima a lane per split, then every split's (O, l) with no branch in the loop,
+// the lane's two dims at a time.
+__global__ __launch_bounds__(64) void kv4_combine_kernel(const float *__restrict__ ws_o,
                                                          const float *__restrict__ ws_ml, int splits, int bh,
                                                          __half *__restrict__ out) {
-  const int row = blockIdx.x, d = threadIdx.x;
+  const int row = blockIdx.x, lane = threadIdx.x;
   float mm = -INFINITY;
-  for (int s = 0; s < splits; ++s) mm = fmaxf(mm, ws_ml[2 * (static_cast<size_t>(s) * bh + row)]);
-  float acc = 0.0f, ll = 0.0f;
+  for (int s = lane; s < splits; s += 64) mm = fmaxf(mm, ws_ml[2 * (static_cast<size_t>(s) * bh + row)]);
+  mm = wave_max_f32(mm);                               // finite: split 0 holds the first token
+  float a0 = 0.0f, a1 = 0.0f, ll = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const size_t p = static_cast<size_t>(s) * bh + row;
     const float ms = ws_ml[2 * p];
-    if (ms == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(ms - mm);
+    const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - mm);
     ll += ws_ml[2 * p + 1] * f;
-    acc += ws_o[p * kD + d] * f;
+    const float2 v = *reinterpret_cast<const float2 *>(ws_o + p * kD + 2 * lane);
+    a0 += v.x * f;
+    a1 += v.y * f;
   }
-  out[static_cast<size_t>(row) * kD + d] = __float2half_rn(acc / ll);
+  const float inv = 1.0f / ll;
+  __half2 r;
+  r.x = __float2half_rn(a0 * inv);
+  r.y = __float2half_rn(a1 * inv);
+  *reinterpret_cast<__half2 *>(out + static_cast<size_t>(row) * kD + 2 * lane) = r;
 }
 
 }  // namespace
@@ -512,7 +544,7 @@ void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, co
                      static_cast<int>(num_pages), seq_lens, static_cast<int>(max_len), static_cast<int>(h),
                      static_cast<int>(h_kv), bps, c2, static_cast<__half *>(out), wo, wml);
   if (splits > 1)
-    hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(kD), 0, st, wo, wml, splits,
+    hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(64), 0, st, wo, wml, splits,
                        static_cast<int>(B * h), static_cast<__half *>(out));
 }
 

@@ -8,8 +8,9 @@ method quantizes and reorders weights offline).  Weight buffers are rotated over
 copies totalling >= 1 GiB so that the 256 MB MALL and the L2 do not serve them.
 
 Prints ONE JSON line (rank 0) with the throughput, the roofline fraction of the
-dominant kernel (timed with HIP events on the stream the kernels run on) and the
-CPU oracle timed on the host cores.
+dominant kernel (timed with HIP events on the stream the kernels run on), the CPU
+oracle timed on the host cores and, as context, the KV4 decode attention of
+Llama-3-8B at 64 sequences x 1024 cached tokens (kv4_attention; --no-kv4 skips it).
 
 --sweep runs every layer shape / batch size of the workload registry and writes a
 table to gpurun_out/sweep.json (not the headline line); with --format channel it
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--kv4", action="store_true", help="measure the KV4 decode attention and KV write")
+    ap.add_argument("--no-kv4", action="store_true", help="skip the KV4 attention figure of the headline line")
     ap.add_argument("--format", choices=("group", "channel"), default="group",
                     help="weight format: per-group g128 (default) or the per-channel variant")
     return ap.parse_args()
@@ -370,26 +372,32 @@ class KvCase:
         q.kv4_write(self.k1, self.v1, self.pos, t, self.pool)
 
 
+def kv4_case_metrics(S, q, torch, dev, launches):
+    from w4a8_mixed_precision_amd import workloads as wl
+    c = KvCase(S, dev, q)
+    for _ in range(3):
+        c.attend(q)
+    torch.cuda.synchronize()
+    ta = time_launches(lambda: c.attend(q), launches, torch)
+    tw = time_launches(lambda: c.write(q), launches, torch)
+    r = {"shape": S.name, "B": S.B, "seq_len": S.seq_len, "h": S.h, "h_kv": S.h_kv, "splits": c.splits,
+         "attention_us": ta * 1e6, "bytes_per_launch": c.bytes, "GBps": c.bytes / ta / 1e9,
+         "hbm_frac": c.bytes / ta / 1e9 / HBM_PEAK_GBPS, "TFLOPs": c.flops / ta / 1e12,
+         "tokens_per_s": S.B * S.seq_len / ta,
+         "write_us": tw * 1e6, "write_bytes": S.B * S.h_kv * (4 * wl.KV_HEAD_DIM + wl.KV_TOKEN_HEAD_BYTES),
+         "rotation_sets": c.nsets}
+    del c
+    torch.cuda.empty_cache()
+    return r
+
+
 def kv4_bench(q, torch, dev, launches):
     from w4a8_mixed_precision_amd import workloads as wl
     rows = []
     for S in wl.KV_SHAPES:
-        c = KvCase(S, dev, q)
-        for _ in range(3):
-            c.attend(q)
-        torch.cuda.synchronize()
-        ta = time_launches(lambda: c.attend(q), launches, torch)
-        tw = time_launches(lambda: c.write(q), launches, torch)
-        r = {"shape": S.name, "B": S.B, "seq_len": S.seq_len, "h": S.h, "h_kv": S.h_kv, "splits": c.splits,
-             "attention_us": ta * 1e6, "bytes_per_launch": c.bytes, "GBps": c.bytes / ta / 1e9,
-             "hbm_frac": c.bytes / ta / 1e9 / HBM_PEAK_GBPS, "TFLOPs": c.flops / ta / 1e12,
-             "tokens_per_s": S.B * S.seq_len / ta,
-             "write_us": tw * 1e6, "write_bytes": S.B * S.h_kv * (4 * wl.KV_HEAD_DIM + wl.KV_TOKEN_HEAD_BYTES),
-             "rotation_sets": c.nsets}
+        r = kv4_case_metrics(S, q, torch, dev, launches)
         rows.append(r)
         print(json.dumps(r), flush=True)
-        del c
-        torch.cuda.empty_cache()
     os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
     with open(os.path.join(ROOT, "gpurun_out", "kv4.json"), "w") as f:
         json.dump(rows, f, indent=1)
@@ -522,6 +530,8 @@ def main():
         "cases": per_case,
         "offline_pack_ms": pack_s * 1e3,
         "copy_ceiling": copy_ceiling(qoq, torch, dev),
+        "kv4_attention": None if args.no_kv4 else kv4_case_metrics(wl.find_kv("llama3_8b_b64_l1024"), qoq, torch, dev,
+                                                                    args.kernel_launches),
         "host_wall_s": t_host,
     }
     if not args.no_cpu_baseline:

@@ -142,6 +142,7 @@ def _run_attention(gpu, rng, lens, h, h_kv, kscale=1.0, vscale=1.0):
     q = (rng.standard_normal((B, h, D)) * 1.0).astype(np.float16)
     o = host(qoq.kv4_decode_attention(to_dev(q, gpu), pool, dpt, to_dev(np.array(lens, np.int32), gpu), h_kv,
                                       max_len))
+    worst = 0.0
     for b in range(B):
         ref = kv.attention_reference(q[b], ks[b], vs[b], h_kv).astype(np.float64)
         vq, vs_, vz = kv.kv_quantize(vs[b])
@@ -149,10 +150,16 @@ def _run_attention(gpu, rng, lens, h, h_kv, kscale=1.0, vscale=1.0):
         err = np.abs(o[b].astype(np.float64) - ref)
         bound = 2.0 ** -8 * vmax + 2.0 ** -9 * np.abs(ref)
         assert np.all(err <= bound), (b, lens[b], float(err.max()), float(vmax))
+        worst = max(worst, float((err / bound).max()))
+    say(f"largest error / bound: {worst:.3f}")
 
 
 @pytest.mark.parametrize("lens,h,h_kv", [([1, 17, 64, 300], 32, 8), ([1000, 65], 64, 8), ([16, 15, 33], 8, 8),
-                                         ([4096], 32, 8), ([129] * 16, 32, 8)])
+                                         ([4096], 32, 8), ([129] * 16, 32, 8),
+                                         ([4096, 5, 100, 2000], 32, 8),    # splits, some empty for short rows
+                                         ([64, 128, 1, 48], 16, 1),        # 16 heads on one KV head
+                                         ([1000, 777], 32, 32),            # no grouping
+                                         ([32768], 32, 8)])                # the long single sequence
 def test_kv4_decode_attention(gpu, lens, h, h_kv):
     say(f"kv4 attention lens={lens[:4]}{'...' if len(lens) > 4 else ''} h={h} h_kv={h_kv} "
         f"splits={qoq.kv4_attention_workspace_bytes(len(lens), h, h_kv, max(lens)) > 0}")
@@ -170,3 +177,19 @@ def test_kv4_decode_attention_batch64(gpu):
     rng = np.random.default_rng(10)
     say("kv4 attention batch 64 x 1024")
     _run_attention(gpu, rng, [1024] * 64, 32, 8)
+
+
+def test_kv4_write_guards(gpu):
+    """Positions past the page table and page ids outside the pool are skipped by the
+    write kernel (its own bounds checks): the pool is left as it was."""
+    h_kv = 2
+    pool = torch.full((4 * qoq.kv4_page_bytes(h_kv),), 0x5A, dtype=torch.uint8, device=gpu)
+    before = host(pool).copy()
+    pt = to_dev(np.array([[7, -1], [2, 3]], np.int32), gpu)          # 7 and -1: not pages of a 4-page pool
+    rng = np.random.default_rng(3)
+    k = to_dev(_kv(rng, 2, h_kv).reshape(2, 1, h_kv, D), gpu)
+    v = to_dev(_kv(rng, 2, h_kv).reshape(2, 1, h_kv, D), gpu)
+    say("kv4_write guards")
+    qoq.kv4_write(k, v, to_dev(np.array([5, 128], np.int32), gpu), pt, pool)   # row 1: position past 2 pages
+    qoq.kv4_write(k, v, to_dev(np.array([70, -3], np.int32), gpu), pt, pool)   # row 0 -> page -1; row 1 negative
+    assert np.array_equal(host(pool), before)

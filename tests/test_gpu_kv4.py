@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from oracle import kv4_oracle as kv
+from tests.kv4_layout import layout_index as _layout_index
 from w4a8_mixed_precision_amd import qoq
 
 pytestmark = pytest.mark.gpu
@@ -37,30 +38,6 @@ def to_dev(a, dev):
 def host(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
-
-
-def _layout_index():
-    """Byte offset (within a (page, head) section) and bit shift of the K and V code
-    of every (slot t, dim d), from the documented page layout: 16-token block at
-    blk * 1024 (+ 4096 for V), lane slot 16 qd + t (K) or 16 qt + dd (V) at 16 bytes
-    each, word u, nibble k."""
-    t = np.arange(P)[:, None]
-    d = np.arange(D)[None, :]
-    blk, tt = t // 16, t % 16
-    # K: dim d = 16 (2u + (k >> 1 & 1)) + 4 qd + 2 (k & 1) + (k >> 2)
-    j, r = d // 16, d % 16
-    qd, rr = r // 4, r % 4
-    u, kpar = j // 2, j % 2
-    k = 4 * (rr % 2) + (rr // 2) + 2 * kpar
-    kb = blk * 1024 + (16 * qd + tt) * 16 + 4 * u + k // 2
-    ksh = 4 * (k % 2)
-    # V: token 4 qt + 2 (k & 1) + (k >> 2) of dim 16 (2u + (k >> 1 & 1)) + dd
-    qt, ti = tt // 4, tt % 4
-    dd = d % 16
-    k = 4 * (ti % 2) + (ti // 2) + 2 * kpar
-    vb = 4096 + blk * 1024 + (16 * qt + dd) * 16 + 4 * u + k // 2
-    vsh = 4 * (k % 2)
-    return kb, np.broadcast_to(ksh, kb.shape), vb, np.broadcast_to(vsh, vb.shape)
 
 
 def read_pages(pool, page_ids, h_kv, ntok):

@@ -413,9 +413,75 @@ def copy_ceiling(q, torch, dev, nbytes=1 << 30, reps=10):
     return {"bytes_per_launch": 2 * nbytes, "us": t * 1e6, "GBps": 2 * nbytes / t / 1e9}
 
 
-def sweep(q, torch, dev, launches, per_channel=False):
+class ReadCeiling:
+    """The library's streaming-read kernel over the same byte count as a case, on
+    slices of one 1 GiB buffer taken in rotation (so the MALL and L2 do not serve
+    them): the practical HBM read ceiling at that size."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(ROTATE_BYTES + (64 << 20), dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def gbps(self, q, torch, nbytes, launches):
+        nbytes = (nbytes + 4095) // 4096 * 4096
+        nsl = max(2, ROTATE_BYTES // nbytes)
+
+        def one():
+            off = (self.i % nsl) * nbytes
+            self.i += 1
+            q.stream_read(self.buf[off:off + nbytes], self.sink)
+        one()
+        torch.cuda.synchronize()
+        return nbytes / time_launches(one, launches, torch) / 1e9
+
+
+def mfma_ceiling(q, torch, dev, iters=2000, blocks=2048):
+    """INT8 ops/s of the library's register-only MFMA loop (practical matrix-core
+    ceiling): blocks x 4 waves x iters x 4 MFMAs x 65536 ops."""
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    q.mfma_peak(iters, blocks, sink)
+    t = time_launches(lambda: q.mfma_peak(iters, blocks, sink), 3, torch, reps=3)
+    return blocks * 4 * iters * 4 * 65536 / t / 1e12
+
+
+def oracle_case(L, M, per_channel=False, cols=256):
+    """Seconds of the CPU oracle (unchanged) for one case, by stage: activation
+    quantization over the whole [M, K]; weight quantization, dequantization,
+    contraction (fp64, exact) and epilogue on `cols` output columns, scaled by N / cols
+    (every stage is linear in N)."""
+    import numpy as np
+    from oracle import qoq_oracle as o
+    from w4a8_mixed_precision_amd import workloads as wl
+    ns = min(cols, L.N)
+    w16 = wl.weights_fp16(L, N=ns)            # the first ns rows of the layer's W
+    x16 = wl.activations_fp16(L, M)
+    t = {}
+    t0 = time.perf_counter()
+    qx, s_x = o.quantize_activations(x16)
+    t["act_quant_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    q0, s_w = o.quantize_weights_level0(w16)
+    q_u4, z, s_u8 = o.quantize_weights_level1(q0)
+    t["pack_s"] = (time.perf_counter() - t0) * L.N / ns
+    t0 = time.perf_counter()
+    w_hat = o.dequantize_level1(q_u4, z, s_u8)
+    acc = o.contract(qx, w_hat)
+    t["contract_s"] = (time.perf_counter() - t0) * L.N / ns
+    t0 = time.perf_counter()
+    o.epilogue(acc, s_x, s_w)
+    t["epilogue_s"] = (time.perf_counter() - t0) * L.N / ns
+    t["step_s"] = t["act_quant_s"] + t["contract_s"] + t["epilogue_s"]
+    t["sample"] = f"{ns} of {L.N} columns, scaled"
+    return {k: (round(v, 6) if isinstance(v, float) else v) for k, v in t.items()}
+
+
+def sweep(q, torch, dev, launches, per_channel=False, with_oracle=True):
     from w4a8_mixed_precision_amd import workloads as wl
     rows = []
+    ceil = ReadCeiling(torch, dev)
+    mfma_tops = mfma_ceiling(q, torch, dev)
+    print(json.dumps({"mfma_ceiling_TOPS": mfma_tops}), flush=True)
     for L in wl.LAYERS:
         sets, pack_s = packed_sets_for(L, dev, q, per_channel=per_channel)
         for M in L.Ms:
@@ -425,6 +491,11 @@ def sweep(q, torch, dev, launches, per_channel=False):
             torch.cuda.synchronize()
             r = run_case_metrics(c, q, torch, launches)
             r.update({"layer": L.name, "pack_ms": pack_s * 1e3})
+            rc = ceil.gbps(q, torch, c.bytes["total"], launches)
+            r.update({"read_ceiling_GBps": rc, "hbm_frac_of_ceiling": r["total_GBps"] / rc,
+                      "mfma_ceiling_TOPS": mfma_tops, "mfma_frac_of_ceiling": r["TOPS"] / mfma_tops})
+            if with_oracle:
+                r["oracle"] = oracle_case(L, M, per_channel)
             rows.append(r)
             print(json.dumps(r), flush=True)
             del c
@@ -456,7 +527,7 @@ def main():
         kv4_bench(qoq, torch, dev, args.kernel_launches)
         return
     if args.sweep:
-        sweep(qoq, torch, dev, args.kernel_launches, args.format == "channel")
+        sweep(qoq, torch, dev, args.kernel_launches, args.format == "channel", not args.no_cpu_baseline)
         return
     if args.format != "group":
         print("the headline line measures the per-group format; use --format channel with --sweep",

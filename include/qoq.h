@@ -364,8 +364,8 @@ int qoq_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, void *stream);
 
 /* MFMA-only throughput kernel: `blocks` workgroups of 4 waves, each wave running
- * `iters` rounds of 8 independent v_mfma_i32_16x16x64_i8 on register operands
- * (32768 INT8 ops each).  Measures the practical INT8 matrix-core ceiling; `sink`
+ * `iters` rounds of 4 independent v_mfma_i32_32x32x32_i8 on register operands
+ * (65536 INT8 ops each; 262144 ops per wave per round).  Measures the practical INT8 matrix-core ceiling; `sink`
  * (4 bytes, device) is written only in a case that does not occur.
  * Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_mfma_peak(int iters, int blocks, void *sink, void *stream);

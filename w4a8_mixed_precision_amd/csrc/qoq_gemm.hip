@@ -218,6 +218,169 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Skinny regime on 32x32x32 MFMAs (17..64 tokens).  On gfx950 the 16x16x64 INT8
+// instruction delivers about 60 % of the ops per cycle of v_mfma_i32_32x32x32_i8,
+// so row blocks of 32 halve the matrix-core time of the few-token kernel where it
+// shows (64 tokens).  Same split of the K groups over the waves, same batches and
+// ring as above; a workgroup owns NP pairs of strips (32 columns each) and 32*MT2
+// rows.  B operand of one pair (lane l: column l % 32, k = 16*(l / 32) + i of a
+// 32-wide k block): slots 16*(l / 32) + c and 16*(l / 32) + 32 + c of the strip
+// holding column l % 32 (c = l % 16) give, from their low and high nibbles, the four
+// 32-wide k blocks of the group.  A operand (row l % 32 of the block, same k): 16
+// bytes per lane per k block, from the tiled layout (two 16-row blocks) or the row.
+// Result: lane l, register i holds D[8*(i / 4) + 4*(l / 32) + i % 4][l % 32].
+// ---------------------------------------------------------------------------
+template <int MT2, int NP, int U>
+struct Skinny32Batch {
+  uint4 p0[U][NP], p1[U][NP];
+  unsigned md[U][NP];
+  v4i a[U][MT2][4];
+};
+
+template <int MT2, int NP, int WAVES, int U, bool PC, bool AT>
+__device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int b, int ngroups, int wave,
+                                              const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
+                                              const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
+                                              int M, int m0, int lane) {
+  const int c32 = lane & 31, hi = lane >> 5, col = lane & 15;
+  const v4i zero4 = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = b * U + u;
+    const bool ok = t < ngroups;
+    // past the wave's last group: in-bounds weight reload, zero activations
+    const int j = wave + WAVES * (ok ? t : 0);
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+      const size_t chunk = static_cast<size_t>(min(strip0 + 2 * np + (c32 >> 4), NS - 1)) * G + j;
+      B.p0[u][np] = packed[chunk * 64 + 16 * hi + col];
+      B.p1[u][np] = packed[chunk * 64 + 16 * hi + 32 + col];
+      B.md[u][np] = PC ? 0u : meta_pair(meta, chunk, col);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt) {
+      const int r = m0 + 32 * mt + c32;
+      const bool oka = ok && r < M;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int8_t *a =
+            AT ? qx + ((static_cast<size_t>(r >> 4) * (K >> 6) + 2 * j + (kb >> 1)) * 64 + ((2 * kb + hi) & 3) * 16 +
+                       (r & 15)) * 16
+               : qx + static_cast<size_t>(oka ? r : 0) * K + 128 * j + 32 * kb + 16 * hi;
+        B.a[u][mt][kb] = oka ? *reinterpret_cast<const v4i *>(a) : zero4;
+      }
+    }
+  }
+}
+
+template <int MT2, int NP, int U, bool PC>
+__device__ __forceinline__ void skinny32_compute(const Skinny32Batch<MT2, NP, U> &B, v16i (&acc)[MT2][NP],
+                                                 int col) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+      v4i b[4];
+      weights_lane<PC>(B.p0[u][np], meta_of(B.md[u][np], col), b[0], b[2]);
+      weights_lane<PC>(B.p1[u][np], meta_of(B.md[u][np], col), b[1], b[3]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) acc[mt][np] = mfma32x32x32(B.a[u][mt][kb], b[kb], acc[mt][np]);
+    }
+}
+
+template <int MT2, int NP, int WAVES, int U, int R, int OUT, bool PC, bool AT = false>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
+    const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
+    const uint16_t *__restrict__ meta, const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
+    const int *__restrict__ trow, void *__restrict__ out, int M, int N, int K, int, int *) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = K >> 7;
+  const int NS = N >> 4;
+  const int col = lane & 15;
+  const int strip0 = blockIdx.x * 2 * NP;
+  const int m0 = blockIdx.y * (32 * MT2);
+
+  v16i acc[MT2][NP];
+#pragma unroll
+  for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+    for (int np = 0; np < NP; ++np) acc[mt][np] = v16i{};
+
+  const int ngroups = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
+  const int nbatch = (ngroups + U - 1) / U;
+
+  Skinny32Batch<MT2, NP, U> ring[R];
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r)
+    if (r < nbatch)
+      skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M,
+                                               m0, lane);
+  for (int b0 = 0; b0 < nbatch; b0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int b = b0 + r;
+      if (b >= nbatch) break;
+      if (b + R - 1 < nbatch)
+        skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
+                                                 strip0, NS, G, K, M, m0, lane);
+      skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col);
+    }
+  }
+
+  constexpr int T = MT2 * NP;   // 32x32 tiles per wave
+  if constexpr (WAVES > 1) {
+    __shared__ int red[WAVES][T * 16][64];
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+      for (int np = 0; np < NP; ++np)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[wave][(mt * NP + np) * 16 + i][lane] = acc[mt][np][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < T * 1024; e += 64 * WAVES) {
+      const int ln = e & 63;
+      const int ti = e >> 6;
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) sum += red[w][ti][ln];
+      const int t = ti >> 4, i = ti & 15;
+      const int mt = t / NP, np = t % NP;
+      const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+      const int c = ln & 31;
+      const int strip = strip0 + 2 * np + (c >> 4);
+      if (m < M && strip < NS) {
+        const int n = strip * 16 + (c & 15);
+        float scale = 0.0f;
+        if (OUT == 0) scale = __half2float(sx[m]) * __half2float(sw[n]);
+        if (PC) sum -= static_cast<int>(zp[n]) * trow[m];
+        store_result(out, OUT, static_cast<size_t>(m) * N + n, sum, scale);
+      }
+    }
+  } else {
+    const int c = lane & 31;
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+      for (int np = 0; np < NP; ++np)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const int strip = strip0 + 2 * np + (c >> 4);
+          if (m < M && strip < NS) {
+            const int n = strip * 16 + (c & 15);
+            float scale = 0.0f;
+            if (OUT == 0) scale = __half2float(sx[m]) * __half2float(sw[n]);
+            const int v = acc[mt][np][i] - (PC ? static_cast<int>(zp[n]) * trow[m] : 0);
+            store_result(out, OUT, static_cast<size_t>(m) * N + n, v, scale);
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Few tokens with the activation quantization fused in (the linear entry point,
 // few rows x K).  The workgroup quantizes the token rows itself, with the routines
 // of the standalone quantizer (per-token absmax, fp16 scale, codes), so codes and
@@ -1129,8 +1292,9 @@ typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const 
                            const uint8_t *, const int *, void *, int, int, int, int, int *);
 
 struct Config {
-  int kind;                 // 0 skinny, 4 wide2, 5 dma2, 6 shared dequantization
-  int a, b, c, d, e;        // skinny: MT, NBW, WAVES, U, R    wide2 / dma2: TM, TN    sd: A stages
+  int kind;                 // 0 skinny, 7 skinny on 32x32 blocks, 4 wide2, 5 dma2, 6 shared dequantization
+  int a, b, c, d, e;        // skinny: MT, NBW, WAVES, U, R   skinny32: MT2, NP, WAVES, U, R
+                            // wide2 / dma2: TM, TN   sd: A stages
   GemmKernel k[2][2];       // [per-group, per-channel][fp16 epilogue, INT32 epilogue]
   const char *name;
   int lds = 0;              // dynamic LDS bytes
@@ -1146,6 +1310,9 @@ struct Config {
 #define QOQ_SKINNY_R(MT, NBW, W, U, R)                                                      \
   {0, MT, NBW, W, U, R, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U, R),                          \
    "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U "_r" #R, 0, QOQ_KT(gemm_skinny_kernel<MT, NBW, W, U, R)},
+#define QOQ_SKINNY32(MT2, NP, W, U, R)                                                                  \
+  {7, MT2, NP, W, U, R, QOQ_K4(gemm_skinny32_kernel<MT2, NP, W, U, R),                                   \
+   "skinny32_mt" #MT2 "_np" #NP "_w" #W "_u" #U "_r" #R, 0, QOQ_KT(gemm_skinny32_kernel<MT2, NP, W, U, R)},
 #define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
 #define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
 #define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
@@ -1160,6 +1327,8 @@ const Config kConfigs[] = {
     QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 1, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3)
+    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
+    QOQ_SKINNY32(1, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(2) QOQ_SD(3)
@@ -1210,7 +1379,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   const Config *cfg = nullptr;
   if (const char *name = getenv("QOQ_GEMM_CONFIG")) {
     for (int i = 0; i < kNumConfigs; ++i)
-      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kind == 0)) cfg = &kConfigs[i];
+      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kt[0])) cfg = &kConfigs[i];
   }
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
@@ -1229,15 +1398,25 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
       //           workgroup with 8 K-split waves, the rest two strips and 16 waves
       //  M <= 64: long K (>= 64 groups): at most two row blocks per workgroup;
       //           short K: all row blocks in one workgroup, 4 strips once N is wide
+      //  17..64 tokens: 32-row blocks on the 32x32x32 MFMA (about 60 % more INT8
+      //           ops per cycle than 16x16x64): wide layers two strip pairs per
+      //           workgroup (one 32-row block up to 32 tokens, two beyond); long K
+      //           one pair with two groups per batch (two pairs for the widest of
+      //           them past 48 tokens); short narrow layers the same up to 32 tokens
+      //           and past 48, 16-row blocks between
       const int mt = static_cast<int>(M >= 64 ? 4 : (M + 15) / 16);   // grid.y covers rows past 64
       if (mt <= 1) {
         cfg = (NS >= 640 && G <= 64) ? find_config(0, 1, 1, 8, 2) : find_config(0, 1, 2, 16, 2);
+      } else if (NS >= 640) {
+        cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2);
       } else if (G >= 64) {
-        cfg = find_config(0, 2, 2, 8, 2);
-      } else if (mt == 4) {
-        cfg = NS >= 1024 ? find_config(0, 4, 4, 8, 1) : find_config(0, 4, 2, 8, 1);
-      } else {
+        cfg = (M <= 48 || NS < 512) ? find_config(7, 1, 1, 8, 2, 2) : find_config(7, 1, 2, 8, 1, 2);
+      } else if (M <= 32) {
+        cfg = find_config(7, 1, 1, 8, 2, 2);
+      } else if (M <= 48) {
         cfg = find_config(0, mt, 2, 8, 2);
+      } else {
+        cfg = find_config(7, 1, 2, 8, 1, 2);
       }
     } else {
       // measured on MI355X over the layer shapes of the workloads: the largest tile
@@ -1271,6 +1450,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   if (cfg->kind == 0) {
     const int mt = cfg->a, nbw = cfg->b, waves = cfg->c;
     p.grid = dim3(static_cast<unsigned>((NS + nbw - 1) / nbw), static_cast<unsigned>((M + 16 * mt - 1) / (16 * mt)));
+    p.block = dim3(64 * waves);
+  } else if (cfg->kind == 7) {
+    const int mt2 = cfg->a, np = cfg->b, waves = cfg->c;
+    p.grid = dim3(static_cast<unsigned>((NS + 2 * np - 1) / (2 * np)),
+                  static_cast<unsigned>((M + 32 * mt2 - 1) / (32 * mt2)));
     p.block = dim3(64 * waves);
   } else if (cfg->kind == 6) {   // 256 x 256 tiles, 8 waves
     const int64_t tiles = ((NS + 15) / 16) * ((M + 255) / 256);

@@ -337,13 +337,11 @@ class KvCase:
         perm = np.random.default_rng(S.B * 7 + S.seq_len).permutation(set_pages).astype(np.int32).reshape(S.B, mp)
         self.tables = [torch.from_numpy(perm + i * set_pages).to(dev) for i in range(self.nsets)]
         base = self.pool[:set_bytes]
-        zero = torch.zeros(S.B, dtype=torch.int32, device=dev)
-        chunk = 4096                                   # tokens per write call while filling
-        for a in range(0, S.seq_len, chunk):
-            n = min(chunk, S.seq_len - a)
-            k = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 0)[a:a + n] for b in range(S.B)])).to(dev)
-            v = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 1)[a:a + n] for b in range(S.B)])).to(dev)
-            q.kv4_write(k, v, zero + a, self.tables[0], base)
+        self.zero = torch.zeros(S.B, dtype=torch.int32, device=dev)
+        # the whole cache written in one call (the prefill write), kept for timing it
+        self.k_all = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 0) for b in range(S.B)])).to(dev)
+        self.v_all = torch.from_numpy(np.stack([wl.kv_fp16(S, b, S.seq_len, 1) for b in range(S.B)])).to(dev)
+        q.kv4_write(self.k_all, self.v_all, self.zero, self.tables[0], base)
         for i in range(1, self.nsets):
             self.pool[i * set_bytes:(i + 1) * set_bytes].copy_(base)
         self.q = torch.from_numpy(wl.kv_queries_fp16(S)).to(dev)
@@ -371,6 +369,12 @@ class KvCase:
         self.i += 1
         q.kv4_write(self.k1, self.v1, self.pos, t, self.pool)
 
+    def write_all(self, q):
+        """The prefill write: every cached token of every sequence in one call."""
+        t = self.tables[self.i % self.nsets]
+        self.i += 1
+        q.kv4_write(self.k_all, self.v_all, self.zero, t, self.pool)
+
 
 def kv4_case_metrics(S, q, torch, dev, launches):
     from w4a8_mixed_precision_amd import workloads as wl
@@ -380,11 +384,14 @@ def kv4_case_metrics(S, q, torch, dev, launches):
     torch.cuda.synchronize()
     ta = time_launches(lambda: c.attend(q), launches, torch)
     tw = time_launches(lambda: c.write(q), launches, torch)
+    tp = time_launches(lambda: c.write_all(q), max(2, launches // 20), torch)
     r = {"shape": S.name, "B": S.B, "seq_len": S.seq_len, "h": S.h, "h_kv": S.h_kv, "splits": c.splits,
          "attention_us": ta * 1e6, "bytes_per_launch": c.bytes, "GBps": c.bytes / ta / 1e9,
          "hbm_frac": c.bytes / ta / 1e9 / HBM_PEAK_GBPS, "TFLOPs": c.flops / ta / 1e12,
          "tokens_per_s": S.B * S.seq_len / ta,
          "write_us": tw * 1e6, "write_bytes": S.B * S.h_kv * (4 * wl.KV_HEAD_DIM + wl.KV_TOKEN_HEAD_BYTES),
+         "prefill_write_us": tp * 1e6,
+         "prefill_write_GBps": S.B * S.seq_len * S.h_kv * (4 * wl.KV_HEAD_DIM + wl.KV_TOKEN_HEAD_BYTES) / tp / 1e9,
          "rotation_sets": c.nsets}
     del c
     torch.cuda.empty_cache()

@@ -196,8 +196,10 @@ int qoq_kv4_page_bytes(int64_t h_kv, int64_t head_dim, size_t *bytes);
  * widened to contain 0 (lo = min(0, min x), hi = max(0, max x)): s = fp16(fp32(hi -
  * lo) / 15), z = rne(-lo / s) in [0, 15], codes clamp(z + rne(x / s), 0, 15) (fp32
  * IEEE quotients; s = 0 for an all-zero vector, codes and z 0); s and z stored as
- * fp16.  One workgroup per (sequence, KV head) writes its tokens in order (a V byte
- * holds two tokens); calls for the same pages must not overlap.
+ * fp16.  One workgroup per (KV head, sequence, 16-token block of positions): a V
+ * word holds four tokens, so each block's words are assembled once, merged with the
+ * tokens already there; calls for the same pages must not overlap.  n_new <= 2^19,
+ * B <= 65535, the sequence's positions below 2^30.
  * Errors: INVALID, UNSUPPORTED, ALIGNMENT, HIP. */
 int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,
                   int64_t head_dim, const int32_t *positions, const int32_t *page_table,

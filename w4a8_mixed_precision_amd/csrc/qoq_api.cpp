@@ -187,7 +187,7 @@ int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new
                   int64_t num_pages, void *stream) {
   if (B < 0 || n_new < 0 || h_kv <= 0 || max_pages <= 0 || num_pages <= 0) return QOQ_ERR_INVALID;
   if (num_pages > INT32_MAX || max_pages > (int64_t{1} << 24)) return QOQ_ERR_UNSUPPORTED;
-  if (head_dim != 128 || h_kv > 1024 || B > 65535 || n_new > (int64_t{1} << 20)) return QOQ_ERR_UNSUPPORTED;
+  if (head_dim != 128 || h_kv > 1024 || B > 65535 || n_new > (int64_t{1} << 19)) return QOQ_ERR_UNSUPPORTED;
   if (B == 0 || n_new == 0) return QOQ_OK;
   if (!k_new || !v_new || !positions || !page_table || !kv_pool) return QOQ_ERR_INVALID;
   if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||

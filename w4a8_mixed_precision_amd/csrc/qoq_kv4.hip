@@ -102,13 +102,16 @@ __device__ __forceinline__ h2 neg_biased(unsigned zz, unsigned base) {
 }
 
 // ---------------------------------------------------------------------------
-// KV write: one wave per (sequence, KV head); the new tokens of the sequence one
-// after another.  Lane l quantizes dims 2l, 2l + 1.  Quantization (per token and
-// head): range widened to contain 0, s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s),
-// q = clamp(z + rne(x / s), 0, 15), fp32 IEEE quotients; s and z stored as fp16.
-// The codes go through LDS so that each 32-bit word of the page is written by one
-// lane: a K word holds one token (plain store), a V word four tokens (the lane that
-// owns the word updates its two nibbles of the token, for every token, in order).
+// KV write: one wave per (KV head, sequence, 16-token block of positions).  The
+// block is the one 16-token block of the page that the new tokens' positions fall
+// in (blockIdx.z counts blocks from the one holding the sequence's first new
+// position), so no two waves of a launch touch the same page words.  Lane l
+// quantizes dims 2l, 2l + 1 of each new token of the block in turn (per token and
+// head: range widened to contain 0, s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s),
+// q = clamp(z + rne(x / s), 0, 15), fp32 IEEE quotients; s and z stored as fp16)
+// and stages the codes in LDS; K words (one token each) are written per token, V
+// words (four tokens each) once for the block, merged with the nibbles of tokens
+// outside the new range.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
@@ -142,7 +145,7 @@ __device__ __forceinline__ void kv_quant2(float x0, float x1, unsigned &c0, unsi
 
 __device__ __forceinline__ unsigned half_bits(__half h) { return __builtin_bit_cast(unsigned short, h); }
 
-// Positions and page ids are data the host cannot check: a token whose position
+// Positions and page ids are data the host cannot check: a block whose position
 // falls outside the page table, or whose page id lies outside the pool, is skipped
 // (a bad table gives wrong contents, never an access outside the buffers).
 __global__ __launch_bounds__(64) void kv4_write_kernel(const __half *__restrict__ k_new,
@@ -150,53 +153,68 @@ __global__ __launch_bounds__(64) void kv4_write_kernel(const __half *__restrict_
                                                        const int *__restrict__ positions,
                                                        const int *__restrict__ page_table, int max_pages,
                                                        int num_pages, uint8_t *__restrict__ pool) {
-  __shared__ uint8_t kcode[kD], vcode[kD];
-  const int b = blockIdx.y, g = blockIdx.x, lane = threadIdx.x;
+  __shared__ uint8_t kcode[16][kD], vcode[16][kD];
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int pos0 = positions[b];                     // the same in every lane
+  if (pos0 < 0 || pos0 >= (1 << 30)) return;         // past any page table (max_pages <= 2^24)
+  const int blk = pos0 / 16 + static_cast<int>(blockIdx.z);     // absolute 16-token block
+  const int p_lo = max(pos0, 16 * blk), p_hi = min(pos0 + n_new, 16 * blk + 16);
+  if (p_lo >= p_hi || blk / 4 >= max_pages) return;
+  const int page = page_table[static_cast<size_t>(b) * max_pages + blk / 4];
+  if (page < 0 || page >= num_pages) return;
+  uint8_t *pg = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
+  const int pb = blk & 3;                            // block within the page
   const int d0 = 2 * lane;
-  for (int i = 0; i < n_new; ++i) {
-    const int pos = positions[b] + i;                  // the same in every lane
-    if (pos < 0 || pos / kP >= max_pages) continue;
-    const int page = page_table[static_cast<size_t>(b) * max_pages + pos / kP];
-    if (page < 0 || page >= num_pages) continue;
-    const int slot = pos % kP, blk = slot >> 4, t = slot & 15;
-    uint8_t *pg = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
-    const size_t src = ((static_cast<size_t>(b) * n_new + i) * h_kv + g) * kD + d0;
+  for (int p = p_lo; p < p_hi; ++p) {
+    const int t = p & 15, slot = p & 63;
+    const size_t src = ((static_cast<size_t>(b) * n_new + (p - pos0)) * h_kv + g) * kD + d0;
     const unsigned kw = *reinterpret_cast<const unsigned *>(k_new + src);
     const unsigned vw = *reinterpret_cast<const unsigned *>(v_new + src);
     unsigned c0, c1;
     __half ksh, kzh, vsh, vzh;
     kv_quant2(half_bits_to_float(kw & 0xffffu), half_bits_to_float(kw >> 16), c0, c1, ksh, kzh);
-    kcode[d0] = static_cast<uint8_t>(c0);
-    kcode[d0 + 1] = static_cast<uint8_t>(c1);
+    kcode[t][d0] = static_cast<uint8_t>(c0);
+    kcode[t][d0 + 1] = static_cast<uint8_t>(c1);
     kv_quant2(half_bits_to_float(vw & 0xffffu), half_bits_to_float(vw >> 16), c0, c1, vsh, vzh);
-    vcode[d0] = static_cast<uint8_t>(c0);
-    vcode[d0 + 1] = static_cast<uint8_t>(c1);
-    __syncthreads();
-    if (lane < 16) {                                   // K: word u of slot (qd, t), this token only
-      const int qd = lane >> 2, u = lane & 3;
-      unsigned w = 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int d = 16 * (2 * u + ((k >> 1) & 1)) + 4 * qd + 2 * (k & 1) + (k >> 2);
-        w |= static_cast<unsigned>(kcode[d]) << (4 * k);
-      }
-      *reinterpret_cast<unsigned *>(pg + kKCodes + blk * 1024 + (16 * qd + t) * 16 + 4 * u) = w;
-    }
-    {                                                  // V: word u of slot (qt, dd), two nibbles
-      const int dd = lane & 15, u = lane >> 4, qt = t >> 2, ti = t & 3;
-      const int k0 = 4 * (ti & 1) + (ti >> 1);         // nibble of dim 16 (2u) + dd; + 2 for 16 (2u + 1) + dd
-      unsigned *wp = reinterpret_cast<unsigned *>(pg + kVCodes + blk * 1024 + (16 * qt + dd) * 16 + 4 * u);
-      const unsigned keep = ~((0xfu << (4 * k0)) | (0xfu << (4 * k0 + 8)));
-      *wp = (*wp & keep) | (static_cast<unsigned>(vcode[32 * u + dd]) << (4 * k0)) |
-            (static_cast<unsigned>(vcode[32 * u + 16 + dd]) << (4 * k0 + 8));
-    }
+    vcode[t][d0] = static_cast<uint8_t>(c0);
+    vcode[t][d0 + 1] = static_cast<uint8_t>(c1);
     if (lane == 0) {
       *reinterpret_cast<unsigned *>(pg + kKStats + 4 * slot) = half_bits(ksh) | (half_bits(kzh) << 16);
       __half *vst = reinterpret_cast<__half *>(pg + kVStats + 16 * (slot >> 2));
       vst[slot & 3] = vsh;
       vst[4 + (slot & 3)] = vzh;
     }
-    __syncthreads();                                   // the staging bytes are reused by the next token
+    __syncthreads();
+    if (lane < 16) {                                 // K: word u of slot (qd, t), this token only
+      const int qd = lane >> 2, u = lane & 3;
+      unsigned w = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = 16 * (2 * u + ((k >> 1) & 1)) + 4 * qd + 2 * (k & 1) + (k >> 2);
+        w |= static_cast<unsigned>(kcode[t][d]) << (4 * k);
+      }
+      *reinterpret_cast<unsigned *>(pg + kKCodes + pb * 1024 + (16 * qd + t) * 16 + 4 * u) = w;
+    }
+  }
+  // V: lane slot L = lane (token quarter qt, dim dd), its four words; nibble k of
+  // word u holds token 4 qt + 2 (k & 1) + (k >> 2) of dim 16 (2u + (k >> 1 & 1)) + dd
+  const int qt = lane >> 4, dd = lane & 15;
+  const int t_lo = p_lo - 16 * blk, t_hi = p_hi - 16 * blk;
+  if (4 * qt + 4 <= t_lo || 4 * qt >= t_hi) return;  // none of this slot's tokens is new
+  const bool whole = 4 * qt >= t_lo && 4 * qt + 4 <= t_hi;
+  unsigned *wp = reinterpret_cast<unsigned *>(pg + kVCodes + pb * 1024 + lane * 16);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    unsigned w = whole ? 0u : wp[u];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = 4 * qt + 2 * (k & 1) + (k >> 2);
+      if (t >= t_lo && t < t_hi) {
+        const int d = 16 * (2 * u + ((k >> 1) & 1)) + dd;
+        w = (w & ~(0xfu << (4 * k))) | (static_cast<unsigned>(vcode[t][d]) << (4 * k));
+      }
+    }
+    wp[u] = w;
   }
 }
 
@@ -521,7 +539,9 @@ size_t kv4_workspace_need(int64_t B, int64_t h, int64_t h_kv, int64_t max_len) {
 void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,
                       const int *positions, const int *page_table, int64_t max_pages, int64_t num_pages, void *pool,
                       hipStream_t st) {
-  hipLaunchKernelGGL(kv4_write_kernel, dim3(static_cast<unsigned>(h_kv), static_cast<unsigned>(B)), dim3(64), 0, st,
+  // 16-token blocks spanned by n_new consecutive positions from any start
+  const unsigned nz = static_cast<unsigned>((n_new + 14) / 16 + 1);
+  hipLaunchKernelGGL(kv4_write_kernel, dim3(static_cast<unsigned>(h_kv), static_cast<unsigned>(B), nz), dim3(64), 0, st,
                      static_cast<const __half *>(k_new), static_cast<const __half *>(v_new), static_cast<int>(n_new),
                      static_cast<int>(h_kv), positions, page_table, static_cast<int>(max_pages),
                      static_cast<int>(num_pages), static_cast<uint8_t *>(pool));

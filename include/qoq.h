@@ -205,6 +205,30 @@ int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new
                   int64_t head_dim, const int32_t *positions, const int32_t *page_table,
                   int64_t max_pages, void *kv_pool, int64_t num_pages, void *stream);
 
+/* SmoothAttention, offline ("QServe: W4A8KV4 ..." summary, SmoothAttention: the keys'
+ * outlier channels are scaled down by lambda and the queries up by the same factor,
+ * Z = (Q Lambda)(K Lambda^-1)^T; review §4.2: folded into W_Q and W_K, no runtime
+ * cost).  Scales from key samples: k_samples fp16 [n, h_kv, 128] (2-byte aligned),
+ * lambda_f32 out [h_kv, 128] (4-byte aligned): for channel i of KV head g,
+ * a_i = max_n |k[n, g, i]|, and the RoPE pair (i, i + 64) shares
+ * lambda = max(a_i, a_{i+64})^alpha (alpha = 0.5: the IEEE fp32 square root; other
+ * alpha in [0, 1]: the double-precision power rounded to fp32); a pair that is 0 on
+ * every sample keeps lambda = 1.  One workgroup per KV head (offline use).
+ * Errors: INVALID (n, h_kv < 1, alpha outside [0, 1]), UNSUPPORTED (head_dim != 128,
+ * h_kv > 65535, n * h_kv > 2^30), ALIGNMENT, HIP. */
+int qoq_smooth_attention_lambda(const void *k_samples, int64_t n, int64_t h_kv, int64_t head_dim,
+                                float alpha, void *lambda_f32, void *stream);
+
+/* Folds lambda into the projections: w_q fp16 [h * 128, d_model] row-major (the query
+ * heads' output channels), w_k fp16 [h_kv * 128, d_model]; row (head, i) of w_q becomes
+ * fp16(fp32(w) * lambda[head / (h / h_kv), i]) and row (g, i) of w_k becomes
+ * fp16(w / lambda[g, i]) (IEEE fp32 quotient).  Outputs may be the inputs (in place).
+ * Errors: INVALID (h % h_kv, sizes < 1, null pointers), UNSUPPORTED (head_dim != 128,
+ * h > 4096, d_model > 2^20), ALIGNMENT (2-byte weights, 4-byte lambda), HIP. */
+int qoq_smooth_attention_fold(const void *w_q, const void *w_k, const void *lambda_f32, int64_t h,
+                              int64_t h_kv, int64_t head_dim, int64_t d_model, void *w_q_out,
+                              void *w_k_out, void *stream);
+
 /* Workspace for qoq_kv4_decode_attention (0 when one workgroup per (sequence, KV
  * head) covers the sequence): split partials, no initialization needed.
  * Errors: INVALID, UNSUPPORTED. */

@@ -38,6 +38,17 @@ R19 Decode attention over the dequantized values is the plain definition, comput
     CUDA-core math mapped to MI355X matrix cores); the comparison tolerance follows
     from that arithmetic (design notes).
 
+R20 SmoothAttention (the summary's SmoothAttention section, its scaling equation and
+    the RoPE constraint; review §4.2): per KV head g and channel i over key samples,
+    a_i = max_n |K[n, g, i]| (exact), the RoPE pair (i, i + D/2) shares
+    lambda_i = lambda_{i+D/2} = max(a_i, a_{i+D/2})^alpha; alpha = 0.5 (the pages'
+    choice) is the IEEE fp32 square root, other alpha the fp64 power rounded to fp32;
+    a pair that never leaves 0 keeps lambda = 1 (the pages leave it open; 1 is the
+    identity).  Folding: W_Q rows of query head h, channel i become fp16(fp32(w) *
+    lambda[h // r, i]), W_K rows of KV head g, channel i become fp16(w / lambda[g, i])
+    (fp32 IEEE quotient), so q' . k' = q . k before rounding (Z = (Q Lambda)(K
+    Lambda^-1)^T).
+
 Pins: tests/test_oracle_kv4_pins.py.
 """
 
@@ -95,3 +106,29 @@ def attention_reference(q16, k16, v16, h_kv: int):
     kq, ks, kz = kv_quantize(k16)
     vq, vs, vz = kv_quantize(v16)
     return decode_attention(q16, kv_dequantize(kq, ks, kz), kv_dequantize(vq, vs, vz), h_kv)
+
+
+def smooth_attention_lambda(k16: np.ndarray, alpha: float = 0.5) -> np.ndarray:
+    """R20: lambda fp32 [H_KV, D] from key samples fp16 [n, H_KV, D]."""
+    a = np.abs(np.asarray(k16, np.float16).astype(np.float32)).max(axis=0)      # [H_KV, D], exact
+    D = a.shape[-1]
+    pair = np.maximum(a[:, : D // 2], a[:, D // 2:])
+    if alpha == 0.5:
+        lam = np.sqrt(pair)                                                      # IEEE fp32 square root
+    else:
+        lam = np.power(pair.astype(np.float64), float(alpha)).astype(np.float32)
+    lam = np.where(pair == 0, np.float32(1), lam).astype(np.float32)
+    return np.concatenate([lam, lam], axis=1)
+
+
+def smooth_attention_fold(wq16: np.ndarray, wk16: np.ndarray, lam: np.ndarray, h: int, h_kv: int):
+    """R20: fold Lambda into the query and key projections.  wq16 fp16 [h*D, d_model],
+    wk16 fp16 [h_kv*D, d_model], lam fp32 [h_kv, D] -> (wq', wk') fp16."""
+    lam = np.asarray(lam, np.float32)
+    D = lam.shape[1]
+    r = h // h_kv
+    row_q = np.repeat(lam, r, axis=0).reshape(h * D, 1)      # query head hq uses KV head hq // r
+    row_k = lam.reshape(h_kv * D, 1)
+    wq = (np.asarray(wq16, np.float16).astype(np.float32) * row_q).astype(np.float16)
+    wk = (np.asarray(wk16, np.float16).astype(np.float32) / row_k).astype(np.float16)
+    return wq, wk

@@ -340,3 +340,17 @@ def test_kv4_validation(L):
     assert at(*args(out=ODD)) == ALIGNMENT
     assert at(*args(B=1, ml=4096, mp=64)) == WORKSPACE                      # needs split partials
     assert at(*args(np_=0)) == INVALID and wr(FAKE, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, FAKE, 0, NUL) == INVALID
+
+
+def test_smooth_attention_validation(L):
+    lam = L.qoq_smooth_attention_lambda
+    assert lam(FAKE, 0, 8, 128, ctypes.c_float(0.5), FAKE, NUL) == INVALID
+    assert lam(FAKE, 10, 8, 128, ctypes.c_float(1.5), FAKE, NUL) == INVALID
+    assert lam(FAKE, 10, 8, 64, ctypes.c_float(0.5), FAKE, NUL) == UNSUPPORTED
+    assert lam(ODD, 10, 8, 128, ctypes.c_float(0.5), FAKE, NUL) == ALIGNMENT
+    fold = L.qoq_smooth_attention_fold
+    assert fold(FAKE, FAKE, FAKE, 30, 8, 128, 4096, FAKE, FAKE, NUL) == INVALID      # h % h_kv
+    assert fold(FAKE, FAKE, FAKE, 32, 8, 64, 4096, FAKE, FAKE, NUL) == UNSUPPORTED
+    assert fold(FAKE, FAKE, NUL, 32, 8, 128, 4096, FAKE, FAKE, NUL) == INVALID
+    assert fold(FAKE, FAKE, ODD, 32, 8, 128, 4096, FAKE, FAKE, NUL) == ALIGNMENT
+

@@ -170,3 +170,44 @@ def test_kv4_write_guards(gpu):
     qoq.kv4_write(k, v, to_dev(np.array([5, 128], np.int32), gpu), pt, pool)   # row 1: position past 2 pages
     qoq.kv4_write(k, v, to_dev(np.array([70, -3], np.int32), gpu), pt, pool)   # row 0 -> page -1; row 1 negative
     assert np.array_equal(host(pool), before)
+
+
+# ---------------------------------------------------------------------------
+# SmoothAttention (offline scales and folding)
+# ---------------------------------------------------------------------------
+def _key_samples(rng, n, h_kv):
+    k = rng.standard_normal((n, h_kv, D)).astype(np.float32)
+    k[:, :, rng.choice(D, 4, replace=False)] *= 12.0
+    k[:, 1 % h_kv, [9, 9 + D // 2]] = 0.0                   # a pair that is always 0
+    return k.astype(np.float16)
+
+
+@pytest.mark.parametrize("n,h_kv", [(1, 1), (37, 2), (4096, 8), (65536, 8)])
+def test_smooth_lambda_exact(gpu, n, h_kv):
+    rng = np.random.default_rng(n + h_kv)
+    k = _key_samples(rng, n, h_kv)
+    dk = to_dev(k, gpu)
+    say(f"smooth lambda n={n} h_kv={h_kv}")
+    for alpha in (0.5, 0.0):
+        got = host(qoq.smooth_attention_lambda(dk, alpha))
+        assert np.array_equal(got.view(np.uint32), kv.smooth_attention_lambda(k, alpha).view(np.uint32))
+    got = host(qoq.smooth_attention_lambda(dk, 0.3)).astype(np.float64)
+    want = kv.smooth_attention_lambda(k, 0.3).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 2.0 ** -23 * want)  # the double power rounded to fp32: one ulp
+
+
+@pytest.mark.parametrize("h,h_kv,dm", [(32, 8, 4096), (8, 8, 640), (16, 1, 1152)])
+def test_smooth_fold_exact(gpu, h, h_kv, dm):
+    rng = np.random.default_rng(h * 7 + dm)
+    wq = (rng.standard_normal((h * D, dm)) * 0.05).astype(np.float16)
+    wk = (rng.standard_normal((h_kv * D, dm)) * 0.05).astype(np.float16)
+    lam = kv.smooth_attention_lambda(_key_samples(rng, 300, h_kv), 0.5)
+    say(f"smooth fold h={h} h_kv={h_kv} d_model={dm}")
+    want_q, want_k = kv.smooth_attention_fold(wq, wk, lam, h, h_kv)
+    dq, dk, dl = to_dev(wq, gpu), to_dev(wk, gpu), to_dev(lam, gpu)
+    gq, gk = qoq.smooth_attention_fold(dq, dk, dl, h, h_kv)
+    assert np.array_equal(host(gq).view(np.uint16), want_q.view(np.uint16))
+    assert np.array_equal(host(gk).view(np.uint16), want_k.view(np.uint16))
+    qoq.smooth_attention_fold(dq, dk, dl, h, h_kv, inplace=True)
+    assert np.array_equal(host(dq).view(np.uint16), want_q.view(np.uint16))
+    assert np.array_equal(host(dk).view(np.uint16), want_k.view(np.uint16))

@@ -139,3 +139,85 @@ def test_attention_brute_force_python():
         for d in range(0, D, 17):
             ref = sum(w[t] * float(V[t, g, d]) for t in range(S)) / tot
             assert abs(o[h, d] - ref) <= 2.0 ** -11 * abs(ref) + 1e-7
+
+
+# ---------------------------------------------------------------------------
+# SmoothAttention (R20)
+# ---------------------------------------------------------------------------
+def _keys_with_outliers(rng, n=200, h_kv=2, D=128):
+    k = rng.standard_normal((n, h_kv, D)).astype(np.float32)
+    k[:, :, [5, 70, 100]] *= 10.0                            # fixed outlier channels per head
+    return k.astype(np.float16)
+
+
+def test_smooth_lambda_pairs_and_closed_form():
+    """lambda_i = lambda_{i+D/2} = sqrt(max(max|K_i|, max|K_{i+D/2}|)), computed here
+    by hand from the samples with Python floats."""
+    rng = np.random.default_rng(20)
+    k = _keys_with_outliers(rng)
+    lam = kv.smooth_attention_lambda(k, 0.5)
+    D = k.shape[2]
+    assert np.array_equal(lam[:, : D // 2], lam[:, D // 2:])
+    for g in range(k.shape[1]):
+        for i in (0, 5, 37, 63):
+            a = max(abs(float(x)) for x in k[:, g, i])
+            b = max(abs(float(x)) for x in k[:, g, i + D // 2])
+            want = np.float32(math.sqrt(max(a, b)))               # sqrt of an fp32 value, rounded to fp32
+            assert lam[g, i] == want and lam[g, i + D // 2] == want
+
+
+def test_smooth_lambda_alpha_zero_and_zero_channels():
+    rng = np.random.default_rng(21)
+    k = _keys_with_outliers(rng)
+    assert np.all(kv.smooth_attention_lambda(k, 0.0) == 1.0)
+    k[:, 0, 3] = 0
+    k[:, 0, 3 + 64] = 0
+    lam = kv.smooth_attention_lambda(k, 0.5)
+    assert lam[0, 3] == 1.0 and lam[0, 67] == 1.0            # a pair that never leaves 0
+
+
+def test_smooth_fold_preserves_scores_and_flattens_keys():
+    """(q Lambda) . (k Lambda^-1) = q . k: scores from the folded projections equal
+    the unfolded ones up to the fp16 rounding of the folded weights; the smoothed
+    keys' channel maxima are max|K_i| / lambda_i <= lambda_i, so the largest is the
+    square root of the largest raw maximum (outliers compressed)."""
+    rng = np.random.default_rng(22)
+    h, h_kv, D, dm = 4, 2, 128, 64
+    wq = (rng.standard_normal((h * D, dm)) * 0.05).astype(np.float16)
+    wk = (rng.standard_normal((h_kv * D, dm)) * 0.05).astype(np.float16)
+    wk[[5, 70, D + 100]] *= 10                               # key outlier channels from the weights
+    x = rng.standard_normal((300, dm)).astype(np.float16)
+    k = (x.astype(np.float64) @ wk.astype(np.float64).T).reshape(300, h_kv, D).astype(np.float16)
+    lam = kv.smooth_attention_lambda(k, 0.5)
+    wq2, wk2 = kv.smooth_attention_fold(wq, wk, lam, h, h_kv)
+    q = x.astype(np.float64) @ wq.astype(np.float64).T
+    kk = x.astype(np.float64) @ wk.astype(np.float64).T
+    q2 = x.astype(np.float64) @ wq2.astype(np.float64).T
+    k2 = x.astype(np.float64) @ wk2.astype(np.float64).T
+    for hq in range(h):
+        g = hq // (h // h_kv)
+        s1 = q[:, hq * D:(hq + 1) * D] @ kk[:, g * D:(g + 1) * D].T
+        s2 = q2[:, hq * D:(hq + 1) * D] @ k2[:, g * D:(g + 1) * D].T
+        scale = np.abs(q[:, hq * D:(hq + 1) * D]) @ np.abs(kk[:, g * D:(g + 1) * D]).T
+        assert np.all(np.abs(s2 - s1) <= 2.0 ** -9 * scale + 1e-12)   # two fp16 roundings of weights
+    kmax = np.abs(k.astype(np.float32)).max(axis=0)
+    smoothed = kmax / lam
+    assert np.all(smoothed <= lam * (1 + 2.0 ** -20))
+    assert np.isclose(smoothed.max(), math.sqrt(kmax.max()), rtol=2.0 ** -20)
+
+
+def test_smooth_reduces_kv4_attention_error():
+    """The method's purpose on keys with outlier channels: KV4 attention over
+    smoothed keys (queries scaled back) is closer to the unquantized attention."""
+    rng = np.random.default_rng(23)
+    n, h_kv, h, D = 256, 2, 4, 128
+    k = _keys_with_outliers(rng, n, h_kv, D)
+    v = rng.standard_normal((n, h_kv, D)).astype(np.float16)
+    q = rng.standard_normal((h, D)).astype(np.float16)
+    exact = kv.decode_attention(q, k, v, h_kv).astype(np.float64)
+    plain = kv.attention_reference(q, k, v, h_kv).astype(np.float64)
+    lam = kv.smooth_attention_lambda(k, 0.5)
+    ks = (k.astype(np.float32) / lam[None]).astype(np.float16)
+    qs = (q.astype(np.float32) * np.repeat(lam, h // h_kv, axis=0)).astype(np.float16)
+    smooth = kv.attention_reference(qs, ks, v, h_kv).astype(np.float64)
+    assert np.abs(smooth - exact).mean() < 0.5 * np.abs(plain - exact).mean()

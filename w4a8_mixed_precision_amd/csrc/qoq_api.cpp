@@ -198,6 +198,28 @@ int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new
   return launch_status();
 }
 
+int qoq_smooth_attention_lambda(const void *k_samples, int64_t n, int64_t h_kv, int64_t head_dim, float alpha,
+                                void *lambda_f32, void *stream) {
+  if (n < 1 || h_kv < 1 || !(alpha >= 0.0f && alpha <= 1.0f)) return QOQ_ERR_INVALID;
+  if (head_dim != 128 || h_kv > 65535 || n > (int64_t{1} << 30) / h_kv) return QOQ_ERR_UNSUPPORTED;
+  if (!k_samples || !lambda_f32) return QOQ_ERR_INVALID;
+  if (!aligned(k_samples, 2) || !aligned(lambda_f32, 4)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_smooth_lambda(k_samples, n, h_kv, alpha, lambda_f32, as_stream(stream));
+  return launch_status();
+}
+
+int qoq_smooth_attention_fold(const void *w_q, const void *w_k, const void *lambda_f32, int64_t h, int64_t h_kv,
+                              int64_t head_dim, int64_t d_model, void *w_q_out, void *w_k_out, void *stream) {
+  if (h < 1 || h_kv < 1 || d_model < 1 || h % h_kv != 0) return QOQ_ERR_INVALID;
+  if (head_dim != 128 || h > 4096 || d_model > (int64_t{1} << 20)) return QOQ_ERR_UNSUPPORTED;
+  if (!w_q || !w_k || !lambda_f32 || !w_q_out || !w_k_out) return QOQ_ERR_INVALID;
+  if (!aligned(w_q, 2) || !aligned(w_k, 2) || !aligned(lambda_f32, 4) || !aligned(w_q_out, 2) ||
+      !aligned(w_k_out, 2))
+    return QOQ_ERR_ALIGNMENT;
+  qoq::launch_smooth_fold(w_q, w_k, lambda_f32, h, h_kv, d_model, w_q_out, w_k_out, as_stream(stream));
+  return launch_status();
+}
+
 static int kv4_attn_checks(int64_t B, int64_t h, int64_t h_kv, int64_t head_dim, int64_t max_len, int64_t max_pages) {
   if (B < 0 || h <= 0 || h_kv <= 0 || max_len <= 0 || max_pages <= 0 || h % h_kv != 0) return QOQ_ERR_INVALID;
   if (head_dim != 128 || h / h_kv > 16 || B > 65535 || h_kv > 1024) return QOQ_ERR_UNSUPPORTED;

@@ -47,6 +47,9 @@ size_t kv4_workspace_need(int64_t B, int64_t h, int64_t h_kv, int64_t max_len);
 void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new, int64_t h_kv,
                       const int *positions, const int *page_table, int64_t max_pages, int64_t num_pages, void *pool,
                       hipStream_t stream);
+void launch_smooth_lambda(const void *k, int64_t n, int64_t h_kv, float alpha, void *lam, hipStream_t stream);
+void launch_smooth_fold(const void *wq, const void *wk, const void *lam, int64_t h, int64_t h_kv, int64_t dm,
+                        void *wq_out, void *wk_out, hipStream_t stream);
 void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, const int *page_table,
                           int64_t max_pages, const int *seq_lens, int64_t B, int64_t h, int64_t h_kv,
                           int64_t max_len, void *out, void *ws, hipStream_t stream);

@@ -520,6 +520,66 @@ __global__ __launch_bounds__(64) void kv4_combine_kernel(const float *__restrict
   *reinterpret_cast<__half2 *>(out + static_cast<size_t>(row) * kD + 2 * lane) = r;
 }
 
+// ---------------------------------------------------------------------------
+// SmoothAttention ("QServe: W4A8KV4 ..." summary, SmoothAttention: Z = (Q Lambda)
+// (K Lambda^-1)^T, lambda_i = max|K_i|^alpha with the RoPE pair constraint
+// lambda_i = lambda_{i+D/2} = max(max|K_i|, max|K_{i+D/2}|)^alpha; review §4.2:
+// folded offline into the query and key projections).  Offline kernels: the
+// scales from key samples, and the folding into W_Q, W_K.
+// ---------------------------------------------------------------------------
+constexpr int kSmoothRowGroups = 8;                // sample rows split over the waves of a workgroup
+
+// one workgroup per KV head: 8 x 128 threads (row group, dim) take the channel
+// maxima over the samples, then the pair maximum and its power; a pair that never
+// leaves 0 keeps lambda = 1
+__global__ __launch_bounds__(kSmoothRowGroups * kD) void smooth_lambda_kernel(const __half *__restrict__ k, int n,
+                                                                             int h_kv, float alpha,
+                                                                             float *__restrict__ lam) {
+  __shared__ float part[kSmoothRowGroups][kD];
+  const int g = blockIdx.x, d = threadIdx.x % kD, rg = threadIdx.x / kD;
+  float m = 0.0f;
+#pragma unroll 4
+  for (int i = rg; i < n; i += kSmoothRowGroups)
+    m = fmaxf(m, fabsf(__half2float(k[(static_cast<size_t>(i) * h_kv + g) * kD + d])));
+  part[rg][d] = m;
+  __syncthreads();
+  if (threadIdx.x < kD / 2) {
+    float p = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kSmoothRowGroups; ++r) p = fmaxf(p, fmaxf(part[r][d], part[r][d + kD / 2]));
+    float l;
+    if (p == 0.0f)
+      l = 1.0f;
+    else if (alpha == 0.5f)
+      l = __builtin_sqrtf(p);                        // IEEE square root
+    else
+      l = static_cast<float>(pow(static_cast<double>(p), static_cast<double>(alpha)));
+    lam[g * kD + d] = l;
+    lam[g * kD + d + kD / 2] = l;
+  }
+}
+
+// W_Q rows of query head hq, channel i: fp16(fp32(w) * lambda[hq / r, i]); W_K rows
+// of KV head g, channel i: fp16(w / lambda[g, i]) (IEEE quotient).  In place allowed.
+__global__ __launch_bounds__(256) void smooth_fold_kernel(const __half *__restrict__ wq, const __half *__restrict__ wk,
+                                                         const float *__restrict__ lam, int h, int h_kv, int dm,
+                                                         __half *__restrict__ wq_out, __half *__restrict__ wk_out) {
+  const size_t nq = static_cast<size_t>(h) * kD * dm, nk = static_cast<size_t>(h_kv) * kD * dm;
+  const int r = h / h_kv;
+  for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < nq + nk;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    if (e < nq) {
+      const size_t row = e / dm;
+      const int hq = static_cast<int>(row / kD), i = static_cast<int>(row % kD);
+      wq_out[e] = mul_round_half(__half2float(wq[e]), lam[(hq / r) * kD + i]);
+    } else {
+      const size_t f = e - nq, row = f / dm;
+      const int g = static_cast<int>(row / kD), i = static_cast<int>(row % kD);
+      wk_out[f] = __float2half_rn(__fdiv_rn(__half2float(wk[f]), lam[g * kD + i]));
+    }
+  }
+}
+
 }  // namespace
 
 int kv4_splits(int64_t B, int64_t h_kv, int64_t max_len) {
@@ -566,6 +626,26 @@ void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, co
   if (splits > 1)
     hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(64), 0, st, wo, wml, splits,
                        static_cast<int>(B * h), static_cast<__half *>(out));
+}
+
+}  // namespace qoq
+
+namespace qoq {
+
+void launch_smooth_lambda(const void *k, int64_t n, int64_t h_kv, float alpha, void *lam, hipStream_t st) {
+  hipLaunchKernelGGL(smooth_lambda_kernel, dim3(static_cast<unsigned>(h_kv)), dim3(kSmoothRowGroups * kD), 0, st,
+                     static_cast<const __half *>(k), static_cast<int>(n), static_cast<int>(h_kv), alpha,
+                     static_cast<float *>(lam));
+}
+
+void launch_smooth_fold(const void *wq, const void *wk, const void *lam, int64_t h, int64_t h_kv, int64_t dm,
+                        void *wq_out, void *wk_out, hipStream_t st) {
+  const size_t total = static_cast<size_t>(h + h_kv) * kD * dm;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((total + 255) / 256, 8192));
+  hipLaunchKernelGGL(smooth_fold_kernel, dim3(blocks), dim3(256), 0, st, static_cast<const __half *>(wq),
+                     static_cast<const __half *>(wk), static_cast<const float *>(lam), static_cast<int>(h),
+                     static_cast<int>(h_kv), static_cast<int>(dm), static_cast<__half *>(wq_out),
+                     static_cast<__half *>(wk_out));
 }
 
 }  // namespace qoq

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "qoq_kv4_page_bytes": ([_c_i64, _c_i64, ctypes.POINTER(_c_sz)], ctypes.c_int),
     "qoq_kv4_write": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
                       ctypes.c_int),
+    "qoq_smooth_attention_lambda": ([_c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_smooth_attention_fold": ([_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+                                  ctypes.c_int),
     "qoq_kv4_attention_workspace_bytes": ([_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)],
                                           ctypes.c_int),
     "qoq_kv4_decode_attention": ([_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -341,6 +344,33 @@ def kv4_write(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor,
                                h_kv, D, _dev(positions, "positions", torch.int32),
                                _dev(page_table, "page_table", torch.int32), page_table.shape[1],
                                _dev(pool, "pool", torch.uint8), num_pages, _stream(k_new)))
+
+
+def smooth_attention_lambda(k_samples: torch.Tensor, alpha: float = 0.5, out=None):
+    """k_samples fp16 [n, h_kv, 128] -> lambda fp32 [h_kv, 128]."""
+    n, h_kv, D = k_samples.shape
+    lam = torch.empty((h_kv, D), dtype=torch.float32, device=k_samples.device) if out is None else out
+    _check("qoq_smooth_attention_lambda",
+           lib().qoq_smooth_attention_lambda(_dev(k_samples, "k_samples", torch.float16), n, h_kv, D, float(alpha),
+                                             _dev(lam, "lambda", torch.float32), _stream(k_samples)))
+    return lam
+
+
+def smooth_attention_fold(w_q: torch.Tensor, w_k: torch.Tensor, lam: torch.Tensor, h: int, h_kv: int,
+                          inplace: bool = False):
+    """w_q fp16 [h*128, d_model], w_k fp16 [h_kv*128, d_model], lambda fp32 [h_kv, 128]
+    -> (w_q', w_k') with Lambda folded in."""
+    if w_q.dim() != 2 or w_k.dim() != 2 or w_q.shape[1] != w_k.shape[1] or w_q.shape[0] != h * KV4_HEAD_DIM \
+            or w_k.shape[0] != h_kv * KV4_HEAD_DIM or tuple(lam.shape) != (h_kv, KV4_HEAD_DIM):
+        raise ValueError("smooth_attention_fold: shapes of w_q, w_k, lambda disagree with h, h_kv")
+    qo = w_q if inplace else torch.empty_like(w_q)
+    ko = w_k if inplace else torch.empty_like(w_k)
+    _check("qoq_smooth_attention_fold",
+           lib().qoq_smooth_attention_fold(_dev(w_q, "w_q", torch.float16), _dev(w_k, "w_k", torch.float16),
+                                           _dev(lam, "lambda", torch.float32), h, h_kv, KV4_HEAD_DIM, w_q.shape[1],
+                                           _dev(qo, "w_q_out", torch.float16), _dev(ko, "w_k_out", torch.float16),
+                                           _stream(w_q)))
+    return qo, ko
 
 
 def kv4_attention_workspace_bytes(B: int, h: int, h_kv: int, max_len: int) -> int:

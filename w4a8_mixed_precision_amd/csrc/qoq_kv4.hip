@@ -492,19 +492,30 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 }
 
 // o[b, head] = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m) (base-2 maxima); a split
-// with no tokens has m = -inf, O = 0, l = 0 and adds nothing.  One wave per (b, head):
-// the maxima a lane per split, then every split's (O, l) with no branch in the loop,
-// the lane's two dims at a time.
-__global__ __launch_bounds__(64) void kv4_combine_kernel(const float *__restrict__ ws_o,
-                                                         const float *__restrict__ ws_ml, int splits, int bh,
-                                                         __half *__restrict__ out) {
-  const int row = blockIdx.x, lane = threadIdx.x;
+// with no tokens has m = -inf, O = 0, l = 0 and adds nothing.  One workgroup of
+// kCombineWaves waves per (b, head): the maxima a thread per split, then wave w
+// takes splits w, w + kCombineWaves, ... with no branch in the loop, two dims per
+// lane, and the waves' sums meet in LDS.
+constexpr int kCombineWaves = 4;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void kv4_combine_kernel(const float *__restrict__ ws_o,
+                                                                        const float *__restrict__ ws_ml,
+                                                                        int splits, int bh,
+                                                                        __half *__restrict__ out) {
+  __shared__ float red_m[kCombineWaves];
+  __shared__ float red_o[kCombineWaves][2 * 64 + 1];
+  const int row = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float mm = -INFINITY;
-  for (int s = lane; s < splits; s += 64) mm = fmaxf(mm, ws_ml[2 * (static_cast<size_t>(s) * bh + row)]);
-  mm = wave_max_f32(mm);                               // finite: split 0 holds the first token
+  for (int s = threadIdx.x; s < splits; s += 64 * kCombineWaves)
+    mm = fmaxf(mm, ws_ml[2 * (static_cast<size_t>(s) * bh + row)]);
+  mm = wave_max_f32(mm);
+  if (lane == 0) red_m[wave] = mm;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) mm = fmaxf(mm, red_m[w]);   // finite: split 0 holds the first token
   float a0 = 0.0f, a1 = 0.0f, ll = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
+#pragma unroll 4
+  for (int s = wave; s < splits; s += kCombineWaves) {
     const size_t p = static_cast<size_t>(s) * bh + row;
     const float ms = ws_ml[2 * p];
     const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - mm);
@@ -513,10 +524,22 @@ __global__ __launch_bounds__(64) void kv4_combine_kernel(const float *__restrict
     a0 += v.x * f;
     a1 += v.y * f;
   }
-  const float inv = 1.0f / ll;
+  red_o[wave][2 * lane] = a0;
+  red_o[wave][2 * lane + 1] = a1;
+  if (lane == 0) red_o[wave][128] = ll;
+  __syncthreads();
+  if (wave != 0) return;
+  float s0 = 0.0f, s1 = 0.0f, sl = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    s0 += red_o[w][2 * lane];
+    s1 += red_o[w][2 * lane + 1];
+    sl += red_o[w][128];
+  }
+  const float inv = 1.0f / sl;
   __half2 r;
-  r.x = __float2half_rn(a0 * inv);
-  r.y = __float2half_rn(a1 * inv);
+  r.x = __float2half_rn(s0 * inv);
+  r.y = __float2half_rn(s1 * inv);
   *reinterpret_cast<__half2 *>(out + static_cast<size_t>(row) * kD + 2 * lane) = r;
 }
 
@@ -624,7 +647,8 @@ void launch_kv4_attention(const void *q, const void *pool, int64_t num_pages, co
                      static_cast<int>(num_pages), seq_lens, static_cast<int>(max_len), static_cast<int>(h),
                      static_cast<int>(h_kv), bps, c2, static_cast<__half *>(out), wo, wml);
   if (splits > 1)
-    hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(64), 0, st, wo, wml, splits,
+    hipLaunchKernelGGL(kv4_combine_kernel, dim3(static_cast<unsigned>(B * h)), dim3(64 * kCombineWaves), 0, st, wo,
+                       wml, splits,
                        static_cast<int>(B * h), static_cast<__half *>(out));
 }
 

@@ -177,14 +177,17 @@ int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t
  * Head dim 128, 64 tokens per page.  The pool is caller-owned device memory of
  * num_pages x qoq_kv4_page_bytes bytes (16-byte aligned); a page holds, for each KV
  * head, the K and V codes of its 64 token slots (in the operand order of the
- * attention kernel's matrix instructions) followed by the fp16 K scales, K zeros, V
- * scales and V zeros of the slots.  page_table: int32 [B, max_pages], the pool page
+ * attention kernel's matrix instructions) followed by each slot's fp16 K scale and
+ * zero (one 32-bit word per token) and each four slots' fp16 V scales then V zeros
+ * (16 bytes per four tokens); the byte-level layout is described with the kernels
+ * (qoq_kv4.hip).  page_table: int32 [B, max_pages], the pool page
  * of each 64-token span of each sequence (pages of different sequences distinct).
  * num_pages: pages in the pool.  Positions, page ids and seq_lens are device data the
  * host cannot check; the kernels guard them: the write skips a token whose position
  * falls outside the table or whose page id lies outside [0, num_pages), the attention
  * clamps page ids to that range and seq_lens to [1, max_len] (a bad table gives wrong
- * values, never an access outside the buffers).
+ * values, never an access outside the buffers).  The write skips a whole 16-token
+ * block when its position or page is out of range.
  * ------------------------------------------------------------------------------ */
 
 /* Bytes of one page (all h_kv heads).  Errors: INVALID, UNSUPPORTED (head_dim != 128). */

@@ -83,6 +83,7 @@ class Case:
         self.ws = None
         self.lws = None
         self.prod = None
+        self.sws = None
         self.i = 0
 
     def workspace(self, q):
@@ -140,7 +141,11 @@ class Case:
         kind, t = self.prod
         out = (self.qt if self.tiled else self.qx, self.sx, None)
         if kind == "silu":
-            q.silu_mul_quantize(t[:, :self.L.K], t[:, self.L.K:], tiled=self.tiled, out=out)
+            need = q.silu_mul_quantize_workspace_bytes(self.M, self.L.K)
+            if need and (self.sws is None or self.sws.numel() < need):
+                self.sws = torch.empty(need, dtype=torch.uint8, device=self.x.device)
+            q.silu_mul_quantize(t[:, :self.L.K], t[:, self.L.K:], tiled=self.tiled, out=out,
+                                workspace=self.sws if need else None)
         else:
             q.rmsnorm_quantize(self.x, t, 1e-5, tiled=self.tiled, out=out)
 

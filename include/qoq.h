@@ -160,6 +160,21 @@ int qoq_silu_mul_quantize(const void *gate_fp16, const void *up_fp16, int64_t ld
                           int64_t K, int32_t layout, void *qx, void *s_x_fp16, int32_t *t_x,
                           void *stream);
 
+/* The same result without the code sums, for a few long rows split over workgroups
+ * without repetition: pass 1 forms each 2048-value slice of a row and writes its
+ * maximum magnitude to the workspace, pass 2 quantizes every slice with the row
+ * maximum (the same codes and scales as qoq_silu_mul_quantize, bit for bit).
+ * workspace: caller-owned device memory of qoq_silu_mul_quantize_workspace_bytes
+ * (one 32-bit value per row and slice; 0 bytes, and one pass, above 64 rows or
+ * below 2049 values per row), 4-byte aligned, no initialization, nothing kept
+ * between calls; overlapping calls need separate workspaces.
+ * Errors: as qoq_silu_mul_quantize, WORKSPACE when the workspace is NULL or smaller
+ * than reported. */
+int qoq_silu_mul_quantize_workspace_bytes(int64_t M, int64_t K, size_t *bytes);
+int qoq_silu_mul_quantize_ws(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M,
+                             int64_t K, int32_t layout, void *qx, void *s_x_fp16, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* The same kernels without the quantization (the unfused pipeline's normalization and
  * activation kernels): the fp16 values the fused entry points quantize, [M,K]
  * row-major fp16, 16-byte aligned.  Same arguments and errors otherwise. */

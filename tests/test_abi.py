@@ -354,3 +354,16 @@ def test_smooth_attention_validation(L):
     assert fold(FAKE, FAKE, NUL, 32, 8, 128, 4096, FAKE, FAKE, NUL) == INVALID
     assert fold(FAKE, FAKE, ODD, 32, 8, 128, 4096, FAKE, FAKE, NUL) == ALIGNMENT
 
+
+def test_silu_split_validation(L):
+    b = ctypes.c_size_t(0)
+    assert L.qoq_silu_mul_quantize_workspace_bytes(1, 29568, ctypes.byref(b)) == OK and b.value == 4 * 15
+    assert L.qoq_silu_mul_quantize_workspace_bytes(65, 29568, ctypes.byref(b)) == OK and b.value == 0
+    assert L.qoq_silu_mul_quantize_workspace_bytes(1, 12, ctypes.byref(b)) == INVALID
+    f = L.qoq_silu_mul_quantize_ws
+    assert f(FAKE, FAKE, 29568, 1, 29568, 0, FAKE, FAKE, NUL, 0, NUL) == WORKSPACE
+    assert f(FAKE, FAKE, 29568, 1, 29568, 0, FAKE, FAKE, FAKE, 59, NUL) == WORKSPACE
+    assert f(FAKE, FAKE, 29568, 1, 29568, 0, FAKE, FAKE, ODD, 60, NUL) == ALIGNMENT
+    assert f(FAKE, FAKE, 100, 1, 29568, 0, FAKE, FAKE, FAKE, 60, NUL) == INVALID        # ld < K
+    assert f(FAKE, FAKE, 29568, 0, 29568, 0, FAKE, FAKE, NUL, 0, NUL) == OK             # M = 0
+

@@ -162,3 +162,23 @@ def test_rmsnorm_fp16_values(gpu):
         say(f"rmsnorm fp16 M={M} K={K}")
         y = host(qoq.rmsnorm(to_dev(x, gpu), to_dev(gamma, gpu), EPS))
         assert np.array_equal(y.view(np.uint16), fq.rmsnorm_fp16(x, gamma, EPS).view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K", [(1, 29568), (1, 14336), (3, 2056), (16, 14336), (64, 14336), (7, 32768)])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_silu_split_matches_one_pass(gpu, M, K, tiled):
+    """The two-pass split entry point gives the one-pass kernel's codes and scales bit
+    for bit, and both match the oracle."""
+    if tiled and K % 64:
+        pytest.skip("tiled layout: K % 64 == 0")
+    say(f"silu split M={M} K={K} tiled={tiled}")
+    gu = np.concatenate([_rows(M, K, M * 11 + K, 2.0), _rows(M, K, M * 11 + K + 1, 1.5)], axis=1)
+    d = to_dev(gu, gpu)
+    assert qoq.silu_mul_quantize_workspace_bytes(M, K) > 0
+    a = qoq.silu_mul_quantize(d[:, :K], d[:, K:], tiled=tiled, split=True)
+    b = qoq.silu_mul_quantize(d[:, :K], d[:, K:], tiled=tiled, split=False)
+    qa, qb = host(a[0]), host(b[0])
+    if tiled:                                              # rows past M are padding, never written
+        qa, qb = untile(qa, M, K), untile(qb, M, K)
+    assert np.array_equal(qa, qb) and np.array_equal(host(a[1]).view(np.uint16), host(b[1]).view(np.uint16))
+    _check(a, fq.silu_mul_quantize(gu[:, :K], gu[:, K:]), M, K, tiled)

@@ -164,6 +164,34 @@ int qoq_rmsnorm(const void *x_fp16, const void *gamma_fp16, float eps, int64_t M
   return launch_status();
 }
 
+int qoq_silu_mul_quantize_workspace_bytes(int64_t M, int64_t K, size_t *bytes) {
+  if (M < 0 || K <= 0 || K % 8 != 0 || !bytes) return QOQ_ERR_INVALID;
+  if (K > qoq::kFusedMaxK || M > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  *bytes = qoq::silu_split_workspace(M, K);
+  return QOQ_OK;
+}
+
+int qoq_silu_mul_quantize_ws(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K,
+                             int32_t layout, void *qx, void *s_x_fp16, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  if (ld < K || ld % 8 != 0) return QOQ_ERR_INVALID;
+  const int st = fused_common_checks(M, K, layout, qx, s_x_fp16, nullptr);
+  if (st != 1) return st;
+  if (!gate_fp16 || !up_fp16) return QOQ_ERR_INVALID;
+  if (ld > kMaxDim) return QOQ_ERR_UNSUPPORTED;
+  if (!aligned(gate_fp16, 16) || !aligned(up_fp16, 16)) return QOQ_ERR_ALIGNMENT;
+  const size_t need = qoq::silu_split_workspace(M, K);
+  if (need == 0) {                                  // one pass, as qoq_silu_mul_quantize
+    qoq::launch_silu_mul_quantize(gate_fp16, up_fp16, ld, M, K, layout, qx, s_x_fp16, nullptr, as_stream(stream));
+    return launch_status();
+  }
+  if (!workspace || workspace_bytes < need) return QOQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_silu_mul_quantize_split(gate_fp16, up_fp16, ld, M, K, layout == 1, qx, s_x_fp16, workspace,
+                                      as_stream(stream));
+  return launch_status();
+}
+
 int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t M, int64_t K, void *h_fp16,
                  void *stream) {
   if (M < 0 || K <= 0 || K % 8 != 0 || ld < K || ld % 8 != 0) return QOQ_ERR_INVALID;

@@ -224,6 +224,31 @@ __device__ __noinline__ unsigned decide_h16(float gf, float uf, float h32) {
   return (lb & 1u) ? hb : lb;                      // a tie (only in principle): to even
 }
 
+// fp16 bits of SiLU(gate) * up for the 8 values of a chunk (every lane of the wave
+// calls it: the rare exact decision is a wave-uniform branch)
+__device__ __forceinline__ uint4 silu_chunk8(uint4 gv, uint4 uv) {
+  const unsigned gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  const unsigned uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  float gf[8], uf[8], h[8];
+  unsigned r[8];
+  bool open = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const unsigned sh = 16 * (i & 1);
+    gf[i] = half_bits_to_float((gw[i >> 1] >> sh) & 0xffffu);
+    uf[i] = half_bits_to_float((uw[i >> 1] >> sh) & 0xffffu);
+    h[i] = silu_mul_fast(gf[i], uf[i]);
+    r[i] = round_h16(h[i]);
+    open |= r[i] == 0xffffffffu;
+  }
+  if (__ballot(open) != 0) {                       // uniform: rare
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (r[i] == 0xffffffffu) r[i] = decide_h16(gf[i], uf[i], h[i]);
+  }
+  return make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+}
+
 template <int CH, bool TILED, bool ROWSUM, bool OUT16 = false>
 __global__ __launch_bounds__(kFThreads) void silu_mul_quant_kernel(const __half *__restrict__ gate,
                                                                    const __half *__restrict__ up, int ld, int K,
@@ -246,26 +271,7 @@ __global__ __launch_bounds__(kFThreads) void silu_mul_quant_kernel(const __half 
   unsigned amax = 0;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const unsigned gw[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
-    const unsigned uw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
-    float gf[8], uf[8], h[8];
-    unsigned r[8];
-    bool open = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned sh = 16 * (i & 1);
-      gf[i] = half_bits_to_float((gw[i >> 1] >> sh) & 0xffffu);
-      uf[i] = half_bits_to_float((uw[i >> 1] >> sh) & 0xffffu);
-      h[i] = silu_mul_fast(gf[i], uf[i]);
-      r[i] = round_h16(h[i]);
-      open |= r[i] == 0xffffffffu;
-    }
-    if (__ballot(open) != 0) {                     // uniform: rare
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (r[i] == 0xffffffffu) r[i] = decide_h16(gf[i], uf[i], h[i]);
-    }
-    a[c] = make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+    a[c] = silu_chunk8(a[c], b[c]);
     amax = absmax_bits8(a[c], amax);               // past the row: gate = up = 0 -> 0
   }
   if (OUT16) {
@@ -274,6 +280,55 @@ __global__ __launch_bounds__(kFThreads) void silu_mul_quant_kernel(const __half 
   }
   amax = block_max_u32(amax, ured);
   quantize_row<CH, TILED, ROWSUM>(a, amax, row, K, qx, sx, tx, ired);
+}
+
+// ---------------------------------------------------------------------------
+// A few rows with a long K, split without repetition: the kernel above spreads a
+// row over several workgroups that each form the whole row (every part needs the
+// row maximum), which makes one decode row of Qwen-72B's down projection a
+// vector-ALU job for one compute unit.  Here the row is cut into slices of
+// kSliceChunks chunks (2048 values); pass 1 forms each slice's values and writes
+// their maximum magnitude (fp16 bits) to ws[row * slices + slice]; pass 2 takes the
+// row maximum from those, forms its slice's values again and quantizes them (the
+// same routines, so the codes are identical).  Two launches instead of one.
+// ---------------------------------------------------------------------------
+constexpr int kSliceChunks = kFThreads;             // one chunk of 8 values per thread
+
+__global__ __launch_bounds__(kFThreads) void silu_slice_max_kernel(const __half *__restrict__ gate,
+                                                                   const __half *__restrict__ up, int ld, int K,
+                                                                   unsigned *__restrict__ ws) {
+  __shared__ unsigned ured[kFThreads / 64];
+  const int row = blockIdx.x, slice = blockIdx.y, slices = gridDim.y;
+  const int nchunk = K >> 3, idx = slice * kSliceChunks + threadIdx.x;
+  const uint4 *gr = reinterpret_cast<const uint4 *>(gate + static_cast<size_t>(row) * ld);
+  const uint4 *ur = reinterpret_cast<const uint4 *>(up + static_cast<size_t>(row) * ld);
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const uint4 y = silu_chunk8(idx < nchunk ? gr[idx] : zero, idx < nchunk ? ur[idx] : zero);
+  const unsigned amax = block_max_u32(absmax_bits8(y, 0u), ured);
+  if (threadIdx.x == 0) ws[static_cast<size_t>(row) * slices + slice] = amax;
+}
+
+template <bool TILED>
+__global__ __launch_bounds__(kFThreads) void silu_slice_quant_kernel(const __half *__restrict__ gate,
+                                                                     const __half *__restrict__ up, int ld, int K,
+                                                                     const unsigned *__restrict__ ws,
+                                                                     int8_t *__restrict__ qx,
+                                                                     __half *__restrict__ sx) {
+  __shared__ unsigned ured[kFThreads / 64];
+  const int row = blockIdx.x, slice = blockIdx.y, slices = gridDim.y;
+  const int nchunk = K >> 3, idx = slice * kSliceChunks + threadIdx.x;
+  const uint4 *gr = reinterpret_cast<const uint4 *>(gate + static_cast<size_t>(row) * ld);
+  const uint4 *ur = reinterpret_cast<const uint4 *>(up + static_cast<size_t>(row) * ld);
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const uint4 gv = idx < nchunk ? gr[idx] : zero, uv = idx < nchunk ? ur[idx] : zero;
+  unsigned part = 0;
+  for (int i = threadIdx.x; i < slices; i += kFThreads) part = max(part, ws[static_cast<size_t>(row) * slices + i]);
+  const unsigned amax = block_max_u32(part, ured);
+  const uint4 y = silu_chunk8(gv, uv);
+  const __half sh = sym_scale(amax, static_cast<float>(kXQmax));
+  if (threadIdx.x == 0 && slice == 0) sx[row] = sh;
+  const float s = __half2float(sh);
+  if (idx < nchunk) store_codes<TILED>(qx, row, K, idx, quant_chunk8(y, s, act_rcp(s)));
 }
 
 // workgroups per row: as for the standalone quantizer (a few tokens spread a row
@@ -325,6 +380,31 @@ void launch_silu_ch(const __half *g, const __half *u, int ld, int K, bool tiled,
 }
 
 }  // namespace
+
+int silu_split_slices(int64_t M, int64_t K) {
+  if (M > kSiluSplitMaxM) return 0;
+  const int64_t slices = (K / 8 + kSliceChunks - 1) / kSliceChunks;
+  return slices > 1 ? static_cast<int>(slices) : 0;
+}
+
+size_t silu_split_workspace(int64_t M, int64_t K) {
+  return static_cast<size_t>(M) * silu_split_slices(M, K) * sizeof(unsigned);
+}
+
+void launch_silu_mul_quantize_split(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, bool tiled,
+                                    void *qx, void *sx, void *ws, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(M), static_cast<unsigned>(silu_split_slices(M, K)));
+  const __half *gp = static_cast<const __half *>(gate), *upp = static_cast<const __half *>(up);
+  const int k = static_cast<int>(K), l = static_cast<int>(ld);
+  hipLaunchKernelGGL(silu_slice_max_kernel, grid, dim3(kFThreads), 0, st, gp, upp, l, k, static_cast<unsigned *>(ws));
+  if (tiled)
+    hipLaunchKernelGGL(silu_slice_quant_kernel<true>, grid, dim3(kFThreads), 0, st, gp, upp, l, k,
+                       static_cast<const unsigned *>(ws), static_cast<int8_t *>(qx), static_cast<__half *>(sx));
+  else
+    hipLaunchKernelGGL(silu_slice_quant_kernel<false>, grid, dim3(kFThreads), 0, st, gp, upp, l, k,
+                       static_cast<const unsigned *>(ws), static_cast<int8_t *>(qx), static_cast<__half *>(sx));
+}
+
 
 // tiled == -1: the fp16 output of the normalization itself into qx (no quantization)
 void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_t M, int64_t K, int tiled,

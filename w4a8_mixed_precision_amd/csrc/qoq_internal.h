@@ -28,6 +28,16 @@ void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, voi
 constexpr int64_t kFusedMaxK = 32768;
 void launch_rmsnorm_quantize(const void *x, const void *gamma, float eps, int64_t M, int64_t K, int tiled,
                              void *qx, void *sx, void *tx, hipStream_t stream);
+// SwiGLU + quantization of a few long rows in two passes over 2048-value slices,
+// with a workspace of one 32-bit maximum per (row, slice); 0 slices: not split
+#ifndef QOQ_SILU_SPLIT_MAX_M
+#define QOQ_SILU_SPLIT_MAX_M 64
+#endif
+constexpr int64_t kSiluSplitMaxM = QOQ_SILU_SPLIT_MAX_M;
+int silu_split_slices(int64_t M, int64_t K);
+size_t silu_split_workspace(int64_t M, int64_t K);
+void launch_silu_mul_quantize_split(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, bool tiled,
+                                    void *qx, void *sx, void *ws, hipStream_t stream);
 void launch_silu_mul_quantize(const void *gate, const void *up, int64_t ld, int64_t M, int64_t K, int tiled,
                               void *qx, void *sx, void *tx, hipStream_t stream);
 

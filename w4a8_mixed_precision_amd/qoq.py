@@ -51,6 +51,9 @@ _SIGNATURES = {
                               ctypes.c_int),
     "qoq_rmsnorm": ([_c_vp, _c_vp, ctypes.c_float, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
     "qoq_silu_mul": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_silu_mul_quantize_workspace_bytes": ([_c_i64, _c_i64, ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "qoq_silu_mul_quantize_ws": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp],
+                                 ctypes.c_int),
     "qoq_kv4_page_bytes": ([_c_i64, _c_i64, ctypes.POINTER(_c_sz)], ctypes.c_int),
     "qoq_kv4_write": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
                       ctypes.c_int),
@@ -270,9 +273,12 @@ def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float, tiled: bo
     return qx, s_x, t
 
 
-def silu_mul_quantize(gate: torch.Tensor, up: torch.Tensor, tiled: bool = False, rowsum: bool = False, out=None):
-    """SiLU(gate) * up + per-token INT8 quantization in one kernel.  gate, up: fp16
-    [M, K] views with the same row stride (e.g. the halves of a gate+up output)."""
+def silu_mul_quantize(gate: torch.Tensor, up: torch.Tensor, tiled: bool = False, rowsum: bool = False, out=None,
+                      split: bool = True, workspace=None):
+    """SiLU(gate) * up + per-token INT8 quantization.  gate, up: fp16 [M, K] views with
+    the same row stride (e.g. the halves of a gate+up output).  Without code sums, a
+    few long rows take the two-pass split entry point (split=False forces the one-pass
+    kernel); workspace: None = the cached one of this device and stream."""
     M, K = gate.shape
     if up.shape != gate.shape or gate.stride(1) != 1 or up.stride(1) != 1 or gate.stride(0) != up.stride(0):
         raise ValueError("gate and up must be [M, K] views with unit column stride and the same row stride")
@@ -280,12 +286,45 @@ def silu_mul_quantize(gate: torch.Tensor, up: torch.Tensor, tiled: bool = False,
     for t_, n_ in ((gate, "gate"), (up, "up")):
         if not isinstance(t_, torch.Tensor) or t_.device.type != "cuda" or t_.dtype != torch.float16:
             raise TypeError(f"{n_} must be an fp16 HIP device tensor")
+    if not rowsum and split:
+        need = silu_mul_quantize_workspace_bytes(M, K)
+        if need:
+            ws = workspace if workspace is not None else _silu_workspace(gate, need)
+            _check("qoq_silu_mul_quantize_ws",
+                   lib().qoq_silu_mul_quantize_ws(ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(up.data_ptr()),
+                                                  gate.stride(0), M, K, 1 if tiled else 0,
+                                                  _dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
+                                                  _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+                                                  _stream(gate)))
+            return qx, s_x, t
     _check("qoq_silu_mul_quantize",
            lib().qoq_silu_mul_quantize(ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(up.data_ptr()),
                                        gate.stride(0), M, K, 1 if tiled else 0, _dev(qx, "qx", torch.int8),
                                        _dev(s_x, "s_x", torch.float16),
                                        None if t is None else _dev(t, "t", torch.int32), _stream(gate)))
     return qx, s_x, t
+
+
+def silu_mul_quantize_workspace_bytes(M: int, K: int) -> int:
+    b = _c_sz(0)
+    _check("qoq_silu_mul_quantize_workspace_bytes", lib().qoq_silu_mul_quantize_workspace_bytes(M, K, ctypes.byref(b)))
+    return int(b.value)
+
+
+_silu_workspaces = {}
+
+
+def _silu_workspace(t: torch.Tensor, need: int):
+    """The cached two-pass SwiGLU workspace of t's device and current stream."""
+    key = (t.device.index, torch.cuda.current_stream(t.device).cuda_stream)
+    ws = _silu_workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the SwiGLU workspace for this shape does not exist yet and cannot be allocated "
+                               "during graph capture: call once before capturing or pass workspace=")
+        ws = torch.empty(max(need, 2 * ws.numel() if ws is not None else 0), dtype=torch.uint8, device=t.device)
+        _silu_workspaces[key] = ws
+    return ws
 
 
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out=None):

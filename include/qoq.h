@@ -209,13 +209,13 @@ int qoq_silu_mul(const void *gate_fp16, const void *up_fp16, int64_t ld, int64_t
 int qoq_kv4_page_bytes(int64_t h_kv, int64_t head_dim, size_t *bytes);
 
 /* KV write: quantize n_new new tokens per sequence into the cache.  k_new, v_new: fp16
- * [B, n_new, h_kv, 128] (4-byte aligned); token i of sequence b goes to position
+ * [B, n_new, h_kv, 128] (16-byte aligned); token i of sequence b goes to position
  * positions[b] + i.  Per token and KV head, over the 128 values x with the range
  * widened to contain 0 (lo = min(0, min x), hi = max(0, max x)): s = fp16(fp32(hi -
  * lo) / 15), z = rne(-lo / s) in [0, 15], codes clamp(z + rne(x / s), 0, 15) (fp32
  * IEEE quotients; s = 0 for an all-zero vector, codes and z 0); s and z stored as
- * fp16.  One workgroup per (KV head, sequence, 16-token block of positions): a V
- * word holds four tokens, so each block's words are assembled once, merged with the
+ * fp16.  One wave per (KV head, sequence, 16-token block of positions): a V word
+ * holds four tokens, so each block's words are assembled once, merged with the
  * tokens already there; calls for the same pages must not overlap.  n_new <= 2^19,
  * B <= 65535, the sequence's positions below 2^30.
  * Errors: INVALID, UNSUPPORTED, ALIGNMENT, HIP. */

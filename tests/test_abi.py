@@ -329,6 +329,7 @@ def test_kv4_validation(L):
     assert wr(FAKE, FAKE, 0, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == OK
     assert wr(NUL, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == INVALID
     assert wr(FAKE, FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, ODD, 16, NUL) == ALIGNMENT
+    assert wr(ctypes.c_void_p(0x10004), FAKE, 2, 1, 8, 128, FAKE, FAKE, 4, FAKE, 16, NUL) == ALIGNMENT   # 16-byte loads
     at = L.qoq_kv4_decode_attention
     args = lambda **kw: [kw.get(k, v) for k, v in dict(q=FAKE, pool=FAKE, np_=16, pt=FAKE, mp=4, sl=FAKE, B=2, h=32, hkv=8,
                                                            hd=128, ml=256, out=FAKE, ws=NUL, wb=0, st=NUL).items()]

@@ -83,8 +83,14 @@ def test_kv4_write_bit_exact(gpu):
     v = _kv(rng, B * n_tot, h_kv, 0.3).reshape(B, n_tot, h_kv, D)
     k[0, 5] = 0                                             # an all-zero vector
     v[1, 7] = np.abs(v[1, 7]) + np.float16(2)               # one-signed, away from 0
-    # tokens 0..36 at once, then one at a time up to 60, then 61..149 at once
-    spans = [(0, 37)] + [(i, i + 1) for i in range(37, 61)] + [(61, n_tot)]
+    halves = (np.arange(D) % 31 / 2).astype(np.float16)       # 0 .. 15 in steps of 1/2: s = 1, z = 0,
+    for t in (9, 40):                                       # every odd value an exact tie x / s
+        k[2, t, 1] = halves
+        v[2, t, 3] = halves[::-1]
+    # tokens 0..36 at once (block kernel), one at a time up to 52 and three at once
+    # (per-token kernel), five at once inside one block, then 61..149 at once (block
+    # kernel, partial first and last blocks merged with what is there)
+    spans = [(0, 37)] + [(i, i + 1) for i in range(37, 53)] + [(53, 56), (56, 61), (61, n_tot)]
     dpt = to_dev(pt, gpu)
     for a, e in spans:
         say(f"kv4_write tokens {a}..{e - 1}")

@@ -218,7 +218,7 @@ int qoq_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n_new
   if (head_dim != 128 || h_kv > 1024 || B > 65535 || n_new > (int64_t{1} << 19)) return QOQ_ERR_UNSUPPORTED;
   if (B == 0 || n_new == 0) return QOQ_OK;
   if (!k_new || !v_new || !positions || !page_table || !kv_pool) return QOQ_ERR_INVALID;
-  if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(positions, 4) || !aligned(page_table, 4) ||
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(positions, 4) || !aligned(page_table, 4) ||
       !aligned(kv_pool, 16))
     return QOQ_ERR_ALIGNMENT;
   qoq::launch_kv4_write(k_new, v_new, B, n_new, h_kv, positions, page_table, max_pages, num_pages, kv_pool,

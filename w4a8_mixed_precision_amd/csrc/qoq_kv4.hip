@@ -102,22 +102,192 @@ __device__ __forceinline__ h2 neg_biased(unsigned zz, unsigned base) {
 }
 
 // ---------------------------------------------------------------------------
-// KV write: one wave per (KV head, sequence, 16-token block of positions).  The
-// block is the one 16-token block of the page that the new tokens' positions fall
-// in (blockIdx.z counts blocks from the one holding the sequence's first new
-// position), so no two waves of a launch touch the same page words.  Lane l
-// quantizes dims 2l, 2l + 1 of each new token of the block in turn (per token and
-// head: range widened to contain 0, s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s),
-// q = clamp(z + rne(x / s), 0, 15), fp32 IEEE quotients; s and z stored as fp16)
-// and stages the codes in LDS; K words (one token each) are written per token, V
-// words (four tokens each) once for the block, merged with the nibbles of tokens
-// outside the new range.
+// KV write: one wave per (KV head, sequence, 16-token block of positions), four
+// consecutive blocks per workgroup (single-wave workgroups leave most of the chip
+// idle: the dispatcher, not the work, sets the pace).  The block is the one 16-token
+// block of the page that the new tokens' positions fall in (counted from the one
+// holding the sequence's first new position), so no two waves of a launch touch the
+// same page words.  Lane
+// l = 4 t + u holds dims 32 u .. 32 u + 31 of token t of the block (K and V, all
+// loads issued at once); per token and head: range widened to contain 0,
+// s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s), q = clamp(z + rne(x / s), 0, 15),
+// fp32 IEEE quotients, s and z stored as fp16; min and max over the token's four
+// lanes by two xor steps.  Word u of every K slot of token t takes its nibbles from
+// dims 32 u .. 32 u + 31 only, so lane (t, u) builds those four words in registers;
+// the wave's K stores cover 256 contiguous bytes each.  A V word holds four tokens,
+// so the V codes go through LDS and each V word is assembled once for the block,
+// merged with the nibbles of tokens outside the new range.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
+__device__ __forceinline__ float quad_max_f32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 64));
+  return fmaxf(v, __shfl_xor(v, 2, 64));
+}
+__device__ __forceinline__ float quad_min_f32(float v) {
+  v = fminf(v, __shfl_xor(v, 1, 64));
+  return fminf(v, __shfl_xor(v, 2, 64));
+}
+
+// codes of the lane's 32 values and the token's (s, z); the token's 128 values sit
+// in four consecutive lanes
+__device__ __forceinline__ void kv_quant32(const float (&x)[32], unsigned (&c)[32], __half &sh, __half &zh) {
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
+  }
+  lo = fminf(quad_min_f32(lo), 0.0f);
+  hi = fmaxf(quad_max_f32(hi), 0.0f);
+  float range = hi - lo;
+  __asm__ volatile("" : "+v"(range));                 // fp32 difference, then the divide
+  sh = __float2half_rn(__fdiv_rn(range, 15.0f));
+  const float s = __half2float(sh);
+  if (s == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = 0u;
+    zh = __float2half_rn(0.0f);
+    return;
+  }
+  const float z = rintf(__fdiv_rn(-lo, s));
+  zh = __float2half_rn(z);
+  // x / s as x * fp32(1 / s): |x / s| < 2^5 here (s is fp16(range / 15) and |x| is
+  // at most the range, the worst case being s rounded down to the smallest fp16
+  // subnormal), so the product is within 2^-17 of the correctly rounded quotient
+  // and rint decides the same way unless it lies within 2^-12 of a half-integer;
+  // those rare values take the IEEE divide (a branch the wave takes only when one
+  // of its lanes needs it)
+  const float y = __fdiv_rn(1.0f, s);
+  float q[32];
+  float gap = 1.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    q[j] = x[j] * y;
+    gap = fminf(gap, half_gap(q[j]));
+  }
+  if (__ballot(gap < 0x1p-12f) != 0) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (half_gap(q[j]) < 0x1p-12f) q[j] = __fdiv_rn(x[j], s);
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) c[j] = static_cast<unsigned>(fminf(fmaxf(z + rintf(q[j]), 0.0f), 15.0f));
+}
+
+__device__ __forceinline__ unsigned half_bits(__half h) { return __builtin_bit_cast(unsigned short, h); }
+
+__device__ __forceinline__ void halves_to_f32(const uint4 (&w)[4], float (&x)[32]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned d[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * i + 2 * e] = half_bits_to_float(d[e] & 0xffffu);
+      x[8 * i + 2 * e + 1] = half_bits_to_float(d[e] >> 16);
+    }
+  }
+}
+
+constexpr int kWriteWaves = 4;                     // 16-token blocks (one per wave) per workgroup
+
+// Positions and page ids are data the host cannot check: a block whose position
+// falls outside the page table, or whose page id lies outside the pool, is skipped
+// (a bad table gives wrong contents, never an access outside the buffers).
+__global__ __launch_bounds__(64 * kWriteWaves) __attribute__((amdgpu_waves_per_eu(4))) void kv4_write_block_kernel(
+    const __half *__restrict__ k_new, const __half *__restrict__ v_new, int n_new, int h_kv,
+    const int *__restrict__ positions, const int *__restrict__ page_table, int max_pages, int num_pages,
+    uint8_t *__restrict__ pool) {
+  __shared__ __attribute__((aligned(16))) uint8_t vcode_all[kWriteWaves][16][kD];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint8_t(&vcode)[16][kD] = vcode_all[wave];
+  const int pos0 = positions[b];                     // the same in the whole workgroup
+  if (pos0 < 0 || pos0 >= (1 << 30)) return;         // past any page table (max_pages <= 2^24)
+  const int blk = pos0 / 16 + kWriteWaves * static_cast<int>(blockIdx.z) + wave;   // absolute 16-token block
+  const int p_lo = max(pos0, 16 * blk), p_hi = min(pos0 + n_new, 16 * blk + 16);
+  int page = -1;
+  if (p_lo < p_hi && blk / 4 < max_pages) page = page_table[static_cast<size_t>(b) * max_pages + blk / 4];
+  // the same in the whole wave; an inactive wave skips its work but meets the barrier
+  const bool active = page >= 0 && page < num_pages;
+  uint8_t *pg = pool + (static_cast<size_t>(active ? page : 0) * h_kv + g) * kKv4PageBytes;
+  const int pb = blk & 3;                            // block within the page
+  if (active) {
+    const int t = lane >> 2, u = lane & 3;
+    const int p = 16 * blk + t;
+    const bool fresh = p >= p_lo && p < p_hi;        // the same in the token's four lanes
+
+    float kx[32], vx[32];
+    {
+      uint4 kw[4], vw[4];
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      const size_t src = ((static_cast<size_t>(b) * n_new + (fresh ? p - pos0 : 0)) * h_kv + g) * kD + 32 * u;
+      const uint4 *kp = reinterpret_cast<const uint4 *>(k_new + src);
+      const uint4 *vp = reinterpret_cast<const uint4 *>(v_new + src);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kw[i] = fresh ? kp[i] : zero;
+        vw[i] = fresh ? vp[i] : zero;
+      }
+      halves_to_f32(kw, kx);
+      halves_to_f32(vw, vx);
+    }
+    unsigned kc[32], vc[32];
+    __half ksh, kzh, vsh, vzh;
+    kv_quant32(kx, kc, ksh, kzh);
+    kv_quant32(vx, vc, vsh, vzh);
+
+    if (fresh) {
+      // K: word u of slot (qd, t); nibble k holds dim 32 u + 16 (k >> 1 & 1) + 4 qd + 2 (k & 1) + (k >> 2)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        unsigned w = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w |= kc[16 * ((k >> 1) & 1) + 4 * qd + 2 * (k & 1) + (k >> 2)] << (4 * k);
+        *reinterpret_cast<unsigned *>(pg + kKCodes + pb * 1024 + (16 * qd + t) * 16 + 4 * u) = w;
+      }
+      if (u == 0) {
+        const int slot = p & 63;
+        *reinterpret_cast<unsigned *>(pg + kKStats + 4 * slot) = half_bits(ksh) | (half_bits(kzh) << 16);
+        __half *vst = reinterpret_cast<__half *>(pg + kVStats + 16 * (slot >> 2));
+        vst[slot & 3] = vsh;
+        vst[4 + (slot & 3)] = vzh;
+      }
+    }
+    unsigned d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = vc[4 * i] | (vc[4 * i + 1] << 8) | (vc[4 * i + 2] << 16) | (vc[4 * i + 3] << 24);
+    uint4 *dst = reinterpret_cast<uint4 *>(&vcode[t][32 * u]);
+    dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+    dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+  }
+  __syncthreads();
+  if (!active) return;
+  // V: lane slot L = lane (token quarter qt, dim dd), its four words; nibble k of
+  // word w holds token 4 qt + 2 (k & 1) + (k >> 2) of dim 16 (2w + (k >> 1 & 1)) + dd
+  const int qt = lane >> 4, dd = lane & 15;
+  const int t_lo = p_lo - 16 * blk, t_hi = p_hi - 16 * blk;
+  if (4 * qt + 4 <= t_lo || 4 * qt >= t_hi) return;  // none of this slot's tokens is new
+  const bool whole = 4 * qt >= t_lo && 4 * qt + 4 <= t_hi;
+  unsigned *wp = reinterpret_cast<unsigned *>(pg + kVCodes + pb * 1024 + lane * 16);
+#pragma unroll
+  for (int wu = 0; wu < 4; ++wu) {
+    unsigned w = whole ? 0u : wp[wu];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int tk = 4 * qt + 2 * (k & 1) + (k >> 2);
+      if (tk >= t_lo && tk < t_hi) {
+        const int dk = 16 * (2 * wu + ((k >> 1) & 1)) + dd;
+        w = (w & ~(0xfu << (4 * k))) | (static_cast<unsigned>(vcode[tk][dk]) << (4 * k));
+      }
+    }
+    wp[wu] = w;
+  }
+}
+
 __device__ __forceinline__ float wave_min_f32(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
@@ -143,16 +313,16 @@ __device__ __forceinline__ void kv_quant2(float x0, float x1, unsigned &c0, unsi
   c1 = static_cast<unsigned>(fminf(fmaxf(z + rintf(__fdiv_rn(x1, s)), 0.0f), 15.0f));
 }
 
-__device__ __forceinline__ unsigned half_bits(__half h) { return __builtin_bit_cast(unsigned short, h); }
-
-// Positions and page ids are data the host cannot check: a block whose position
-// falls outside the page table, or whose page id lies outside the pool, is skipped
-// (a bad table gives wrong contents, never an access outside the buffers).
-__global__ __launch_bounds__(64) void kv4_write_kernel(const __half *__restrict__ k_new,
-                                                       const __half *__restrict__ v_new, int n_new, int h_kv,
-                                                       const int *__restrict__ positions,
-                                                       const int *__restrict__ page_table, int max_pages,
-                                                       int num_pages, uint8_t *__restrict__ pool) {
+// Few new tokens per sequence (decode): lane l quantizes dims 2l, 2l + 1 of each new
+// token of the block in turn (same arithmetic as above, min and max over the whole
+// wave), stages the codes in LDS and writes each token's K words as it goes; V words
+// as above.  Per token: two quotients per lane instead of the block kernel's 32 for
+// each of the 16 tokens it covers whether new or not.
+__global__ __launch_bounds__(64) void kv4_write_tokens_kernel(const __half *__restrict__ k_new,
+                                                              const __half *__restrict__ v_new, int n_new, int h_kv,
+                                                              const int *__restrict__ positions,
+                                                              const int *__restrict__ page_table, int max_pages,
+                                                              int num_pages, uint8_t *__restrict__ pool) {
   __shared__ uint8_t kcode[16][kD], vcode[16][kD];
   const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int pos0 = positions[b];                     // the same in every lane
@@ -605,6 +775,11 @@ __global__ __launch_bounds__(256) void smooth_fold_kernel(const __half *__restri
 
 }  // namespace
 
+// up to this many new tokens per sequence the per-token write kernel (measured on
+// MI355X: decode writes of one token per sequence take about half the time of the
+// block kernel, which quantizes all 16 token slots of a block)
+constexpr int64_t kWriteFewTokens = 4;
+
 int kv4_splits(int64_t B, int64_t h_kv, int64_t max_len) {
   const int64_t nblk = (max_len + 15) / 16;
   const int64_t want = (kKv4TargetWorkgroups + B * h_kv - 1) / (B * h_kv);
@@ -624,7 +799,11 @@ void launch_kv4_write(const void *k_new, const void *v_new, int64_t B, int64_t n
                       hipStream_t st) {
   // 16-token blocks spanned by n_new consecutive positions from any start
   const unsigned nz = static_cast<unsigned>((n_new + 14) / 16 + 1);
-  hipLaunchKernelGGL(kv4_write_kernel, dim3(static_cast<unsigned>(h_kv), static_cast<unsigned>(B), nz), dim3(64), 0, st,
+  const bool few = n_new <= kWriteFewTokens;
+  const unsigned gz = few ? nz : (nz + kWriteWaves - 1) / kWriteWaves;
+  hipLaunchKernelGGL(few ? kv4_write_tokens_kernel : kv4_write_block_kernel,
+                     dim3(static_cast<unsigned>(h_kv), static_cast<unsigned>(B), gz), dim3(few ? 64 : 64 * kWriteWaves),
+                     0, st,
                      static_cast<const __half *>(k_new), static_cast<const __half *>(v_new), static_cast<int>(n_new),
                      static_cast<int>(h_kv), positions, page_table, static_cast<int>(max_pages),
                      static_cast<int>(num_pages), static_cast<uint8_t *>(pool));

@@ -106,6 +106,28 @@ def test_kv4_write_bit_exact(gpu):
         assert np.array_equal(vz.view(np.uint16), wz.view(np.uint16))
 
 
+def test_kv4_prefill_write_full_shape(gpu):
+    """The prefill write of the throughput measurement's Llama-3-8B decode shape (64
+    sequences x 1024 tokens x 8 KV heads in one call, the same seeded inputs) on a
+    shuffled page table: three sampled sequences read back bit for bit."""
+    from w4a8_mixed_precision_amd import workloads as wl
+    S = wl.find_kv("llama3_8b_b64_l1024")
+    pt = _pages(np.random.default_rng(12), S.B, S.seq_len // P)
+    pool = torch.zeros((pt.size + 3) * qoq.kv4_page_bytes(S.h_kv), dtype=torch.uint8, device=gpu)
+    k = np.stack([wl.kv_fp16(S, b, S.seq_len, 0) for b in range(S.B)])
+    v = np.stack([wl.kv_fp16(S, b, S.seq_len, 1) for b in range(S.B)])
+    say(f"kv4_write prefill {S.name}")
+    qoq.kv4_write(to_dev(k, gpu), to_dev(v, gpu), to_dev(np.zeros(S.B, np.int32), gpu), to_dev(pt, gpu), pool)
+    poolh = host(pool)
+    for b in (0, 29, S.B - 1):
+        kc, ks, kz, vc, vs, vz = read_pages(poolh, pt[b], S.h_kv, S.seq_len)
+        for codes, sc, zp, x in ((kc, ks, kz, k[b]), (vc, vs, vz, v[b])):
+            wq, ws, wz = kv.kv_quantize(x)
+            assert np.array_equal(codes, wq), b
+            assert np.array_equal(sc.view(np.uint16), ws.view(np.uint16)), b
+            assert np.array_equal(zp.view(np.uint16), wz.view(np.uint16)), b
+
+
 def _run_attention(gpu, rng, lens, h, h_kv, kscale=1.0, vscale=1.0):
     B = len(lens)
     max_len = max(lens)

@@ -847,9 +847,8 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // prefetched register is never copied, so the compiler can wait for exactly the
 // loads it needs).  A fragments are read one k block ahead of the MFMAs that use
 // them.  Per group j: dequantize B(j); copy A(j+2) and load B(j+2); MFMAs of j;
-// wait for A(j+1)'s copies; barrier.  The copies and the register loads both count
-// in vmcnt but do not retire in order with each other, so a wait for a copy counts
-// only the copies issued after it.
+// wait for A(j+1)'s copies; barrier.  The copies and the register loads share
+// vmcnt and retire in issue order.
 // ---------------------------------------------------------------------------
 template <int TN>
 struct DBSet {
@@ -925,9 +924,11 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
       for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(af[kb & 1][tm], b[kb][tn], acc[tm][tn]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A(j+1) was copied one group ago.  Copies retire in order among themselves but
-  // not in order with register loads, so the count allows only the copies issued
-  // after A(j+1) (this group's TM) to be outstanding.
+  // A(j+1) was copied one group ago.  Vector-memory reads (the copies into LDS
+  // included) retire in issue order, so a count of TM leaves at most the last TM
+  // operations of this group (code and metadata loads) in flight: A(j+1) and B(j+1)
+  // have landed, and so have this group's A(j+2) copies.  Waiting only for what
+  // came before this group (a count of TM + 3 TN) measured the same on MI355X.
   QOQ_WAIT_VMCNT(TM);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);

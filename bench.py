@@ -73,10 +73,10 @@ class Case:
         self.sx = torch.empty(M, dtype=torch.float16, device=dev)
         self.tx = torch.empty(M, dtype=torch.int32, device=dev)
         self.out = torch.empty((M, L.N), dtype=torch.float16, device=dev)
-        # up to 64 tokens the linear step feeds the GEMM tiled codes; the GEMM and
-        # quantizer timings below use the same kernels
+        # up to 64 tokens the step feeds the GEMM tiled codes (both weight formats);
+        # the GEMM and quantizer timings below use the same kernels
         from w4a8_mixed_precision_amd import qoq
-        self.tiled = (not per_channel) and M <= qoq.TILED_MAX_M
+        self.tiled = M <= qoq.TILED_MAX_M
         self.qt = torch.empty(qoq.tiled_bytes(M, L.K), dtype=torch.int8, device=dev) if self.tiled else None
         self.ops = wl.algorithmic_ops(M, L.N, L.K)
         self.bytes = wl.algorithmic_bytes(M, L.N, L.K, per_channel)
@@ -117,7 +117,9 @@ class Case:
     def gemm_only(self, q):
         p, m, s = self.sets[self.i % len(self.sets)]
         self.i += 1
-        if self.pc:
+        if self.pc and self.tiled:
+            q.w4a8_gemm_pc_tiled(self.qt, self.sx, self.tx, p, m, s, self.M, self.L.N, self.L.K, out=self.out)
+        elif self.pc:
             q.w4a8_gemm_pc(self.qx, self.sx, self.tx, p, m, s, self.L.N, out=self.out,
                            workspace=self.workspace(q))
         elif self.tiled:
@@ -156,7 +158,9 @@ class Case:
         return 2 * M * K + 2 * K + M * K + 2 * M
 
     def quant_only(self, q):
-        if self.pc:
+        if self.pc and self.tiled:
+            q.quantize_activations_rowsum_tiled(self.x, out=(self.qt, self.sx, self.tx))
+        elif self.pc:
             q.quantize_activations_rowsum(self.x, out=(self.qx, self.sx, self.tx))
         elif self.tiled:
             q.quantize_activations_tiled(self.x, out=(self.qt, self.sx))
@@ -305,7 +309,8 @@ def run_case_metrics(c, q, torch, launches):
     return {
         "M": c.M, "K": c.L.K, "N": c.L.N,
         "plan": q.gemm_tiled_plan(c.M, c.L.N, c.L.K) + ":tiled" if c.tiled else q.gemm_plan(c.M, c.L.N, c.L.K),
-        "linear_plan": "quant_rowsum+gemm_pc" if c.pc else q.linear_plan(c.M, c.L.N, c.L.K),
+        "linear_plan": (("quant_rowsum_tiled+gemm_pc_tiled" if c.tiled else "quant_rowsum+gemm_pc") if c.pc
+                        else q.linear_plan(c.M, c.L.N, c.L.K)),
         "linear_us": s * 1e6, "format": "channel" if c.pc else "group",
         "gemm_us": g * 1e6, "quant_us": a * 1e6,
         "TOPS": c.ops / g / 1e12,

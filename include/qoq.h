@@ -130,6 +130,13 @@ int qoq_quantize_activations_rowsum(const void *x_fp16, int64_t M, int64_t K, vo
 int qoq_quantize_activations_tiled(const void *x_fp16, int64_t M, int64_t K, void *qx_tiled,
                                    void *s_x_fp16, void *stream);
 
+/* qoq_quantize_activations_tiled plus the per-token code sums t_x of
+ * qoq_quantize_activations_rowsum (INT32 [M], 4-byte aligned): the inputs of the
+ * per-channel GEMM on tiled codes (qoq_w4a8_gemm_pc_tiled).  M <= 64, K % 64 == 0.
+ * Errors: INVALID, UNSUPPORTED (M > 64), ALIGNMENT, HIP. */
+int qoq_quantize_activations_rowsum_tiled(const void *x_fp16, int64_t M, int64_t K, void *qx_tiled,
+                                          void *s_x_fp16, int32_t *t_x, void *stream);
+
 /* The producers of the GEMM's INT8 activations with the quantization fused in
  * ("QServe：把 W4A8KV4 ..." review, runtime precision mapping §3.2 and data path
  * step 2: fused into the preceding normalization kernel for the QKV projection and
@@ -335,6 +342,19 @@ int qoq_w4a8_gemm_pc(const void *qx_i8, const void *s_x_fp16, const int32_t *t_x
 int qoq_w4a8_gemm_pc_i32(const void *qx_i8, const int32_t *t_x, const void *packed_w,
                          const void *zeros, int32_t *acc_i32, int64_t M, int64_t N, int64_t K,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* qoq_w4a8_gemm_pc for M <= 64 with the activation codes in the tiled layout of
+ * qoq_quantize_activations_rowsum_tiled (t_x as written by it): same arithmetic and
+ * results; the few-token kernels of qoq_w4a8_gemm_tiled (same plan, no workspace).
+ * Errors: as qoq_w4a8_gemm_pc, UNSUPPORTED for M > 64. */
+int qoq_w4a8_gemm_pc_tiled(const void *qx_tiled, const void *s_x_fp16, const int32_t *t_x,
+                           const void *packed_w, const void *zeros, const void *s_w_fp16,
+                           void *out_fp16, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* The same with the INT32 epilogue (acc exactly, as qoq_w4a8_gemm_pc_i32). */
+int qoq_w4a8_gemm_pc_tiled_i32(const void *qx_tiled, const int32_t *t_x, const void *packed_w,
+                               const void *zeros, int32_t *acc_i32, int64_t M, int64_t N, int64_t K,
+                               void *stream);
 
 /* Workspace in bytes qoq_w4a8_linear needs for this problem: 0 when the fused
  * kernel serves it (qoq_linear_plan names a fused configuration), otherwise room for

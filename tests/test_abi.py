@@ -240,6 +240,23 @@ def test_tiled_plans_and_validation(L):
     gi = L.qoq_w4a8_gemm_tiled_i32
     assert gi(FAKE, FAKE, FAKE, FAKE, 65, 6144, 4096, NUL) == UNSUPPORTED
     assert gi(FAKE, FAKE, FAKE, ODD, 4, 6144, 4096, NUL) == ALIGNMENT
+    # per-channel weights on tiled codes
+    qr = L.qoq_quantize_activations_rowsum_tiled
+    assert qr(FAKE, 65, 4096, FAKE, FAKE, FAKE, NUL) == UNSUPPORTED
+    assert qr(FAKE, 4, 96, FAKE, FAKE, FAKE, NUL) == INVALID              # K % 64
+    assert qr(FAKE, 0, 4096, NUL, NUL, NUL, NUL) == OK
+    assert qr(FAKE, 4, 4096, FAKE, FAKE, NUL, NUL) == INVALID             # no code sums
+    assert qr(FAKE, 4, 4096, FAKE, FAKE, ctypes.c_void_p(0x10002), NUL) == ALIGNMENT
+    gp = L.qoq_w4a8_gemm_pc_tiled
+    assert gp(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65, 6144, 4096, NUL) == UNSUPPORTED
+    assert gp(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4000, NUL) == INVALID
+    assert gp(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 6144, 4096, NUL) == OK
+    assert gp(FAKE, FAKE, NUL, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4096, NUL) == INVALID   # t_x
+    assert gp(FAKE, FAKE, FAKE, FAKE, NUL, FAKE, FAKE, 4, 6144, 4096, NUL) == INVALID   # zeros
+    assert gp(ODD, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 6144, 4096, NUL) == ALIGNMENT
+    gpi = L.qoq_w4a8_gemm_pc_tiled_i32
+    assert gpi(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 6144, 4096, NUL) == UNSUPPORTED
+    assert gpi(FAKE, FAKE, FAKE, FAKE, ODD, 4, 6144, 4096, NUL) == ALIGNMENT
 
 
 def test_linear_validation(L):

@@ -169,3 +169,95 @@ def test_pc_layers_sampled(gpu, name, M):
     want = o.contract(qx, o.dequantize_per_channel(q, z))
     assert np.array_equal(acc[np.ix_(rows, cols)], want)
     check_fp16(out[np.ix_(rows, cols)], want, sx, sw)
+
+
+# ---------------------------------------------------------------------------
+# Tiled activation codes (M <= 64): the quantizer with code sums writing the tiled
+# layout, and the per-channel few-token kernels reading it
+# ---------------------------------------------------------------------------
+def untile(qt, M, K):
+    """Row-major [M, K] view of tiled codes: block (rb, kb) = 1 KB at
+    (rb * K/64 + kb) * 1024; inside it, row r's bytes k = 16 q .. +15 at (16 q + r) * 16."""
+    Mp = (M + 15) // 16 * 16
+    a = qt[: Mp * K].reshape(Mp // 16, K // 64, 4, 16, 16)        # rb, kb, q, r, byte
+    return a.transpose(0, 3, 1, 2, 4).reshape(Mp, K)[:M]
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 4096), (33, 1152), (64, 8192)])
+def test_rowsum_tiled_bit_exact(gpu, M, K):
+    say(f"tiled activation codes with row sums M={M} K={K}")
+    rng = np.random.default_rng(M * 3 + K)
+    x16 = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    x16[0, : K // 2] = np.float16(60000)
+    if M > 2:
+        x16[2] = 0
+    qt, sx, t = qoq.quantize_activations_rowsum_tiled(to_dev(x16, gpu))
+    qo, so = o.quantize_activations(x16)
+    assert np.array_equal(untile(host(qt), M, K), qo)
+    assert np.array_equal(host(sx).view(np.uint16), so.view(np.uint16))
+    assert np.array_equal(host(t), o.activation_row_sums(qo))
+
+
+def _pc_tiled(dev, x16, w16, config=None):
+    if config:
+        os.environ["QOQ_GEMM_CONFIG"] = config
+    try:
+        M, K = x16.shape
+        N = w16.shape[0]
+        packed, zeros, s_w = qoq.quantize_pack_weights(to_dev(w16, dev), group=0)
+        qt, s_x, t = qoq.quantize_activations_rowsum_tiled(to_dev(x16, dev))
+        acc = qoq.w4a8_gemm_pc_tiled_i32(qt, t, packed, zeros, M, N, K)
+        out = qoq.w4a8_gemm_pc_tiled(qt, s_x, t, packed, zeros, s_w, M, N, K)
+        return host(acc), host(out)
+    finally:
+        os.environ.pop("QOQ_GEMM_CONFIG", None)
+
+
+TILED_SHAPES = [(1, 16, 128), (3, 48, 256), (17, 64, 384), (37, 144, 1152), (64, 272, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", TILED_SHAPES)
+def test_pc_tiled_exact(gpu, M, N, K):
+    say(f"per-channel gemm on tiled codes M={M} N={N} K={K} plan={qoq.gemm_tiled_plan(M, N, K)}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+    w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+    w16[:, :2] += np.float16(0.2)                              # asymmetric rows: zeros away from 8
+    r = o.w4a8_pc_reference(x16, w16)
+    acc, out = _pc_tiled(gpu, x16, w16)
+    assert np.array_equal(acc, r["acc"])
+    check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+@pytest.mark.parametrize("config", [c for c in _configs() if c.startswith("skinny")])
+def test_pc_tiled_every_config_exact(gpu, config):
+    """Every few-token configuration forced on tiled codes (ragged row blocks, strips
+    past the end of the grid, waves without groups on the short K)."""
+    for (M, N, K) in [(1, 16, 128), (21, 80, 1152), (64, 272, 896), (50, 48, 512)]:
+        say(f"per-channel tiled gemm config={config} M={M} N={N} K={K}")
+        rng = np.random.default_rng(M + N + K + 1)
+        x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+        r = o.w4a8_pc_reference(x16, w16)
+        acc, out = _pc_tiled(gpu, x16, w16, config=config)
+        assert np.array_equal(acc, r["acc"])
+        check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+def test_pc_tiled_layer_sampled(gpu):
+    """Llama-3-8B fused QKV at 64 tokens, full size, in the planner's configuration;
+    sampled rows x columns against the oracle."""
+    name, M = "llama3_8b_qkv", 64
+    L = wl.find(name)
+    say(f"per-channel tiled gemm {name} M={M} plan={qoq.gemm_tiled_plan(M, L.N, L.K)}")
+    w16 = _layer_weights(name)
+    x16 = wl.activations_fp16(L, M)
+    acc, out = _pc_tiled(gpu, x16, w16)
+    rng = np.random.default_rng(M + 1)
+    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, 24)])
+    cols = np.unique(np.r_[0:16, L.N - 16:L.N, rng.integers(0, L.N, 200)])
+    q, z, sw = o.quantize_weights_per_channel(w16[cols])
+    qx, sx = o.quantize_activations(x16[rows])
+    want = o.contract(qx, o.dequantize_per_channel(q, z))
+    assert np.array_equal(acc[np.ix_(rows, cols)], want)
+    check_fp16(out[np.ix_(rows, cols)], want, sx, sw)

@@ -119,6 +119,18 @@ int qoq_quantize_activations_tiled(const void *x_fp16, int64_t M, int64_t K, voi
   return launch_status();
 }
 
+int qoq_quantize_activations_rowsum_tiled(const void *x_fp16, int64_t M, int64_t K, void *qx_tiled,
+                                          void *s_x_fp16, int32_t *t_x, void *stream) {
+  if (M < 0 || K <= 0 || K % 64 != 0) return QOQ_ERR_INVALID;
+  if (M > qoq::kTiledMaxM || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !qx_tiled || !s_x_fp16 || !t_x) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(qx_tiled, 16) || !aligned(s_x_fp16, 2) || !aligned(t_x, 4))
+    return QOQ_ERR_ALIGNMENT;
+  qoq::launch_quantize_activations_rowsum_tiled(x_fp16, M, K, qx_tiled, s_x_fp16, t_x, as_stream(stream));
+  return launch_status();
+}
+
 static int fused_common_checks(int64_t M, int64_t K, int32_t layout, const void *qx, const void *s_x,
                                const int32_t *t_x) {
   if (M < 0 || K <= 0 || K % 8 != 0 || (layout != 0 && layout != 1)) return QOQ_ERR_INVALID;
@@ -319,6 +331,34 @@ int qoq_w4a8_gemm_tiled_i32(const void *qx_tiled, const void *packed_w, const vo
 const char *qoq_gemm_tiled_plan(int64_t M, int64_t N, int64_t K) {
   if (check_gemm(M, N, K, 128) != QOQ_OK || M == 0 || M > qoq::kTiledMaxM) return "invalid";
   return qoq::gemm_tiled_plan_name(M, N, K);
+}
+
+static int gemm_pc_tiled_common(const void *qx_tiled, const void *s_x_fp16, const int32_t *t_x,
+                                const void *packed_w, const void *zeros, const void *s_w_fp16, void *out,
+                                int out_kind, int64_t M, int64_t N, int64_t K, void *stream) {
+  int st = check_gemm(M, N, K, 128);
+  if (st != QOQ_OK) return st;
+  if (M > qoq::kTiledMaxM) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!qx_tiled || !t_x || !packed_w || !zeros || !out) return QOQ_ERR_INVALID;
+  if (out_kind == 0 && (!s_x_fp16 || !s_w_fp16)) return QOQ_ERR_INVALID;
+  if (!aligned(qx_tiled, 16) || !aligned(packed_w, 16) || !aligned(out, 16) || !aligned(t_x, 4))
+    return QOQ_ERR_ALIGNMENT;
+  if (out_kind == 0 && (!aligned(s_x_fp16, 2) || !aligned(s_w_fp16, 2))) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_w4a8_gemm_pc_tiled(qx_tiled, s_x_fp16, t_x, packed_w, zeros, s_w_fp16, out, out_kind, M, N, K,
+                                 as_stream(stream));
+  return launch_status();
+}
+
+int qoq_w4a8_gemm_pc_tiled(const void *qx_tiled, const void *s_x_fp16, const int32_t *t_x, const void *packed_w,
+                           const void *zeros, const void *s_w_fp16, void *out_fp16, int64_t M, int64_t N, int64_t K,
+                           void *stream) {
+  return gemm_pc_tiled_common(qx_tiled, s_x_fp16, t_x, packed_w, zeros, s_w_fp16, out_fp16, 0, M, N, K, stream);
+}
+
+int qoq_w4a8_gemm_pc_tiled_i32(const void *qx_tiled, const int32_t *t_x, const void *packed_w, const void *zeros,
+                               int32_t *acc_i32, int64_t M, int64_t N, int64_t K, void *stream) {
+  return gemm_pc_tiled_common(qx_tiled, nullptr, t_x, packed_w, zeros, nullptr, acc_i32, 1, M, N, K, stream);
 }
 
 static int gemm_pc_common(const void *qx_i8, const void *s_x_fp16, const int32_t *t_x, const void *packed_w,

@@ -243,7 +243,6 @@ __device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int 
                                               const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
                                               int M, int m0, int lane) {
   const int c32 = lane & 31, hi = lane >> 5, col = lane & 15;
-  const v4i zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = b * U + u;
@@ -1334,12 +1333,14 @@ struct Config {
   GemmKernel k[2][2];       // [per-group, per-channel][fp16 epilogue, INT32 epilogue]
   const char *name;
   int lds = 0;              // dynamic LDS bytes
-  GemmKernel kt[2] = {nullptr, nullptr};   // skinny, per-group, tiled codes: [fp16, INT32]
+  // few-token kernels on tiled activation codes: [per-group, per-channel][fp16, INT32]
+  GemmKernel kt[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
 };
 
 #define QOQ_K4(...) {{__VA_ARGS__, 0, false>, __VA_ARGS__, 1, false>}, {__VA_ARGS__, 0, true>, __VA_ARGS__, 1, true>}}
 // skinny names carry the ring depth only when it is not 2
-#define QOQ_KT(...) {__VA_ARGS__, 0, false, true>, __VA_ARGS__, 1, false, true>}
+#define QOQ_KT(...) \
+  {{__VA_ARGS__, 0, false, true>, __VA_ARGS__, 1, false, true>}, {__VA_ARGS__, 0, true, true>, __VA_ARGS__, 1, true, true>}}
 #define QOQ_SKINNY(MT, NBW, W, U)                                                                      \
   {0, MT, NBW, W, U, 2, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U, 2), "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U, \
    0, QOQ_KT(gemm_skinny_kernel<MT, NBW, W, U, 2)},
@@ -1415,7 +1416,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   const Config *cfg = nullptr;
   if (const char *name = getenv("QOQ_GEMM_CONFIG")) {
     for (int i = 0; i < kNumConfigs; ++i)
-      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kt[0])) cfg = &kConfigs[i];
+      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kt[0][0])) cfg = &kConfigs[i];
   }
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
@@ -1568,10 +1569,22 @@ void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const v
 void launch_w4a8_gemm_tiled(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
                             void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const Plan p = make_plan(M, N, K, true);
-  hipLaunchKernelGGL(p.cfg->kt[out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
+  hipLaunchKernelGGL(p.cfg->kt[0][out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
                      static_cast<const __half *>(sx), static_cast<const uint4 *>(packed),
                      static_cast<const uint16_t *>(meta), static_cast<const __half *>(sw), nullptr, nullptr, out,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), 1, nullptr);
+}
+
+// per-channel weights on tiled codes: the same plan, the kernels' per-channel instances
+void launch_w4a8_gemm_pc_tiled(const void *qx, const void *sx, const void *tx, const void *packed, const void *zeros,
+                               const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
+                               hipStream_t st) {
+  const Plan p = make_plan(M, N, K, true);
+  hipLaunchKernelGGL(p.cfg->kt[1][out_kind], p.grid, p.block, 0, st, static_cast<const int8_t *>(qx),
+                     static_cast<const __half *>(sx), static_cast<const uint4 *>(packed), nullptr,
+                     static_cast<const __half *>(sw), static_cast<const uint8_t *>(zeros),
+                     static_cast<const int *>(tx), out, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                     1, nullptr);
 }
 
 const char *gemm_tiled_plan_name(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, true).cfg->name; }

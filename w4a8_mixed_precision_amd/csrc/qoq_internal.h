@@ -20,6 +20,8 @@ void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void
                                        hipStream_t stream);
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream);
+void launch_quantize_activations_rowsum_tiled(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
+                                              hipStream_t stream);
 
 // producers with the quantization fused in (tiled 1: codes in the tiled layout,
 // M <= kTiledMaxM; 0: row-major; -1: no quantization, the fp16 value itself into
@@ -78,6 +80,9 @@ void launch_w4a8_gemm_pc(const void *qx, const void *sx, const void *tx, const v
 constexpr int64_t kTiledMaxM = 64;
 void launch_w4a8_gemm_tiled(const void *qx, const void *sx, const void *packed, const void *meta, const void *sw,
                             void *out, int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+void launch_w4a8_gemm_pc_tiled(const void *qx, const void *sx, const void *tx, const void *packed, const void *zeros,
+                               const void *sw, void *out, int out_kind, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream);
 const char *gemm_tiled_plan_name(int64_t M, int64_t N, int64_t K);
 size_t gemm_workspace_need(int64_t M, int64_t N, int64_t K);
 int gemm_plan_splits(int64_t M, int64_t N, int64_t K);

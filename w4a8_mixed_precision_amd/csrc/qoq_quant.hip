@@ -135,6 +135,13 @@ void launch_quantize_activations_tiled(const void *x, int64_t M, int64_t K, void
 }
 
 // one part per row: the code sum needs every code of the row
+void launch_quantize_activations_rowsum_tiled(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
+                                              hipStream_t stream) {
+  hipLaunchKernelGGL((quantize_act_kernel<true, true>), dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
+                     static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
+                     static_cast<__half *>(sx), static_cast<int *>(tx));
+}
+
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream) {
   hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,

@@ -65,6 +65,10 @@ _SIGNATURES = {
     "qoq_kv4_decode_attention": ([_c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                   _c_i64, _c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
     "qoq_quantize_activations_rowsum": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_quantize_activations_rowsum_tiled": ([_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_w4a8_gemm_pc_tiled": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+                               ctypes.c_int),
+    "qoq_w4a8_gemm_pc_tiled_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz,
                           _c_vp], ctypes.c_int),
     "qoq_w4a8_gemm_pc_i32": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp],
@@ -571,6 +575,50 @@ def w4a8_gemm_tiled_i32(qx_tiled, packed, meta, M: int, N: int, K: int, out=None
            lib().qoq_w4a8_gemm_tiled_i32(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(packed, "packed", torch.uint8),
                                          _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K,
                                          _stream(qx_tiled)))
+    return out
+
+
+def quantize_activations_rowsum_tiled(x: torch.Tensor, out=None):
+    """X fp16 [M, K] (M <= 64) -> (qx_tiled int8 [round_up(M, 16) * K], s_x fp16 [M],
+    t int32 [M] = sum_k qx): the inputs of w4a8_gemm_pc_tiled."""
+    M, K = x.shape
+    if out is None:
+        qx = torch.empty(tiled_bytes(M, K), dtype=torch.int8, device=x.device)
+        s_x = torch.empty(M, dtype=torch.float16, device=x.device)
+        t = torch.empty(M, dtype=torch.int32, device=x.device)
+    else:
+        qx, s_x, t = out
+    if qx.numel() < tiled_bytes(M, K):
+        raise ValueError(f"qx_tiled holds {qx.numel()} bytes, {tiled_bytes(M, K)} needed")
+    _check("qoq_quantize_activations_rowsum_tiled",
+           lib().qoq_quantize_activations_rowsum_tiled(_dev(x, "x", torch.float16), M, K, _dev(qx, "qx", torch.int8),
+                                                       _dev(s_x, "s_x", torch.float16), _dev(t, "t", torch.int32),
+                                                       _stream(x)))
+    return qx, s_x, t
+
+
+def w4a8_gemm_pc_tiled(qx_tiled, s_x, t, packed, zeros, s_w, M: int, N: int, K: int, out=None):
+    """w4a8_gemm_pc on tiled activation codes (M <= 64): out fp16 [M, N]."""
+    _check_tiled(qx_tiled, M, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=qx_tiled.device)
+    _check("qoq_w4a8_gemm_pc_tiled",
+           lib().qoq_w4a8_gemm_pc_tiled(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(s_x, "s_x", torch.float16),
+                                        _dev(t, "t", torch.int32), _dev(packed, "packed", torch.uint8),
+                                        _dev(zeros, "zeros", torch.uint8), _dev(s_w, "s_w", torch.float16),
+                                        _dev(out, "out", torch.float16), M, N, K, _stream(qx_tiled)))
+    return out
+
+
+def w4a8_gemm_pc_tiled_i32(qx_tiled, t, packed, zeros, M: int, N: int, K: int, out=None):
+    """Exact INT32 accumulators of the per-channel GEMM from tiled codes (M <= 64)."""
+    _check_tiled(qx_tiled, M, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=qx_tiled.device)
+    _check("qoq_w4a8_gemm_pc_tiled_i32",
+           lib().qoq_w4a8_gemm_pc_tiled_i32(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(t, "t", torch.int32),
+                                            _dev(packed, "packed", torch.uint8), _dev(zeros, "zeros", torch.uint8),
+                                            _dev(out, "acc", torch.int32), M, N, K, _stream(qx_tiled)))
     return out
 
 

@@ -243,15 +243,13 @@ __device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int 
                                               const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
                                               int M, int m0, int lane) {
   const int c32 = lane & 31, hi = lane >> 5, col = lane & 15;
+  const v4i zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = b * U + u;
     const bool ok = t < ngroups;
-    // past the wave's last group: its last group again (just fetched), zeroed by
-    // skinny32_compute.  Every load is unconditional and unmasked: a value merged
-    // from a conditional load, or selected right after its load, is consumed there,
-    // and the wait for it counts the prefetches issued behind it too.
-    const int j = min(wave + WAVES * (ok ? t : max(ngroups - 1, 0)), G - 1);
+    // past the wave's last group: in-bounds weight reload, zero activations
+    const int j = wave + WAVES * (ok ? t : 0);
 #pragma unroll
     for (int np = 0; np < NP; ++np) {
       const size_t chunk = static_cast<size_t>(min(strip0 + 2 * np + (c32 >> 4), NS - 1)) * G + j;
@@ -261,40 +259,35 @@ __device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int 
     }
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt) {
-      // rows past M read row M - 1 (in bounds); their results are never stored
-      const int rc = min(m0 + 32 * mt + c32, M - 1);
+      const int r = m0 + 32 * mt + c32;
+      const bool oka = ok && r < M;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int8_t *a =
-            AT ? qx + ((static_cast<size_t>(rc >> 4) * (K >> 6) + 2 * j + (kb >> 1)) * 64 + ((2 * kb + hi) & 3) * 16 +
-                       (rc & 15)) * 16
-               : qx + static_cast<size_t>(rc) * K + 128 * j + 32 * kb + 16 * hi;
-        B.a[u][mt][kb] = *reinterpret_cast<const v4i *>(a);
+            AT ? qx + ((static_cast<size_t>(r >> 4) * (K >> 6) + 2 * j + (kb >> 1)) * 64 + ((2 * kb + hi) & 3) * 16 +
+                       (r & 15)) * 16
+               : qx + static_cast<size_t>(oka ? r : 0) * K + 128 * j + 32 * kb + 16 * hi;
+        B.a[u][mt][kb] = oka ? *reinterpret_cast<const v4i *>(a) : zero4;
       }
     }
   }
 }
 
 template <int MT2, int NP, int U, bool PC>
-// batch b of a wave with ngroups groups: a slot past its last group adds zero
 __device__ __forceinline__ void skinny32_compute(const Skinny32Batch<MT2, NP, U> &B, v16i (&acc)[MT2][NP],
-                                                 int col, int b, int ngroups) {
-  const v4i zero4 = {0, 0, 0, 0};
+                                                 int col) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool ok = b * U + u < ngroups;     // uniform
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int np = 0; np < NP; ++np) {
-      v4i w[4];
-      weights_lane<PC>(B.p0[u][np], meta_of(B.md[u][np], col), w[0], w[2]);
-      weights_lane<PC>(B.p1[u][np], meta_of(B.md[u][np], col), w[1], w[3]);
+      v4i b[4];
+      weights_lane<PC>(B.p0[u][np], meta_of(B.md[u][np], col), b[0], b[2]);
+      weights_lane<PC>(B.p1[u][np], meta_of(B.md[u][np], col), b[1], b[3]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < MT2; ++mt)
-          acc[mt][np] = mfma32x32x32(ok ? B.a[u][mt][kb] : zero4, w[kb], acc[mt][np]);
+        for (int mt = 0; mt < MT2; ++mt) acc[mt][np] = mfma32x32x32(B.a[u][mt][kb], b[kb], acc[mt][np]);
     }
-  }
 }
 
 template <int MT2, int NP, int WAVES, int U, int R, int OUT, bool PC, bool AT = false>
@@ -319,48 +312,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
   const int ngroups = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
   const int nbatch = (ngroups + U - 1) / U;
 
-  // Ring of R batches, R - 1 in flight ahead of the one computed.  With at least two
-  // whole trips per wave, every load is unconditional: the loop runs whole trips
-  // (its last prefetches may reload the wave's last group) and the last batches,
-  // fewer than R and already loaded, follow it; a conditional prefetch made the
-  // compiler's wait before each batch also drain the batch just issued (measured
-  // at 64 tokens: 2-5 % slower).  Shorter waves prefetch only batches that exist:
-  // there the reloads cost more than the drain (QKV at 32 tokens, two batches per
-  // wave: 6 % slower).
   Skinny32Batch<MT2, NP, U> ring[R];
-  if (nbatch >= 2 * R) {
 #pragma unroll
-    for (int r = 0; r < R - 1; ++r)
-      skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0,
-                                               lane);
-    int b = 0;
-    for (; b + R <= nbatch; b += R) {
+  for (int r = 0; r < R - 1; ++r)
+    if (r < nbatch)
+      skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M,
+                                               m0, lane);
+  for (int b0 = 0; b0 < nbatch; b0 += R) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + r + R - 1, ngroups, wave, packed, meta,
-                                                 qx, strip0, NS, G, K, M, m0, lane);
-        skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col, b + r, ngroups);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R - 1; ++r)
-      if (b + r < nbatch) skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col, b + r, ngroups);
-  } else {
-#pragma unroll
-    for (int r = 0; r < R - 1; ++r)
-      if (r < nbatch)
-        skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M,
-                                                 m0, lane);
-    for (int b0 = 0; b0 < nbatch; b0 += R) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int b = b0 + r;
-        if (b >= nbatch) break;
-        if (b + R - 1 < nbatch)
-          skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta,
-                                                   qx, strip0, NS, G, K, M, m0, lane);
-        skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col, b, ngroups);
-      }
+    for (int r = 0; r < R; ++r) {
+      const int b = b0 + r;
+      if (b >= nbatch) break;
+      if (b + R - 1 < nbatch)
+        skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
+                                                 strip0, NS, G, K, M, m0, lane);
+      skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col);
     }
   }
 
@@ -1364,7 +1330,7 @@ const Config kConfigs[] = {
     QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 1, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3)
-    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
+    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
     QOQ_SKINNY32(1, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)

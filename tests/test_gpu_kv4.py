@@ -184,6 +184,34 @@ def test_kv4_decode_attention_batch64(gpu):
     _run_attention(gpu, rng, [1024] * 64, 32, 8)
 
 
+def test_kv4_attention_clamps_lengths(gpu):
+    """Sequence lengths are device data the host cannot check: 0 attends over the
+    first token, a length past max_len over max_len tokens (the documented clamp to
+    [1, max_len]); nothing outside the page table or the pool is read."""
+    rng = np.random.default_rng(21)
+    h, h_kv, n, max_len = 32, 8, 100, 100
+    max_pages = (max_len + P - 1) // P
+    pt = _pages(rng, 2, max_pages)
+    pool = torch.empty((pt.size + 3) * qoq.kv4_page_bytes(h_kv), dtype=torch.uint8, device=gpu)
+    pool.fill_(0xA5)
+    dpt = to_dev(pt, gpu)
+    ks = [_kv(rng, n, h_kv) for _ in range(2)]
+    vs = [_kv(rng, n, h_kv) for _ in range(2)]
+    for b in range(2):
+        qoq.kv4_write(to_dev(ks[b][None], gpu), to_dev(vs[b][None], gpu), to_dev(np.zeros(1, np.int32), gpu),
+                      dpt[b:b + 1], pool)
+    q = rng.standard_normal((2, h, D)).astype(np.float16)
+    say("kv4 attention lengths 0 and 1000 against max_len 100")
+    o = host(qoq.kv4_decode_attention(to_dev(q, gpu), pool, dpt, to_dev(np.array([0, 1000], np.int32), gpu), h_kv,
+                                      max_len))
+    for b, used in ((0, 1), (1, max_len)):
+        ref = kv.attention_reference(q[b], ks[b][:used], vs[b][:used], h_kv).astype(np.float64)
+        vq, vs_, vz = kv.kv_quantize(vs[b][:used])
+        vmax = np.abs(kv.kv_dequantize(vq, vs_, vz).astype(np.float64)).max()
+        err = np.abs(o[b].astype(np.float64) - ref)
+        assert np.all(err <= 2.0 ** -10 * (vmax + np.abs(ref))), (b, float(err.max()))
+
+
 def test_kv4_write_guards(gpu):
     """Positions past the page table and page ids outside the pool are skipped by the
     write kernel (its own bounds checks): the pool is left as it was."""

@@ -244,17 +244,18 @@ def test_pc_tiled_every_config_exact(gpu, config):
         check_fp16(out, r["acc"], r["s_x"], r["s_w"])
 
 
-def test_pc_tiled_layer_sampled(gpu):
-    """Llama-3-8B fused QKV at 64 tokens, full size, in the planner's configuration;
-    sampled rows x columns against the oracle."""
-    name, M = "llama3_8b_qkv", 64
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_pc_tiled_layer_sampled(gpu, M):
+    """Llama-3-8B fused QKV at the decode batch sizes, full size, in the planner's
+    configuration; sampled rows x columns against the oracle."""
+    name = "llama3_8b_qkv"
     L = wl.find(name)
     say(f"per-channel tiled gemm {name} M={M} plan={qoq.gemm_tiled_plan(M, L.N, L.K)}")
     w16 = _layer_weights(name)
     x16 = wl.activations_fp16(L, M)
     acc, out = _pc_tiled(gpu, x16, w16)
     rng = np.random.default_rng(M + 1)
-    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, 24)])
+    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, min(M, 24))])
     cols = np.unique(np.r_[0:16, L.N - 16:L.N, rng.integers(0, L.N, 200)])
     q, z, sw = o.quantize_weights_per_channel(w16[cols])
     qx, sx = o.quantize_activations(x16[rows])

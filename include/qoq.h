@@ -217,11 +217,13 @@ int qoq_kv4_page_bytes(int64_t h_kv, int64_t head_dim, size_t *bytes);
 
 /* KV write: quantize n_new new tokens per sequence into the cache.  k_new, v_new: fp16
  * [B, n_new, h_kv, 128] (16-byte aligned); token i of sequence b goes to position
- * positions[b] + i.  Per token and KV head, over the 128 values x with the range
- * widened to contain 0 (lo = min(0, min x), hi = max(0, max x)): s = fp16(fp32(hi -
- * lo) / 15), z = rne(-lo / s) in [0, 15], codes clamp(z + rne(x / s), 0, 15) (fp32
- * IEEE quotients; s = 0 for an all-zero vector, codes and z 0); s and z stored as
- * fp16.  One wave per (KV head, sequence, 16-token block of positions): a V word
+ * positions[b] + i.  Per token and KV head, over the range [lo, hi] = [min x, max x]
+ * of its 128 values ("QServe ..." summary, integer quantization; review §3.2, FP16
+ * scale and zero per head): s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s), codes
+ * clamp(z + rne(x / s), 0, 15) (fp32 IEEE quotients).  Where s = 0 (a constant
+ * vector) or |z| > 1024 (q - z would leave FP16's exact integers), the same over
+ * [min(lo, 0), max(hi, 0)] (z in [0, 15] then); s = 0 for an all-zero vector,
+ * codes and z 0; s and z stored as fp16.  One wave per (KV head, sequence, 16-token block of positions): a V word
  * holds four tokens, so each block's words are assembled once, merged with the
  * tokens already there; calls for the same pages must not overlap.  n_new <= 2^19,
  * B <= 65535, the sequence's positions below 2^30.
@@ -384,8 +386,8 @@ int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_
 
 /* Name of the kernel configuration qoq_w4a8_linear uses for this shape: a fused
  * configuration, or the qoq_gemm_tiled_plan (M <= 64) / qoq_gemm_plan name when it
- * quantizes and multiplies in two kernels ("invalid" for a shape it rejects).  QOQ_LINEAR_CONFIG=<fused name> or
- * "unfused" in the environment forces the choice where the shape allows it. */
+ * quantizes and multiplies in two kernels ("invalid" for a shape it rejects).  A linear
+ * override (qoq_set_plan_override) forces the choice where the shape allows it. */
 const char *qoq_linear_plan(int64_t M, int64_t N, int64_t K);
 
 /* Name of the index-th fused linear configuration, NULL past the last. */
@@ -397,15 +399,32 @@ const char *qoq_gemm_plan(int64_t M, int64_t N, int64_t K);
 
 /* Split-K factor of that plan (1 = no split; > 1 = workgroups per output tile, which
  * then needs the workspace), or a negative qoq_status for a shape the GEMM rejects
- * (INVALID also for M == 0).  QOQ_GEMM_SPLITS=<n> in the environment forces n
+ * (INVALID also for M == 0).  A split override (qoq_set_plan_override) forces n
  * (clamped to [1, min(16, K/128)]) for the kernels that support split-K. */
 int qoq_gemm_plan_splits(int64_t M, int64_t N, int64_t K);
 
 /* Name of the index-th kernel configuration the library contains (0-based), NULL past
- * the last.  Setting the environment variable QOQ_GEMM_CONFIG to one of these names
- * makes the GEMM entry points use that configuration for every shape (a measurement
- * and verification override; results are identical, only speed changes). */
+ * the last.  Forcing one of these names (qoq_set_plan_override) makes the GEMM entry
+ * points use that configuration for every shape. */
 const char *qoq_gemm_config_name(int index);
+
+/* Planner overrides, for measurement and verification only: results are identical
+ * under every override, only the speed changes.
+ *   gemm_config    a name from qoq_gemm_config_name, used for every GEMM shape
+ *                  (tiled-code entry points take it only if it is a few-token
+ *                  configuration); NULL or "" = none
+ *   splits         split-K factor for the kernels that support it (clamped to
+ *                  [1, min(16, K/128)]); 0 = none
+ *   regime         "skinny" (few-token kernels) or "tiled" (tile kernels); NULL or
+ *                  "" = none
+ *   linear_config  a name from qoq_linear_config_name or "unfused"; NULL or "" = none
+ * The call replaces all four values at once (all NULL / 0 clears them).  Their
+ * initial values come from the environment, read once per process:
+ * QOQ_GEMM_CONFIG, QOQ_GEMM_SPLITS, QOQ_GEMM_REGIME, QOQ_LINEAR_CONFIG.  The values
+ * are process-wide: set them only while no other thread plans or launches a GEMM.
+ * Errors: INVALID for an unknown name or a negative split factor (nothing changes). */
+int qoq_set_plan_override(const char *gemm_config, int32_t splits, const char *regime,
+                          const char *linear_config);
 
 /* ---- diagnostics (verification and measurement; not on the GEMM path) ---- */
 

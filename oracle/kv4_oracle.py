@@ -23,13 +23,17 @@ Readings (also listed with the design notes):
 
 R17 "Per-head dynamic" quantization is per token and per KV head: the D values of
     one head's key (or value) vector of one token share one (s, z).  UINT4 codes
-    (q_min = 0, q_max = 15) over the vector's range widened to contain 0 (as the
-    weights' groups, reading R4: z then lies in [0, 15], so q - z is a small exact
-    integer in FP16 arithmetic; without it z = rne(-X_min / s) grows without bound
-    for one-signed vectors with a narrow range); s = fp16(fp32(hi - lo) / 15) (fp32
-    IEEE, then fp16; the stored value is the one used); z = rne(-lo / s) (fp32),
-    stored as fp16 (exact); codes q = clamp(z + rne(x / s), 0, 15) (fp32 quotient,
-    reading R2 of the weights).  An all-zero vector: s = 0, every code and z are 0.
+    (q_min = 0, q_max = 15) by the summary's asymmetric quantizer over the vector's
+    own range [lo, hi] = [min x, max x]: s = fp16(fp32(hi - lo) / 15) (fp32 IEEE,
+    then fp16; the stored value is the one used), z = rne(-lo / s) (fp32 quotient),
+    stored as FP16 (the review's per-head FP16 zero); codes q = clamp(z + rne(x /
+    s), 0, 15) (fp32 quotient, zero added after rounding as reading R2 of the
+    weights).  The zero is an integer, so q - z is exact in FP16 arithmetic while
+    |z| <= 1024 (|q - z| <= 1039 < 2048).  Where that quantizer has no usable
+    result -- s = 0 (a constant vector) or |z| > 1024 (a narrow range far from 0,
+    where one step is below 1/68 of the offset) -- the range widened to contain 0
+    is used instead (lo = min(lo, 0), hi = max(hi, 0): z then lies in [0, 15]).
+    An all-zero vector: s = 0, every code and z are 0.
 R18 The dequantized cache value is K_hat = fp16((q - z) * s): q - z is an exact
     small integer and the product is rounded once to fp16 (the pages' FP16 math).
 R19 Decode attention over the dequantized values is the plain definition, computed
@@ -57,19 +61,30 @@ from __future__ import annotations
 import numpy as np
 
 Q_MAX = 15
+Z_LIMIT = 1024          # |z| beyond this: the widened range is used (R17)
+
+
+def _scale_zero(lo: np.ndarray, hi: np.ndarray):
+    """s = fp16(fp32(hi - lo) / 15) and z = rne(fp32(-lo / s)) (0 where s = 0)."""
+    rng = (hi - lo).astype(np.float32)
+    s = (rng / np.float32(Q_MAX)).astype(np.float16)
+    s32 = s.astype(np.float32)
+    safe = np.where(s32 == 0, np.float32(1), s32)
+    z = np.where(s32 == 0, np.float32(0), np.rint(-lo / safe)).astype(np.float32)
+    return s, s32, safe, z
 
 
 def kv_quantize(x16: np.ndarray):
     """Per-vector asymmetric UINT4 (R17).  x16: fp16 [..., D] -> (codes uint8
     [..., D], s fp16 [...], z fp16 [...])."""
     x = np.asarray(x16, dtype=np.float16).astype(np.float32)
-    lo = np.minimum(x.min(axis=-1), np.float32(0))
-    hi = np.maximum(x.max(axis=-1), np.float32(0))
-    rng = (hi - lo).astype(np.float32)
-    s = (rng / np.float32(Q_MAX)).astype(np.float16)
-    s32 = s.astype(np.float32)
-    safe = np.where(s32 == 0, np.float32(1), s32)
-    z = np.where(s32 == 0, np.float32(0), np.rint(-lo / safe)).astype(np.float32)
+    lo = x.min(axis=-1)
+    hi = x.max(axis=-1)
+    s, s32, safe, z = _scale_zero(lo, hi)
+    widen = (s32 == 0) | (np.abs(z) > Z_LIMIT)
+    lo = np.where(widen, np.minimum(lo, np.float32(0)), lo)
+    hi = np.where(widen, np.maximum(hi, np.float32(0)), hi)
+    s, s32, safe, z = _scale_zero(lo, hi)
     q = np.where(s32[..., None] == 0, 0, z[..., None] + np.rint(x / safe[..., None]))
     q = np.clip(q, 0, Q_MAX).astype(np.uint8)
     return q, s, z.astype(np.float16)

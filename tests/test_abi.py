@@ -55,21 +55,30 @@ def test_config_names():
 
 
 @pytest.mark.parametrize("regime", [None, "skinny", "tiled"])
-def test_plan_defined_for_every_shape(regime, monkeypatch):
+def test_plan_defined_for_every_shape(regime):
     """The planner (host code) returns a real configuration for every batch size,
     also under the measurement overrides."""
-    if regime:
-        monkeypatch.setenv("QOQ_GEMM_REGIME", regime)
     names = set(qoq.gemm_configs())
-    for (N, K) in [(16, 128), (6144, 4096), (4096, 14336), (59136, 8192), (8192, 29568)]:
-        for M in list(range(1, 300)) + [511, 512, 1023, 4096, 8192, 100000]:
-            assert qoq.gemm_plan(M, N, K) in names, (M, N, K, regime)
+    with qoq.plan_override(regime=regime):
+        for (N, K) in [(16, 128), (6144, 4096), (4096, 14336), (59136, 8192), (8192, 29568)]:
+            for M in list(range(1, 300)) + [511, 512, 1023, 4096, 8192, 100000]:
+                assert qoq.gemm_plan(M, N, K) in names, (M, N, K, regime)
     for name in names:
-        monkeypatch.setenv("QOQ_GEMM_CONFIG", name)
-        assert qoq.gemm_plan(77, 6144, 4096) == name
+        with qoq.plan_override(config=name):
+            assert qoq.gemm_plan(77, 6144, 4096) == name
 
 
-def test_split_plan_and_workspace(monkeypatch):
+def test_plan_override_rejects_unknown_names():
+    """Unknown names and negative split factors are refused and change nothing."""
+    before = qoq.gemm_plan(300, 6144, 4096)
+    for kw in ({"config": "no_such_config"}, {"regime": "sideways"}, {"linear": "nothing"}, {"splits": -1}):
+        with pytest.raises(qoq.QoQError) as e:
+            qoq.set_plan_override(**kw)
+        assert e.value.status == INVALID
+    assert qoq.gemm_plan(300, 6144, 4096) == before
+
+
+def test_split_plan_and_workspace():
     """Split-K plans: factor, workspace size (splits x M x N INT32 partial sums),
     and the override."""
     # down projection at M = 256: 128 x 128 tiles, 2 x 32 = 64 of them -> 8 splits
@@ -79,15 +88,14 @@ def test_split_plan_and_workspace(monkeypatch):
     assert qoq.gemm_workspace_bytes(256, 4096, 14336) == sp * 256 * 4096 * 4
     assert qoq.gemm_plan_splits(1, 6144, 4096) == 1 and qoq.gemm_workspace_bytes(1, 6144, 4096) == 0
     assert qoq.gemm_workspace_bytes(0, 6144, 4096) == 0
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "dma2_tm4_tn2")
     for want, K in [(3, 4096), (16, 4096), (2, 256), (1, 128)]:
-        monkeypatch.setenv("QOQ_GEMM_SPLITS", str(want))
-        assert qoq.gemm_plan_splits(300, 1024, K) == min(want, K // 128)
-    monkeypatch.setenv("QOQ_GEMM_SPLITS", "1")
-    assert qoq.gemm_workspace_bytes(300, 1024, 4096) == 0
-    monkeypatch.setenv("QOQ_GEMM_CONFIG", "skinny_mt1_nb1_w8_u2")   # no split-K support
-    monkeypatch.setenv("QOQ_GEMM_SPLITS", "8")
-    assert qoq.gemm_plan_splits(300, 1024, 4096) == 1
+        with qoq.plan_override(config="dma2_tm4_tn2", splits=want):
+            assert qoq.gemm_plan_splits(300, 1024, K) == min(want, K // 128)
+    with qoq.plan_override(config="dma2_tm4_tn2", splits=1):
+        assert qoq.gemm_workspace_bytes(300, 1024, 4096) == 0
+    skinny = [n for n in qoq.gemm_configs() if n.startswith("skinny")][0]
+    with qoq.plan_override(config=skinny, splits=8):               # no split-K support
+        assert qoq.gemm_plan_splits(300, 1024, 4096) == 1
     with pytest.raises(qoq.QoQError):
         qoq.gemm_plan_splits(0, 1024, 4096)
 
@@ -176,6 +184,57 @@ def test_diag_validation(L):
     assert L.qoq_dequantize_packed(ODD, FAKE, 32, 256, 128, FAKE, NUL) == ALIGNMENT
 
 
+def test_binding_size_checks():
+    """The binding compares every buffer with (M, N, K) before the library sees a
+    pointer: packed codes, group metadata (or per-channel zeros), channel scales,
+    token scales, code sums and the output shape (ValueError, nothing launched)."""
+    import torch
+    M, N, K = 4, 64, 256
+    i8 = lambda *sh: torch.zeros(sh, dtype=torch.int8)
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    f16 = lambda *sh: torch.zeros(sh, dtype=torch.float16)
+    i16 = lambda n: torch.zeros(n, dtype=torch.int16)
+    i32 = lambda *sh: torch.zeros(sh, dtype=torch.int32)
+    qx, sx, t = i8(M, K), f16(M), i32(M)
+    good = dict(packed=u8(N * K // 2), meta=i16(N * K // 128), s_w=f16(N))
+    bad = [dict(good, packed=u8(N * K // 2 - 16)), dict(good, meta=i16(N * K // 128 - 1)), dict(good, s_w=f16(N - 1))]
+    for b in bad:
+        with pytest.raises(ValueError):
+            qoq.w4a8_gemm(qx, sx, b["packed"], b["meta"], b["s_w"], N)
+        with pytest.raises(ValueError):
+            qoq.w4a8_linear(f16(M, K), b["packed"], b["meta"], b["s_w"], N)
+        with pytest.raises(ValueError):
+            qoq.w4a8_gemm_tiled(i8(16 * K), sx, b["packed"], b["meta"], b["s_w"], M, N, K)
+    for b in bad[:2]:
+        with pytest.raises(ValueError):
+            qoq.w4a8_gemm_i32(qx, b["packed"], b["meta"], N)
+        with pytest.raises(ValueError):
+            qoq.dequantize_packed(b["packed"], b["meta"], N, K)
+    with pytest.raises(ValueError):                                     # token scales
+        qoq.w4a8_gemm(qx, f16(M - 1), good["packed"], good["meta"], good["s_w"], N)
+    with pytest.raises(ValueError):
+        qoq.w4a8_linear(f16(M, K), good["packed"], good["meta"], good["s_w"], N, s_x=f16(M - 1))
+    with pytest.raises(ValueError):                                     # output shape
+        qoq.w4a8_gemm(qx, sx, good["packed"], good["meta"], good["s_w"], N, out=f16(M, N - 16))
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_i32(qx, good["packed"], good["meta"], N, out=i32(M + 1, N))
+    with pytest.raises(ValueError):
+        qoq.w4a8_linear(f16(M, K), good["packed"], good["meta"], good["s_w"], N, out=f16(N, M))
+    # per-channel: one zero byte per column, code sums per token
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_pc(qx, sx, t, good["packed"], u8(N - 1), good["s_w"], N)
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_pc(qx, sx, i32(M - 1), good["packed"], u8(N), good["s_w"], N)
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_pc_i32(qx, t, u8(N * K // 2 - 1), u8(N), N)
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_pc_tiled(i8(16 * K), sx, t, good["packed"], u8(N - 1), good["s_w"], M, N, K)
+    with pytest.raises(ValueError):
+        qoq.w4a8_gemm_pc_tiled_i32(i8(16 * K), t, good["packed"], u8(N), M, N, K, out=i32(M, N + 16))
+    with pytest.raises(ValueError):                                     # attention output shape
+        qoq.kv4_decode_attention(f16(2, 8, 128), u8(8704), i32(2, 1), i32(2), 1, 64, out=f16(2, 8, 64))
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 256), dtype=torch.float16)
@@ -183,7 +242,7 @@ def test_binding_rejects_cpu_tensors():
         qoq.quantize_activations(x)
 
 
-def test_linear_plan_and_workspace(monkeypatch):
+def test_linear_plan_and_workspace():
     """Fused linear for a few tokens and K <= 8192 (no workspace); two kernels
     otherwise: tiled codes (whole 16-row blocks) and s_X up to 64 tokens, row-major
     codes, s_X and the GEMM's own workspace beyond."""
@@ -207,15 +266,15 @@ def test_linear_plan_and_workspace(monkeypatch):
         assert qoq.linear_workspace_bytes(M, N, K) == r256(M * K) + r256(2 * M) + qoq.gemm_workspace_bytes(M, N, K)
     assert qoq.linear_workspace_bytes(0, 6144, 4096) == 0
     assert qoq.linear_plan(0, 6144, 4096) == "invalid"
-    monkeypatch.setenv("QOQ_LINEAR_CONFIG", "unfused")
-    assert qoq.linear_plan(1, 6144, 4096) == qoq.gemm_tiled_plan(1, 6144, 4096)
-    assert qoq.linear_workspace_bytes(1, 6144, 4096) == 16 * 4096 + 256
+    with qoq.plan_override(linear="unfused"):
+        assert qoq.linear_plan(1, 6144, 4096) == qoq.gemm_tiled_plan(1, 6144, 4096)
+        assert qoq.linear_workspace_bytes(1, 6144, 4096) == 16 * 4096 + 256
     for name in fused:                             # forced: any shape the kernel can hold
-        monkeypatch.setenv("QOQ_LINEAR_CONFIG", name)
-        assert qoq.linear_plan(4, 6144, 4096) == name
-        assert qoq.linear_plan(8, 6144, 2048) == name
-        assert qoq.linear_plan(1, 59136, 8192) == name
-        assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
+        with qoq.plan_override(linear=name):
+            assert qoq.linear_plan(4, 6144, 4096) == name
+            assert qoq.linear_plan(8, 6144, 2048) == name
+            assert qoq.linear_plan(1, 59136, 8192) == name
+            assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
 
 
 def test_tiled_plans_and_validation(L):

@@ -82,7 +82,11 @@ def test_kv4_write_bit_exact(gpu):
     k = _kv(rng, B * n_tot, h_kv).reshape(B, n_tot, h_kv, D)
     v = _kv(rng, B * n_tot, h_kv, 0.3).reshape(B, n_tot, h_kv, D)
     k[0, 5] = 0                                             # an all-zero vector
-    v[1, 7] = np.abs(v[1, 7]) + np.float16(2)               # one-signed, away from 0
+    v[1, 7] = np.abs(v[1, 7]) + np.float16(2)               # one-signed, away from 0: z < 0
+    v[1, 8] = -v[1, 7]                                      # all negative: z > 15
+    k[1, 11] = np.float16(3.25)                             # constant: widened range
+    k[0, 12] = (np.float16(40) + k[0, 12] * np.float16(0.01)).astype(np.float16)   # narrow, far: widened
+    k[0, 13] = (np.float16(2) + np.abs(k[0, 13]) * np.float16(0.3)).astype(np.float16)
     halves = (np.arange(D) % 31 / 2).astype(np.float16)       # 0 .. 15 in steps of 1/2: s = 1, z = 0,
     for t in (9, 40):                                       # every odd value an exact tie x / s
         k[2, t, 1] = halves

@@ -20,6 +20,8 @@ from oracle import qoq_oracle as o
 from w4a8_mixed_precision_amd import qoq
 from w4a8_mixed_precision_amd import workloads as wl
 
+from fp16_sweep import EXHAUSTIVE_ABSMAX, exhaustive_rows
+
 pytestmark = pytest.mark.gpu
 
 RTOL = 1e-3
@@ -128,6 +130,31 @@ def _act_cases():
 @pytest.mark.parametrize("name,x", list(_act_cases()), ids=lambda v: v if isinstance(v, str) else "")
 def test_quantize_activations_bit_exact(gpu, name, x):
     say(f"quantize_activations {name} {x.shape}")
+    qx, sx = qoq.quantize_activations(to_dev(x, gpu))
+    want_q, want_s = o.quantize_activations(x)
+    assert np.array_equal(host(qx), want_q)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+
+
+@pytest.mark.parametrize("absmax", EXHAUSTIVE_ABSMAX)
+def test_quantize_activations_every_fp16(gpu, absmax):
+    """Every finite fp16 input through the per-token quantizer (row-major codes),
+    at each absmax: codes and scales bit-exact against the oracle's IEEE divide."""
+    x = exhaustive_rows(absmax)
+    say(f"quantize_activations every fp16 <= {absmax}: {x.shape}")
+    qx, sx = qoq.quantize_activations(to_dev(x, gpu))
+    want_q, want_s = o.quantize_activations(x)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+    got = host(qx)
+    bad = np.argwhere(got != want_q)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: x={x[tuple(bad[0])]}"
+
+
+def test_quantize_activations_every_fp16_one_launch(gpu):
+    """The same rows for all absmax values in one launch (many rows: one workgroup
+    per row instead of several per row)."""
+    x = np.concatenate([exhaustive_rows(a) for a in EXHAUSTIVE_ABSMAX], axis=0)
+    say(f"quantize_activations every fp16, one launch {x.shape}")
     qx, sx = qoq.quantize_activations(to_dev(x, gpu))
     want_q, want_s = o.quantize_activations(x)
     assert np.array_equal(host(qx), want_q)
@@ -248,23 +275,13 @@ def test_dequant_matches_oracle_layer(gpu):
 # GEMM
 # ---------------------------------------------------------------------------
 def _gemm_full(dev, x16, w16, regime=None, config=None, splits=None):
-    if regime:
-        os.environ["QOQ_GEMM_REGIME"] = regime
-    if config:
-        os.environ["QOQ_GEMM_CONFIG"] = config
-    if splits:
-        os.environ["QOQ_GEMM_SPLITS"] = str(splits)
-    try:
+    with qoq.plan_override(config=config, splits=splits or 0, regime=regime):
         N = w16.shape[0]
         packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, dev))
         qx, s_x = qoq.quantize_activations(to_dev(x16, dev))
         acc = qoq.w4a8_gemm_i32(qx, packed, meta, N)
         out = qoq.w4a8_gemm(qx, s_x, packed, meta, s_w, N)
         return host(acc), host(out)
-    finally:
-        os.environ.pop("QOQ_GEMM_REGIME", None)
-        os.environ.pop("QOQ_GEMM_CONFIG", None)
-        os.environ.pop("QOQ_GEMM_SPLITS", None)
 
 
 SMALL_SHAPES = [  # (M, N, K): tiles, ragged tails and the degenerate sizes
@@ -319,14 +336,9 @@ def test_split_k_exact(gpu, config, splits):
     fp16 to the oracle."""
     for (M, N, K) in [(70, 272, 2048), (129, 528, 1920), (5, 16, 2048)]:
         say(f"gemm split-K config={config} splits={splits} M={M} N={N} K={K}")
-        os.environ["QOQ_GEMM_CONFIG"] = config
-        os.environ["QOQ_GEMM_SPLITS"] = str(splits)
-        try:
+        with qoq.plan_override(config=config, splits=splits):
             assert qoq.gemm_plan_splits(M, N, K) == min(splits, K // 128)
             assert qoq.gemm_workspace_bytes(M, N, K) == min(splits, K // 128) * M * N * 4
-        finally:
-            os.environ.pop("QOQ_GEMM_CONFIG", None)
-            os.environ.pop("QOQ_GEMM_SPLITS", None)
         rng = np.random.default_rng(M * 3 + N + K + splits)
         x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
         w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
@@ -334,6 +346,9 @@ def test_split_k_exact(gpu, config, splits):
         acc, out = _gemm_full(gpu, x16, w16, config=config, splits=splits)
         assert np.array_equal(acc, r["acc"])
         check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+SPLIT_REUSE_CONFIG = "dma2_tm4_tn1"
 
 
 def test_split_k_workspace_reuse(gpu):
@@ -344,13 +359,8 @@ def test_split_k_workspace_reuse(gpu):
     cases = [(129, 528, 1920, 5), (70, 272, 2048, 16), (300, 160, 1024, 2), (129, 528, 1920, 3)]
     need = 0
     for (M, N, K, sp) in cases:
-        os.environ["QOQ_GEMM_CONFIG"] = "wide2_tm2_tn1"
-        os.environ["QOQ_GEMM_SPLITS"] = str(sp)
-        try:
+        with qoq.plan_override(config=SPLIT_REUSE_CONFIG, splits=sp):
             need = max(need, qoq.gemm_workspace_bytes(M, N, K))
-        finally:
-            os.environ.pop("QOQ_GEMM_CONFIG", None)
-            os.environ.pop("QOQ_GEMM_SPLITS", None)
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=gpu)
     for rep in range(2):
         for (M, N, K, sp) in cases:
@@ -360,14 +370,9 @@ def test_split_k_workspace_reuse(gpu):
             r = o.w4a8_reference(x16, w16)
             packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
             qx, s_x = qoq.quantize_activations(to_dev(x16, gpu))
-            os.environ["QOQ_GEMM_CONFIG"] = "wide2_tm2_tn1"
-            os.environ["QOQ_GEMM_SPLITS"] = str(sp)
-            try:
+            with qoq.plan_override(config=SPLIT_REUSE_CONFIG, splits=sp):
                 acc = qoq.w4a8_gemm_i32(qx, packed, meta, N, workspace=ws)
                 out = qoq.w4a8_gemm(qx, s_x, packed, meta, s_w, N, workspace=ws)
-            finally:
-                os.environ.pop("QOQ_GEMM_CONFIG", None)
-                os.environ.pop("QOQ_GEMM_SPLITS", None)
             assert np.array_equal(host(acc), r["acc"]), (rep, M, N, K, sp)
             check_fp16(host(out), r["acc"], r["s_x"], r["s_w"])
 
@@ -463,16 +468,12 @@ def test_regimes_agree_on_layer(gpu):
 # ---------------------------------------------------------------------------
 # linear = quantize + GEMM in one call (fused kernel for few tokens)
 # ---------------------------------------------------------------------------
-def _linear(dev, x16, packed, meta, s_w, N, config=None):
-    if config:
-        os.environ["QOQ_LINEAR_CONFIG"] = config
-    try:
+def _linear(dev, x16, packed, meta, s_w, N, config=None, workspace=None):
+    with qoq.plan_override(linear=config):
         x = to_dev(x16, dev)
         s_x = torch.empty(x16.shape[0], dtype=torch.float16, device=dev)
-        out = qoq.w4a8_linear(x, packed, meta, s_w, N, s_x=s_x)
+        out = qoq.w4a8_linear(x, packed, meta, s_w, N, s_x=s_x, workspace=workspace)
         return host(out), host(s_x)
-    finally:
-        os.environ.pop("QOQ_LINEAR_CONFIG", None)
 
 
 def _linear_configs():
@@ -506,6 +507,60 @@ def test_linear_matches_two_step_and_oracle(gpu, config):
         assert np.array_equal(sx.view(np.uint16), host(sx_d).view(np.uint16))
         r = o.w4a8_reference(x16, w16)
         check_fp16(out, r["acc"], r["s_x"], r["s_w"])
+
+
+LINEAR_LARGE = [("ragged", 65, 144, 256), ("llama3_8b_down", 256, 4096, 14336),
+                ("llama3_8b_gate_up", 1024, 28672, 4096), ("llama3_8b_gate_up_prefill", 4096, 28672, 4096)]
+
+
+@pytest.mark.parametrize("name,M,N,K", LINEAR_LARGE)
+def test_linear_large_m(gpu, name, M, N, K):
+    """qoq_w4a8_linear past 64 tokens, in the planner's launch configuration: the
+    row-major codes, s_X and (split-K plans) the INT32 partial sums share one caller
+    workspace, filled with garbage first.  The fp16 output is bit-equal to quantize
+    + GEMM through the separate entry points and the token scales to the oracle's;
+    against the oracle on sampled rows x columns (every element for the ragged
+    shape): exact INT32 accumulators of the same codes and the fp16 output."""
+    rng = np.random.default_rng(M + N + K)
+    if name == "ragged":
+        x16 = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+        x16[:, rng.choice(K, 3, replace=False)] *= 20
+        x16[7] = 0                                     # an all-zero token
+        w16 = (rng.standard_normal((N, K)) * 0.03).astype(np.float16)
+    else:
+        L = wl.find(name)
+        assert (L.N, L.K) == (N, K)
+        w16 = _layer_weights(name)
+        x16 = wl.activations_fp16(L, M)
+    say(f"linear {name} M={M} N={N} K={K} plan={qoq.linear_plan(M, N, K)} "
+        f"splits={qoq.gemm_plan_splits(M, N, K)} workspace={qoq.linear_workspace_bytes(M, N, K)}")
+    packed, meta, s_w = qoq.quantize_pack_weights(to_dev(w16, gpu))
+    need = qoq.linear_workspace_bytes(M, N, K)
+    assert need > 0
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=gpu)
+    x = to_dev(x16, gpu)
+    s_x = torch.empty(M, dtype=torch.float16, device=gpu)
+    out = qoq.w4a8_linear(x, packed, meta, s_w, N, s_x=s_x, workspace=ws)
+    qx_d, sx_d = qoq.quantize_activations(x)
+    acc_d = qoq.w4a8_gemm_i32(qx_d, packed, meta, N)
+    ref = qoq.w4a8_gemm(qx_d, sx_d, packed, meta, s_w, N)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(s_x.view(torch.int16), sx_d.view(torch.int16))
+    if name == "ragged":
+        rows, cols = np.arange(M), np.arange(N)
+    else:
+        rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, 24)])
+        cols = np.unique(np.r_[0:16, N - 16:N, rng.integers(0, N, 200)])
+    q0, sw = o.quantize_weights_level0(w16[cols])
+    q, z, s = o.quantize_weights_level1(q0)
+    qx, sx = o.quantize_activations(x16[rows])
+    want = o.contract(qx, o.dequantize_level1(q, z, s))
+    ri = torch.from_numpy(rows).to(gpu)
+    ci = torch.from_numpy(cols).to(gpu)
+    assert np.array_equal(host(acc_d[ri][:, ci]), want)
+    check_fp16(host(out[ri][:, ci]), want, sx, sw)
+    assert np.array_equal(host(s_x)[rows].view(np.uint16), sx.view(np.uint16))
 
 
 def test_linear_layers_sampled(gpu):

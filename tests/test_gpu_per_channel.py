@@ -89,20 +89,13 @@ def test_rowsum_bit_exact(gpu, M, K):
 
 
 def _pc_full(dev, x16, w16, regime=None, config=None, splits=None):
-    env = {"QOQ_GEMM_REGIME": regime, "QOQ_GEMM_CONFIG": config, "QOQ_GEMM_SPLITS": str(splits) if splits else None}
-    for k, v in env.items():
-        if v:
-            os.environ[k] = v
-    try:
+    with qoq.plan_override(config=config, splits=splits or 0, regime=regime):
         N = w16.shape[0]
         packed, zeros, s_w = qoq.quantize_pack_weights(to_dev(w16, dev), group=0)
         qx, s_x, t = qoq.quantize_activations_rowsum(to_dev(x16, dev))
         acc = qoq.w4a8_gemm_pc_i32(qx, t, packed, zeros, N)
         out = qoq.w4a8_gemm_pc(qx, s_x, t, packed, zeros, s_w, N)
         return host(acc), host(out)
-    finally:
-        for k in env:
-            os.environ.pop(k, None)
 
 
 SHAPES = [(1, 16, 128), (8, 512, 512), (3, 48, 256), (17, 64, 384), (65, 144, 256), (100, 272, 512),
@@ -199,9 +192,7 @@ def test_rowsum_tiled_bit_exact(gpu, M, K):
 
 
 def _pc_tiled(dev, x16, w16, config=None):
-    if config:
-        os.environ["QOQ_GEMM_CONFIG"] = config
-    try:
+    with qoq.plan_override(config=config):
         M, K = x16.shape
         N = w16.shape[0]
         packed, zeros, s_w = qoq.quantize_pack_weights(to_dev(w16, dev), group=0)
@@ -209,8 +200,6 @@ def _pc_tiled(dev, x16, w16, config=None):
         acc = qoq.w4a8_gemm_pc_tiled_i32(qt, t, packed, zeros, M, N, K)
         out = qoq.w4a8_gemm_pc_tiled(qt, s_x, t, packed, zeros, s_w, M, N, K)
         return host(acc), host(out)
-    finally:
-        os.environ.pop("QOQ_GEMM_CONFIG", None)
 
 
 TILED_SHAPES = [(1, 16, 128), (3, 48, 256), (17, 64, 384), (37, 144, 1152), (64, 272, 512)]

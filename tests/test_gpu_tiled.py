@@ -18,6 +18,8 @@ from oracle import qoq_oracle as o
 from w4a8_mixed_precision_amd import qoq
 from w4a8_mixed_precision_amd import workloads as wl
 
+from fp16_sweep import EXHAUSTIVE_ABSMAX, exhaustive_rows
+
 pytestmark = pytest.mark.gpu
 
 RTOL = 1e-3
@@ -84,16 +86,31 @@ def test_quantize_tiled_bit_exact(gpu, name, x):
 
 
 def _tiled_gemm(dev, x16, packed, meta, s_w, N, config=None):
-    if config:
-        os.environ["QOQ_GEMM_CONFIG"] = config
-    try:
+    with qoq.plan_override(config=config):
         M, K = x16.shape
         qt, sx = qoq.quantize_activations_tiled(to_dev(x16, dev))
         acc = qoq.w4a8_gemm_tiled_i32(qt, packed, meta, M, N, K)
         out = qoq.w4a8_gemm_tiled(qt, sx, packed, meta, s_w, M, N, K)
         return host(acc), host(out)
-    finally:
-        os.environ.pop("QOQ_GEMM_CONFIG", None)
+
+
+@pytest.mark.parametrize("absmax", EXHAUSTIVE_ABSMAX)
+def test_quantize_tiled_every_fp16(gpu, absmax):
+    """Every finite fp16 input through the tiled quantizer (and its code-sum form),
+    at each absmax of the row-major exhaustive test: codes, scales and code sums
+    bit-exact against the oracle."""
+    x = exhaustive_rows(absmax)
+    M, K = x.shape
+    assert M <= qoq.TILED_MAX_M
+    say(f"quantize_activations_tiled every fp16 <= {absmax}: {x.shape}")
+    want_q, want_s = o.quantize_activations(x)
+    qt, sx = qoq.quantize_activations_tiled(to_dev(x, gpu))
+    assert np.array_equal(untile(host(qt), M, K), want_q)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+    qt, sx, t = qoq.quantize_activations_rowsum_tiled(to_dev(x, gpu))
+    assert np.array_equal(untile(host(qt), M, K), want_q)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+    assert np.array_equal(host(t), o.activation_row_sums(want_q))
 
 
 def _skinny_configs():

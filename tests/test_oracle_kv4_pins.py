@@ -11,16 +11,22 @@ from oracle import kv4_oracle as kv
 from tests.exact_float import FP16, FP32, round_float, rne_int
 
 
+def _scale_zero_exact(lo, hi):
+    s = round_float(round_float(round_float(hi - lo, FP32) / 15, FP32), FP16)
+    return s, (rne_int(round_float(-lo / s, FP32)) if s != 0 else 0)
+
+
 def _quant_exact(x16):
-    """R17 by rationals: lo = min(0, min x), hi = max(0, max x), s = RN16(RN32(RN32(hi
-    - lo) / 15)), z = rne(RN32(-lo / s)), q = clamp(z + rne(RN32(x / s)), 0, 15)."""
+    """R17 by rationals: over [lo, hi] = [min x, max x], s = RN16(RN32(RN32(hi - lo) /
+    15)), z = rne(RN32(-lo / s)); if s = 0 or |z| > 1024, the same over [min(lo, 0),
+    max(hi, 0)]; q = clamp(z + rne(RN32(x / s)), 0, 15)."""
     xs = [Fraction(float(v)) for v in x16]
-    lo, hi = min(min(xs), 0), max(max(xs), 0)
-    rng32 = round_float(hi - lo, FP32)
-    s = round_float(round_float(rng32 / 15, FP32), FP16)
+    lo, hi = min(xs), max(xs)
+    s, z = _scale_zero_exact(lo, hi)
+    if s == 0 or abs(z) > 1024:
+        s, z = _scale_zero_exact(min(lo, 0), max(hi, 0))
     if s == 0:
         return [0] * len(xs), s, 0
-    z = rne_int(round_float(-lo / s, FP32))
     q = [min(max(z + rne_int(round_float(x / s, FP32)), 0), 15) for x in xs]
     return q, s, z
 
@@ -28,36 +34,61 @@ def _quant_exact(x16):
 @pytest.mark.parametrize("scale", [1e-3, 0.7, 40.0])
 def test_kv_quantize_matches_exact_rationals(scale):
     rng = np.random.default_rng(int(scale * 1000))
-    x = (rng.standard_normal((6, 128)) * scale).astype(np.float16)
-    x[1] = np.abs(x[1])                              # one-signed vectors: z = 0 / 15
+    x = (rng.standard_normal((10, 128)) * scale).astype(np.float16)
+    x[1] = np.abs(x[1])                              # one-signed vectors: z < 0 / z > 15
     x[2] = -np.abs(x[2])
+    x[3] = np.abs(x[3]) + np.float16(3 * scale)      # one-signed, offset from 0
+    x[4] = -x[3]
+    x[5] = (np.float16(40 * scale) + x[5] * np.float16(0.02)).astype(np.float16)   # narrow, far from 0
+    x[6] = np.float16(2.5 * scale)                   # constant: s = 0 over its own range
+    x[7] = (np.float16(1000 * scale) + np.abs(x[7]) * np.float16(0.01)).astype(np.float16)  # |z| > 1024
+    x[8, :64] = np.float16(scale)                    # two values only
+    x[8, 64:] = np.float16(3 * scale)
     q, s, z = kv.kv_quantize(x)
-    for i in range(6):
+    for i in range(10):
         wq, ws, wz = _quant_exact(x[i])
         assert [int(v) for v in q[i]] == wq
         assert Fraction(float(s[i])) == ws and float(z[i]) == wz
 
 
 def test_kv_quantize_error_bound():
-    """|x - (q - z) s| <= s / 2 (+ the fp16 rounding of s, relative 2^-11 of the
-    range) for every element; zeros in [0, 15]; codes span [0, 15]."""
+    """|x - (q - z) s| <= s / 2 (+ the fp16 rounding of s: relative 2^-11 of the
+    range, 15 s) for every element; zeros are integers in [-1024, 1024]; codes span
+    [0, 15]; one-signed vectors take the step of their own range (the widened range
+    would double it or more)."""
     rng = np.random.default_rng(3)
     x = (rng.standard_normal((200, 128)) * rng.uniform(0.01, 10, (200, 1))).astype(np.float16)
     x[::7] = np.abs(x[::7]) + np.float16(3)              # one-signed, offset away from 0
     q, s, z = kv.kv_quantize(x)
-    xd = (q.astype(np.float64) - z.astype(np.float64)[:, None]) * s.astype(np.float64)[:, None]
+    s64 = s.astype(np.float64)[:, None]
+    xd = (q.astype(np.float64) - z.astype(np.float64)[:, None]) * s64
     err = np.abs(xd - x.astype(np.float64))
-    span = (np.maximum(x.max(1), 0) - np.minimum(x.min(1), 0)).astype(np.float64)
-    assert np.all(err <= s.astype(np.float64)[:, None] / 2 + span[:, None] * 2.0 ** -10)
+    assert np.all(err <= s64 / 2 + 15 * s64 * 2.0 ** -10)
     assert q.max() == 15 and q.min() == 0
-    assert np.all((z >= 0) & (z <= 15)) and np.array_equal(z, np.rint(z))
+    assert np.all(np.abs(z) <= 1024) and np.array_equal(z, np.rint(z))
+    own = (x[::7].max(1).astype(np.float32) - x[::7].min(1).astype(np.float32)) / 15
+    assert np.allclose(s[::7].astype(np.float32), own, rtol=2.0 ** -10)
+    assert np.all(z[::7] < 0)
 
 
 def test_kv_quantize_degenerate_vectors():
-    x = np.zeros((3, 128), np.float16)
+    """All zero; constant (own range 0: the widened range [0, 2.5]); a single
+    non-zero; a narrow range far from 0 (z beyond 1024: widened); a two-valued
+    one-signed vector (own range: exact)."""
+    x = np.zeros((6, 128), np.float16)
     x[1] = 2.5                                            # constant: lo = 0, s = 1/6, z = 0, q = 15
     x[2, 7] = -0.375                                      # a single non-zero
+    x[3] = 100.0
+    x[3, ::2] = 100.0625                                  # own range 1/16: z = -24000 -> widened
+    x[4, :64] = 1.0                                       # own range [1, 2.5]: s = 0.1, z = -10
+    x[4, 64:] = 2.5
+    x[5] = -x[4]                                          # [-2.5, -1]: s = 0.1, z = 25
     q, s, z = kv.kv_quantize(x)
+    assert float(s[3]) == float(np.float16(np.float32(100.0625) / 15)) and float(z[3]) == 0
+    assert np.all(q[3] == 15)
+    assert float(s[4]) == float(np.float16(0.1)) and float(z[4]) == -10
+    assert np.all(q[4, :64] == 0) and np.all(q[4, 64:] == 15)
+    assert float(z[5]) == 25 and np.all(q[5, :64] == 15) and np.all(q[5, 64:] == 0)
     back = kv.kv_dequantize(q, s, z).astype(np.float64)
     assert float(s[0]) == 0 and float(z[0]) == 0 and not q[0].any() and not back[0].any()
     assert float(z[1]) == 0 and np.all(q[1] == 15) and np.allclose(back[1], 2.5, rtol=2.0 ** -10)

@@ -490,6 +490,11 @@ int qoq_gemm_plan_splits(int64_t M, int64_t N, int64_t K) {
 
 const char *qoq_gemm_config_name(int index) { return qoq::gemm_config_name(index); }
 
+int qoq_set_plan_override(const char *gemm_config, int32_t splits, const char *regime,
+                          const char *linear_config) {
+  return qoq::set_plan_override(gemm_config, splits, regime, linear_config) == 0 ? QOQ_OK : QOQ_ERR_INVALID;
+}
+
 int qoq_dequantize_packed(const void *packed_w, const void *group_meta, int64_t N, int64_t K, int32_t group,
                           void *w_i8, void *stream) {
   int st = check_nk(N, K, group);

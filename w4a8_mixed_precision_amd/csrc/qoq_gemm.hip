@@ -826,6 +826,11 @@ __global__ __launch_bounds__(256, 2) void gemm_wide2_kernel(const int8_t *__rest
 // ---------------------------------------------------------------------------
 // Copy-engine helpers: global -> LDS copies (global_load_lds) count in vmcnt like
 // loads, so a wave waits for the copies it needs with a vmcnt-only wait.
+// The rule every such wait follows: copies retire in issue order among
+// themselves, but not in order with register loads.  A wait for copy c may
+// therefore leave in flight only copies issued after c: the count is the number
+// of copies issued after c (register loads issued after c are then waited for as
+// well, which costs time but not correctness).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -848,7 +853,7 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // loads it needs).  A fragments are read one k block ahead of the MFMAs that use
 // them.  Per group j: dequantize B(j); copy A(j+2) and load B(j+2); MFMAs of j;
 // wait for A(j+1)'s copies; barrier.  The copies and the register loads share
-// vmcnt and retire in issue order.
+// vmcnt; the waits follow the copy rule above.
 // ---------------------------------------------------------------------------
 template <int TN>
 struct DBSet {
@@ -924,11 +929,10 @@ __device__ __forceinline__ void dma2_step(int j, int G, DBSet<TN> &cur, int8_t *
       for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma32x32x32(af[kb & 1][tm], b[kb][tn], acc[tm][tn]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A(j+1) was copied one group ago.  Vector-memory reads (the copies into LDS
-  // included) retire in issue order, so a count of TM leaves at most the last TM
-  // operations of this group (code and metadata loads) in flight: A(j+1) and B(j+1)
-  // have landed, and so have this group's A(j+2) copies.  Waiting only for what
-  // came before this group (a count of TM + 3 TN) measured the same on MI355X.
+  // A(j+1) was copied one group ago.  The only copies issued after it are this
+  // group's TM copies of A(j+2), so vmcnt(TM) guarantees A(j+1) is in LDS (the
+  // copy rule above); B(j+2)'s register loads, issued after those copies, are
+  // partly waited for as well.
   QOQ_WAIT_VMCNT(TM);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -1142,10 +1146,9 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // A(j+1) must be resident.  Copies retire in order among themselves but not in
-  // order with register loads, so the count allows only the copies issued after
-  // A(j+1) to be outstanding: AS == 3, this step's 4 copies of A(j+2); AS == 2, none
-  // (A(j+1) is this step's copy).
+  // A(j+1) must be resident.  By the copy rule above the count may include only
+  // the copies issued after A(j+1)'s: AS == 3, this step's 4 copies of A(j+2);
+  // AS == 2, none (A(j+1) is this step's copy).
   QOQ_WAIT_VMCNT(AS == 3 ? 4 : 0);
   QOQ_WAIT_LGKMCNT0();                          // this wave's B(j+1) fragments are in LDS
   __builtin_amdgcn_s_barrier();
@@ -1287,6 +1290,22 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const int *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// Measurement overrides of the planner (results never depend on them, only the
+// speed does): a configuration forced for every shape, a split-K factor, the
+// few-token or the tile regime, the linear entry point's fused configuration.
+// They are taken from the environment once per process (QOQ_GEMM_CONFIG,
+// QOQ_GEMM_SPLITS, QOQ_GEMM_REGIME, QOQ_LINEAR_CONFIG) and replaced through
+// qoq_set_plan_override; the launch path copies them under a mutex.
+// ---------------------------------------------------------------------------
+struct Overrides {
+  int config = -1;          // index into kConfigs, -1: none
+  int splits = 0;           // 0: none
+  int regime = 0;           // 0: none, 1: few-token kernels, 2: tile kernels
+  int linear = -2;          // -2: none, -1: unfused, >= 0: index into kXqConfigs
+};
+Overrides current_overrides();
+
+// ---------------------------------------------------------------------------
 // planning: which kernel and launch shape for (M, N, K)
 // ---------------------------------------------------------------------------
 typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const uint16_t *, const __half *,
@@ -1362,12 +1381,9 @@ constexpr int64_t kTargetWorkgroups = 512;
 constexpr int64_t kMinSplitGroups = 4;
 constexpr int64_t kMaxSplits = 16;
 
-int choose_splits(int64_t tiles, int64_t G) {
+int choose_splits(int64_t tiles, int64_t G, int forced) {
   int64_t s = (kTargetWorkgroups + tiles / 2) / tiles;   // rounded
-  if (const char *f = getenv("QOQ_GEMM_SPLITS")) {        // measurement override
-    const long v = strtol(f, nullptr, 10);
-    if (v >= 1) return static_cast<int>(std::min<int64_t>(std::min<int64_t>(v, kMaxSplits), G));
-  }
+  if (forced >= 1) return static_cast<int>(std::min<int64_t>(std::min<int64_t>(forced, kMaxSplits), G));
   s = std::min<int64_t>(s, std::max<int64_t>(1, G / kMinSplitGroups));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits)));
 }
@@ -1377,23 +1393,18 @@ int choose_splits(int64_t tiles, int64_t G) {
 Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   const int64_t NS = N / 16;
   const int64_t G = K / 128;
-  // measurement overrides (not needed for correct use): QOQ_GEMM_REGIME=skinny|tiled,
-  // QOQ_GEMM_CONFIG=<name of a configuration in kConfigs>
+  const Overrides ov = current_overrides();
   const Config *cfg = nullptr;
-  if (const char *name = getenv("QOQ_GEMM_CONFIG")) {
-    for (int i = 0; i < kNumConfigs; ++i)
-      if (strcmp(kConfigs[i].name, name) == 0 && (!tiled_a || kConfigs[i].kt[0][0])) cfg = &kConfigs[i];
-  }
+  if (ov.config >= 0 && (!tiled_a || kConfigs[ov.config].kt[0][0])) cfg = &kConfigs[ov.config];
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
   bool split_k = true;   // may the plan split K (kinds 4 and 5)
   if (!cfg) {
-    const char *force = getenv("QOQ_GEMM_REGIME");
     // 49..64 tokens on a wide layer: 64-row MFMA tiles beat the split-K-by-wave
     // skinny kernel (the weights are read once either way)
     bool tiled = M > 64 || (M > 48 && NS >= 1024);
-    if (force && force[0] == 's') tiled = false;
-    if (force && force[0] == 't') tiled = true;
+    if (ov.regime == 1) tiled = false;
+    if (ov.regime == 2) tiled = true;
     if (tiled_a) tiled = false;
     if (!tiled) {
       // measured on MI355X (config sweep over the layer shapes of the workloads):
@@ -1461,8 +1472,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     p.block = dim3(64 * waves);
   } else if (cfg->kind == 6) {   // 256 x 256 tiles, 8 waves
     const int64_t tiles = ((NS + 15) / 16) * ((M + 255) / 256);
-    if (split_k || getenv("QOQ_GEMM_SPLITS")) {
-      p.splits = choose_splits(tiles, G);
+    if (split_k || ov.splits > 0) {
+      p.splits = choose_splits(tiles, G, ov.splits);
       if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     }
     p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
@@ -1471,8 +1482,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
     const int64_t tiles = nx * ny;
-    if (split_k || getenv("QOQ_GEMM_SPLITS")) {
-      p.splits = choose_splits(tiles, G);
+    if (split_k || ov.splits > 0) {
+      p.splits = choose_splits(tiles, G, ov.splits);
       if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     }
     p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
@@ -1596,15 +1607,11 @@ constexpr int64_t kXqMaxRepeat = 32 << 20;    // quantization costs more than a 
 
 bool xq_fits(const XqConfig *c, int64_t M, int64_t K) { return M * (K / 8) <= int64_t{kXqPerThread} * 64 * c->waves; }
 
-// measurement override: QOQ_LINEAR_CONFIG=<fused configuration name> | unfused
 const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
   if (M > 16 || K > kXqMaxK) return nullptr;      // the kernel's own limits (16 LDS code rows)
-  const char *force = getenv("QOQ_LINEAR_CONFIG");
-  if (force) {
-    if (strcmp(force, "unfused") == 0) return nullptr;
-    for (int i = 0; i < kNumXq; ++i)
-      if (strcmp(kXqConfigs[i].name, force) == 0) return xq_fits(&kXqConfigs[i], M, K) ? &kXqConfigs[i] : nullptr;
-  }
+  const Overrides ov = current_overrides();
+  if (ov.linear == -1) return nullptr;
+  if (ov.linear >= 0) return xq_fits(&kXqConfigs[ov.linear], M, K) ? &kXqConfigs[ov.linear] : nullptr;
   if (M > kXqMaxM) return nullptr;
   // measured on MI355X (decode layers of the workloads, M = 1, 2): two strips and 8
   // waves per workgroup; fused only while the quantization every workgroup repeats
@@ -1676,6 +1683,75 @@ const char *linear_config_name(int index) {
 
 const char *gemm_config_name(int index) {
   return (index >= 0 && index < kNumConfigs) ? kConfigs[index].name : nullptr;
+}
+
+namespace {
+
+std::mutex g_override_mu;
+std::once_flag g_override_env_once;
+Overrides g_override;
+
+int config_index(const char *name) {
+  for (int i = 0; i < kNumConfigs; ++i)
+    if (strcmp(kConfigs[i].name, name) == 0) return i;
+  return -1;
+}
+
+int linear_index(const char *name) {
+  if (strcmp(name, "unfused") == 0) return -1;
+  for (int i = 0; i < kNumXq; ++i)
+    if (strcmp(kXqConfigs[i].name, name) == 0) return i;
+  return -3;
+}
+
+// 1 / 2 for the two regime names, 0 for none, -1 for anything else
+int regime_code(const char *r) {
+  if (!r || !r[0]) return 0;
+  if (strcmp(r, "skinny") == 0) return 1;
+  if (strcmp(r, "tiled") == 0) return 2;
+  return -1;
+}
+
+// the environment's values, taken once (unknown names are ignored)
+void read_env_overrides() {
+  Overrides o;
+  if (const char *c = getenv("QOQ_GEMM_CONFIG")) o.config = config_index(c);
+  if (const char *f = getenv("QOQ_GEMM_SPLITS")) o.splits = static_cast<int>(std::max(0L, strtol(f, nullptr, 10)));
+  if (const char *r = getenv("QOQ_GEMM_REGIME")) o.regime = std::max(0, regime_code(r));
+  if (const char *l = getenv("QOQ_LINEAR_CONFIG")) {
+    const int v = linear_index(l);
+    o.linear = v >= -1 ? v : -2;
+  }
+  std::lock_guard<std::mutex> lk(g_override_mu);
+  g_override = o;
+}
+
+Overrides current_overrides() {
+  std::call_once(g_override_env_once, read_env_overrides);
+  std::lock_guard<std::mutex> lk(g_override_mu);
+  return g_override;
+}
+
+}  // namespace
+
+int set_plan_override(const char *gemm_config, int splits, const char *regime, const char *linear_config) {
+  Overrides o;
+  if (gemm_config && gemm_config[0]) {
+    o.config = config_index(gemm_config);
+    if (o.config < 0) return -1;
+  }
+  if (splits < 0) return -1;
+  o.splits = splits;
+  o.regime = regime_code(regime);
+  if (o.regime < 0) return -1;
+  if (linear_config && linear_config[0]) {
+    o.linear = linear_index(linear_config);
+    if (o.linear < -1) return -1;
+  }
+  std::call_once(g_override_env_once, read_env_overrides);   // the environment never overwrites it later
+  std::lock_guard<std::mutex> lk(g_override_mu);
+  g_override = o;
+  return 0;
 }
 
 }  // namespace qoq

@@ -97,6 +97,9 @@ size_t linear_workspace_need(int64_t M, int64_t N, int64_t K);
 const char *linear_plan_name(int64_t M, int64_t N, int64_t K);
 const char *linear_config_name(int index);
 const char *gemm_config_name(int index);
+// planner overrides for measurement and verification (qoq_set_plan_override):
+// 0, or -1 for an unknown name or a negative split factor
+int set_plan_override(const char *gemm_config, int splits, const char *regime, const char *linear_config);
 
 void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, int64_t K, void *w_i8,
                               hipStream_t stream);

@@ -95,7 +95,9 @@ __device__ __forceinline__ unsigned and_or(unsigned w, unsigned mask, unsigned b
 __device__ __forceinline__ h2 pair_lo(unsigned w, const NibbleMasks &nm) { return bits_h2(and_or(w, nm.lo, kBase1024)); }
 __device__ __forceinline__ h2 pair_hi(unsigned w, const NibbleMasks &nm) { return bits_h2(and_or(w, nm.hi, kBase64)); }
 
-// -(base + z) for a pair of fp16 zeros (exact: z is an integer in [0, 15])
+// -(base + z) for a pair of fp16 zeros (exact: z is an integer in [-1024, 1024], so
+// base + z lies within FP16's exact integers for base 64 and 1024, and so does
+// (base + c) - (base + z) = c - z)
 __device__ __forceinline__ h2 neg_biased(unsigned zz, unsigned base) {
   const h2 v = bits_h2(zz) + bits_h2(base);
   return bits_h2(__builtin_bit_cast(unsigned, v) ^ 0x80008000u);
@@ -109,8 +111,9 @@ __device__ __forceinline__ h2 neg_biased(unsigned zz, unsigned base) {
 // holding the sequence's first new position), so no two waves of a launch touch the
 // same page words.  Lane
 // l = 4 t + u holds dims 32 u .. 32 u + 31 of token t of the block (K and V, all
-// loads issued at once); per token and head: range widened to contain 0,
-// s = fp16(fp32(hi - lo) / 15), z = rne(-lo / s), q = clamp(z + rne(x / s), 0, 15),
+// loads issued at once); per token and head: the vector's own range (widened to
+// contain 0 only where kv_scale_zero says so), s = fp16(fp32(hi - lo) / 15),
+// z = rne(-lo / s), q = clamp(z + rne(x / s), 0, 15),
 // fp32 IEEE quotients, s and z stored as fp16; min and max over the token's four
 // lanes by two xor steps.  Word u of every K slot of token t takes its nibbles from
 // dims 32 u .. 32 u + 31 only, so lane (t, u) builds those four words in registers;
@@ -132,6 +135,27 @@ __device__ __forceinline__ float quad_min_f32(float v) {
   return fminf(v, __shfl_xor(v, 2, 64));
 }
 
+// Scale and zero of one vector from its minimum and maximum: the quantizer over
+// the vector's own range, s = fp16(fp32(hi - lo) / 15), z = rne(fp32(-lo / s));
+// where that has no usable result (s = 0: a constant vector; |z| > kZLimit: a
+// narrow range far from 0, where q - z would leave FP16's exact integers) the same
+// over the range widened to contain 0, which puts z in [0, 15].  s == 0 on return
+// only for an all-zero vector (z = 0 then).
+constexpr float kZLimit = 1024.0f;
+
+__device__ __forceinline__ void kv_scale_zero_once(float lo, float hi, __half &sh, float &s, float &z) {
+  float range = hi - lo;
+  __asm__ volatile("" : "+v"(range));                 // fp32 difference, then the divide
+  sh = __float2half_rn(__fdiv_rn(range, 15.0f));
+  s = __half2float(sh);
+  z = s == 0.0f ? 0.0f : rintf(__fdiv_rn(-lo, s));
+}
+
+__device__ __forceinline__ void kv_scale_zero(float lo, float hi, __half &sh, float &s, float &z) {
+  kv_scale_zero_once(lo, hi, sh, s, z);
+  if (s == 0.0f || fabsf(z) > kZLimit) kv_scale_zero_once(fminf(lo, 0.0f), fmaxf(hi, 0.0f), sh, s, z);
+}
+
 // codes of the lane's 32 values and the token's (s, z); the token's 128 values sit
 // in four consecutive lanes
 __device__ __forceinline__ void kv_quant32(const float (&x)[32], unsigned (&c)[32], __half &sh, __half &zh) {
@@ -141,26 +165,21 @@ __device__ __forceinline__ void kv_quant32(const float (&x)[32], unsigned (&c)[3
     lo = fminf(lo, x[j]);
     hi = fmaxf(hi, x[j]);
   }
-  lo = fminf(quad_min_f32(lo), 0.0f);
-  hi = fmaxf(quad_max_f32(hi), 0.0f);
-  float range = hi - lo;
-  __asm__ volatile("" : "+v"(range));                 // fp32 difference, then the divide
-  sh = __float2half_rn(__fdiv_rn(range, 15.0f));
-  const float s = __half2float(sh);
+  float s, z;
+  kv_scale_zero(quad_min_f32(lo), quad_max_f32(hi), sh, s, z);
   if (s == 0.0f) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) c[j] = 0u;
     zh = __float2half_rn(0.0f);
     return;
   }
-  const float z = rintf(__fdiv_rn(-lo, s));
   zh = __float2half_rn(z);
-  // x / s as x * fp32(1 / s): |x / s| < 2^5 here (s is fp16(range / 15) and |x| is
-  // at most the range, the worst case being s rounded down to the smallest fp16
-  // subnormal), so the product is within 2^-17 of the correctly rounded quotient
-  // and rint decides the same way unless it lies within 2^-12 of a half-integer;
-  // those rare values take the IEEE divide (a branch the wave takes only when one
-  // of its lanes needs it)
+  // x / s as x * fp32(1 / s): |x / s| <= |z| + 15.5 <= 1040 here (x lies in the
+  // range, whose low end is -z s to half a step), so the product (two roundings)
+  // and the correctly rounded quotient differ by at most 1040 (2^-23 + 2^-24) <
+  // 2^-12, and rint decides the same way unless the product lies within 2^-12 of a
+  // half-integer; those rare values take the IEEE divide (a branch the wave takes
+  // only when one of its lanes needs it)
   const float y = __fdiv_rn(1.0f, s);
   float q[32];
   float gap = 1.0f;
@@ -296,18 +315,13 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 
 // codes of the lane's two values and the vector's (s, z)
 __device__ __forceinline__ void kv_quant2(float x0, float x1, unsigned &c0, unsigned &c1, __half &sh, __half &zh) {
-  const float lo = fminf(wave_min_f32(fminf(x0, x1)), 0.0f);
-  const float hi = fmaxf(wave_max_f32(fmaxf(x0, x1)), 0.0f);
-  float range = hi - lo;
-  __asm__ volatile("" : "+v"(range));                 // fp32 difference, then the divide
-  sh = __float2half_rn(__fdiv_rn(range, 15.0f));
-  const float s = __half2float(sh);
+  float s, z;
+  kv_scale_zero(wave_min_f32(fminf(x0, x1)), wave_max_f32(fmaxf(x0, x1)), sh, s, z);
   if (s == 0.0f) {
     c0 = c1 = 0u;
     zh = __float2half_rn(0.0f);
     return;
   }
-  const float z = rintf(__fdiv_rn(-lo, s));
   zh = __float2half_rn(z);
   c0 = static_cast<unsigned>(fminf(fmaxf(z + rintf(__fdiv_rn(x0, s)), 0.0f), 15.0f));
   c1 = static_cast<unsigned>(fminf(fmaxf(z + rintf(__fdiv_rn(x1, s)), 0.0f), 15.0f));

@@ -80,6 +80,7 @@ _SIGNATURES = {
     "qoq_linear_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_gemm_plan_splits": ([_c_i64, _c_i64, _c_i64], ctypes.c_int),
     "qoq_gemm_config_name": ([ctypes.c_int], ctypes.c_char_p),
+    "qoq_set_plan_override": ([ctypes.c_char_p, _c_i32, ctypes.c_char_p, ctypes.c_char_p], ctypes.c_int),
     "qoq_dequantize_packed": ([_c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp], ctypes.c_int),
     "qoq_stream_copy": ([_c_vp, _c_vp, _c_sz, _c_vp], ctypes.c_int),
     "qoq_mfma_probe": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
@@ -151,6 +152,40 @@ def _dev_tensor(t, name: str):
     return t
 
 
+# Host-side size checks: the library sees only pointers, so a buffer that is too
+# small for (M, N, K) would be read or written past its end on the device.
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_bytes(t, name: str, need: int):
+    if isinstance(t, torch.Tensor) and _nbytes(t) < need:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, {need} needed")
+
+
+def _check_weights(packed, meta, s_w, N: int, K: int, per_channel: bool = False):
+    """Packed codes N*K/2 bytes; group metadata 2 bytes per (column, group of 128)
+    (per-channel: one zero byte per column); N fp16 channel scales."""
+    if N <= 0 or K <= 0:
+        return                      # the library rejects the shape itself
+    _check_bytes(packed, "packed", N * K // 2)
+    if per_channel:
+        _check_bytes(meta, "zeros", N)
+    else:
+        _check_bytes(meta, "meta", 2 * N * (K // GROUP))
+    _check_bytes(s_w, "s_w", 2 * N)
+
+
+def _check_rows(t, name: str, M: int, elem: int):
+    """A per-token vector (s_x fp16, t int32) must hold M entries."""
+    _check_bytes(t, name, elem * M)
+
+
+def _check_out(out, M: int, N: int):
+    if not isinstance(out, torch.Tensor) or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape ({M}, {N}), got {getattr(out, 'shape', None)}")
+
+
 # ---------------------------------------------------------------------------
 # sizes
 # ---------------------------------------------------------------------------
@@ -176,6 +211,34 @@ def gemm_plan_splits(M: int, N: int, K: int) -> int:
     if v < 0:
         raise QoQError("qoq_gemm_plan_splits", v)
     return v
+
+
+_override = {"config": None, "splits": 0, "regime": None, "linear": None}
+
+
+def set_plan_override(config=None, splits: int = 0, regime=None, linear=None):
+    """Replace the planner overrides (qoq_set_plan_override): a configuration forced
+    for every GEMM shape, a split-K factor, "skinny" / "tiled", a linear
+    configuration or "unfused".  All None / 0 clears them."""
+    enc = lambda v: None if v is None else str(v).encode()
+    _check("qoq_set_plan_override", lib().qoq_set_plan_override(enc(config), int(splits), enc(regime), enc(linear)))
+    _override.update(config=config, splits=int(splits), regime=regime, linear=linear)
+
+
+class plan_override:
+    """Context manager: the given overrides for the body, the previous ones after."""
+
+    def __init__(self, config=None, splits: int = 0, regime=None, linear=None):
+        self.new = dict(config=config, splits=splits, regime=regime, linear=linear)
+
+    def __enter__(self):
+        self.old = dict(_override)
+        set_plan_override(**self.new)
+        return self
+
+    def __exit__(self, *exc):
+        set_plan_override(**self.old)
+        return False
 
 
 def gemm_configs() -> list:
@@ -432,6 +495,8 @@ def kv4_decode_attention(q: torch.Tensor, pool: torch.Tensor, page_table: torch.
     num_pages = _kv4_pool_pages(pool, h_kv)
     if out is None:
         out = torch.empty_like(q)
+    if not isinstance(out, torch.Tensor) or tuple(out.shape) != (B, h, D):
+        raise ValueError(f"out must have shape ({B}, {h}, {D}), got {getattr(out, 'shape', None)}")
     need = kv4_attention_workspace_bytes(B, h, h_kv, max_len)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -467,8 +532,12 @@ def quantize_activations_rowsum(x: torch.Tensor, out=None):
 def w4a8_gemm_pc(qx, s_x, t, packed, zeros, s_w, N: int, out=None, workspace=None):
     """Per-channel weights: out fp16 [M, N] = fp16((sum qx q - z t) * (s_x * s_w))."""
     M, K = qx.shape
+    _check_weights(packed, zeros, s_w, N, K, per_channel=True)
+    _check_rows(s_x, "s_x", M, 2)
+    _check_rows(t, "t", M, 4)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=qx.device)
+    _check_out(out, M, N)
     ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, GROUP)
     _check("qoq_w4a8_gemm_pc",
            lib().qoq_w4a8_gemm_pc(_dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
@@ -481,8 +550,12 @@ def w4a8_gemm_pc(qx, s_x, t, packed, zeros, s_w, N: int, out=None, workspace=Non
 def w4a8_gemm_pc_i32(qx, t, packed, zeros, N: int, out=None, workspace=None):
     """Per-channel weights: acc int32 [M, N] = sum_k qx (q - z), exact."""
     M, K = qx.shape
+    _check_bytes(packed, "packed", N * K // 2 if N > 0 else 0)
+    _check_bytes(zeros, "zeros", max(N, 0))
+    _check_rows(t, "t", M, 4)
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=qx.device)
+    _check_out(out, M, N)
     ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, GROUP)
     _check("qoq_w4a8_gemm_pc_i32",
            lib().qoq_w4a8_gemm_pc_i32(_dev(qx, "qx", torch.int8), _dev(t, "t", torch.int32),
@@ -524,8 +597,11 @@ def w4a8_gemm(qx, s_x, packed, meta, s_w, N: int, out=None, group: int = GROUP, 
     """out fp16 [M, N] = fp16(acc * (s_x[m] * s_w[n])).  workspace: None = the cached
     one of this device and stream (see qoq_gemm_workspace_bytes for the contract)."""
     M, K = qx.shape
+    _check_weights(packed, meta, s_w, N, K)
+    _check_rows(s_x, "s_x", M, 2)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=qx.device)
+    _check_out(out, M, N)
     ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, group)
     _check("qoq_w4a8_gemm",
            lib().qoq_w4a8_gemm(_dev(qx, "qx", torch.int8), _dev(s_x, "s_x", torch.float16),
@@ -538,8 +614,11 @@ def w4a8_gemm(qx, s_x, packed, meta, s_w, N: int, out=None, group: int = GROUP, 
 def w4a8_gemm_i32(qx, packed, meta, N: int, out=None, group: int = GROUP, workspace=None):
     """acc int32 [M, N]: the exact integer accumulators of the same main loop."""
     M, K = qx.shape
+    _check_bytes(packed, "packed", N * K // 2 if N > 0 else 0)
+    _check_bytes(meta, "meta", 2 * N * (K // GROUP) if N > 0 else 0)
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=qx.device)
+    _check_out(out, M, N)
     ws_ptr, ws_bytes = _workspace_args(workspace, _dev_tensor(qx, "qx"), M, N, K, group)
     _check("qoq_w4a8_gemm_i32",
            lib().qoq_w4a8_gemm_i32(_dev(qx, "qx", torch.int8), _dev(packed, "packed", torch.uint8),
@@ -556,8 +635,11 @@ def _check_tiled(qx, M, K):
 def w4a8_gemm_tiled(qx_tiled, s_x, packed, meta, s_w, M: int, N: int, K: int, out=None):
     """qoq_w4a8_gemm on tiled activation codes (M <= 64): out fp16 [M, N]."""
     _check_tiled(qx_tiled, M, K)
+    _check_weights(packed, meta, s_w, N, K)
+    _check_rows(s_x, "s_x", M, 2)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=qx_tiled.device)
+    _check_out(out, M, N)
     _check("qoq_w4a8_gemm_tiled",
            lib().qoq_w4a8_gemm_tiled(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(s_x, "s_x", torch.float16),
                                      _dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16),
@@ -569,8 +651,11 @@ def w4a8_gemm_tiled(qx_tiled, s_x, packed, meta, s_w, M: int, N: int, K: int, ou
 def w4a8_gemm_tiled_i32(qx_tiled, packed, meta, M: int, N: int, K: int, out=None):
     """Exact INT32 accumulators from tiled activation codes (M <= 64)."""
     _check_tiled(qx_tiled, M, K)
+    _check_bytes(packed, "packed", N * K // 2 if N > 0 else 0)
+    _check_bytes(meta, "meta", 2 * N * (K // GROUP) if N > 0 else 0)
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=qx_tiled.device)
+    _check_out(out, M, N)
     _check("qoq_w4a8_gemm_tiled_i32",
            lib().qoq_w4a8_gemm_tiled_i32(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(packed, "packed", torch.uint8),
                                          _dev(meta, "meta", torch.int16), _dev(out, "acc", torch.int32), M, N, K,
@@ -600,8 +685,12 @@ def quantize_activations_rowsum_tiled(x: torch.Tensor, out=None):
 def w4a8_gemm_pc_tiled(qx_tiled, s_x, t, packed, zeros, s_w, M: int, N: int, K: int, out=None):
     """w4a8_gemm_pc on tiled activation codes (M <= 64): out fp16 [M, N]."""
     _check_tiled(qx_tiled, M, K)
+    _check_weights(packed, zeros, s_w, N, K, per_channel=True)
+    _check_rows(s_x, "s_x", M, 2)
+    _check_rows(t, "t", M, 4)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=qx_tiled.device)
+    _check_out(out, M, N)
     _check("qoq_w4a8_gemm_pc_tiled",
            lib().qoq_w4a8_gemm_pc_tiled(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(s_x, "s_x", torch.float16),
                                         _dev(t, "t", torch.int32), _dev(packed, "packed", torch.uint8),
@@ -613,8 +702,12 @@ def w4a8_gemm_pc_tiled(qx_tiled, s_x, t, packed, zeros, s_w, M: int, N: int, K: 
 def w4a8_gemm_pc_tiled_i32(qx_tiled, t, packed, zeros, M: int, N: int, K: int, out=None):
     """Exact INT32 accumulators of the per-channel GEMM from tiled codes (M <= 64)."""
     _check_tiled(qx_tiled, M, K)
+    _check_bytes(packed, "packed", N * K // 2 if N > 0 else 0)
+    _check_bytes(zeros, "zeros", max(N, 0))
+    _check_rows(t, "t", M, 4)
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=qx_tiled.device)
+    _check_out(out, M, N)
     _check("qoq_w4a8_gemm_pc_tiled_i32",
            lib().qoq_w4a8_gemm_pc_tiled_i32(_dev(qx_tiled, "qx_tiled", torch.int8), _dev(t, "t", torch.int32),
                                             _dev(packed, "packed", torch.uint8), _dev(zeros, "zeros", torch.uint8),
@@ -630,8 +723,11 @@ def gemm_tiled_plan(M: int, N: int, K: int) -> str:
 # diagnostics
 # ---------------------------------------------------------------------------
 def dequantize_packed(packed, meta, N: int, K: int, group: int = GROUP, out=None):
+    _check_bytes(packed, "packed", N * K // 2 if N > 0 else 0)
+    _check_bytes(meta, "meta", 2 * N * (K // GROUP) if N > 0 else 0)
     if out is None:
         out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check_bytes(out, "w_i8", N * K if N > 0 else 0)
     _check("qoq_dequantize_packed",
            lib().qoq_dequantize_packed(_dev(packed, "packed", torch.uint8), _dev(meta, "meta", torch.int16), N, K,
                                        group, _dev(out, "w_i8", torch.int8), _stream(packed)))
@@ -724,8 +820,12 @@ def w4a8_linear(x: torch.Tensor, packed, meta, s_w, N: int, out=None, s_x=None, 
     """out fp16 [M, N] = quantize(x) then the W4A8 GEMM, in one library call.
     s_x: optional fp16 [M] tensor that receives the token scales."""
     M, K = x.shape
+    _check_weights(packed, meta, s_w, N, K)
+    if s_x is not None:
+        _check_rows(s_x, "s_x", M, 2)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check_out(out, M, N)
     if workspace is None:
         workspace = linear_workspace_for(_dev_tensor(x, "x"), M, N, K, group)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)

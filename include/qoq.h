@@ -57,7 +57,8 @@ typedef enum {
   QOQ_ERR_UNSUPPORTED = -2,  /* group != 128, K beyond the exact-INT32 limit */
   QOQ_ERR_ALIGNMENT = -3,    /* pointer not aligned as the call requires */
   QOQ_ERR_WORKSPACE = -4,    /* workspace smaller than qoq_gemm_workspace_bytes */
-  QOQ_ERR_HIP = -5           /* the HIP runtime reported an error at launch */
+  QOQ_ERR_HIP = -5,          /* the HIP runtime reported an error at launch */
+  QOQ_ERR_SCRATCH = -6       /* the shape needs more than QOQ_SCRATCH_BYTES of scratch */
 } qoq_status;
 
 /* Library ABI version (increments when a signature, an entry point or the storage
@@ -383,6 +384,26 @@ int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_
                     const void *s_w_fp16, void *out_fp16, void *s_x_fp16, int64_t M, int64_t N,
                     int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* Size of the library's static scratch array (one per GPU, held until the process
+ * ends) that qoq_w4a8_linear_noalloc uses in place of a workspace. */
+#define QOQ_SCRATCH_BYTES (64u << 20)
+
+/* qoq_w4a8_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels, arguments, results and errors, minus the workspace.  The codes, token
+ * scales and split-K partial sums go to a static device array of QOQ_SCRATCH_BYTES
+ * (its address looked up once per device, on the first call with that device
+ * current); no call allocates or frees anything.  A shape whose
+ * qoq_linear_workspace_bytes exceeds QOQ_SCRATCH_BYTES returns QOQ_ERR_SCRATCH
+ * before anything is launched.  Every byte the kernels read from the array is
+ * written earlier in the same call, so it needs no clearing.  All calls on one GPU
+ * share its array: calls that may overlap in time on one GPU (other streams, other
+ * threads) race and must be serialized by the caller.
+ * Errors: INVALID, UNSUPPORTED, ALIGNMENT, SCRATCH, HIP. */
+int qoq_w4a8_linear_noalloc(const void *x_fp16, const void *packed_w, const void *group_meta,
+                            const void *s_w_fp16, void *out_fp16, void *s_x_fp16, int64_t M,
+                            int64_t N, int64_t K, int32_t group, void *stream);
 
 /* Name of the kernel configuration qoq_w4a8_linear uses for this shape: a fused
  * configuration, or the qoq_gemm_tiled_plan (M <= 64) / qoq_gemm_plan name when it

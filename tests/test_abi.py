@@ -7,7 +7,7 @@ import pytest
 
 from w4a8_mixed_precision_amd import qoq
 
-OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR = 0, -1, -2, -3, -4, -5
+OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5, -6
 FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
 ODD = ctypes.c_void_p(0x10001)        # misaligned
 NUL = ctypes.c_void_p(0)
@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert qoq.version() >= 1
-    for s in (OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR):
+    for s in (OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE, HIPERR, SCRATCH):
         assert qoq.status_string(s)
     assert qoq.status_string(12345) == "unknown status"
 
@@ -444,3 +444,21 @@ def test_silu_split_validation(L):
     assert f(FAKE, FAKE, 100, 1, 29568, 0, FAKE, FAKE, FAKE, 60, NUL) == INVALID        # ld < K
     assert f(FAKE, FAKE, 29568, 0, 29568, 0, FAKE, FAKE, NUL, 0, NUL) == OK             # M = 0
 
+
+
+def test_linear_noalloc_validation(L):
+    """Argument checks of the allocation-free linear entry point, all before the
+    scratch array is looked up or anything is launched: shapes, pointers, alignment,
+    and shapes whose workspace would exceed QOQ_SCRATCH_BYTES."""
+    f = L.qoq_w4a8_linear_noalloc
+    assert qoq.SCRATCH_BYTES == 64 << 20
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NUL, 0, 6144, 4096, 128, NUL) == OK          # nothing to do
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NUL, 4, 6144, 4096, 64, NUL) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NUL, 4, 6150, 4096, 128, NUL) == INVALID
+    assert f(NUL, FAKE, FAKE, FAKE, FAKE, NUL, 4, 6144, 4096, 128, NUL) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, NUL, NUL, 4, 6144, 4096, 128, NUL) == INVALID
+    assert f(ODD, FAKE, FAKE, FAKE, FAKE, NUL, 4, 6144, 4096, 128, NUL) == ALIGNMENT
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, ODD, 4, 6144, 4096, 128, NUL) == ALIGNMENT
+    for M, N, K in [(8192, 4096, 14336), (4096, 4096, 29568)]:
+        assert qoq.linear_workspace_bytes(M, N, K) > qoq.SCRATCH_BYTES
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, NUL, M, N, K, 128, NUL) == SCRATCH

@@ -55,6 +55,7 @@ const char *qoq_status_string(int status) {
     case QOQ_ERR_ALIGNMENT: return "pointer alignment requirement not met";
     case QOQ_ERR_WORKSPACE: return "workspace smaller than required";
     case QOQ_ERR_HIP: return "HIP runtime error at launch";
+    case QOQ_ERR_SCRATCH: return "shape needs more scratch than the static array holds (QOQ_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -470,6 +471,27 @@ int qoq_w4a8_linear(const void *x_fp16, const void *packed_w, const void *group_
     if (!aligned(workspace, 256)) return QOQ_ERR_ALIGNMENT;
   }
   qoq::launch_w4a8_linear(x_fp16, packed_w, group_meta, s_w_fp16, out_fp16, s_x_fp16, M, N, K, workspace,
+                          as_stream(stream));
+  return launch_status();
+}
+
+int qoq_w4a8_linear_noalloc(const void *x_fp16, const void *packed_w, const void *group_meta,
+                            const void *s_w_fp16, void *out_fp16, void *s_x_fp16, int64_t M, int64_t N,
+                            int64_t K, int32_t group, void *stream) {
+  static_assert(qoq::kScratchBytes == QOQ_SCRATCH_BYTES, "scratch size in the header");
+  int st = check_gemm(M, N, K, group);
+  if (st != QOQ_OK) return st;
+  if (M > kMaxDim || K > kMaxDim / 2) return QOQ_ERR_UNSUPPORTED;
+  if (M == 0) return QOQ_OK;
+  if (!x_fp16 || !packed_w || !group_meta || !s_w_fp16 || !out_fp16) return QOQ_ERR_INVALID;
+  if (!aligned(x_fp16, 16) || !aligned(packed_w, 16) || !aligned(group_meta, 16) || !aligned(out_fp16, 16) ||
+      !aligned(s_w_fp16, 2) || !aligned(s_x_fp16, 2))
+    return QOQ_ERR_ALIGNMENT;
+  const size_t need = qoq::linear_workspace_need(M, N, K);
+  if (need > qoq::kScratchBytes) return QOQ_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (need > 0 && qoq::linear_scratch(&ws) != hipSuccess) return QOQ_ERR_HIP;
+  qoq::launch_w4a8_linear(x_fp16, packed_w, group_meta, s_w_fp16, out_fp16, s_x_fp16, M, N, K, ws,
                           as_stream(stream));
   return launch_status();
 }

@@ -1677,6 +1677,38 @@ void launch_w4a8_linear(const void *x, const void *packed, const void *meta, con
   launch_w4a8_gemm(qx, sx, packed, meta, sw, out, 0, M, N, K, gws, st);
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of qoq_w4a8_linear_noalloc: a file-scope device array, one copy
+// on every GPU the code object is loaded on.  Host code never uses the array's
+// name as an address (on the host it names a stand-in, not device memory): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and is kept per device.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t linear_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 const char *linear_config_name(int index) {
   return (index >= 0 && index < kNumXq) ? kXqConfigs[index].name : nullptr;
 }

@@ -94,6 +94,10 @@ const char *gemm_plan_name(int64_t M, int64_t N, int64_t K);
 void launch_w4a8_linear(const void *x, const void *packed, const void *meta, const void *sw, void *out,
                         void *sx_out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream);
 size_t linear_workspace_need(int64_t M, int64_t N, int64_t K);
+// device address of the static scratch array on the current device (looked up once
+// per device); hipSuccess or the lookup's error
+hipError_t linear_scratch(void **ptr);
+constexpr size_t kScratchBytes = size_t{64} << 20;
 const char *linear_plan_name(int64_t M, int64_t N, int64_t K);
 const char *linear_config_name(int index);
 const char *gemm_config_name(int index);

@@ -77,6 +77,8 @@ _SIGNATURES = {
     "qoq_w4a8_linear": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp, _c_sz,
                          _c_vp], ctypes.c_int),
     "qoq_linear_plan": ([_c_i64, _c_i64, _c_i64], ctypes.c_char_p),
+    "qoq_w4a8_linear_noalloc": ([_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_vp],
+                                ctypes.c_int),
     "qoq_linear_config_name": ([ctypes.c_int], ctypes.c_char_p),
     "qoq_gemm_plan_splits": ([_c_i64, _c_i64, _c_i64], ctypes.c_int),
     "qoq_gemm_config_name": ([ctypes.c_int], ctypes.c_char_p),
@@ -836,4 +838,25 @@ def w4a8_linear(x: torch.Tensor, packed, meta, s_w, N: int, out=None, s_x=None, 
                                  _dev(meta, "meta", torch.int16), _dev(s_w, "s_w", torch.float16),
                                  _dev(out, "out", torch.float16), sx_ptr, M, N, K, group, ws_ptr, ws_bytes,
                                  _stream(x)))
+    return out
+
+
+SCRATCH_BYTES = 64 << 20        # QOQ_SCRATCH_BYTES
+
+
+def w4a8_linear_noalloc(x: torch.Tensor, packed, meta, s_w, N: int, out=None, s_x=None, group: int = GROUP):
+    """qoq_w4a8_linear_noalloc: w4a8_linear without a workspace (the library's static
+    scratch array instead); pass `out` to make the whole call allocation-free."""
+    M, K = x.shape
+    _check_weights(packed, meta, s_w, N, K)
+    if s_x is not None:
+        _check_rows(s_x, "s_x", M, 2)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check_out(out, M, N)
+    sx_ptr = _dev(s_x, "s_x", torch.float16) if s_x is not None else ctypes.c_void_p(0)
+    _check("qoq_w4a8_linear_noalloc",
+           lib().qoq_w4a8_linear_noalloc(_dev(x, "x", torch.float16), _dev(packed, "packed", torch.uint8),
+                                         _dev(meta, "meta", torch.int16), _dev(s_w, "s_w", torch.float16),
+                                         _dev(out, "out", torch.float16), sx_ptr, M, N, K, group, _stream(x)))
     return out

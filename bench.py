@@ -1,16 +1,24 @@
 """Benchmark of the W4A8 per-group GEMM path on one MI355X.
 
-Default workload: the Llama-3-8B fused QKV projection (K=4096, N=6144, group 128)
-at decode batches M = 1, 16 and 64.  One step = for each M, the per-token INT8
-activation quantizer followed by the W4A8 GEMM with its fp16 epilogue, on inputs
-already resident in HBM; the weights are packed once, offline, before timing (the
-method quantizes and reorders weights offline).  Weight buffers are rotated over
-copies totalling >= 1 GiB so that the 256 MB MALL and the L2 do not serve them.
+Default workload: the metric's range M = 1 .. 4096 in one step, group 128:
+  Llama-3-8B fused QKV (K=4096, N=6144) at decode batches M = 1, 16, 64;
+  Qwen-72B-class gate+up (K=8192, N=59136) and down (K=29568, N=8192) at M = 1
+  (the largest weight streams: the bandwidth-bound regime);
+  Llama-3-8B gate+up (K=4096, N=28672) and down (K=14336, N=4096) at M = 4096
+  prompt tokens (the INT8 matrix-core-bound regime).
+One step = for each case, the per-token INT8 activation quantization followed by
+the W4A8 GEMM with its fp16 epilogue (one qoq_w4a8_linear call), on inputs already
+resident in HBM; the weights are packed once, offline, before timing (the method
+quantizes and reorders weights offline).  Weight buffers are rotated over copies
+totalling >= 1 GiB per layer so that the 256 MB MALL and the L2 do not serve them.
 
 Prints ONE JSON line (rank 0) with the throughput, the roofline fraction of the
-dominant kernel (timed with HIP events on the stream the kernels run on), the CPU
-oracle timed on the host cores and, as context, the KV4 decode attention of
-Llama-3-8B at 64 sequences x 1024 cached tokens (kv4_attention; --no-kv4 skips it).
+dominant kernel (timed with HIP events on the stream the kernels run on), one
+roofline block per regime (HBM: Qwen-72B gate+up at M = 1; MFMA: Llama-3-8B gate+up
+at M = 4096), the CPU oracle timed on the host cores on a column sample of the same
+step and, as context, the KV4 decode attention of Llama-3-8B at 64 sequences x 1024
+cached tokens (kv4_attention; --no-kv4 skips it).  --layer / --ms time one layer
+instead of the default step.
 
 --sweep runs every layer shape / batch size of the workload registry and writes a
 table to gpurun_out/sweep.json (not the headline line); with --format channel it
@@ -32,12 +40,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W4A8 GEMM TOPS and weight GB/s vs MI355X roofline, M=1..4096"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_llama3_8b_qkv.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_step.md")
 GEMM_SOURCES = [os.path.join(ROOT, "w4a8_mixed_precision_amd", "csrc", f)
                 for f in ("qoq_gemm.hip", "qoq_device.h")]
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 ROTATE_BYTES = 1 << 30
+
+# the default step: (layer, batch sizes); the regime blocks of the line
+STEP = (("llama3_8b_qkv", (1, 16, 64)), ("qwen72b_gate_up", (1,)), ("qwen72b_down", (1,)),
+        ("llama3_8b_gate_up_prefill", (4096,)), ("llama3_8b_down_prefill", (4096,)))
+REGIMES = {"hbm": ("qwen72b_gate_up", 1), "mfma": ("llama3_8b_gate_up_prefill", 4096)}
 
 
 def parse():
@@ -45,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layer", default="llama3_8b_qkv")
+    ap.add_argument("--layer", default="", help="time this layer alone (default: the mixed step)")
     ap.add_argument("--ms", default="")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +66,17 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--kv4", action="store_true", help="measure the KV4 decode attention and KV write")
     ap.add_argument("--no-kv4", action="store_true", help="skip the KV4 attention figure of the headline line")
+    ap.add_argument("--profile-plan", action="store_true",
+                    help="time every configuration (and split-K factor) on the workloads' layer shapes over a grid "
+                         "of M and write the fastest per point as the dispatch table "
+                         "(gpurun_out/qoq_plan_table.inc, gpurun_out/plan_profile.json)")
+    ap.add_argument("--profile-layers", default="",
+                    help="with --profile-plan: only these layers' (N, K) (comma-separated names); the results go "
+                         "to gpurun_out/plan_profile_<names>.json for --profile-merge")
+    ap.add_argument("--profile-merge", nargs="*", default=None,
+                    help="merge profile files into the dispatch table and the committed profile (no GPU)")
+    ap.add_argument("--check-plan", action="store_true",
+                    help="time the planner's choice against the best configurations of the committed profile")
     ap.add_argument("--format", choices=("group", "channel"), default="group",
                     help="weight format: per-group g128 (default) or the per-channel variant")
     return ap.parse_args()
@@ -260,44 +284,76 @@ def time_launches(fn, n, torch, reps=3):
     return time_graph(g, reps, torch) / n
 
 
-def cpu_baseline(L, Ms, seconds):
-    """The CPU oracle (unchanged) over the same step: activation quantization,
-    dequantization of the stored codes, exact contraction, fp32 epilogue."""
+def cpu_baseline_step(plan, seconds, cols=256):
+    """The CPU oracle (unchanged) over a column sample of the step: per case the
+    activation quantization over the whole [M, K], then dequantization of the stored
+    codes, exact fp64 contraction and fp32 epilogue on the first `cols` output
+    columns, scaled by N / cols (those stages are linear in N); whole sampled steps
+    are repeated until `seconds` have passed."""
     import numpy as np
     from oracle import qoq_oracle as o
     from w4a8_mixed_precision_amd import workloads as wl
-    w16 = wl.weights_fp16(L)
-    q0, s_w = o.quantize_weights_level0(w16)
-    q_u4, z, s_u8 = o.quantize_weights_level1(q0)
-    xs = {M: wl.activations_fp16(L, M) for M in Ms}
-    ops = sum(wl.algorithmic_ops(M, L.N, L.K) for M in Ms)
-    t0 = time.perf_counter()
-    steps = 0
-    while True:
+    prep = []
+    for name, Ms in plan:
+        L = wl.find(name)
+        ns = min(cols, L.N)
+        q0, s_w = o.quantize_weights_level0(wl.weights_fp16(L, N=ns))
+        q_u4, z, s_u8 = o.quantize_weights_level1(q0)
         for M in Ms:
-            qx, s_x = o.quantize_activations(xs[M])
-            w_hat = o.dequantize_level1(q_u4, z, s_u8)
-            acc = o.contract(qx, w_hat)
+            prep.append((L, M, ns, wl.activations_fp16(L, M), q_u4, z, s_u8, s_w))
+    ops = sum(wl.algorithmic_ops(M, L.N, L.K) for (L, M, *_rest) in prep)
+    t_begin = time.perf_counter()
+    per_step = []
+    while True:
+        t_step = 0.0
+        for (L, M, ns, x16, q_u4, z, s_u8, s_w) in prep:
+            t0 = time.perf_counter()
+            qx, s_x = o.quantize_activations(x16)
+            t1 = time.perf_counter()
+            acc = o.contract(qx, o.dequantize_level1(q_u4, z, s_u8))
             o.epilogue(acc, s_x, s_w)
-        steps += 1
-        el = time.perf_counter() - t0
+            t2 = time.perf_counter()
+            t_step += (t1 - t0) + (t2 - t1) * L.N / ns
+        per_step.append(t_step)
+        el = time.perf_counter() - t_begin
         if el >= seconds:
             break
-    per_step = el / steps
+    s_step = float(np.median(per_step))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count()
     return {
-        "value": ops / per_step / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-        "sample": f"{steps} full step(s) of {L.name} M={list(Ms)} (activation quant + dequant + exact "
-                  f"fp64 contraction + epilogue), {el:.1f} s, host cpu_count={os.cpu_count()}",
-        "s_per_step": per_step,
+        "value": ops / s_step / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"{len(per_step)} column-sampled step(s) of the same cases ({cols} output columns per layer, "
+                  f"dequant + exact fp64 contraction + epilogue scaled by N/{cols}; activation quant over the "
+                  f"whole [M, K]), median {s_step:.2f} s per full step, {el:.1f} s of CPU work, "
+                  f"host cpu_count={os.cpu_count()}",
+        "s_per_step": s_step,
     }
 
 
+def roofline_of(r, c):
+    """Roofline object of one case's GEMM launch: the bound with the longer time at
+    the published peaks, achieved = algorithmic bytes (or ops) / measured launch."""
+    t = r["gemm_us"] * 1e-6
+    if c.ops / (INT8_PEAK_TOPS * 1e12) > c.bytes["total"] / (HBM_PEAK_GBPS * 1e9):
+        bound, unit, peak, achieved = "mfma", "TOPS", INT8_PEAK_TOPS, c.ops / t / 1e12
+    else:
+        bound, unit, peak, achieved = "hbm", "GB/s", HBM_PEAK_GBPS, c.bytes["total"] / t / 1e9
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": measured_traffic(r["plan"], r["M"], r["N"], r["K"]),
+            "kernel": r["plan"], "layer": c.L.name, "M": r["M"], "N": r["N"], "K": r["K"],
+            "bytes_per_launch": c.bytes["total"], "ops_per_launch": c.ops, "launch_us": r["gemm_us"]}
+
+
 def run_case_metrics(c, q, torch, launches):
+    # the GEMM-only timing reads the codes the quantizer writes: write them from the
+    # case's activations first (codes never written are zeros or stale memory, and
+    # zero operands draw less power, which lets the matrix cores clock higher)
+    c.quant_only(q)
+    torch.cuda.synchronize()
     g = time_launches(lambda: c.gemm_only(q), launches, torch)
     a = time_launches(lambda: c.quant_only(q), launches, torch)
     s = time_launches(lambda: c.step(q), launches, torch)
@@ -462,6 +518,22 @@ def mfma_ceiling(q, torch, dev, iters=2000, blocks=2048):
     return blocks * 4 * iters * 4 * 65536 / t / 1e12
 
 
+def mfma_ceiling_data(q, torch, c, iters=1000, blocks=2048):
+    """INT8 ops/s of the same register-only MFMA loop fed with this case's own
+    operands (its activation codes and its dequantized weights): the matrix-core
+    ceiling for the data the GEMM multiplies (the clock under MFMA load depends on
+    the operands' toggling).  blocks x 4 waves x iters x 8 MFMAs x 65536 ops."""
+    p, m, _s = c.sets[0]
+    w = q.dequantize_packed(p, m, c.L.N, c.L.K)
+    c.quant_only(q)
+    sink = torch.zeros(16, dtype=torch.int32, device=w.device)
+    q.mfma_peak_operands(c.qx, w, iters, blocks, sink)
+    t = time_launches(lambda: q.mfma_peak_operands(c.qx, w, iters, blocks, sink), 3, torch, reps=3)
+    del w
+    torch.cuda.empty_cache()
+    return blocks * 4 * iters * 8 * 65536 / t / 1e12
+
+
 def oracle_case(L, M, per_channel=False, cols=256):
     """Seconds of the CPU oracle (unchanged) for one case, by stage: activation
     quantization over the whole [M, K]; weight quantization, dequantization,
@@ -525,8 +597,233 @@ def sweep(q, torch, dev, launches, per_channel=False, with_oracle=True):
     return rows
 
 
+# M grids of the profiling sweep: tiled activation codes (the linear entry point up
+# to 64 tokens) and row-major codes (the GEMM entry point, and the linear one beyond)
+PROFILE_M_TILED = (1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64)
+PROFILE_M_ROW = (1, 8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
+PROFILE_SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+PROFILE_FILE = os.path.join(ROOT, "profiles", "plan_profile_mi355x.json")
+PLAN_TABLE = os.path.join(ROOT, "w4a8_mixed_precision_amd", "csrc", "qoq_plan_table.inc")
+
+
+def warm_up(fn, torch, seconds=0.03):
+    """Run fn back to back for about `seconds` of GPU time before timing: after the
+    host has left the GPU idle (building a case's inputs), the clock takes a few
+    milliseconds to come back up, and the first configuration timed would pay for it."""
+    t = time_launches(fn, 2, torch, reps=1)
+    g = capture(fn, int(max(2, min(256, seconds / max(t, 1e-7)))), torch)
+    g.replay()
+    torch.cuda.synchronize()
+    del g
+
+
+def time_adaptive(fn, torch, target_s=2e-3):
+    """Seconds per launch of fn: one short graph to estimate, then a graph of about
+    target_s, best of two replays."""
+    t0 = time_launches(fn, 2, torch, reps=1)
+    n = int(max(2, min(64, target_s / max(t0, 1e-7))))
+    g = capture(fn, n, torch)
+    best = min(time_graph(g, 1, torch) for _ in range(2)) / n
+    del g
+    return best
+
+
+def profile_candidates(q, M, N, tiled):
+    """(config, splits) pairs worth timing at M: few-token kernels (the only ones
+    on tiled codes) up to 128 tokens, tile kernels from 16 tokens with every split
+    factor whose INT32 partial sums stay within 512 MiB."""
+    out = []
+    for name in q.gemm_configs():
+        few = name.startswith("skinny")
+        if tiled and not few:
+            continue
+        if few and M > 128:
+            continue
+        if few:
+            out.append((name, 0))
+        elif M >= 16:
+            out += [(name, sp) for sp in PROFILE_SPLITS if sp == 1 or sp * M * N * 4 <= 512 << 20]
+    return out
+
+
+def profile_plan(q, torch, dev, only=""):
+    """The measured dispatch table: for every (N, K) of the workloads and every M of
+    the grids, each candidate configuration timed on real codes with the weights
+    rotated; the fastest per point becomes a table row."""
+    from w4a8_mixed_precision_amd import workloads as wl
+    shapes = []
+    for L in wl.LAYERS:
+        if only and L.name not in only.split(","):
+            continue
+        if (L.N, L.K) not in [(x.N, x.K) for x in shapes]:
+            shapes.append(L)
+    points = []
+    for L in shapes:
+        sets, _ = packed_sets_for(L, dev, q, max_sets=64)
+        for tiled, grid in ((1, PROFILE_M_TILED), (0, PROFILE_M_ROW)):
+            for M in grid:
+                c = Case(L, M, dev, sets)
+                c.tiled = bool(tiled)
+                c.quant_only(q)
+                torch.cuda.synchronize()
+                warm_up(lambda: c.gemm_only(q), torch)
+                res = []
+                for cfg, sp in profile_candidates(q, M, L.N, tiled):
+                    with q.plan_override(config=cfg, splits=sp):
+                        c.workspace(q)
+                        try:
+                            t = time_adaptive(lambda: c.gemm_only(q), torch)
+                        except Exception as ex:        # a configuration the shape cannot take
+                            print(json.dumps({"skip": cfg, "splits": sp, "err": str(ex)[:80]}), file=sys.stderr)
+                            continue
+                    res.append((t, cfg, sp))
+                res.sort()
+                t_best, cfg, sp = res[0]
+                pt = {"N": L.N, "K": L.K, "tiled": tiled, "M": M, "best": cfg, "splits": sp,
+                      "best_us": t_best * 1e6,
+                      "top": [{"config": c_, "splits": s_, "us": round(t_ * 1e6, 3)} for t_, c_, s_ in res[:8]]}
+                points.append(pt)
+                print(json.dumps({k: pt[k] for k in ("N", "K", "tiled", "M", "best", "splits", "best_us")}),
+                      flush=True)
+                del c
+        del sets
+        torch.cuda.empty_cache()
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    tag = only.replace(",", "+") if only else "all"
+    path = os.path.join(ROOT, "gpurun_out", f"plan_profile_{tag}.json")
+    with open(path, "w") as f:
+        json.dump({"points": points, "M_tiled": PROFILE_M_TILED, "M_row": PROFILE_M_ROW,
+                   "splits": PROFILE_SPLITS}, f, indent=1)
+    profile_merge([path])
+
+
+COVER_TOL = 0.03       # run-to-run spread of one configuration is about this
+
+
+def cover_configs(points, tol=COVER_TOL):
+    """The fewest configurations such that at every profiled point one of them is
+    within tol of the fastest (greedy set cover: repeatedly keep the configuration
+    that is near-best at the most points not yet covered).  Configurations that win
+    only by noise drop out of the table."""
+    near = []
+    for p in points:
+        best = p["top"][0]["us"]
+        near.append({t["config"] for t in p["top"] if t["us"] <= best * (1 + tol)})
+    keep, todo = set(), set(range(len(points)))
+    while todo:
+        count = {}
+        for i in todo:
+            for c in near[i]:
+                count[c] = count.get(c, 0) + 1
+        c = max(sorted(count), key=lambda k: count[k])
+        keep.add(c)
+        todo = {i for i in todo if c not in near[i]}
+    return keep
+
+
+def profile_merge(paths):
+    """Profile files -> the committed profile (profiles/) and the dispatch table
+    (the fastest configuration per point)."""
+    points = []
+    for pth in paths:
+        with open(pth) as f:
+            points += json.load(f)["points"]
+    points.sort(key=lambda p: (p["N"], p["K"], p["tiled"], p["M"]))
+    keep = cover_configs(points)
+    rows = []
+    for p in points:
+        alt = [t for t in p["top"] if t["config"] in keep]
+        pick = min(alt, key=lambda t: t["us"])
+        p["table"] = {"config": pick["config"], "splits": pick["splits"], "us": pick["us"]}
+        rows.append((p["N"], p["K"], p["tiled"], p["M"], pick["config"], max(pick["splits"], 1)))
+    compact = [{"N": p["N"], "K": p["K"], "tiled": p["tiled"], "M": p["M"], "best": p["best"],
+                "splits": p["splits"], "best_us": round(p["best_us"], 3), "table": p["table"],
+                "top": p["top"][:4]} for p in points]
+    with open(PROFILE_FILE, "w") as f:
+        json.dump({"command": "python -m w4a8_mixed_precision_amd.build --all-configs; python bench.py "
+                              "--profile-plan [--profile-layers ...]; python bench.py --profile-merge <files>",
+                   "kept_configs": sorted(keep), "cover_tolerance": COVER_TOL,
+                   "M_tiled": PROFILE_M_TILED, "M_row": PROFILE_M_ROW, "splits": PROFILE_SPLITS,
+                   "points": compact}, f, separators=(",", ":"))
+    with open(PLAN_TABLE, "w") as f:
+        f.write("// The measured dispatch table: QOQ_PLAN_ROW(N, K, tiled codes, M, configuration,\n"
+                "// split-K factor), the fastest configuration per point of the profiling sweep on\n"
+                "// MI355X (python bench.py --profile-plan; real activation codes, weights rotated over\n"
+                "// >= 1 GiB, graph-timed).  Rows of one (N, K, layout) are sorted by M.\n")
+        for r in rows:
+            f.write('QOQ_PLAN_ROW(%d, %d, %d, %d, "%s", %d)\n' % r)
+    print(f"wrote {PLAN_TABLE} ({len(rows)} rows) and {PROFILE_FILE}", flush=True)
+
+
+def check_plan(q, torch, dev, tol=0.05):
+    """The planner's choice against the best configurations of the committed
+    profile, timed side by side at every profiled point: the ratio of the
+    planner's time to the best of them."""
+    from w4a8_mixed_precision_amd import workloads as wl
+    with open(PROFILE_FILE) as f:
+        prof = json.load(f)
+    by_shape = {}
+    for pt in prof["points"]:
+        by_shape.setdefault((pt["N"], pt["K"]), []).append(pt)
+    out = []
+    for (N, K), pts in by_shape.items():
+        L = next(x for x in wl.LAYERS if (x.N, x.K) == (N, K))
+        sets, _ = packed_sets_for(L, dev, q, max_sets=64)
+        for pt in pts:
+            M, tiled = pt["M"], pt["tiled"]
+            c = Case(L, M, dev, sets)
+            c.tiled = bool(tiled)
+            c.quant_only(q)
+            torch.cuda.synchronize()
+            plan = q.gemm_tiled_plan(M, N, K) if tiled else q.gemm_plan(M, N, K)
+            c.workspace(q)
+            warm_up(lambda: c.gemm_only(q), torch)
+            t_plan = time_adaptive(lambda: c.gemm_only(q), torch)
+            # the fastest configurations of the profile that the library still holds
+            # (the others were dropped from the build), timed now beside the plan
+            kept = set(q.gemm_configs())
+            t_alt = [t_plan]
+            for alt in [a for a in pt["top"] if a["config"] in kept][:3]:
+                with q.plan_override(config=alt["config"], splits=alt["splits"]):
+                    c.workspace(q)
+                    t_alt.append(time_adaptive(lambda: c.gemm_only(q), torch))
+            r = {"N": N, "K": K, "tiled": tiled, "M": M, "plan": plan, "plan_us": t_plan * 1e6,
+                 "best_now_us": min(t_alt) * 1e6, "ratio": t_plan / min(t_alt),
+                 "profile_best": pt["best"], "profile_best_us": pt["best_us"],
+                 "ratio_to_profile_best": t_plan * 1e6 / pt["best_us"]}
+            out.append(r)
+            print(json.dumps(r), flush=True)
+            del c
+        del sets
+        torch.cuda.empty_cache()
+    worst = max(r["ratio"] for r in out)
+    summary = {"points": len(out), "worst_ratio": worst, "within_tol": sum(r["ratio"] <= 1 + tol for r in out),
+               "tol": tol, "median_ratio_to_profile_best": sorted(r["ratio_to_profile_best"] for r in out)[len(out) // 2],
+               "worst_ratio_to_profile_best": max(r["ratio_to_profile_best"] for r in out)}
+    with open(os.path.join(ROOT, "gpurun_out", "plan_check.json"), "w") as f:
+        json.dump({"summary": summary, "points": out}, f, indent=1)
+    with open(os.path.join(ROOT, "gpurun_out", "plan_check.md"), "w") as f:
+        f.write("# Dispatch table check (MI355X)\n\nCommand: `python bench.py --check-plan` (the planner's choice "
+                "timed beside the fastest configurations of the committed profile that the library holds, at every "
+                "profiled point; real codes, weights rotated, graph-timed after a warm-up).\n\n")
+        f.write(f"Points: {summary['points']}; within {tol:.0%} of the best timed beside it: "
+                f"{summary['within_tol']}; worst ratio {summary['worst_ratio']:.3f}; median ratio to the "
+                f"profile's best (all 41 candidates, other run) {summary['median_ratio_to_profile_best']:.3f}, "
+                f"worst {summary['worst_ratio_to_profile_best']:.3f}.\n\n")
+        f.write("| N | K | codes | M | plan | plan us | best now us | ratio | profile best | profile us |\n"
+                "|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in out:
+            f.write(f"| {r['N']} | {r['K']} | {'tiled' if r['tiled'] else 'row'} | {r['M']} | {r['plan']} | "
+                    f"{r['plan_us']:.2f} | {r['best_now_us']:.2f} | {r['ratio']:.3f} | {r['profile_best']} | "
+                    f"{r['profile_best_us']:.2f} |\n")
+    print(json.dumps(summary), flush=True)
+
+
 def main():
     args = parse()
+    if args.profile_merge is not None:
+        profile_merge(args.profile_merge)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's sharding is "
               f"described in DESIGN.md and is not measured here", file=sys.stderr)
@@ -543,6 +840,12 @@ def main():
     if args.kv4:
         kv4_bench(qoq, torch, dev, args.kernel_launches)
         return
+    if args.profile_plan:
+        profile_plan(qoq, torch, dev, args.profile_layers)
+        return
+    if args.check_plan:
+        check_plan(qoq, torch, dev)
+        return
     if args.sweep:
         sweep(qoq, torch, dev, args.kernel_launches, args.format == "channel", not args.no_cpu_baseline)
         return
@@ -551,18 +854,22 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    L = wl.find(args.layer)
-    Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else L.Ms
-    sets, pack_s = packed_sets_for(L, dev, qoq)
-    cases = [Case(L, M, dev, sets) for M in Ms]
+    plan = ((args.layer, tuple(int(m) for m in args.ms.split(",")) if args.ms else wl.find(args.layer).Ms),) \
+        if args.layer else STEP
+    cases, pack_ms = [], {}
+    for name, Ms in plan:
+        L = wl.find(name)
+        sets, pack_s = packed_sets_for(L, dev, qoq)
+        pack_ms[name] = pack_s * 1e3
+        cases += [Case(L, M, dev, sets) for M in Ms]
 
     def step():
         for c in cases:
             c.step(qoq)
 
     # warmup steps run eagerly; the K timed steps are one HIP graph of exactly K steps
-    # (each step rotates to the next packed-weight copy), replayed once between a
-    # synchronize on both sides and timed with HIP events on the replay stream.
+    # (each step rotates to the next packed-weight copy of every layer), replayed once
+    # between a synchronize on both sides and timed with HIP events on the replay stream.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -579,19 +886,34 @@ def main():
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host0
     step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    del g_steps
 
-    per_case = [run_case_metrics(c, qoq, torch, args.kernel_launches) for c in cases]
+    per_case = []
+    for c in cases:
+        r = run_case_metrics(c, qoq, torch, args.kernel_launches)
+        r["layer"] = c.L.name
+        per_case.append(r)
+        print(json.dumps({"case": r["layer"], "M": r["M"], "gemm_us": round(r["gemm_us"], 2),
+                          "linear_us": round(r["linear_us"], 2), "roofline_frac": round(r["roofline_frac"], 3)}),
+              file=sys.stderr, flush=True)
     ops = sum(c.ops for c in cases)
     wbytes = sum(c.bytes["weight"] for c in cases)
-    # dominant kernel: the GEMM launch with the largest time in the step; its bound
-    # is whichever of HBM bytes and INT8 MFMA ops takes longer at the published peaks
+    # dominant kernel: the GEMM launch with the largest time in the step
     dom = max(per_case, key=lambda r: r["gemm_us"])
-    dom_case = cases[per_case.index(dom)]
-    t_launch = dom["gemm_us"] * 1e-6
-    if dom_case.ops / (INT8_PEAK_TOPS * 1e12) > dom_case.bytes["total"] / (HBM_PEAK_GBPS * 1e9):
-        bound, unit, peak, achieved = "mfma", "TOPS", INT8_PEAK_TOPS, dom_case.ops / t_launch / 1e12
-    else:
-        bound, unit, peak, achieved = "hbm", "GB/s", HBM_PEAK_GBPS, dom_case.bytes["total"] / t_launch / 1e9
+    regimes = {}
+    for k, (name, M) in REGIMES.items():
+        for r, c in zip(per_case, cases):
+            if (r["layer"], r["M"]) == (name, M):
+                regimes[k] = roofline_of(r, c)
+    if "mfma" in regimes:
+        c = cases[[(r["layer"], r["M"]) for r in per_case].index(REGIMES["mfma"])]
+        data_tops = mfma_ceiling_data(qoq, torch, c)
+        const_tops = mfma_ceiling(qoq, torch, dev)
+        regimes["mfma"].update({"ceiling_TOPS_same_data": data_tops,
+                                "frac_of_ceiling_same_data": regimes["mfma"]["achieved"] / data_tops,
+                                "ceiling_TOPS_constant_operands": const_tops})
+    workload = "; ".join(f"{name} M={','.join(str(m) for m in Ms)} (K={wl.find(name).K} N={wl.find(name).N})"
+                         for name, Ms in plan)
     result = {
         "metric": METRIC,
         "value": ops / step_s / 1e12,
@@ -605,25 +927,23 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{L.name}: W4A8 g128 GEMM K={L.K} N={L.N}, M in {list(Ms)}, "
-                               f"per-token INT8 activation quant + GEMM + fp16 epilogue per M "
-                               f"(one qoq_w4a8_linear call per M)",
-                   "K": L.K, "N": L.N, "M": list(Ms), "group": 128},
+        "config": {"workload": "W4A8 g128 linear per case (per-token INT8 activation quant + GEMM + fp16 "
+                               "epilogue, one qoq_w4a8_linear call): " + workload,
+                   "cases": [{"layer": name, "K": wl.find(name).K, "N": wl.find(name).N, "M": list(Ms)}
+                             for name, Ms in plan],
+                   "group": 128},
         "weight_GBps_step": wbytes / step_s / 1e9,
-        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak,
-                     "traffic": measured_traffic(dom["plan"], dom["M"], L.N, L.K),
-                     "kernel": dom["plan"], "M": dom["M"],
-                     "bytes_per_launch": dom_case.bytes["total"], "launch_us": dom["gemm_us"]},
+        "roofline": roofline_of(dom, cases[per_case.index(dom)]),
+        "regimes": regimes,
         "cases": per_case,
-        "offline_pack_ms": pack_s * 1e3,
+        "offline_pack_ms": pack_ms,
         "copy_ceiling": copy_ceiling(qoq, torch, dev),
         "kv4_attention": None if args.no_kv4 else kv4_case_metrics(wl.find_kv("llama3_8b_b64_l1024"), qoq, torch, dev,
                                                                     args.kernel_launches),
         "host_wall_s": t_host,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(L, Ms, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_step(plan, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

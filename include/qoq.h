@@ -474,6 +474,15 @@ int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int b
  * Errors: INVALID, ALIGNMENT, HIP. */
 int qoq_mfma_peak(int iters, int blocks, void *sink, void *stream);
 
+/* qoq_mfma_peak on operands read from memory: each lane loads eight A fragments
+ * from `a` and eight B fragments from `b` (16 bytes each, at positions spread over
+ * the buffers; a_bytes, b_bytes >= 16) and the loop cycles through them.  Fed with
+ * a GEMM's own activation codes and dequantized weights it gives the matrix-core
+ * ceiling for that data: the chip's clock under MFMA load depends on how much the
+ * operands toggle.  Errors: INVALID, ALIGNMENT, HIP. */
+int qoq_mfma_peak_operands(const void *a, size_t a_bytes, const void *b, size_t b_bytes, int iters,
+                           int blocks, void *sink, void *stream);
+
 /* One v_mfma_i32_16x16x64_i8 on a single wave: lane l supplies 16 A bytes at
  * a_frag + 16*l and 16 B bytes at b_frag + 16*l and receives its 4 INT32 results at
  * d_frag + 16*l.  Used to pin the operand and result lane layout.

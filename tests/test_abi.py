@@ -78,14 +78,61 @@ def test_plan_override_rejects_unknown_names():
     assert qoq.gemm_plan(300, 6144, 4096) == before
 
 
+def _table_rows():
+    """Rows of the measured dispatch table as compiled into the library."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(qoq.LIB_PATH), "..", "csrc", "qoq_plan_table.inc")
+    rows = re.findall(r'QOQ_PLAN_ROW\((\d+), (\d+), (\d), (\d+), "([^"]+)", (\d+)\)', open(path).read())
+    return [(int(n), int(k), int(t), int(m), c, int(sp)) for n, k, t, m, c, sp in rows]
+
+
+def test_plan_table_rows():
+    """The planner takes the table's configuration (and split factor) at every
+    profiled point, and between two points the row of the nearer M (in ratio); the
+    table covers every (N, K) of the workloads in both code layouts."""
+    rows = _table_rows()
+    assert len(rows) >= 200
+    for (N, K, t, M, cfg, sp) in rows:
+        plan = qoq.gemm_tiled_plan(M, N, K) if t else qoq.gemm_plan(M, N, K)
+        assert plan == cfg, (N, K, t, M, plan, cfg)
+        if not t and not cfg.startswith("skinny"):
+            assert qoq.gemm_plan_splits(M, N, K) == min(sp, K // 128)
+    from w4a8_mixed_precision_amd import workloads as wl
+    for L in wl.LAYERS:
+        for t in (0, 1):
+            assert any((N, K, tt) == (L.N, L.K, t) for (N, K, tt, *_r) in rows), (L.name, t)
+    # nearest in ratio: 1536 lies between 1024 and 2048 (ratio 1.5 vs 1.33 -> 2048)
+    by_m = {M: cfg for (N, K, t, M, cfg, sp) in rows if (N, K, t) == (28672, 4096, 0)}
+    assert qoq.gemm_plan(1400, 28672, 4096) == by_m[1536]
+    assert qoq.gemm_plan(100000, 28672, 4096) == by_m[8192]
+
+
+def test_every_config_is_in_the_table():
+    """Every configuration compiled into the library is the table's choice at some
+    profiled point (the rest were dropped from the build)."""
+    used = {r[4] for r in _table_rows()}
+    names = qoq.gemm_configs()
+    assert set(names) == used, (set(names) - used, used - set(names))
+
+
+def test_plan_rules_outside_the_table():
+    """Shapes the table does not cover get a configuration from the rules."""
+    names = set(qoq.gemm_configs())
+    for (N, K) in [(1024, 2048), (12288, 5120), (2048, 33280)]:
+        for M in (1, 16, 40, 64, 100, 300, 1000, 5000):
+            assert qoq.gemm_plan(M, N, K) in names
+            assert qoq.gemm_tiled_plan(min(M, 64), N, K) in names
+
+
 def test_split_plan_and_workspace():
     """Split-K plans: factor, workspace size (splits x M x N INT32 partial sums),
     and the override."""
-    # down projection at M = 256: 128 x 128 tiles, 2 x 32 = 64 of them -> 8 splits
-    assert qoq.gemm_plan(256, 4096, 14336) == "dma2_tm4_tn1"
-    sp = qoq.gemm_plan_splits(256, 4096, 14336)
-    assert sp == 8
-    assert qoq.gemm_workspace_bytes(256, 4096, 14336) == sp * 256 * 4096 * 4
+    split_rows = [r for r in _table_rows() if r[2] == 0 and r[5] > 1]
+    assert split_rows
+    N, K, _t, M, cfg, sp = split_rows[0]
+    assert qoq.gemm_plan(M, N, K) == cfg and qoq.gemm_plan_splits(M, N, K) == sp
+    assert qoq.gemm_workspace_bytes(M, N, K) == sp * M * N * 4
     assert qoq.gemm_plan_splits(1, 6144, 4096) == 1 and qoq.gemm_workspace_bytes(1, 6144, 4096) == 0
     assert qoq.gemm_workspace_bytes(0, 6144, 4096) == 0
     for want, K in [(3, 4096), (16, 4096), (2, 256), (1, 128)]:
@@ -103,7 +150,7 @@ def test_split_plan_and_workspace():
 def test_workspace_validation(L):
     """Shapes whose plan splits K need the workspace: NULL or short -> WORKSPACE,
     not 16-byte aligned -> ALIGNMENT (checked before any launch)."""
-    M, N, K = 256, 4096, 14336
+    N, K, _t, M, _c, _s = [r for r in _table_rows() if r[2] == 0 and r[5] > 1][0]
     need = qoq.gemm_workspace_bytes(M, N, K)
     assert need > 0
     f = L.qoq_w4a8_gemm
@@ -118,9 +165,7 @@ def test_workspace_validation(L):
 def test_workspace_and_plan():
     assert qoq.gemm_workspace_bytes(16, 6144, 4096) == 0
     assert qoq.gemm_plan(1, 6144, 4096).startswith("skinny")
-    assert qoq.gemm_plan(4096, 28672, 4096) == "dma2_tm4_tn2"
-    assert qoq.gemm_plan(256, 28672, 4096) == "wide2_tm4_tn1"
-    assert qoq.gemm_plan(1024, 4096, 14336) == "dma2_tm4_tn2"
+    assert qoq.gemm_plan(4096, 28672, 4096).startswith(("dma2", "sd", "wide2"))
     assert qoq.gemm_plan(1, 17, 4096) == "invalid"
     assert qoq.gemm_plan(0, 16, 128) == "invalid"
 
@@ -247,7 +292,7 @@ def test_linear_plan_and_workspace():
     otherwise: tiled codes (whole 16-row blocks) and s_X up to 64 tokens, row-major
     codes, s_X and the GEMM's own workspace beyond."""
     fused = qoq.linear_configs()
-    assert len(fused) >= 2
+    assert len(fused) >= 1
     assert qoq.linear_plan(1, 6144, 4096) in fused
     assert qoq.linear_plan(2, 512, 512) in fused
     assert qoq.linear_plan(1, 59136, 8192) in fused

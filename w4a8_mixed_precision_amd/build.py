@@ -2,6 +2,8 @@
 
 Every source is compiled on each call (the build is the "does it compile" check);
 objects go to ``_build/`` and the shared library into ``_lib/`` inside the package.
+``--all-configs`` adds the GEMM configurations the dispatch table does not use
+(the candidate set of ``bench.py --profile-plan``); the product build leaves them out.
 """
 from __future__ import annotations
 
@@ -37,10 +39,10 @@ def _hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -51,12 +53,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, all_configs: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    extra = ["-DQOQ_ALL_CONFIGS"] if all_configs else []
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, extra), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,4 +72,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(all_configs="--all-configs" in sys.argv[1:])

@@ -543,6 +543,14 @@ int qoq_stream_read(const void *src, size_t bytes, void *sink, int unroll, int b
   return launch_status();
 }
 
+int qoq_mfma_peak_operands(const void *a, size_t a_bytes, const void *b, size_t b_bytes, int iters, int blocks,
+                           void *sink, void *stream) {
+  if (!a || !b || !sink || iters <= 0 || blocks <= 0 || a_bytes < 16 || b_bytes < 16) return QOQ_ERR_INVALID;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sink, 4)) return QOQ_ERR_ALIGNMENT;
+  qoq::launch_mfma_peak_operands(a, a_bytes, b, b_bytes, iters, blocks, sink, as_stream(stream));
+  return launch_status();
+}
+
 int qoq_mfma_peak(int iters, int blocks, void *sink, void *stream) {
   if (iters <= 0 || blocks <= 0 || !sink) return QOQ_ERR_INVALID;
   if (!aligned(sink, 4)) return QOQ_ERR_ALIGNMENT;

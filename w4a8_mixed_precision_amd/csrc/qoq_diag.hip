@@ -108,6 +108,41 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, int seed, int
   if (x == 0x7fffffff) sink[0] = x;
 }
 
+// The same loop on operands taken from memory: lane l of wave w of block b loads
+// eight A and eight B fragments (16 bytes each) from a and b at positions spread
+// over the buffers, then runs iters rounds of eight MFMAs cycling through them, so
+// the matrix units see the toggling of real data (the chip's clock under MFMA load
+// depends on it: constant operands let it run faster than GEMM data does).
+__global__ __launch_bounds__(256) void mfma_peak_operands_kernel(const v4i *__restrict__ a, size_t na,
+                                                                 const v4i *__restrict__ b, size_t nb, int iters,
+                                                                 int *__restrict__ sink) {
+  const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  v4i fa[8], fb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    fa[i] = a[(t * 8 + i * 131 + 17) % na];
+    fb[i] = b[(t * 8 + i * 257 + 5) % nb];
+  }
+  v16i acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = v16i{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i & 3] = mfma32x32x32(fa[i], fb[(i * 5 + 3) & 7], acc[i & 3]);
+  }
+  int x = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x ^= acc[i][0] ^ acc[i][5] ^ acc[i][10] ^ acc[i][15];
+  if (x == 0x7fffffff) sink[0] = x;
+}
+
+void launch_mfma_peak_operands(const void *a, size_t a_bytes, const void *b, size_t b_bytes, int iters, int blocks,
+                               void *sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_peak_operands_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const v4i *>(a), a_bytes / 16, static_cast<const v4i *>(b), b_bytes / 16, iters,
+                     static_cast<int *>(sink));
+}
+
 void launch_mfma_peak(int iters, int blocks, void *sink, hipStream_t stream) {
   hipLaunchKernelGGL(mfma_peak_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, iters, 3,
                      static_cast<int *>(sink));

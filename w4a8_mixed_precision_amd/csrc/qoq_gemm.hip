@@ -1340,20 +1340,28 @@ struct Config {
 #define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
 
 const Config kConfigs[] = {
-    QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(1, 1, 4, 4)
-    QOQ_SKINNY(1, 2, 4, 4) QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(1, 2, 16, 2)
-    QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
-    QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(3, 2, 8, 2)
-    QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(4, 2, 8, 1)
-    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(1, 1, 16, 2, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
-    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 1, 3)
-    QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
-    QOQ_SKINNY_R(4, 4, 8, 1, 3)
-    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
-    QOQ_SKINNY32(1, 2, 8, 1, 2)
+    // the configurations the measured dispatch table uses (qoq_plan_table.inc): the
+    // profiling sweep times 41, and keeps the fewest that are near-best (within 3 %)
+    // at every profiled point
+    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2)
+    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3)
+    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
-    QOQ_DMA2(2, 1) QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
+    QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(2) QOQ_SD(3)
+#ifdef QOQ_ALL_CONFIGS
+    // the rest of the profiling sweep's candidates (build.py --all-configs): none is
+    // needed for the table, so the product build leaves them out
+    QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 1, 4, 4) QOQ_SKINNY(1, 2, 4, 4)
+    QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
+    QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
+    QOQ_SKINNY(1, 4, 8, 2) QOQ_SKINNY(4, 4, 8, 1)
+    QOQ_SKINNY_R(1, 1, 16, 2, 3) QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
+    QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
+    QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
+    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
+    QOQ_DMA2(2, 2)
+#endif
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1388,6 +1396,87 @@ int choose_splits(int64_t tiles, int64_t G, int forced) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits)));
 }
 
+// ---------------------------------------------------------------------------
+// The measured dispatch table ("ADAngel" page: an offline policy map from the
+// profiled shape to the fastest kernel, looked up at run time): one row per
+// (N, K, activation-code layout, M) of the workloads' layer shapes, naming the
+// configuration (and split-K factor) that was fastest on MI355X in the profiling
+// sweep (`bench.py --profile-plan`, which writes qoq_plan_table.inc).  A shape the
+// table covers takes the row with the nearest M (nearest in ratio); other shapes
+// fall back to the rules below.
+// ---------------------------------------------------------------------------
+struct PlanRow {
+  int64_t N, K;
+  int tiled;
+  int64_t M;
+  const char *config;
+  int splits;
+};
+const PlanRow kPlanRows[] = {
+#define QOQ_PLAN_ROW(N, K, T, M, C, S) {N, K, T, M, C, S},
+#include "qoq_plan_table.inc"
+#undef QOQ_PLAN_ROW
+    {0, 0, 0, 0, nullptr, 0}};   // end marker
+constexpr int kNumPlanRows = sizeof(kPlanRows) / sizeof(kPlanRows[0]) - 1;
+
+struct PlanIndex {
+  const Config *cfg[kNumPlanRows + 1];
+  struct Range {
+    int64_t N, K;
+    int tiled, begin, end;      // rows [begin, end), sorted by M
+  } ranges[64];
+  int nranges = 0;
+};
+PlanIndex g_plan_index;
+std::once_flag g_plan_once;
+
+void build_plan_index() {
+  PlanIndex &ix = g_plan_index;
+  for (int i = 0; i < kNumPlanRows; ++i) {
+    ix.cfg[i] = nullptr;
+    for (int c = 0; c < kNumConfigs; ++c)
+      if (strcmp(kConfigs[c].name, kPlanRows[i].config) == 0 && (!kPlanRows[i].tiled || kConfigs[c].kt[0][0]))
+        ix.cfg[i] = &kConfigs[c];
+    const PlanRow &r = kPlanRows[i];
+    const bool same = ix.nranges > 0 && ix.ranges[ix.nranges - 1].N == r.N && ix.ranges[ix.nranges - 1].K == r.K &&
+                      ix.ranges[ix.nranges - 1].tiled == r.tiled;
+    if (same) {
+      ix.ranges[ix.nranges - 1].end = i + 1;
+    } else if (ix.nranges < 64) {
+      ix.ranges[ix.nranges++] = {r.N, r.K, r.tiled, i, i + 1};
+    }
+  }
+}
+
+// the table's configuration for this shape (nullptr when the table does not cover
+// it); splits receives the row's split-K factor
+const Config *table_plan(int64_t M, int64_t N, int64_t K, bool tiled_a, int &splits) {
+  std::call_once(g_plan_once, build_plan_index);
+  const PlanIndex &ix = g_plan_index;
+  for (int r = 0; r < ix.nranges; ++r) {
+    const auto &rg = ix.ranges[r];
+    if (rg.N != N || rg.K != K || rg.tiled != static_cast<int>(tiled_a)) continue;
+    int best = rg.begin;
+    for (int i = rg.begin + 1; i < rg.end; ++i) {
+      // between rows a < b: M is nearer to a in ratio iff M * M < a * b
+      if (kPlanRows[i].M <= M || M * M >= kPlanRows[i - 1].M * kPlanRows[i].M) best = i;
+      else break;
+    }
+    if (!ix.cfg[best]) return nullptr;
+    splits = kPlanRows[best].splits;
+    return ix.cfg[best];
+  }
+  return nullptr;
+}
+
+// split-K factor of a tile plan: the override, else the table's row, else the
+// rule (when the rules allow splitting)
+int plan_splits(int64_t tiles, int64_t G, int forced, int table_splits, bool split_k) {
+  if (forced > 0) return choose_splits(tiles, G, forced);
+  if (table_splits > 0) return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({table_splits, kMaxSplits, G})));
+  return split_k ? choose_splits(tiles, G, 0) : 1;
+}
+
 // tiled_a: the activation codes are in the tiled layout (M <= kTiledMaxM), which
 // only the few-token kernels read
 Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
@@ -1399,6 +1488,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
   bool split_k = true;   // may the plan split K (kinds 4 and 5)
+  int table_splits = 0;  // split-K factor of the table's row (0: no row)
+  if (!cfg && ov.regime == 0) cfg = table_plan(M, N, K, tiled_a, table_splits);
   if (!cfg) {
     // 49..64 tokens on a wide layer: 64-row MFMA tiles beat the split-K-by-wave
     // skinny kernel (the weights are read once either way)
@@ -1407,30 +1498,16 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     if (ov.regime == 2) tiled = true;
     if (tiled_a) tiled = false;
     if (!tiled) {
-      // measured on MI355X (config sweep over the layer shapes of the workloads):
+      // shapes outside the measured table (rules distilled from the same sweeps):
       //  M <= 16: one 16-row block; wide layers with short K stream one strip per
       //           workgroup with 8 K-split waves, the rest two strips and 16 waves
-      //  M <= 64: long K (>= 64 groups): at most two row blocks per workgroup;
-      //           short K: all row blocks in one workgroup, 4 strips once N is wide
-      //  17..64 tokens: 32-row blocks on the 32x32x32 MFMA (about 60 % more INT8
-      //           ops per cycle than 16x16x64): wide layers two strip pairs per
-      //           workgroup (one 32-row block up to 32 tokens, two beyond); long K
-      //           one pair with two groups per batch (two pairs for the widest of
-      //           them past 48 tokens); short narrow layers the same up to 32 tokens
-      //           and past 48, 16-row blocks between
-      const int mt = static_cast<int>(M >= 64 ? 4 : (M + 15) / 16);   // grid.y covers rows past 64
-      if (mt <= 1) {
+      //  17..64 tokens: 32-row blocks on the 32x32x32 MFMA (about 60 % more INT8 ops
+      //           per cycle than 16x16x64), two strip pairs per workgroup, one 32-row
+      //           block up to 32 tokens and two beyond
+      if (M <= 16) {
         cfg = (NS >= 640 && G <= 64) ? find_config(0, 1, 1, 8, 2) : find_config(0, 1, 2, 16, 2);
-      } else if (NS >= 640) {
-        cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2);
-      } else if (G >= 64) {
-        cfg = (M <= 48 || NS < 512) ? find_config(7, 1, 1, 8, 2, 2) : find_config(7, 1, 2, 8, 1, 2);
-      } else if (M <= 32) {
-        cfg = find_config(7, 1, 1, 8, 2, 2);
-      } else if (M <= 48) {
-        cfg = find_config(0, mt, 2, 8, 2);
       } else {
-        cfg = find_config(7, 1, 2, 8, 1, 2);
+        cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2);
       }
     } else {
       // measured on MI355X over the layer shapes of the workloads: the largest tile
@@ -1472,20 +1549,16 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     p.block = dim3(64 * waves);
   } else if (cfg->kind == 6) {   // 256 x 256 tiles, 8 waves
     const int64_t tiles = ((NS + 15) / 16) * ((M + 255) / 256);
-    if (split_k || ov.splits > 0) {
-      p.splits = choose_splits(tiles, G, ov.splits);
-      if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
-    }
+    p.splits = plan_splits(tiles, G, ov.splits, table_splits, split_k);
+    if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
     p.block = dim3(512);
   } else {   // wide2 / dma2: 32-row blocks, 4 waves x 2*TN strips
     const int tm = cfg->a, tn = cfg->b;
     const int64_t nx = (NS + 8 * tn - 1) / (8 * tn), ny = (M + 32 * tm - 1) / (32 * tm);
     const int64_t tiles = nx * ny;
-    if (split_k || ov.splits > 0) {
-      p.splits = choose_splits(tiles, G, ov.splits);
-      if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
-    }
+    p.splits = plan_splits(tiles, G, ov.splits, table_splits, split_k);
+    if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     p.grid = dim3(static_cast<unsigned>(tiles * p.splits));
     p.block = dim3(256);
   }
@@ -1595,8 +1668,9 @@ struct XqConfig {
   {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, R>, "skinny_xq_nb" #NBW "_w" #W "_u" #U "_r" #R, \
    skinny_xq_red_bytes<NBW, W, U>()},
 
-const XqConfig kXqConfigs[] = {QOQ_XQ(1, 16, 2) QOQ_XQ(2, 16, 2) QOQ_XQ(1, 8, 2) QOQ_XQ(2, 8, 2)
-                               QOQ_XQ_R(2, 16, 2, 3) QOQ_XQ_R(2, 8, 2, 3)};
+// measured on MI355X (decode layers of the workloads, M = 1, 2): two strips and 8
+// waves per workgroup were fastest of the fused configurations timed
+const XqConfig kXqConfigs[] = {QOQ_XQ(2, 8, 2)};
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);
 std::once_flag g_xq_once[kNumXq];
 
@@ -1613,11 +1687,10 @@ const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
   if (ov.linear == -1) return nullptr;
   if (ov.linear >= 0) return xq_fits(&kXqConfigs[ov.linear], M, K) ? &kXqConfigs[ov.linear] : nullptr;
   if (M > kXqMaxM) return nullptr;
-  // measured on MI355X (decode layers of the workloads, M = 1, 2): two strips and 8
-  // waves per workgroup; fused only while the quantization every workgroup repeats
-  // (workgroups x M x K elements) stays bounded
+  // fused only while the quantization every workgroup repeats (workgroups x M x K
+  // elements) stays bounded
   const int64_t NS = N / 16;
-  const XqConfig *c = &kXqConfigs[3];
+  const XqConfig *c = &kXqConfigs[0];
   if ((NS + c->nbw - 1) / c->nbw * M * K > kXqMaxRepeat) return nullptr;
   return xq_fits(c, M, K) ? c : nullptr;
 }

@@ -110,6 +110,8 @@ void launch_dequantize_packed(const void *packed, const void *meta, int64_t N, i
 void launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 void launch_stream_read(const void *src, size_t bytes, void *sink, int unroll, int blocks, hipStream_t stream);
 void launch_mfma_peak(int iters, int blocks, void *sink, hipStream_t stream);
+void launch_mfma_peak_operands(const void *a, size_t a_bytes, const void *b, size_t b_bytes, int iters, int blocks,
+                               void *sink, hipStream_t stream);
 void launch_mfma_probe32(const void *a, const void *b, void *d, hipStream_t stream);
 void launch_mfma_probe(const void *a, const void *b, void *d, hipStream_t stream);
 

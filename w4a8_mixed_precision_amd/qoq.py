@@ -88,6 +88,8 @@ _SIGNATURES = {
     "qoq_mfma_probe": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_mfma_probe32": ([_c_vp, _c_vp, _c_vp, _c_vp], ctypes.c_int),
     "qoq_mfma_peak": ([ctypes.c_int, ctypes.c_int, _c_vp, _c_vp], ctypes.c_int),
+    "qoq_mfma_peak_operands": ([_c_vp, _c_sz, _c_vp, _c_sz, ctypes.c_int, ctypes.c_int, _c_vp, _c_vp],
+                               ctypes.c_int),
     "qoq_stream_read": ([_c_vp, _c_sz, _c_vp, ctypes.c_int, ctypes.c_int, _c_vp], ctypes.c_int),
 }
 
@@ -752,6 +754,13 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, unroll: int = 4, blocks: 
 
 def mfma_peak(iters: int, blocks: int, sink: torch.Tensor):
     _check("qoq_mfma_peak", lib().qoq_mfma_peak(iters, blocks, _dev(sink, "sink"), _stream(sink)))
+
+
+def mfma_peak_operands(a: torch.Tensor, b: torch.Tensor, iters: int, blocks: int, sink: torch.Tensor):
+    """qoq_mfma_peak_operands: the MFMA loop on fragments read from a and b."""
+    _check("qoq_mfma_peak_operands",
+           lib().qoq_mfma_peak_operands(_dev(a, "a"), _nbytes(a), _dev(b, "b"), _nbytes(b), iters, blocks,
+                                        _dev(sink, "sink"), _stream(a)))
 
 
 def mfma_probe(a: torch.Tensor, b: torch.Tensor):

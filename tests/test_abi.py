@@ -221,6 +221,13 @@ def test_diag_validation(L):
     assert L.qoq_stream_read(ODD, 32, FAKE, 4, 8, NUL) == ALIGNMENT
     assert L.qoq_mfma_peak(0, 8, FAKE, NUL) == INVALID
     assert L.qoq_mfma_peak(8, 8, ODD, NUL) == ALIGNMENT
+    f = L.qoq_mfma_peak_operands
+    assert f(NUL, 64, FAKE, 64, 8, 8, FAKE, NUL) == INVALID
+    assert f(FAKE, 8, FAKE, 64, 8, 8, FAKE, NUL) == INVALID        # fewer than one fragment
+    assert f(FAKE, 64, FAKE, 64, 0, 8, FAKE, NUL) == INVALID
+    assert f(FAKE, 64, FAKE, 64, 8, 0, FAKE, NUL) == INVALID
+    assert f(ODD, 64, FAKE, 64, 8, 8, FAKE, NUL) == ALIGNMENT
+    assert f(FAKE, 64, FAKE, 64, 8, 8, ODD, NUL) == ALIGNMENT
     assert L.qoq_mfma_probe(NUL, FAKE, FAKE, NUL) == INVALID
     assert L.qoq_mfma_probe32(FAKE, NUL, FAKE, NUL) == INVALID
     assert L.qoq_mfma_probe32(FAKE, FAKE, ODD, NUL) == ALIGNMENT

@@ -70,6 +70,18 @@ def test_mfma_probe_layout(gpu):
             assert d[l, i] == D[4 * (l // 16) + i, l % 16]
 
 
+def test_mfma_peak_operands_runs(gpu):
+    """The data-fed MFMA loop (the matrix-core ceiling for a GEMM's own operands)
+    reads 16-byte fragments at positions taken modulo each buffer's length, finishes,
+    and leaves its sink alone."""
+    say("mfma peak on operands")
+    a = torch.randint(-127, 128, (4096,), dtype=torch.int8, device=gpu)
+    b = torch.randint(-121, 122, (8208,), dtype=torch.int8, device=gpu)     # 513 fragments
+    sink = torch.zeros(4, dtype=torch.int32, device=gpu)
+    qoq.mfma_peak_operands(a, b, 4, 8, sink)
+    assert not host(sink).any()
+
+
 def test_mfma32_probe_layout(gpu):
     """v_mfma_i32_32x32x32_i8: lane l supplies row (l % 32) of A and column (l % 32)
     of B as 16 bytes of k = 16*(l // 32) .. +15; register r of lane l holds

@@ -137,6 +137,13 @@ def _act_cases():
     t[3] = t[1] - np.sign(t[1]) * 2.0 ** -11
     t[3, 300] = 2.9765625
     yield "ties_K512", t.astype(np.float16)
+    # many short rows (the wave-per-row kernel): ragged K, a row count that is not a
+    # multiple of the four rows per workgroup, the zero and subnormal rows again
+    x = (rng.standard_normal((1027, 136)) * 2).astype(np.float16)
+    x[5] = 0.0
+    x[6] *= np.float16(1e-6)
+    x[1026, 3] = np.float16(65504.0)
+    yield "many_rows_K136", x
 
 
 @pytest.mark.parametrize("name,x", list(_act_cases()), ids=lambda v: v if isinstance(v, str) else "")
@@ -171,6 +178,20 @@ def test_quantize_activations_every_fp16_one_launch(gpu):
     want_q, want_s = o.quantize_activations(x)
     assert np.array_equal(host(qx), want_q)
     assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+
+
+def test_quantize_activations_every_fp16_short_rows(gpu):
+    """Every finite fp16 value at every absmax again, as rows of 128 (several
+    thousand rows: the wave-per-row kernel), codes and scales bit-exact."""
+    x = np.concatenate([exhaustive_rows(a, K=128) for a in EXHAUSTIVE_ABSMAX], axis=0)
+    assert x.shape[0] >= 1024
+    say(f"quantize_activations every fp16, short rows {x.shape}")
+    qx, sx = qoq.quantize_activations(to_dev(x, gpu))
+    want_q, want_s = o.quantize_activations(x)
+    assert np.array_equal(host(sx).view(np.uint16), want_s.view(np.uint16))
+    got = host(qx)
+    bad = np.argwhere(got != want_q)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: x={x[tuple(bad[0])]}"
 
 
 def test_quantize_activations_large_sampled(gpu):

@@ -73,7 +73,7 @@ def test_pc_pack_layers(gpu, name):
     _check_pack(gpu, wl.weights_fp16(L))
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (7, 4096), (33, 1152), (64, 8192)])
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 4096), (33, 1152), (64, 8192), (1027, 136), (2048, 4096)])
 def test_rowsum_bit_exact(gpu, M, K):
     say(f"activation row sums M={M} K={K}")
     rng = np.random.default_rng(M + K)

@@ -112,6 +112,57 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const __half 
   }
 }
 
+// Many short rows: one wave per row, four rows per workgroup, the row held in
+// registers (up to kRowChunks 16-byte chunks per lane) and its maximum taken within
+// the wave, with no LDS and no barrier.  For thousands of rows of a few KB a
+// 256-thread workgroup per row spends more on its setup and barrier than on its
+// data.  Same arithmetic as quantize_act_kernel, row-major codes.
+constexpr int kRowChunks = 8;                       // rows up to K = 64 x 8 x 8 = 4096
+constexpr int64_t kRowKernelMinRows = 1024;
+
+template <bool ROWSUM>
+__global__ __launch_bounds__(256) void quantize_act_rows_kernel(const __half *__restrict__ x, int M, int K,
+                                                                int8_t *__restrict__ qx, __half *__restrict__ sx,
+                                                                int *__restrict__ tx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;                             // whole waves; no barrier below
+  const int nchunk = K >> 3;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(row) * K);
+  uint2 *qr = reinterpret_cast<uint2 *>(qx + static_cast<size_t>(row) * K);
+  uint4 v[kRowChunks];
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int idx = lane + 64 * c;
+    v[c] = idx < nchunk ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  unsigned amax = 0;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) amax = absmax_bits8(v[c], amax);
+  amax = wave_max_u32(amax);
+  const __half sh = sym_scale(amax, static_cast<float>(kXQmax));
+  const float s = __half2float(sh);
+  const float rcp = act_rcp(s);
+  if (lane == 0) sx[row] = sh;
+  int tsum = 0;
+#pragma unroll
+  for (int c = 0; c < kRowChunks; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nchunk) {
+      const uint2 q = quant_chunk8(v[c], s, rcp);
+      qr[idx] = q;
+      if (ROWSUM) tsum += code_sum8(q);
+    }
+  }
+  if (ROWSUM) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tsum += __shfl_xor(tsum, off, 64);
+    if (lane == 0) tx[row] = tsum;
+  }
+}
+
+static bool use_rows_kernel(int64_t M, int64_t K) { return M >= kRowKernelMinRows && K <= 64 * 8 * kRowChunks; }
+
 // workgroups per row: enough to give a few rows about 256 workgroups, at most one
 // per register slot in use; one when the row does not fit the registers
 unsigned row_parts(int64_t M, int64_t K) {
@@ -122,6 +173,12 @@ unsigned row_parts(int64_t M, int64_t K) {
 
 void launch_quantize_activations(const void *x, int64_t M, int64_t K, void *qx, void *sx,
                                  hipStream_t stream) {
+  if (use_rows_kernel(M, K)) {
+    hipLaunchKernelGGL(quantize_act_rows_kernel<false>, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
+                       stream, static_cast<const __half *>(x), static_cast<int>(M), static_cast<int>(K),
+                       static_cast<int8_t *>(qx), static_cast<__half *>(sx), nullptr);
+    return;
+  }
   hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<unsigned>(M), row_parts(M, K)),
                      dim3(kActThreads), 0, stream, static_cast<const __half *>(x), static_cast<int>(K),
                      static_cast<int8_t *>(qx), static_cast<__half *>(sx), nullptr);
@@ -144,6 +201,12 @@ void launch_quantize_activations_rowsum_tiled(const void *x, int64_t M, int64_t 
 
 void launch_quantize_activations_rowsum(const void *x, int64_t M, int64_t K, void *qx, void *sx, void *tx,
                                         hipStream_t stream) {
+  if (use_rows_kernel(M, K)) {
+    hipLaunchKernelGGL(quantize_act_rows_kernel<true>, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
+                       stream, static_cast<const __half *>(x), static_cast<int>(M), static_cast<int>(K),
+                       static_cast<int8_t *>(qx), static_cast<__half *>(sx), static_cast<int *>(tx));
+    return;
+  }
   hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<unsigned>(M)), dim3(kActThreads), 0, stream,
                      static_cast<const __half *>(x), static_cast<int>(K), static_cast<int8_t *>(qx),
                      static_cast<__half *>(sx), static_cast<int *>(tx));

@@ -1047,9 +1047,9 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
 //   16 contiguous bytes).
 //   A (256 x 128 per group) comes by copy engine into an AS-stage ring with the
 //   row-pair XOR swizzle; each wave reads only its own 64 rows.
-//   Per group j: dequantize j+1 (codes loaded two groups earlier) into B buffer
-//   (j+1) & 1; copy A(j+AS-1) and load the codes of j+3 into the register set just
-//   consumed; MFMAs of j from A stage j % AS and B buffer j & 1; wait for A(j+1);
+//   Per group j: load the codes of j+3 (three register sets, group g in set g % 3);
+//   dequantize j+1 (codes loaded two groups earlier) into B buffer (j+1) & 1; copy
+//   A(j+AS-1); MFMAs of j from A stage j % AS and B buffer j & 1; wait for A(j+1);
 //   barrier (which also publishes B(j+1)).
 // ---------------------------------------------------------------------------
 constexpr int kSdStageA = 256 * 128;             // A bytes per stage
@@ -1141,22 +1141,25 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
 // units work side by side.
 template <int AS, int Q, bool MF, bool PC>
 __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, int wave, int lane,
-                                        const int8_t *const (&asrc)[4], SdCodes &cur,
+                                        const int8_t *const (&asrc)[4], const SdCodes &deq, SdCodes &fill,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                         unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
   int8_t *bbuf = lds + AS * kSdStageA;
+  // group j+3's codes go out first, into the set that held group j (dequantized a
+  // group ago): the copy wait at the bottom cannot leave register loads issued after
+  // the copies in flight, so codes loaded there would be waited for at once
+  sd_load_codes<PC>(fill, packed, meta, boff, moff, min(j + 3, G - 1));
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (MF) {
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // group j+1 is dequantized from this set (loaded two groups ago) into B buffer
-  // (j+1) & 1, which every wave finished reading before the last barrier; then the
-  // set is refilled with group j+3's codes and group j+AS-1's A copies are issued
-  // (its stage held group j-1)
-  sd_dequant<Q, PC>(bbuf, wave, lane, cur);
+  // group j+1 is dequantized (codes loaded two groups ago) into B buffer (j+1) & 1,
+  // which every wave finished reading before the last barrier; then group j+AS-1's
+  // A copies are issued (its stage held group j-1)
+  sd_dequant<Q, PC>(bbuf, wave, lane, deq);
   __builtin_amdgcn_sched_barrier(0);
   sd_copy_a<AS>(min(j + AS - 1, G - 1), lds, asrc, wave);
-  sd_load_codes<PC>(cur, packed, meta, boff, moff, min(j + 3, G - 1));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!MF) {
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
@@ -1171,17 +1174,26 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// code set g % 3 holds group g: the loop is unrolled by six (B buffer j & 1, sets j % 3)
 template <int AS, bool MF, bool PC>
 __device__ __forceinline__ void sd_loop(int G, int8_t *__restrict__ lds, int wave, int lane,
-                                        const int8_t *const (&asrc)[4], SdCodes &set0, SdCodes &set1,
+                                        const int8_t *const (&asrc)[4], SdCodes &s0, SdCodes &s1, SdCodes &s2,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                         unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
   int j = 0;
-  for (; j + 1 < G; j += 2) {
-    sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
-    sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, set0, packed, meta, boff, moff, acc);
+  for (; j + 5 < G; j += 6) {
+    sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC>(j + 5, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
   }
-  if (j < G) sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, set1, packed, meta, boff, moff, acc);
+  if (j < G) sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+  if (j + 1 < G) sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+  if (j + 2 < G) sd_step<AS, 0, MF, PC>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
+  if (j + 3 < G) sd_step<AS, 1, MF, PC>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+  if (j + 4 < G) sd_step<AS, 0, MF, PC>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
 }
 
 template <int AS, int OUT, bool PC>
@@ -1227,12 +1239,13 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = v16i{};
 
-  // prologue: A(0) .. A(AS-2); codes 0 and 1; dequantize group 0 into B buffer 0;
-  // codes of group 2 into the set just consumed
+  // prologue: A(0) .. A(AS-2); codes 0, 1, 2 into sets 0, 1, 2; dequantize group 0
+  // into B buffer 0
   for (int g = 0; g < AS - 1; ++g) sd_copy_a<AS>(min(g, G - 1), lds, asrc, wave);
-  SdCodes set0, set1;
+  SdCodes set0, set1, set2;
   sd_load_codes<PC>(set0, packed, meta, boff, moff, 0);
   sd_load_codes<PC>(set1, packed, meta, boff, moff, min(1, G - 1));
+  sd_load_codes<PC>(set2, packed, meta, boff, moff, min(2, G - 1));
   {
     v4i b[4];
     weights_lane<PC>(set0.p0, set0.md, b[0], b[2]);
@@ -1241,14 +1254,13 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
   }
-  sd_load_codes<PC>(set0, packed, meta, boff, moff, min(2, G - 1));
   QOQ_WAIT_VMCNT(0);
   __syncthreads();
 
   if (wave < 4)
-    sd_loop<AS, false, PC>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+    sd_loop<AS, false, PC>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
   else
-    sd_loop<AS, true, PC>(G, lds, wave, lane, asrc, set0, set1, packed, meta, boff, moff, acc);
+    sd_loop<AS, true, PC>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
   QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
   __syncthreads();
   const int wm0 = m0 + 64 * (wave & 3);

@@ -602,8 +602,11 @@ def sweep(q, torch, dev, launches, per_channel=False, with_oracle=True):
 PROFILE_M_TILED = (1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64)
 PROFILE_M_ROW = (1, 8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
 PROFILE_SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+PROFILE_M_LINEAR = (1, 2, 4, 8)
 PROFILE_FILE = os.path.join(ROOT, "profiles", "plan_profile_mi355x.json")
 PLAN_TABLE = os.path.join(ROOT, "w4a8_mixed_precision_amd", "csrc", "qoq_plan_table.inc")
+LINEAR_TABLE = os.path.join(ROOT, "w4a8_mixed_precision_amd", "csrc", "qoq_linear_table.inc")
+XQ_MAX_K = 8192        # the fused kernel's limit on K
 
 
 def warm_up(fn, torch, seconds=0.03):
@@ -688,13 +691,44 @@ def profile_plan(q, torch, dev, only=""):
                 del c
         del sets
         torch.cuda.empty_cache()
+    linear_points = profile_linear(q, torch, dev, shapes)
     os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
     tag = only.replace(",", "+") if only else "all"
     path = os.path.join(ROOT, "gpurun_out", f"plan_profile_{tag}.json")
     with open(path, "w") as f:
-        json.dump({"points": points, "M_tiled": PROFILE_M_TILED, "M_row": PROFILE_M_ROW,
-                   "splits": PROFILE_SPLITS}, f, indent=1)
+        json.dump({"points": points, "linear_points": linear_points, "M_tiled": PROFILE_M_TILED,
+                   "M_row": PROFILE_M_ROW, "M_linear": PROFILE_M_LINEAR, "splits": PROFILE_SPLITS}, f, indent=1)
     profile_merge([path])
+
+
+def profile_linear(q, torch, dev, shapes):
+    """The linear entry point at a few tokens: the pair (quantizer + the GEMM
+    plan, "unfused") and every fused configuration that takes the shape, timed as
+    the whole call on the same rotated weights."""
+    points = []
+    for L in shapes:
+        if L.K > XQ_MAX_K:
+            continue
+        sets, _ = packed_sets_for(L, dev, q, max_sets=64)
+        for M in PROFILE_M_LINEAR:
+            c = Case(L, M, dev, sets)
+            torch.cuda.synchronize()
+            warm_up(lambda: c.step(q), torch)
+            res = []
+            for cfg in ["unfused"] + q.linear_configs():
+                with q.plan_override(linear=cfg):
+                    if cfg != "unfused" and q.linear_plan(M, L.N, L.K) != cfg:
+                        continue                      # the fused kernel does not take this shape
+                    res.append((time_adaptive(lambda: c.step(q), torch), cfg))
+            res.sort()
+            pt = {"N": L.N, "K": L.K, "M": M, "best": res[0][1], "best_us": res[0][0] * 1e6,
+                  "top": [{"config": c_, "us": round(t_ * 1e6, 3)} for t_, c_ in res[:8]]}
+            points.append(pt)
+            print(json.dumps({k: pt[k] for k in ("N", "K", "M", "best", "best_us")}), flush=True)
+            del c
+        del sets
+        torch.cuda.empty_cache()
+    return points
 
 
 COVER_TOL = 0.03       # run-to-run spread of one configuration is about this
@@ -730,6 +764,18 @@ def profile_merge(paths):
             points += json.load(f)["points"]
     points.sort(key=lambda p: (p["N"], p["K"], p["tiled"], p["M"]))
     keep = cover_configs(points)
+    lpoints = []
+    for pth in paths:
+        with open(pth) as f:
+            lpoints += json.load(f).get("linear_points", [])
+    lpoints.sort(key=lambda p: (p["N"], p["K"], p["M"]))
+    lkeep = cover_configs(lpoints)
+    lrows = []
+    for p in lpoints:
+        alt = [t for t in p["top"] if t["config"] in lkeep]
+        pick = min(alt, key=lambda t: t["us"])
+        p["table"] = {"config": pick["config"], "us": pick["us"]}
+        lrows.append((p["N"], p["K"], p["M"], pick["config"]))
     rows = []
     for p in points:
         alt = [t for t in p["top"] if t["config"] in keep]
@@ -739,12 +785,20 @@ def profile_merge(paths):
     compact = [{"N": p["N"], "K": p["K"], "tiled": p["tiled"], "M": p["M"], "best": p["best"],
                 "splits": p["splits"], "best_us": round(p["best_us"], 3), "table": p["table"],
                 "top": p["top"][:4]} for p in points]
+    lcompact = [{"N": p["N"], "K": p["K"], "M": p["M"], "best": p["best"], "best_us": round(p["best_us"], 3),
+                 "table": p["table"], "top": p["top"][:4]} for p in lpoints]
     with open(PROFILE_FILE, "w") as f:
         json.dump({"command": "python -m w4a8_mixed_precision_amd.build --all-configs; python bench.py "
                               "--profile-plan [--profile-layers ...]; python bench.py --profile-merge <files>",
-                   "kept_configs": sorted(keep), "cover_tolerance": COVER_TOL,
-                   "M_tiled": PROFILE_M_TILED, "M_row": PROFILE_M_ROW, "splits": PROFILE_SPLITS,
-                   "points": compact}, f, separators=(",", ":"))
+                   "kept_configs": sorted(keep), "kept_linear_configs": sorted(lkeep), "cover_tolerance": COVER_TOL,
+                   "M_tiled": PROFILE_M_TILED, "M_row": PROFILE_M_ROW, "M_linear": PROFILE_M_LINEAR,
+                   "splits": PROFILE_SPLITS, "points": compact, "linear_points": lcompact}, f, separators=(",", ":"))
+    with open(LINEAR_TABLE, "w") as f:
+        f.write("// The measured linear table: QOQ_LINEAR_ROW(N, K, M, configuration), the fastest of\n"
+                "// the fused quantize + GEMM configurations and the quantizer + GEMM pair (\"unfused\")\n"
+                "// per point of the profiling sweep on MI355X (python bench.py --profile-plan).\n")
+        for r in lrows:
+            f.write('QOQ_LINEAR_ROW(%d, %d, %d, "%s")\n' % r)
     with open(PLAN_TABLE, "w") as f:
         f.write("// The measured dispatch table: QOQ_PLAN_ROW(N, K, tiled codes, M, configuration,\n"
                 "// split-K factor), the fastest configuration per point of the profiling sweep on\n"
@@ -752,7 +806,8 @@ def profile_merge(paths):
                 "// >= 1 GiB, graph-timed).  Rows of one (N, K, layout) are sorted by M.\n")
         for r in rows:
             f.write('QOQ_PLAN_ROW(%d, %d, %d, %d, "%s", %d)\n' % r)
-    print(f"wrote {PLAN_TABLE} ({len(rows)} rows) and {PROFILE_FILE}", flush=True)
+    print(f"wrote {PLAN_TABLE} ({len(rows)} rows), {LINEAR_TABLE} ({len(lrows)} rows) and {PROFILE_FILE}",
+          flush=True)
 
 
 def check_plan(q, torch, dev, tol=0.05):
@@ -796,12 +851,42 @@ def check_plan(q, torch, dev, tol=0.05):
             del c
         del sets
         torch.cuda.empty_cache()
+    # the linear entry point at a few tokens: the planner's choice (fused or the
+    # pair) against the profile's fastest alternatives that the library holds
+    lout = []
+    lby = {}
+    for pt in prof.get("linear_points", []):
+        lby.setdefault((pt["N"], pt["K"]), []).append(pt)
+    for (N, K), pts in lby.items():
+        L = next(x for x in wl.LAYERS if (x.N, x.K) == (N, K))
+        sets, _ = packed_sets_for(L, dev, q, max_sets=64)
+        for pt in pts:
+            M = pt["M"]
+            c = Case(L, M, dev, sets)
+            torch.cuda.synchronize()
+            plan = q.linear_plan(M, N, K)
+            warm_up(lambda: c.step(q), torch)
+            t_plan = time_adaptive(lambda: c.step(q), torch)
+            kept = set(q.linear_configs()) | {"unfused"}
+            t_alt = [t_plan]
+            for alt in [a for a in pt["top"] if a["config"] in kept][:3]:
+                with q.plan_override(linear=alt["config"]):
+                    t_alt.append(time_adaptive(lambda: c.step(q), torch))
+            r = {"N": N, "K": K, "M": M, "plan": plan, "plan_us": t_plan * 1e6, "best_now_us": min(t_alt) * 1e6,
+                 "ratio": t_plan / min(t_alt), "profile_best": pt["best"], "profile_best_us": pt["best_us"]}
+            lout.append(r)
+            print(json.dumps(r), flush=True)
+            del c
+        del sets
+        torch.cuda.empty_cache()
     worst = max(r["ratio"] for r in out)
     summary = {"points": len(out), "worst_ratio": worst, "within_tol": sum(r["ratio"] <= 1 + tol for r in out),
                "tol": tol, "median_ratio_to_profile_best": sorted(r["ratio_to_profile_best"] for r in out)[len(out) // 2],
-               "worst_ratio_to_profile_best": max(r["ratio_to_profile_best"] for r in out)}
+               "worst_ratio_to_profile_best": max(r["ratio_to_profile_best"] for r in out),
+               "linear_points": len(lout), "linear_within_tol": sum(r["ratio"] <= 1 + tol for r in lout),
+               "linear_worst_ratio": max((r["ratio"] for r in lout), default=None)}
     with open(os.path.join(ROOT, "gpurun_out", "plan_check.json"), "w") as f:
-        json.dump({"summary": summary, "points": out}, f, indent=1)
+        json.dump({"summary": summary, "points": out, "linear_points": lout}, f, indent=1)
     with open(os.path.join(ROOT, "gpurun_out", "plan_check.md"), "w") as f:
         f.write("# Dispatch table check (MI355X)\n\nCommand: `python bench.py --check-plan` (the planner's choice "
                 "timed beside the fastest configurations of the committed profile that the library holds, at every "
@@ -816,6 +901,16 @@ def check_plan(q, torch, dev, tol=0.05):
             f.write(f"| {r['N']} | {r['K']} | {'tiled' if r['tiled'] else 'row'} | {r['M']} | {r['plan']} | "
                     f"{r['plan_us']:.2f} | {r['best_now_us']:.2f} | {r['ratio']:.3f} | {r['profile_best']} | "
                     f"{r['profile_best_us']:.2f} |\n")
+        if lout:
+            f.write(f"\nLinear entry point (quantize + GEMM in one call) at a few tokens: {summary['linear_points']} "
+                    f"points, within {tol:.0%}: {summary['linear_within_tol']}, worst ratio "
+                    f"{summary['linear_worst_ratio']:.3f}.\n\n")
+            f.write("| N | K | M | plan | plan us | best now us | ratio | profile best | profile us |\n"
+                    "|---|---|---|---|---|---|---|---|---|\n")
+            for r in lout:
+                f.write(f"| {r['N']} | {r['K']} | {r['M']} | {r['plan']} | {r['plan_us']:.2f} | "
+                        f"{r['best_now_us']:.2f} | {r['ratio']:.3f} | {r['profile_best']} | "
+                        f"{r['profile_best_us']:.2f} |\n")
     print(json.dumps(summary), flush=True)
 
 

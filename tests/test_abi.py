@@ -116,6 +116,38 @@ def test_every_config_is_in_the_table():
     assert set(names) == used, (set(names) - used, used - set(names))
 
 
+def _linear_rows():
+    """Rows of the measured linear table as compiled into the library."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(qoq.LIB_PATH), "..", "csrc", "qoq_linear_table.inc")
+    rows = re.findall(r'QOQ_LINEAR_ROW\((\d+), (\d+), (\d+), "([^"]+)"\)', open(path).read())
+    return [(int(n), int(k), int(m), c) for n, k, m, c in rows]
+
+
+def test_linear_table_rows():
+    """The linear entry point takes the table's choice at every profiled point: the
+    named fused kernel, or the quantizer + GEMM pair (then the GEMM plan of the
+    tiled codes); every fused configuration in the build except the rule's default
+    is the table's choice somewhere; beyond the largest profiled M the pair."""
+    rows = _linear_rows()
+    fused = qoq.linear_configs()
+    assert rows and all(c in fused or c == "unfused" for (_n, _k, _m, c) in rows)
+    for (N, K, M, cfg) in rows:
+        plan = qoq.linear_plan(M, N, K)
+        if cfg == "unfused":
+            assert plan == qoq.gemm_tiled_plan(M, N, K), (N, K, M, plan)
+        else:
+            assert plan == cfg, (N, K, M, plan, cfg)
+    used = {c for (_n, _k, _m, c) in rows}
+    assert set(fused[1:]) <= used, set(fused[1:]) - used
+    N, K, _m, _c = rows[-1]
+    assert qoq.linear_plan(16, N, K) == qoq.gemm_tiled_plan(16, N, K)
+    # outside the table the rule: the first fused configuration up to two tokens
+    assert qoq.linear_plan(1, 4096, 1024) == fused[0]
+    assert qoq.linear_plan(3, 4096, 1024) == qoq.gemm_tiled_plan(3, 4096, 1024)
+
+
 def test_plan_rules_outside_the_table():
     """Shapes the table does not cover get a configuration from the rules."""
     names = set(qoq.gemm_configs())
@@ -302,7 +334,7 @@ def test_linear_plan_and_workspace():
     assert len(fused) >= 1
     assert qoq.linear_plan(1, 6144, 4096) in fused
     assert qoq.linear_plan(2, 512, 512) in fused
-    assert qoq.linear_plan(1, 59136, 8192) in fused
+    assert qoq.linear_plan(1, 59136, 8192) == qoq.gemm_tiled_plan(1, 59136, 8192)   # measured: the pair
     assert qoq.linear_workspace_bytes(1, 6144, 4096) == 0
     assert qoq.linear_plan(3, 6144, 4096) == qoq.gemm_tiled_plan(3, 6144, 4096)
     assert qoq.linear_plan(2, 131072, 8192) == qoq.gemm_tiled_plan(2, 131072, 8192)   # too much repeated work

@@ -1373,7 +1373,7 @@ const Config kConfigs[] = {
     // at every profiled point
     QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1)
     QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3)
-    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2)
+    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(3)
@@ -1387,7 +1387,7 @@ const Config kConfigs[] = {
     QOQ_SKINNY_R(1, 1, 16, 2, 3) QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
-    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
+    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3)
     QOQ_DMA2(2, 2) QOQ_SD(2)
 #endif
 };
@@ -1696,11 +1696,61 @@ struct XqConfig {
   {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, R>, "skinny_xq_nb" #NBW "_w" #W "_u" #U "_r" #R, \
    skinny_xq_red_bytes<NBW, W, U>()},
 
-// measured on MI355X (decode layers of the workloads, M = 1, 2): two strips and 8
-// waves per workgroup were fastest of the fused configurations timed
-const XqConfig kXqConfigs[] = {QOQ_XQ(2, 8, 2)};
+// The fused configurations the measured linear table uses (qoq_linear_table.inc);
+// the first is the one the rule below falls back to for shapes outside the table
+const XqConfig kXqConfigs[] = {
+    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1)
+#ifdef QOQ_ALL_CONFIGS
+    QOQ_XQ_R(2, 8, 1, 3) QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
+#endif
+};
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);
 std::once_flag g_xq_once[kNumXq];
+
+// The measured linear table: for the decode shapes of the workloads, whether one
+// fused kernel (and which) or the quantizer + GEMM pair was fastest at M tokens
+// (bench.py --profile-plan, real activations, weights rotated; "unfused" names the
+// pair).  A covered (N, K) takes the row with the nearest M up to the largest
+// profiled M, and the pair beyond it.
+struct LinearRow {
+  int64_t N, K, M;
+  const char *config;
+};
+const LinearRow kLinearRows[] = {
+#define QOQ_LINEAR_ROW(N, K, M, C) {N, K, M, C},
+#include "qoq_linear_table.inc"
+#undef QOQ_LINEAR_ROW
+    {0, 0, 0, nullptr}};   // end marker
+constexpr int kNumLinearRows = sizeof(kLinearRows) / sizeof(kLinearRows[0]) - 1;
+
+int xq_index(const char *name) {
+  for (int i = 0; i < kNumXq; ++i)
+    if (strcmp(kXqConfigs[i].name, name) == 0) return i;
+  return -1;
+}
+
+// covered: whether the table has rows for (N, K); the result: the row's fused
+// configuration, or nullptr for the pair (or past the largest profiled M)
+const XqConfig *linear_table_plan(int64_t M, int64_t N, int64_t K, bool &covered) {
+  covered = false;
+  int first = -1, last = -1;
+  for (int i = 0; i < kNumLinearRows; ++i)
+    if (kLinearRows[i].N == N && kLinearRows[i].K == K) {
+      if (first < 0) first = i;
+      last = i;
+    }
+  if (first < 0) return nullptr;
+  covered = true;
+  if (M > kLinearRows[last].M) return nullptr;
+  int best = first;
+  for (int i = first + 1; i <= last; ++i) {
+    // between rows a < b: M is nearer to a in ratio iff M * M < a * b
+    if (kLinearRows[i].M <= M || M * M >= kLinearRows[i - 1].M * kLinearRows[i].M) best = i;
+    else break;
+  }
+  const int idx = xq_index(kLinearRows[best].config);
+  return idx >= 0 ? &kXqConfigs[idx] : nullptr;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -1714,6 +1764,13 @@ const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
   const Overrides ov = current_overrides();
   if (ov.linear == -1) return nullptr;
   if (ov.linear >= 0) return xq_fits(&kXqConfigs[ov.linear], M, K) ? &kXqConfigs[ov.linear] : nullptr;
+  if (ov.config < 0 && ov.regime == 0) {
+    bool covered = false;
+    const XqConfig *t = linear_table_plan(M, N, K, covered);
+    if (covered) return t && xq_fits(t, M, K) ? t : nullptr;
+  }
+  // shapes outside the table: the first configuration up to two tokens, while the
+  // quantization every workgroup repeats stays bounded
   if (M > kXqMaxM) return nullptr;
   // fused only while the quantization every workgroup repeats (workgroups x M x K
   // elements) stays bounded

@@ -370,9 +370,11 @@ int qoq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, s
  * W4A8 GEMM with its fp16 epilogue — the same arithmetic, codes, scales and fp16
  * results as qoq_quantize_activations + qoq_w4a8_gemm ("QServe ..." summary: the
  * activation quantization is fused into the kernel that feeds the GEMM, so it costs
- * no pass of its own).  For one or two tokens (M <= 2, K <= 8192, see qoq_linear_plan)
- * one kernel does both: each workgroup quantizes the token rows into LDS and runs the
- * GEMM on them; up to 64 tokens the codes go through the tiled layout
+ * no pass of its own).  For a few tokens, where the library's measured table (or, for
+ * shapes it does not cover, M <= 2 and K <= 8192) says it is faster (see
+ * qoq_linear_plan), one kernel does both: each workgroup quantizes the token rows
+ * into LDS and runs the GEMM on them; otherwise up to 64 tokens the codes go through
+ * the tiled layout
  * (qoq_quantize_activations_tiled + qoq_w4a8_gemm_tiled); beyond, row-major.
  * x_fp16 [M,K] row-major fp16 (16-byte aligned); packed_w / group_meta / s_w_fp16 as
  * for qoq_w4a8_gemm; out_fp16 [M,N] (16-byte aligned); s_x_fp16: NULL, or [M] fp16

@@ -342,9 +342,9 @@ def test_linear_plan_and_workspace():
     assert qoq.linear_plan(17, 6144, 4096) == qoq.gemm_tiled_plan(17, 6144, 4096)
     assert qoq.linear_plan(64, 28672, 4096) == qoq.gemm_tiled_plan(64, 28672, 4096)
     assert qoq.linear_plan(65, 6144, 4096) == qoq.gemm_plan(65, 6144, 4096)
-    assert qoq.linear_plan(1, 4096, 14336) == qoq.gemm_tiled_plan(1, 4096, 14336)   # K beyond the fused limit
+    assert qoq.linear_plan(1, 4096, 20480) == qoq.gemm_tiled_plan(1, 4096, 20480)   # outside the table: K > 8192
     r256 = lambda v: (v + 255) // 256 * 256
-    for M, N, K in [(17, 6144, 4096), (1, 4096, 14336), (64, 28672, 4096)]:
+    for M, N, K in [(17, 6144, 4096), (1, 4096, 20480), (64, 28672, 4096)]:
         assert qoq.linear_workspace_bytes(M, N, K) == r256((M + 15) // 16 * 16 * K) + r256(2 * M)
     for M, N, K in [(65, 6144, 4096), (256, 4096, 14336)]:
         assert qoq.linear_workspace_bytes(M, N, K) == r256(M * K) + r256(2 * M) + qoq.gemm_workspace_bytes(M, N, K)

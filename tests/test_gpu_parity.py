@@ -521,9 +521,9 @@ def test_linear_matches_two_step_and_oracle(gpu, config):
     """Every linear configuration forced: fp16 output bit-equal to quantize +
     GEMM through the separate entry points, token scales equal to the
     quantizer's, and the fp16 output to the oracle; ragged N, K from one group to
-    the fused limit, M from 1 to 16, and two-kernel shapes (M > 16, K > 8192)."""
+    the fused limit, M from 1 to 16, long K (the fused kernel up to its LDS budget), and two-kernel shapes (M > 16)."""
     shapes = [(1, 16, 128), (3, 80, 1152), (8, 272, 4096), (16, 48, 8192), (16, 528, 640), (13, 6144, 4096),
-              (17, 80, 1152), (2, 32, 8320), (40, 272, 256)]
+              (17, 80, 1152), (2, 32, 8320), (40, 272, 256), (1, 48, 14336), (2, 80, 29568), (1, 16, 29568)]
     for (M, N, K) in shapes:
         say(f"linear config={config} M={M} N={N} K={K} plan={qoq.linear_plan(M, N, K)}")
         rng = np.random.default_rng(M * 31 + N + K)

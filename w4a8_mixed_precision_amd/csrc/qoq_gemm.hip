@@ -393,7 +393,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
 // LDS: 16 fp32 token scales and their reciprocals, then M code rows; the same space
 // holds the partial sums of the waves once the main loop is done.
 // ---------------------------------------------------------------------------
-constexpr int kXqMaxK = 8192;                   // LDS: 16 code rows of K + 16 bytes
+constexpr int kXqMaxK = 8192;                   // the rule's limit (16 code rows of K + 16 bytes)
+constexpr int kXqCodeBytes = 16 * (kXqMaxK + 16);   // LDS for the code rows: M * (K + 16) at most
 constexpr int kXqHead = 128;                    // LDS: 16 token scales and reciprocals
 constexpr int kXqPerThread = 8;                 // chunks per thread: M * K / 8 <= 8 * threads
 
@@ -1372,8 +1373,9 @@ const Config kConfigs[] = {
     // profiling sweep times 41, and keeps the fewest that are near-best (within 3 %)
     // at every profiled point
     QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1)
-    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3)
-    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32(1, 1, 8, 2, 2)
+    QOQ_SKINNY(2, 1, 8, 2)
+    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
+    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
     QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(3)
@@ -1381,13 +1383,13 @@ const Config kConfigs[] = {
     // the rest of the profiling sweep's candidates (build.py --all-configs): none is
     // needed for the table, so the product build leaves them out
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 1, 4, 4) QOQ_SKINNY(1, 2, 4, 4)
-    QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
+    QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
     QOQ_SKINNY(1, 4, 8, 2)
-    QOQ_SKINNY_R(1, 1, 16, 2, 3) QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
+    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
-    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3)
+    QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
     QOQ_DMA2(2, 2) QOQ_SD(2)
 #endif
 };
@@ -1760,7 +1762,7 @@ constexpr int64_t kXqMaxRepeat = 32 << 20;    // quantization costs more than a 
 bool xq_fits(const XqConfig *c, int64_t M, int64_t K) { return M * (K / 8) <= int64_t{kXqPerThread} * 64 * c->waves; }
 
 const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
-  if (M > 16 || K > kXqMaxK) return nullptr;      // the kernel's own limits (16 LDS code rows)
+  if (M > 16 || M * (K + 16) > kXqCodeBytes) return nullptr;      // the kernel's own limits (LDS code rows)
   const Overrides ov = current_overrides();
   if (ov.linear == -1) return nullptr;
   if (ov.linear >= 0) return xq_fits(&kXqConfigs[ov.linear], M, K) ? &kXqConfigs[ov.linear] : nullptr;
@@ -1769,9 +1771,9 @@ const XqConfig *xq_plan(int64_t M, int64_t N, int64_t K) {
     const XqConfig *t = linear_table_plan(M, N, K, covered);
     if (covered) return t && xq_fits(t, M, K) ? t : nullptr;
   }
-  // shapes outside the table: the first configuration up to two tokens, while the
-  // quantization every workgroup repeats stays bounded
-  if (M > kXqMaxM) return nullptr;
+  // shapes outside the table: the first configuration up to two tokens and K = 8192,
+  // while the quantization every workgroup repeats stays bounded
+  if (M > kXqMaxM || K > kXqMaxK) return nullptr;
   // fused only while the quantization every workgroup repeats (workgroups x M x K
   // elements) stays bounded
   const int64_t NS = N / 16;
@@ -1813,7 +1815,7 @@ void launch_w4a8_linear(const void *x, const void *packed, const void *meta, con
     const int lds = xq_lds_bytes(c, M, K);
     std::call_once(g_xq_once[idx], [c] {
       (void)hipFuncSetAttribute(reinterpret_cast<const void *>(c->k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kXqHead + 16 * (kXqMaxK + 16));
+                                kXqHead + kXqCodeBytes);
     });
     const int64_t NS = N / 16;
     hipLaunchKernelGGL(c->k, dim3(static_cast<unsigned>((NS + c->nbw - 1) / c->nbw)), dim3(64 * c->waves), lds, st,

@@ -1119,20 +1119,28 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
   const int8_t *bj = lds + AS * kSdStageA + Q * kSdBufB + (wave >> 2) * 4 * 4096 + 16 * lane;
   const int r = lane & 31, hi = lane >> 5;
   const int rbase = 64 * (wave & 3);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    v4i a[2], bf[4];
+  auto read_a = [&](int kb, v4i (&a)[2]) {
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm) {
       const int row = rbase + 32 * tm + r;
       a[tm] = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * kb + hi) ^ ((row >> 1) & 7)));
     }
+  };
+  v4i a[2][2], bf[4];
+  read_a(0, a[0]);
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096 + 1024 * kb);
+  for (int tn = 0; tn < 4; ++tn) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096);
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb + 1 < 4) read_a(kb + 1, a[(kb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32x32x32(a[tm], bf[tn], acc[tm][tn]);
+    for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm) acc[tm][tn] = mfma32x32x32(a[kb & 1][tm], bf[tn], acc[tm][tn]);
+      if (kb + 1 < 4) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096 + 1024 * (kb + 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 

@@ -1147,7 +1147,9 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
 // One group.  Waves w and w + 4 share a SIMD and meet at the same barriers, so
 // they run the step's two phases in opposite orders (MF = MFMAs first for waves
 // 4..7): while one dequantizes (vector ALU) the other issues MFMAs, and the two
-// units work side by side.
+// units work side by side.  A wave raises its issue priority for its MFMA phase, so
+// when both waves of the SIMD have an instruction ready the matrix unit is fed
+// first and the dequantization fills the gaps.
 template <int AS, int Q, bool MF, bool PC>
 __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, int wave, int lane,
                                         const int8_t *const (&asrc)[4], const SdCodes &deq, SdCodes &fill,
@@ -1160,7 +1162,9 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   sd_load_codes<PC>(fill, packed, meta, boff, moff, min(j + 3, G - 1));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MF) {
+    __builtin_amdgcn_s_setprio(1);
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // group j+1 is dequantized (codes loaded two groups ago) into B buffer (j+1) & 1,
@@ -1171,7 +1175,9 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   sd_copy_a<AS>(min(j + AS - 1, G - 1), lds, asrc, wave);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!MF) {
+    __builtin_amdgcn_s_setprio(1);
     sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // A(j+1) must be resident.  By the copy rule above the count may include only

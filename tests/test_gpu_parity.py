@@ -381,7 +381,7 @@ def test_split_k_exact(gpu, config, splits):
         check_fp16(out, r["acc"], r["s_x"], r["s_w"])
 
 
-SPLIT_REUSE_CONFIG = "dma2_tm4_tn1"
+SPLIT_REUSE_CONFIG = "dma2_tm4_tn2"
 
 
 def test_split_k_workspace_reuse(gpu):

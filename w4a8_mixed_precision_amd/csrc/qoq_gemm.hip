@@ -1386,25 +1386,24 @@ const Config kConfigs[] = {
     // the configurations the measured dispatch table uses (qoq_plan_table.inc): the
     // profiling sweep times 41, and keeps the fewest that are near-best (within 3 %)
     // at every profiled point
-    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(4, 4, 8, 1)
-    QOQ_SKINNY(2, 1, 8, 2)
+    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(1, 4, 8, 2)
     QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
     QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
-    QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
+    QOQ_DMA2(2, 1) QOQ_DMA2(4, 2)
     QOQ_SD(3)
 #ifdef QOQ_ALL_CONFIGS
     // the rest of the profiling sweep's candidates (build.py --all-configs): none is
     // needed for the table, so the product build leaves them out
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 1, 4, 4) QOQ_SKINNY(1, 2, 4, 4)
-    QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2)
+    QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
-    QOQ_SKINNY(1, 4, 8, 2)
+    QOQ_SKINNY(4, 4, 8, 1)
     QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
     QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
-    QOQ_DMA2(2, 2) QOQ_SD(2)
+    QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_SD(2)
 #endif
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
@@ -1573,7 +1572,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
       } else if (t256 >= 96) {
         cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, split K
       } else {
-        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128, split K
+        cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, split K
       }
     }
   }
@@ -1715,9 +1714,9 @@ struct XqConfig {
 // The fused configurations the measured linear table uses (qoq_linear_table.inc);
 // the first is the one the rule below falls back to for shapes outside the table
 const XqConfig kXqConfigs[] = {
-    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1)
+    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1) QOQ_XQ_R(2, 8, 1, 3)
 #ifdef QOQ_ALL_CONFIGS
-    QOQ_XQ_R(2, 8, 1, 3) QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
+    QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
 #endif
 };
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);

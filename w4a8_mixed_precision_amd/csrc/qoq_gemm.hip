@@ -64,6 +64,22 @@ __device__ __forceinline__ unsigned meta_pair(const uint16_t *__restrict__ meta,
 
 __device__ __forceinline__ unsigned meta_of(unsigned pair, int col) { return pair >> (16 * (col & 1)); }
 
+// A packed-code load.  NT (streaming): the load carries the non-temporal hint, so
+// the caches keep these lines only briefly.  Few tokens read every weight once, and
+// on the long weight streams this raises the rate HBM delivers them at (Qwen-72B
+// gate+up, 248 MB: 5.4 -> 5.8 TB/s measured); on short streams the hint costs a
+// little latency, so both forms are configurations and the measured table chooses.
+template <bool NT>
+__device__ __forceinline__ uint4 load_codes(const uint4 *__restrict__ p) {
+  if constexpr (NT) {
+    typedef unsigned u4v_nt __attribute__((ext_vector_type(4)));
+    const u4v_nt v = __builtin_nontemporal_load(reinterpret_cast<const u4v_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
 template <int MT, int NBW, int U>
 struct SkinnyBatch {
   uint4 p[U][NBW];
@@ -74,7 +90,7 @@ struct SkinnyBatch {
 
 // Issues every load of batch b (groups t = b*U .. b*U+U-1 of this wave).  Only
 // scalars come in, so no pointer array can end up in private (scratch) memory.
-template <int MT, int NBW, int WAVES, int U, bool PC, bool AT>
+template <int MT, int NBW, int WAVES, int U, bool PC, bool AT, bool NT>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, int ngroups, int wave,
                                             const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                             const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
@@ -94,7 +110,7 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NBW, U> &B, int b, i
     for (int nb = 0; nb < NBW; ++nb) {
       // strips past the end repeat the last one; their results are dropped at the store
       const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
-      B.p[u][nb] = packed[chunk * 64 + lane];
+      B.p[u][nb] = load_codes<NT>(packed + chunk * 64 + lane);
       B.md[u][nb] = PC ? 0u : meta_pair(meta, chunk, col);
     }
 #pragma unroll
@@ -127,7 +143,7 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<MT, NBW, U> &B,
     }
 }
 
-template <int MT, int NBW, int WAVES, int U, int R, int OUT, bool PC, bool AT = false>
+template <int MT, int NBW, int WAVES, int U, int R, int OUT, bool PC, bool AT = false, bool NT = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
   for (int r = 0; r < R - 1; ++r)
     if (r < nbatch)
-      skinny_load<MT, NBW, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0,
+      skinny_load<MT, NBW, WAVES, U, PC, AT, NT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M, m0,
                                              lane);
   for (int b0 = 0; b0 < nbatch; b0 += R) {
 #pragma unroll
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       const int b = b0 + r;
       if (b >= nbatch) break;
       if (b + R - 1 < nbatch)
-        skinny_load<MT, NBW, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
+        skinny_load<MT, NBW, WAVES, U, PC, AT, NT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
                                                strip0, NS, G, K, M, m0, lane);
       skinny_compute<MT, NBW, U, PC>(ring[r], acc, col);
     }
@@ -237,7 +253,7 @@ struct Skinny32Batch {
   v4i a[U][MT2][4];
 };
 
-template <int MT2, int NP, int WAVES, int U, bool PC, bool AT>
+template <int MT2, int NP, int WAVES, int U, bool PC, bool AT, bool NT>
 __device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int b, int ngroups, int wave,
                                               const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                               const int8_t *__restrict__ qx, int strip0, int NS, int G, int K,
@@ -253,8 +269,8 @@ __device__ __forceinline__ void skinny32_load(Skinny32Batch<MT2, NP, U> &B, int 
 #pragma unroll
     for (int np = 0; np < NP; ++np) {
       const size_t chunk = static_cast<size_t>(min(strip0 + 2 * np + (c32 >> 4), NS - 1)) * G + j;
-      B.p0[u][np] = packed[chunk * 64 + 16 * hi + col];
-      B.p1[u][np] = packed[chunk * 64 + 16 * hi + 32 + col];
+      B.p0[u][np] = load_codes<NT>(packed + chunk * 64 + 16 * hi + col);
+      B.p1[u][np] = load_codes<NT>(packed + chunk * 64 + 16 * hi + 32 + col);
       B.md[u][np] = PC ? 0u : meta_pair(meta, chunk, col);
     }
 #pragma unroll
@@ -290,7 +306,7 @@ __device__ __forceinline__ void skinny32_compute(const Skinny32Batch<MT2, NP, U>
     }
 }
 
-template <int MT2, int NP, int WAVES, int U, int R, int OUT, bool PC, bool AT = false>
+template <int MT2, int NP, int WAVES, int U, int R, int OUT, bool PC, bool AT = false, bool NT = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
     const int8_t *__restrict__ qx, const __half *__restrict__ sx, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, const uint8_t *__restrict__ zp,
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
 #pragma unroll
   for (int r = 0; r < R - 1; ++r)
     if (r < nbatch)
-      skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M,
+      skinny32_load<MT2, NP, WAVES, U, PC, AT, NT>(ring[r], r, ngroups, wave, packed, meta, qx, strip0, NS, G, K, M,
                                                m0, lane);
   for (int b0 = 0; b0 < nbatch; b0 += R) {
 #pragma unroll
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny32_kernel(
       const int b = b0 + r;
       if (b >= nbatch) break;
       if (b + R - 1 < nbatch)
-        skinny32_load<MT2, NP, WAVES, U, PC, AT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
+        skinny32_load<MT2, NP, WAVES, U, PC, AT, NT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, qx,
                                                  strip0, NS, G, K, M, m0, lane);
       skinny32_compute<MT2, NP, U, PC>(ring[r], acc, col);
     }
@@ -1363,12 +1379,20 @@ struct Config {
   int lds = 0;              // dynamic LDS bytes
   // few-token kernels on tiled activation codes: [per-group, per-channel][fp16, INT32]
   GemmKernel kt[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+  int nt = 0;               // few-token kernels: packed codes loaded with the streaming hint
 };
 
 #define QOQ_K4(...) {{__VA_ARGS__, 0, false>, __VA_ARGS__, 1, false>}, {__VA_ARGS__, 0, true>, __VA_ARGS__, 1, true>}}
 // skinny names carry the ring depth only when it is not 2
 #define QOQ_KT(...) \
   {{__VA_ARGS__, 0, false, true>, __VA_ARGS__, 1, false, true>}, {__VA_ARGS__, 0, true, true>, __VA_ARGS__, 1, true, true>}}
+// the same with streaming code loads (names end in "_nt")
+#define QOQ_K4NT(...)                                                                         \
+  {{__VA_ARGS__, 0, false, false, true>, __VA_ARGS__, 1, false, false, true>},                 \
+   {__VA_ARGS__, 0, true, false, true>, __VA_ARGS__, 1, true, false, true>}}
+#define QOQ_KTNT(...)                                                                         \
+  {{__VA_ARGS__, 0, false, true, true>, __VA_ARGS__, 1, false, true, true>},                   \
+   {__VA_ARGS__, 0, true, true, true>, __VA_ARGS__, 1, true, true, true>}}
 #define QOQ_SKINNY(MT, NBW, W, U)                                                                      \
   {0, MT, NBW, W, U, 2, QOQ_K4(gemm_skinny_kernel<MT, NBW, W, U, 2), "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U, \
    0, QOQ_KT(gemm_skinny_kernel<MT, NBW, W, U, 2)},
@@ -1378,19 +1402,30 @@ struct Config {
 #define QOQ_SKINNY32(MT2, NP, W, U, R)                                                                  \
   {7, MT2, NP, W, U, R, QOQ_K4(gemm_skinny32_kernel<MT2, NP, W, U, R),                                   \
    "skinny32_mt" #MT2 "_np" #NP "_w" #W "_u" #U "_r" #R, 0, QOQ_KT(gemm_skinny32_kernel<MT2, NP, W, U, R)},
+#define QOQ_SKINNY_NT(MT, NBW, W, U)                                                                  \
+  {0, MT, NBW, W, U, 2, QOQ_K4NT(gemm_skinny_kernel<MT, NBW, W, U, 2),                                  \
+   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U "_nt", 0, QOQ_KTNT(gemm_skinny_kernel<MT, NBW, W, U, 2), 1},
+#define QOQ_SKINNY_RNT(MT, NBW, W, U, R)                                                              \
+  {0, MT, NBW, W, U, R, QOQ_K4NT(gemm_skinny_kernel<MT, NBW, W, U, R),                                  \
+   "skinny_mt" #MT "_nb" #NBW "_w" #W "_u" #U "_r" #R "_nt", 0, QOQ_KTNT(gemm_skinny_kernel<MT, NBW, W, U, R), 1},
+#define QOQ_SKINNY32_NT(MT2, NP, W, U, R)                                                             \
+  {7, MT2, NP, W, U, R, QOQ_K4NT(gemm_skinny32_kernel<MT2, NP, W, U, R),                               \
+   "skinny32_mt" #MT2 "_np" #NP "_w" #W "_u" #U "_r" #R "_nt", 0,                                     \
+   QOQ_KTNT(gemm_skinny32_kernel<MT2, NP, W, U, R), 1},
 #define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
 #define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
 #define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
 
 const Config kConfigs[] = {
     // the configurations the measured dispatch table uses (qoq_plan_table.inc): the
-    // profiling sweep times 41, and keeps the fewest that are near-best (within 3 %)
+    // profiling sweep times 56, and keeps the fewest that are near-best (within 3 %)
     // at every profiled point
-    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(1, 4, 8, 2)
-    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
-    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2)
+    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY_NT(1, 1, 8, 2) QOQ_SKINNY_R(1, 1, 8, 2, 3)
+    QOQ_SKINNY_NT(1, 2, 16, 2) QOQ_SKINNY_NT(1, 4, 8, 2) QOQ_SKINNY_NT(4, 2, 8, 1)
+    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_RNT(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_RNT(2, 2, 8, 1, 3)
+    QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32_NT(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32_NT(2, 2, 8, 1, 2)
     QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
-    QOQ_DMA2(2, 1) QOQ_DMA2(4, 2)
+    QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
     QOQ_SD(3)
 #ifdef QOQ_ALL_CONFIGS
     // the rest of the profiling sweep's candidates (build.py --all-configs): none is
@@ -1398,21 +1433,23 @@ const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 1, 4, 4) QOQ_SKINNY(1, 2, 4, 4)
     QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
-    QOQ_SKINNY(4, 4, 8, 1)
+    QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(1, 4, 8, 2)
     QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
-    QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
+    QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
     QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
-    QOQ_DMA2(2, 2) QOQ_DMA2(4, 1) QOQ_SD(2)
+    QOQ_DMA2(2, 2) QOQ_SD(2)
+    QOQ_SKINNY_NT(3, 2, 8, 2) QOQ_SKINNY_NT(2, 2, 8, 2) QOQ_SKINNY_NT(4, 4, 8, 1) QOQ_SKINNY_NT(2, 1, 8, 2)
+    QOQ_SKINNY_RNT(1, 1, 16, 2, 3) QOQ_SKINNY_RNT(4, 2, 8, 1, 3) QOQ_SKINNY32_NT(2, 1, 8, 1, 2)
 #endif
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-const Config *find_config(int kind, int a, int b, int c, int d, int e = 0) {
+const Config *find_config(int kind, int a, int b, int c, int d, int e = 0, bool nt = false) {
   if (kind == 0 && e == 0) e = 2;
   for (int i = 0; i < kNumConfigs; ++i) {
     const Config &cf = kConfigs[i];
-    if (cf.kind == kind && cf.a == a && cf.b == b && cf.c == c && cf.d == d && cf.e == e)
+    if (cf.kind == kind && cf.a == a && cf.b == b && cf.c == c && cf.d == d && cf.e == e && (cf.nt != 0) == nt)
       return &cf;
   }
   return nullptr;
@@ -1542,15 +1579,19 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     if (tiled_a) tiled = false;
     if (!tiled) {
       // shapes outside the measured table (rules distilled from the same sweeps):
+      //  streaming code loads once the weights pass 8 MiB
       //  M <= 16: one 16-row block; wide layers with short K stream one strip per
       //           workgroup with 8 K-split waves, the rest two strips and 16 waves
+      //           (small weights: one strip, 8 waves)
       //  17..64 tokens: 32-row blocks on the 32x32x32 MFMA (about 60 % more INT8 ops
       //           per cycle than 16x16x64), two strip pairs per workgroup, one 32-row
       //           block up to 32 tokens and two beyond
+      const bool nt = static_cast<int64_t>(N) * K / 2 >= (8 << 20);
       if (M <= 16) {
-        cfg = (NS >= 640 && G <= 64) ? find_config(0, 1, 1, 8, 2) : find_config(0, 1, 2, 16, 2);
+        if (!nt) cfg = find_config(0, 1, 1, 8, 2);
+        else cfg = (NS >= 640 && G <= 64) ? find_config(0, 1, 1, 8, 2, 2, true) : find_config(0, 1, 2, 16, 2, 2, true);
       } else {
-        cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2);
+        cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2, nt);
       }
     } else {
       // measured on MI355X over the layer shapes of the workloads: the largest tile
@@ -1714,9 +1755,9 @@ struct XqConfig {
 // The fused configurations the measured linear table uses (qoq_linear_table.inc);
 // the first is the one the rule below falls back to for shapes outside the table
 const XqConfig kXqConfigs[] = {
-    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1) QOQ_XQ_R(2, 8, 1, 3)
+    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1)
 #ifdef QOQ_ALL_CONFIGS
-    QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
+    QOQ_XQ_R(2, 8, 1, 3) QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
 #endif
 };
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);

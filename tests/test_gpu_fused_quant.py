@@ -60,7 +60,11 @@ SHAPES = [(1, 64), (1, 4096), (3, 136), (5, 640), (16, 4096), (17, 1152), (33, 8
           (1, 29568), (1, 32768), (70, 1024), (300, 512)]
 
 
-@pytest.mark.parametrize("M,K", SHAPES)
+# many short rows (prompt tokens)
+RMS_SHAPES = SHAPES + [(1027, 136), (1500, 4096)]
+
+
+@pytest.mark.parametrize("M,K", RMS_SHAPES)
 @pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("rowsum", [False, True])
 def test_rmsnorm_quantize_exact(gpu, M, K, tiled, rowsum):
@@ -107,7 +111,7 @@ def test_silu_extreme_gates(gpu):
 
 
 @pytest.mark.parametrize("name,M", [("llama3_8b_qkv", 64), ("qwen72b_qkv", 1), ("llama3_8b_down", 64),
-                                    ("llama3_8b_down_prefill", 2048)])
+                                    ("llama3_8b_down_prefill", 2048), ("llama3_8b_gate_up_prefill", 4096)])
 def test_fused_layer_rows_sampled(gpu, name, M):
     """Layer sizes: RMSNorm on the QKV / gate+up input (K = hidden), SiLU * up on
     the down projection's input (K = intermediate); sampled rows vs the oracle."""
@@ -115,7 +119,7 @@ def test_fused_layer_rows_sampled(gpu, name, M):
     say(f"fused producers {name} M={M} K={L.K}")
     x = wl.activations_fp16(L, M)
     rows = np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, min(M, 6))])
-    if name.endswith("qkv"):
+    if name.endswith("qkv") or "gate_up" in name:      # RMSNorm output feeds QKV and gate+up
         gamma = (1.0 + 0.1 * np.random.default_rng(1).standard_normal(L.K)).astype(np.float16)
         q, s, t = qoq.rmsnorm_quantize(to_dev(x, gpu), to_dev(gamma, gpu), EPS, rowsum=True)
         wq, ws, wt = fq.rmsnorm_quantize(x[rows], gamma, EPS)

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kFThreads) void rmsnorm_quant_kernel(const __half *
 // ---------------------------------------------------------------------------
 // SiLU(gate) * up + quantization.  gate and up rows have stride ld (elements).
 // h = fp16 of the exact gate * up / (1 + exp(-gate)).  Each value is first formed
-// in fp32, h32 = (gate * up) * rcp(1 + expf(-gate)): gate * up is exact (two 11-bit
+// in fp32, h32 = (gate * up) * rcp(1 + e^(-gate)): gate * up is exact (two 11-bit
 // significands) and the rest costs a few ulps, well under 2^-20 relative.  If
 // h32 - e and h32 + e (e = 2^-20 |h32|) round to the same fp16, so does the exact
 // value (rounding is monotone).  Otherwise the two fp16 candidates are adjacent
@@ -198,8 +198,26 @@ __global__ __launch_bounds__(kFThreads) void rmsnorm_quant_kernel(const __half *
 // midpoint), in a branch the wave takes only when one of its lanes needs it.  The
 // fp16 value is therefore RN16 of the fp64 expression, like the oracle's.
 // ---------------------------------------------------------------------------
+// e^(-g) for an fp16 value g, as 2^t with t = -g log2(e) split into n + f (n the
+// nearest integer, |f| <= 1/2), so the hardware base-2 exponential sees only a small
+// argument: -g * kLog2eHi is exact (kLog2eHi = 2955 / 2048 has 12 significant bits,
+// g at most 11), the rest of log2(e) enters through one fma, and 2^n is an exact
+// scaling.  Relative error about 2^-22.5 (the hardware 2^f and two roundings), well
+// inside the 2^-20 the exact-rounding test below allows for.  |t| stays below 2^17
+// for finite fp16 g; beyond the fp32 range the scaling gives 0 or infinity, as e^(-g)
+// rounds there.
+constexpr float kLog2eHi = 1.44287109375f;
+constexpr float kLog2eLo = static_cast<float>(1.4426950408889634 - 1.44287109375);
+
+__device__ __forceinline__ float exp_neg(float g) {
+  const float th = -g * kLog2eHi;
+  const float n = __builtin_rintf(th);
+  const float f = __builtin_fmaf(-g, kLog2eLo, th - n);
+  return __builtin_ldexpf(__builtin_amdgcn_exp2f(f), static_cast<int>(n));
+}
+
 __device__ __forceinline__ float silu_mul_fast(float gf, float uf) {
-  return (gf * uf) * __builtin_amdgcn_rcpf(1.0f + expf(-gf));
+  return (gf * uf) * __builtin_amdgcn_rcpf(1.0f + exp_neg(gf));
 }
 
 // fp16 bits of RN16(h) for h within e of h32, or 0xffffffff when undecided

@@ -1069,12 +1069,15 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
 //   A(j+AS-1); MFMAs of j from A stage j % AS and B buffer j & 1; wait for A(j+1);
 //   barrier (which also publishes B(j+1)).
 // ---------------------------------------------------------------------------
-constexpr int kSdStageA = 256 * 128;             // A bytes per stage
+template <int TM>
+constexpr int sd_stage_a() {                     // A bytes per stage (128 * TM rows)
+  return 128 * TM * 128;
+}
 constexpr int kSdBufB = 8 * 4 * 1024;            // dequantized B bytes per group
 
-template <int AS>
+template <int AS, int TM>
 constexpr int sd_lds_bytes() {
-  return AS * kSdStageA + 2 * kSdBufB;
+  return AS * sd_stage_a<TM>() + 2 * kSdBufB;
 }
 
 struct SdCodes {
@@ -1109,13 +1112,13 @@ __device__ __forceinline__ void copy16_hidden(const void *g, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-template <int AS>
-__device__ __forceinline__ void sd_copy_a(int j, int8_t *__restrict__ lds, const int8_t *const (&asrc)[4],
+template <int AS, int TM>
+__device__ __forceinline__ void sd_copy_a(int j, int8_t *__restrict__ lds, const int8_t *const (&asrc)[2 * TM],
                                           int wave) {
   const uint32_t st = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)lds)) +
-                      static_cast<uint32_t>((j % AS) * kSdStageA);
+                      static_cast<uint32_t>((j % AS) * sd_stage_a<TM>());
 #pragma unroll
-  for (int i = 0; i < 4; ++i) copy16_hidden(asrc[i] + 128 * j, st + 1024 * (wave * 4 + i));
+  for (int i = 0; i < 2 * TM; ++i) copy16_hidden(asrc[i] + 128 * j, st + 1024 * (wave * 2 * TM + i));
 }
 
 template <int Q, bool PC>
@@ -1128,21 +1131,21 @@ __device__ __forceinline__ void sd_dequant(int8_t *__restrict__ bbuf, int wave, 
   for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
 }
 
-template <int AS, int Q>
+template <int AS, int Q, int TM>
 __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, int wave, int lane,
-                                        v16i (&acc)[2][4]) {
-  const int8_t *stage = lds + (j % AS) * kSdStageA;
-  const int8_t *bj = lds + AS * kSdStageA + Q * kSdBufB + (wave >> 2) * 4 * 4096 + 16 * lane;
+                                        v16i (&acc)[TM][4]) {
+  const int8_t *stage = lds + (j % AS) * sd_stage_a<TM>();
+  const int8_t *bj = lds + AS * sd_stage_a<TM>() + Q * kSdBufB + (wave >> 2) * 4 * 4096 + 16 * lane;
   const int r = lane & 31, hi = lane >> 5;
-  const int rbase = 64 * (wave & 3);
-  auto read_a = [&](int kb, v4i (&a)[2]) {
+  const int rbase = 32 * TM * (wave & 3);
+  auto read_a = [&](int kb, v4i (&a)[TM]) {
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
+    for (int tm = 0; tm < TM; ++tm) {
       const int row = rbase + 32 * tm + r;
       a[tm] = *reinterpret_cast<const v4i *>(stage + row * 128 + 16 * ((2 * kb + hi) ^ ((row >> 1) & 7)));
     }
   };
-  v4i a[2][2], bf[4];
+  v4i a[2][TM], bf[4];
   read_a(0, a[0]);
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096);
@@ -1153,7 +1156,7 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm) acc[tm][tn] = mfma32x32x32(a[kb & 1][tm], bf[tn], acc[tm][tn]);
+      for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = mfma32x32x32(a[kb & 1][tm], bf[tn], acc[tm][tn]);
       if (kb + 1 < 4) bf[tn] = *reinterpret_cast<const v4i *>(bj + tn * 4096 + 1024 * (kb + 1));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1166,12 +1169,12 @@ __device__ __forceinline__ void sd_mfma(int j, const int8_t *__restrict__ lds, i
 // units work side by side.  A wave raises its issue priority for its MFMA phase, so
 // when both waves of the SIMD have an instruction ready the matrix unit is fed
 // first and the dequantization fills the gaps.
-template <int AS, int Q, bool MF, bool PC>
+template <int AS, int Q, bool MF, bool PC, int TM>
 __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, int wave, int lane,
-                                        const int8_t *const (&asrc)[4], const SdCodes &deq, SdCodes &fill,
+                                        const int8_t *const (&asrc)[2 * TM], const SdCodes &deq, SdCodes &fill,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
-                                        unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
-  int8_t *bbuf = lds + AS * kSdStageA;
+                                        unsigned boff, unsigned moff, v16i (&acc)[TM][4]) {
+  int8_t *bbuf = lds + AS * sd_stage_a<TM>();
   // group j+3's codes go out first, into the set that held group j (dequantized a
   // group ago): the copy wait at the bottom cannot leave register loads issued after
   // the copies in flight, so codes loaded there would be waited for at once
@@ -1179,7 +1182,7 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MF) {
     __builtin_amdgcn_s_setprio(1);
-    sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    sd_mfma<AS, Q, TM>(j, lds, wave, lane, acc);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1188,46 +1191,46 @@ __device__ __forceinline__ void sd_step(int j, int G, int8_t *__restrict__ lds, 
   // A copies are issued (its stage held group j-1)
   sd_dequant<Q, PC>(bbuf, wave, lane, deq);
   __builtin_amdgcn_sched_barrier(0);
-  sd_copy_a<AS>(min(j + AS - 1, G - 1), lds, asrc, wave);
+  sd_copy_a<AS, TM>(min(j + AS - 1, G - 1), lds, asrc, wave);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!MF) {
     __builtin_amdgcn_s_setprio(1);
-    sd_mfma<AS, Q>(j, lds, wave, lane, acc);
+    sd_mfma<AS, Q, TM>(j, lds, wave, lane, acc);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
   // A(j+1) must be resident.  By the copy rule above the count may include only
-  // the copies issued after A(j+1)'s: AS == 3, this step's 4 copies of A(j+2);
+  // the copies issued after A(j+1)'s: AS == 3, this step's 2 * TM copies of A(j+2);
   // AS == 2, none (A(j+1) is this step's copy).
-  QOQ_WAIT_VMCNT(AS == 3 ? 4 : 0);
+  QOQ_WAIT_VMCNT(AS == 3 ? 2 * TM : 0);
   QOQ_WAIT_LGKMCNT0();                          // this wave's B(j+1) fragments are in LDS
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // code set g % 3 holds group g: the loop is unrolled by six (B buffer j & 1, sets j % 3)
-template <int AS, bool MF, bool PC>
+template <int AS, bool MF, bool PC, int TM>
 __device__ __forceinline__ void sd_loop(int G, int8_t *__restrict__ lds, int wave, int lane,
-                                        const int8_t *const (&asrc)[4], SdCodes &s0, SdCodes &s1, SdCodes &s2,
+                                        const int8_t *const (&asrc)[2 * TM], SdCodes &s0, SdCodes &s1, SdCodes &s2,
                                         const uint4 *__restrict__ packed, const uint16_t *__restrict__ meta,
-                                        unsigned boff, unsigned moff, v16i (&acc)[2][4]) {
+                                        unsigned boff, unsigned moff, v16i (&acc)[TM][4]) {
   int j = 0;
   for (; j + 5 < G; j += 6) {
-    sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
-    sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
-    sd_step<AS, 0, MF, PC>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
-    sd_step<AS, 1, MF, PC>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
-    sd_step<AS, 0, MF, PC>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
-    sd_step<AS, 1, MF, PC>(j + 5, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC, TM>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC, TM>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC, TM>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC, TM>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+    sd_step<AS, 0, MF, PC, TM>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+    sd_step<AS, 1, MF, PC, TM>(j + 5, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
   }
-  if (j < G) sd_step<AS, 0, MF, PC>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
-  if (j + 1 < G) sd_step<AS, 1, MF, PC>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
-  if (j + 2 < G) sd_step<AS, 0, MF, PC>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
-  if (j + 3 < G) sd_step<AS, 1, MF, PC>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
-  if (j + 4 < G) sd_step<AS, 0, MF, PC>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+  if (j < G) sd_step<AS, 0, MF, PC, TM>(j, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+  if (j + 1 < G) sd_step<AS, 1, MF, PC, TM>(j + 1, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
+  if (j + 2 < G) sd_step<AS, 0, MF, PC, TM>(j + 2, G, lds, wave, lane, asrc, s0, s2, packed, meta, boff, moff, acc);
+  if (j + 3 < G) sd_step<AS, 1, MF, PC, TM>(j + 3, G, lds, wave, lane, asrc, s1, s0, packed, meta, boff, moff, acc);
+  if (j + 4 < G) sd_step<AS, 0, MF, PC, TM>(j + 4, G, lds, wave, lane, asrc, s2, s1, packed, meta, boff, moff, acc);
 }
 
-template <int AS, int OUT, bool PC>
+template <int AS, int TM, int OUT, bool PC>
 __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restrict__ qx,
                                                         const __half *__restrict__ sx,
                                                         const uint4 *__restrict__ packed,
@@ -1236,6 +1239,8 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
     const int *__restrict__ trow, void *__restrict__ out,
                                                         int M, int N, int K, int splits, int *__restrict__ ws) {
   static_assert(AS == 2 || AS == 3, "two or three A stages");
+  static_assert(TM == 1 || TM == 2, "tiles of 128 or 256 rows");
+  constexpr int BM = 128 * TM;                  // tile rows
   extern __shared__ __attribute__((aligned(1024))) int8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1244,18 +1249,18 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
   const int Gs = K >> 7;
   const int NS = N >> 4;
   const int nx = (NS + 15) / 16;
-  const int ny = (M + 255) / 256;
+  const int ny = (M + BM - 1) / BM;
   int tx, ty, split;
   split_coords(blockIdx.x, nx, ny, splits, tx, ty, split);
   const int g0 = split * Gs / splits;
   const int G = (split + 1) * Gs / splits - g0;   // groups of this split (>= 1)
-  const int m0 = ty * 256;
+  const int m0 = ty * BM;
 
-  // A copies: wave w moves rows 8*(4w + i) .. +7 of the 256-row stage
-  const int8_t *asrc[4];
+  // A copies: wave w moves rows 8*(2*TM*w + i) .. +7 of the stage
+  const int8_t *asrc[2 * TM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (wave * 4 + i) + (lane >> 3);
+  for (int i = 0; i < 2 * TM; ++i) {
+    const int row = 8 * (wave * 2 * TM + i) + (lane >> 3);
     asrc[i] = qx + static_cast<size_t>(min(m0 + row, M - 1)) * K + 128 * g0 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
   }
   // codes of column block `wave`: strip 16*tx + 2*wave + (c32 >> 4), slots 16*hi + c
@@ -1264,15 +1269,15 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
   const unsigned boff = (strip * static_cast<unsigned>(Gs) + g0) * 64u + 16u * hi + (lane & 15);
   const unsigned moff = (strip * static_cast<unsigned>(Gs) + g0) * 16u + (lane & 15);
 
-  v16i acc[2][4];
+  v16i acc[TM][4];
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = v16i{};
 
   // prologue: A(0) .. A(AS-2); codes 0, 1, 2 into sets 0, 1, 2; dequantize group 0
   // into B buffer 0
-  for (int g = 0; g < AS - 1; ++g) sd_copy_a<AS>(min(g, G - 1), lds, asrc, wave);
+  for (int g = 0; g < AS - 1; ++g) sd_copy_a<AS, TM>(min(g, G - 1), lds, asrc, wave);
   SdCodes set0, set1, set2;
   sd_load_codes<PC>(set0, packed, meta, boff, moff, 0);
   sd_load_codes<PC>(set1, packed, meta, boff, moff, min(1, G - 1));
@@ -1281,7 +1286,7 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
     v4i b[4];
     weights_lane<PC>(set0.p0, set0.md, b[0], b[2]);
     weights_lane<PC>(set0.p1, set0.md, b[1], b[3]);
-    int8_t *dst = lds + AS * kSdStageA + wave * 4096 + 16 * lane;
+    int8_t *dst = lds + AS * sd_stage_a<TM>() + wave * 4096 + 16 * lane;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<v4i *>(dst + 1024 * kb) = b[kb];
   }
@@ -1289,20 +1294,20 @@ __global__ __launch_bounds__(512, 1) void gemm_sd_kernel(const int8_t *__restric
   __syncthreads();
 
   if (wave < 4)
-    sd_loop<AS, false, PC>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
+    sd_loop<AS, false, PC, TM>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
   else
-    sd_loop<AS, true, PC>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
+    sd_loop<AS, true, PC, TM>(G, lds, wave, lane, asrc, set0, set1, set2, packed, meta, boff, moff, acc);
   QOQ_WAIT_VMCNT(0);                            // no copy outlives the kernel
   __syncthreads();
-  const int wm0 = m0 + 64 * (wave & 3);
+  const int wm0 = m0 + 32 * TM * (wave & 3);
   const int wn0 = 16 * (16 * tx + 8 * (wave >> 2));   // first column of this wave
   if (splits > 1) {                             // partial sums of this split -> workspace slice
-    epilogue32<2, 4, 1>(acc, nullptr, lane, wm0, wn0, M, N, nullptr, nullptr,
+    epilogue32<TM, 4, 1>(acc, nullptr, lane, wm0, wn0, M, N, nullptr, nullptr,
                         ws + static_cast<size_t>(split) * M * N);
     return;
   }
-  static_assert(8 * 32 * (64 * 4 + 16) <= sd_lds_bytes<AS>(), "epilogue scratch exceeds the LDS in use");
-  epilogue32<2, 4, OUT, PC>(acc, lds + wave * 32 * (64 * 4 + 16), lane, wm0, wn0, M, N, sx, sw, out, zp, trow);
+  static_assert(8 * 32 * (64 * 4 + 16) <= sd_lds_bytes<AS, TM>(), "epilogue scratch exceeds the LDS in use");
+  epilogue32<TM, 4, OUT, PC>(acc, lds + wave * 32 * (64 * 4 + 16), lane, wm0, wn0, M, N, sx, sw, out, zp, trow);
 }
 
 // ---------------------------------------------------------------------------
@@ -1373,7 +1378,7 @@ typedef void (*GemmKernel)(const int8_t *, const __half *, const uint4 *, const 
 struct Config {
   int kind;                 // 0 skinny, 7 skinny on 32x32 blocks, 4 wide2, 5 dma2, 6 shared dequantization
   int a, b, c, d, e;        // skinny: MT, NBW, WAVES, U, R   skinny32: MT2, NP, WAVES, U, R
-                            // wide2 / dma2: TM, TN   sd: A stages
+                            // wide2 / dma2: TM, TN   sd: A stages, 1 for 128-row tiles
   GemmKernel k[2][2];       // [per-group, per-channel][fp16 epilogue, INT32 epilogue]
   const char *name;
   int lds = 0;              // dynamic LDS bytes
@@ -1414,31 +1419,35 @@ struct Config {
    QOQ_KTNT(gemm_skinny32_kernel<MT2, NP, W, U, R), 1},
 #define QOQ_WIDE2(TM, TN) {4, TM, TN, 0, 0, 0, QOQ_K4(gemm_wide2_kernel<TM, TN), "wide2_tm" #TM "_tn" #TN},
 #define QOQ_DMA2(TM, TN) {5, TM, TN, 0, 0, 0, QOQ_K4(gemm_dma2_kernel<TM, TN), "dma2_tm" #TM "_tn" #TN},
-#define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS), "sd_as" #AS, sd_lds_bytes<AS>()},
+#define QOQ_SD(AS) {6, AS, 0, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS, 2), "sd_as" #AS, sd_lds_bytes<AS, 2>()},
+// 128-row tiles (each wave 32 rows x 128 columns): half the A copies per weight byte
+// of the 128 x 128 tile kernels for mid-size batches
+#define QOQ_SD128(AS) {6, AS, 1, 0, 0, 0, QOQ_K4(gemm_sd_kernel<AS, 1), "sd_m128_as" #AS, sd_lds_bytes<AS, 1>()},
 
 const Config kConfigs[] = {
     // the configurations the measured dispatch table uses (qoq_plan_table.inc): the
-    // profiling sweep times 56, and keeps the fewest that are near-best (within 3 %)
+    // profiling sweep times 58, and keeps the fewest that are near-best (within 3 %)
     // at every profiled point
-    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY_NT(1, 1, 8, 2)
+    QOQ_SKINNY_NT(1, 1, 8, 2) QOQ_SKINNY_R(1, 2, 16, 1, 4)
     QOQ_SKINNY_NT(1, 2, 16, 2) QOQ_SKINNY_NT(1, 4, 8, 2) QOQ_SKINNY_NT(3, 2, 8, 2)
-    QOQ_SKINNY_RNT(1, 2, 16, 1, 4) QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_RNT(2, 2, 8, 1, 3)
+    QOQ_SKINNY_R(2, 2, 8, 1, 3) QOQ_SKINNY_RNT(2, 2, 8, 1, 3)
     QOQ_SKINNY32(1, 2, 8, 1, 2) QOQ_SKINNY32_NT(1, 2, 8, 1, 2) QOQ_SKINNY32(2, 2, 8, 1, 2) QOQ_SKINNY32_NT(2, 2, 8, 1, 2)
-    QOQ_WIDE2(2, 1) QOQ_WIDE2(4, 1)
+    QOQ_WIDE2(2, 1) QOQ_WIDE2(2, 2)
     QOQ_DMA2(2, 1) QOQ_DMA2(4, 1)
-    QOQ_SD(3)
+    QOQ_SD(3) QOQ_SD(2) QOQ_SD128(3)
 #ifdef QOQ_ALL_CONFIGS
     // the rest of the profiling sweep's candidates (build.py --all-configs): none is
     // needed for the table, so the product build leaves them out
+    QOQ_SKINNY(1, 1, 8, 2) QOQ_SKINNY_RNT(1, 2, 16, 1, 4) QOQ_WIDE2(4, 1) QOQ_SD128(2)
     QOQ_SKINNY(1, 1, 8, 4) QOQ_SKINNY(1, 2, 8, 4) QOQ_SKINNY(1, 1, 4, 4) QOQ_SKINNY(1, 2, 4, 4)
     QOQ_SKINNY(1, 1, 16, 2) QOQ_SKINNY(2, 1, 8, 4) QOQ_SKINNY(2, 2, 8, 2) QOQ_SKINNY(2, 1, 8, 2)
     QOQ_SKINNY(3, 1, 8, 2) QOQ_SKINNY(4, 1, 8, 2) QOQ_SKINNY(4, 2, 8, 2) QOQ_SKINNY(4, 2, 8, 1)
     QOQ_SKINNY(4, 4, 8, 1) QOQ_SKINNY(1, 2, 16, 2) QOQ_SKINNY(3, 2, 8, 2) QOQ_SKINNY(1, 4, 8, 2)
-    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(1, 2, 16, 1, 4) QOQ_SKINNY_R(1, 1, 8, 2, 3)
+    QOQ_SKINNY_R(1, 2, 8, 2, 3) QOQ_SKINNY_R(2, 2, 8, 2, 3) QOQ_SKINNY_R(1, 1, 8, 2, 3)
     QOQ_SKINNY_R(2, 2, 8, 1, 4) QOQ_SKINNY_R(4, 2, 8, 1, 3) QOQ_SKINNY_R(4, 2, 8, 1, 4)
     QOQ_SKINNY_R(4, 4, 8, 1, 3) QOQ_SKINNY_R(1, 1, 16, 2, 3)
     QOQ_SKINNY32(2, 1, 8, 1, 2) QOQ_SKINNY32(2, 1, 8, 1, 3) QOQ_SKINNY32(1, 1, 8, 2, 2)
-    QOQ_WIDE2(2, 2) QOQ_DMA2(2, 2) QOQ_DMA2(4, 2) QOQ_SD(2)
+    QOQ_DMA2(2, 2) QOQ_DMA2(4, 2)
     QOQ_SKINNY_NT(2, 2, 8, 2) QOQ_SKINNY_NT(4, 4, 8, 1) QOQ_SKINNY_NT(2, 1, 8, 2) QOQ_SKINNY_NT(4, 2, 8, 1)
     QOQ_SKINNY_RNT(1, 1, 16, 2, 3) QOQ_SKINNY_RNT(4, 2, 8, 1, 3) QOQ_SKINNY32_NT(2, 1, 8, 1, 2)
 #endif
@@ -1579,17 +1588,17 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     if (tiled_a) tiled = false;
     if (!tiled) {
       // shapes outside the measured table (rules distilled from the same sweeps):
-      //  streaming code loads once the weights pass 8 MiB
-      //  M <= 16: one 16-row block; wide layers with short K stream one strip per
-      //           workgroup with 8 K-split waves, the rest two strips and 16 waves
-      //           (small weights: one strip, 8 waves)
+      //  M <= 16: one 16-row block, streaming code loads; wide layers with short K
+      //           (and weights under 8 MiB) one strip per workgroup with 8 K-split
+      //           waves, the rest two strips and 16 waves
+      //  streaming code loads past 16 tokens once the weights pass 8 MiB
       //  17..64 tokens: 32-row blocks on the 32x32x32 MFMA (about 60 % more INT8 ops
       //           per cycle than 16x16x64), two strip pairs per workgroup, one 32-row
       //           block up to 32 tokens and two beyond
       const bool nt = static_cast<int64_t>(N) * K / 2 >= (8 << 20);
       if (M <= 16) {
-        if (!nt) cfg = find_config(0, 1, 1, 8, 2);
-        else cfg = (NS >= 640 && G <= 64) ? find_config(0, 1, 1, 8, 2, 2, true) : find_config(0, 1, 2, 16, 2, 2, true);
+        cfg = (!nt || (NS >= 640 && G <= 64)) ? find_config(0, 1, 1, 8, 2, 2, true)
+                                              : find_config(0, 1, 2, 16, 2, 2, true);
       } else {
         cfg = find_config(7, M <= 32 ? 1 : 2, 2, 8, 1, 2, nt);
       }
@@ -1605,7 +1614,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
       } else if (t256 >= 192 && G >= 96) {
         cfg = find_config(6, 3, 0, 0, 0);       // 256 x 256, long K: split in two
       } else if (t128 >= 320) {
-        cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, A staged by the waves
+        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128, A by the copy engine
         split_k = false;
       } else if (M <= 64) {
         cfg = find_config(4, 2, 1, 0, 0);       // 64 x 128
@@ -1613,11 +1622,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
       } else if (t256 >= 96) {
         cfg = find_config(6, 3, 0, 0, 0);       // 256 x 256, split K
       } else {
-        cfg = find_config(4, 4, 1, 0, 0);       // 128 x 128, split K
+        cfg = find_config(5, 4, 1, 0, 0);       // 128 x 128, split K
       }
     }
   }
-  if (!cfg) cfg = find_config(0, 1, 1, 8, 2);   // present in kConfigs; never reached by the rules above
+  if (!cfg) cfg = find_config(0, 1, 1, 8, 2, 2, true);   // present in kConfigs; never reached by the rules above
   Plan p;
   p.cfg = cfg;
   p.splits = 1;
@@ -1631,8 +1640,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
     p.grid = dim3(static_cast<unsigned>((NS + 2 * np - 1) / (2 * np)),
                   static_cast<unsigned>((M + 32 * mt2 - 1) / (32 * mt2)));
     p.block = dim3(64 * waves);
-  } else if (cfg->kind == 6) {   // 256 x 256 tiles, 8 waves
-    const int64_t tiles = ((NS + 15) / 16) * ((M + 255) / 256);
+  } else if (cfg->kind == 6) {   // 256 (or 128) x 256 tiles, 8 waves
+    const int64_t bm = cfg->b == 1 ? 128 : 256;
+    const int64_t tiles = ((NS + 15) / 16) * ((M + bm - 1) / bm);
     p.splits = plan_splits(tiles, G, ov.splits, table_splits, split_k);
     if (p.splits > 1) p.ws_bytes = sizeof(int) * static_cast<size_t>(p.splits) * M * N;
     p.grid = dim3(static_cast<unsigned>(tiles * p.splits));

@@ -155,6 +155,15 @@ def test_plan_rules_outside_the_table():
         for M in (1, 16, 40, 64, 100, 300, 1000, 5000):
             assert qoq.gemm_plan(M, N, K) in names
             assert qoq.gemm_tiled_plan(min(M, 64), N, K) in names
+    # the rules' own picks (each a configuration of the build, not the fallback):
+    # few-token kernels up to 16 tokens, 32-row blocks to 64, the shared-dequantization
+    # kernel for the largest tile counts, the copy-engine tile kernel for few tiles
+    assert qoq.gemm_plan(1, 12288, 5120) == "skinny_mt1_nb1_w8_u2_nt"     # wide, short K
+    assert qoq.gemm_plan(1, 2048, 33280) == "skinny_mt1_nb2_w16_u2_nt"
+    assert qoq.gemm_plan(8, 1024, 2048) == "skinny_mt1_nb1_w8_u2_nt"
+    assert qoq.gemm_plan(40, 12288, 5120) == "skinny32_mt2_np2_w8_u1_r2_nt"
+    assert qoq.gemm_plan(5000, 12288, 5120) == "sd_as3"
+    assert qoq.gemm_plan(300, 1024, 2048) == "dma2_tm4_tn1"
 
 
 def test_split_plan_and_workspace():

@@ -1056,14 +1056,16 @@ __global__ __launch_bounds__(256, 2) void gemm_dma2_kernel(const int8_t *__restr
 // the register budget of two waves per SIMD caps a wave's tile, so here the rows
 // are spread over waves and the weights are dequantized once per workgroup and
 // shared through LDS:
-//   workgroup = 8 waves (two per SIMD), tile 256 rows x 256 columns; wave w
-//   computes rows 64*(w & 3) .. +63 and columns 128*(w >> 2) .. +127 (TM = 2,
-//   TN = 4) and dequantizes column block w (32 columns, two strips) for the whole
-//   workgroup, writing its B fragments to LDS in MFMA operand order
-//   (bbuf[block][k block][lane], 16 bytes each: every read and write is 64 lanes x
-//   16 contiguous bytes).
-//   A (256 x 128 per group) comes by copy engine into an AS-stage ring with the
-//   row-pair XOR swizzle; each wave reads only its own 64 rows.
+//   workgroup = 8 waves (two per SIMD), tile 128*TM rows x 256 columns; wave w
+//   computes rows 32*TM*(w & 3) .. +32*TM-1 and columns 128*(w >> 2) .. +127 (TM
+//   blocks of 32 rows, TN = 4) and dequantizes column block w (32 columns, two
+//   strips) for the whole workgroup, writing its B fragments to LDS in MFMA operand
+//   order (bbuf[block][k block][lane], 16 bytes each: every read and write is 64
+//   lanes x 16 contiguous bytes).  TM = 2 (256-row tiles) for large batches; TM = 1
+//   (128-row tiles) for mid-size ones, where it copies A half as often per weight
+//   byte as the 128-column tile kernels.
+//   A (128*TM x 128 per group) comes by copy engine into an AS-stage ring with the
+//   row-pair XOR swizzle; each wave reads only its own 32*TM rows.
 //   Per group j: load the codes of j+3 (three register sets, group g in set g % 3);
 //   dequantize j+1 (codes loaded two groups earlier) into B buffer (j+1) & 1; copy
 //   A(j+AS-1); MFMAs of j from A stage j % AS and B buffer j & 1; wait for A(j+1);
@@ -1467,7 +1469,7 @@ const Config *find_config(int kind, int a, int b, int c, int d, int e = 0, bool 
 struct Plan {
   const Config *cfg;
   dim3 grid, block;
-  int splits;           // split-K factor (kinds 4 and 5 only)
+  int splits;           // split-K factor (tile kernels: kinds 4, 5 and 6)
   size_t ws_bytes;      // workspace the launch needs (0 without split-K)
 };
 
@@ -1576,7 +1578,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool tiled_a = false) {
   if (ov.config >= 0 && (!tiled_a || kConfigs[ov.config].kt[0][0])) cfg = &kConfigs[ov.config];
   const int64_t t256 = ((NS + 15) / 16) * ((M + 127) / 128);   // 128 x 256 tiles
   const int64_t t128 = ((NS + 7) / 8) * ((M + 127) / 128);     // 128 x 128 tiles
-  bool split_k = true;   // may the plan split K (kinds 4 and 5)
+  bool split_k = true;   // may the plan split K (tile kernels)
   int table_splits = 0;  // split-K factor of the table's row (0: no row)
   if (!cfg && ov.regime == 0) cfg = table_plan(M, N, K, tiled_a, table_splits);
   if (!cfg) {
